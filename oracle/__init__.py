@@ -1,0 +1,192 @@
+"""fp64 CPU oracle for block-sparse video attention (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+CPU-baseline leg of the benchmark, never by the product path. The arithmetic
+lives in bsa_oracle.c (plain fp64 loops); this file only marshals arrays.
+It shares no code with the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bsa_oracle.c")
+_LIB = os.path.join(_HERE, "libbsa_oracle.so")
+
+DT_BF16, DT_F32, DT_F64 = 0, 1, 2
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (fp64, no contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = C.CDLL(_LIB)
+        i64, p, d = C.c_int64, C.c_void_p, C.c_double
+        L.oracle_radial_window.argtypes = [i64, i64, i64, i64, C.POINTER(i64)]
+        L.oracle_radial_window.restype = C.c_int
+        L.oracle_radial_count_pairs.argtypes = [i64] * 6
+        L.oracle_radial_count_pairs.restype = i64
+        L.oracle_build_mask_radial.argtypes = [i64] * 7 + [p]
+        L.oracle_build_mask_radial.restype = None
+        L.oracle_build_mask_pooled.argtypes = ([i64] * 6 + [C.c_int] + [p, i64, i64, i64] * 2
+                                               + [d, C.c_int, d, p, p, p])
+        L.oracle_build_mask_pooled.restype = C.c_int
+        L.oracle_compact.argtypes = [i64] * 4 + [p, i64, p, p, p]
+        L.oracle_compact.restype = i64
+        L.oracle_attention.argtypes = ([i64] * 6 + [C.c_int] + [p, i64, i64, i64] * 3
+                                       + [d, p, i64, i64, p, p, p, p])
+        L.oracle_attention.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return DT_BF16
+    if a.dtype == np.float32:
+        return DT_F32
+    if a.dtype == np.float64:
+        return DT_F64
+    raise TypeError(f"unsupported oracle input dtype {a.dtype}")
+
+
+def _strides(a: np.ndarray):
+    """Element strides of a [B][N][H][d] array with d contiguous."""
+    if a.ndim != 4 or a.strides[3] != a.itemsize:
+        raise ValueError("expected [B][N][H][d] with contiguous head_dim")
+    return tuple(s // a.itemsize for s in a.strides[:3])
+
+
+# ------------------------------------------------------------------- radial
+def radial_window(d: int, h0: int, beta: int, bk: int):
+    h = C.c_int64(0)
+    kept = lib().oracle_radial_window(d, h0, beta, bk, C.byref(h))
+    return bool(kept), int(h.value)
+
+
+def radial_count_pairs(T, Hs, Ws, h0, beta, bk) -> int:
+    return int(lib().oracle_radial_count_pairs(T, Hs, Ws, h0, beta, bk))
+
+
+def build_mask_radial(T, Hs, Ws, bq, bk, h0, beta) -> np.ndarray:
+    if h0 < bk // 2:
+        raise ValueError("radial window must be at least half a key block")
+    N = T * Hs * Ws
+    nQ, nK = -(-N // bq), -(-N // bk)
+    m = np.zeros((nQ, nK), dtype=np.uint8)
+    lib().oracle_build_mask_radial(T, Hs, Ws, bq, bk, h0, beta, _ptr(m))
+    return m
+
+
+# ------------------------------------------------------------------- pooled
+def build_mask_pooled(q: np.ndarray, k: np.ndarray, bq: int, bk: int, scale: float,
+                      mode: int, param: float, want_scores=False):
+    """Returns (mask [B][H][nQ][nK] uint8, scores or None, margin [B][H][nQ])."""
+    B, N, H, D = q.shape
+    nQ, nK = -(-N // bq), -(-N // bk)
+    dt = _dtype_code(q)
+    assert _dtype_code(k) == dt and k.shape == q.shape
+    mask = np.zeros((B, H, nQ, nK), dtype=np.uint8)
+    scores = np.zeros((B, H, nQ, nK), dtype=np.float64) if want_scores else None
+    margin = np.zeros((B, H, nQ), dtype=np.float64)
+    rc = lib().oracle_build_mask_pooled(
+        B, H, N, D, bq, bk, dt, _ptr(q), *_strides(q), _ptr(k), *_strides(k),
+        float(scale), int(mode), float(param), _ptr(mask),
+        _ptr(scores) if scores is not None else None, _ptr(margin))
+    if rc != 0:
+        raise MemoryError("oracle_build_mask_pooled failed to allocate")
+    return mask, scores, margin
+
+
+# --------------------------------------------------------------- compaction
+def compact(mask: np.ndarray, B: int, H: int, nQ: int, nK: int,
+            mask_head_stride: int, skip: np.ndarray | None = None):
+    """CSR lists (row_ptr int32 [B*H*nQ+1], kv_idx int32 [nnz])."""
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    if skip is not None:
+        skip = np.ascontiguousarray(skip, dtype=np.uint8)
+    L = lib()
+    sp = _ptr(skip) if skip is not None else None
+    nnz = L.oracle_compact(B, H, nQ, nK, _ptr(mask), mask_head_stride, sp, None, None)
+    row_ptr = np.zeros(B * H * nQ + 1, dtype=np.int32)
+    kv_idx = np.zeros(max(nnz, 1), dtype=np.int32)
+    L.oracle_compact(B, H, nQ, nK, _ptr(mask), mask_head_stride, sp,
+                     _ptr(row_ptr), _ptr(kv_idx))
+    return row_ptr, kv_idx[:nnz]
+
+
+# ---------------------------------------------------------------- attention
+def attention(q, k, v, bq: int, bk: int, scale: float, mask: np.ndarray,
+              mask_head_stride: int, rows=None, want_gap=False):
+    """Masked attention for the given rows ((b*H + h)*nQ + a); all rows if None.
+
+    Returns (o [n][bq][D] fp64, lse [n][bq] fp64, gap [n][nK] fp64 or None).
+    """
+    B, N, H, D = q.shape
+    nQ, nK = -(-N // bq), -(-N // bk)
+    dt = _dtype_code(q)
+    assert _dtype_code(k) == dt and _dtype_code(v) == dt
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    if rows is None:
+        rows = np.arange(B * H * nQ, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    n = rows.size
+    o = np.empty((n, bq, D), dtype=np.float64)
+    lse = np.empty((n, bq), dtype=np.float64)
+    gap = np.empty((n, nK), dtype=np.float64) if want_gap else None
+    rc = lib().oracle_attention(
+        B, H, N, D, bq, bk, dt, _ptr(q), *_strides(q), _ptr(k), *_strides(k),
+        _ptr(v), *_strides(v), float(scale), _ptr(mask), mask_head_stride,
+        n, _ptr(rows), _ptr(o), _ptr(lse), _ptr(gap) if gap is not None else None)
+    if rc != 0:
+        raise MemoryError("oracle_attention failed to allocate")
+    return o, lse, gap
+
+
+# ---------------------------------------------------------------- skip carry
+def skip_step(q, k, v, bq: int, bk: int, scale: float, skip_prev: np.ndarray,
+              tau: float, rows=None):
+    """One denoising step of the carried skip mask, decided in fp64.
+
+    LiteAttention summary page, sections 二, 三, 五 and 六: the effective mask of
+    step s is (all tiles) minus the tiles skipped so far; attention runs over it
+    while each visited tile's gap (local max minus running max, in ascending
+    key-block order) is measured; tiles with gap <= -tau (natural-log units)
+    join the skip set, which only grows. Tiles marked at step s are still
+    computed at step s.
+
+    Returns (o, lse, gap, skip_new) with o/lse/gap as in attention() for the
+    given rows (all rows if None) and skip_new [B][H][nQ][nK].
+    """
+    B, N, H, D = q.shape
+    nQ, nK = -(-N // bq), -(-N // bk)
+    eff = (1 - np.asarray(skip_prev, dtype=np.uint8)).reshape(B, H, nQ, nK)
+    o, lse, gap = attention(q, k, v, bq, bk, scale, eff, nQ * nK, rows=rows, want_gap=True)
+    if rows is None:
+        rows = np.arange(B * H * nQ)
+    new = np.array(skip_prev, dtype=np.uint8).reshape(B * H * nQ, nK).copy()
+    marked = np.nan_to_num(gap, nan=np.inf) <= -tau
+    new[np.asarray(rows)] |= marked.astype(np.uint8)
+    return o, lse, gap, new.reshape(B, H, nQ, nK)

@@ -1,0 +1,388 @@
+/*
+ * bsa_oracle.c -- plain, slow fp64 CPU oracle for block-sparse video attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or
+ * load this file: only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it. It shares no code, header, table or helper
+ * with the HIP library; the two meet only in the seeded inputs.
+ *
+ * Arithmetic: IEEE fp64, plain loops in the order written, compiled with
+ * -ffp-contract=off and no fast-math. OpenMP splits independent rows only.
+ *
+ * Pages cited (titles of the web pages that describe the method):
+ *   [Lite]   LiteAttention summary page (arXiv:2511.11062), numbered sections.
+ *   [VMoBA]  VMoBA summary page (arXiv:2506.23858), numbered sections.
+ *   [Radial] "MIT实验室推出Radial Attention：让视频AI生成快如闪电的神奇技术"
+ *            (arXiv:2506.19852), paragraphs on energy decay, the static map
+ *            and the O(n log n) complexity.
+ *   [PARO]   PAROAttention summary page (arXiv:2506.16054), numbered sections.
+ *   [PSA]    "浙江大学突破视频AI瓶颈:金字塔方法提升视频AI效率10倍"
+ *            (arXiv:2512.04025), paragraphs on block-sparse keep/drop and
+ *            average pooling.
+ *
+ * Geometry convention (the pages say only that the 3D video is flattened to
+ * 1D; [PARO] section 二, [VMoBA] section 三): token i <-> (t, y, x) with
+ * i = (t*Hs + y)*Ws + x; frame t(i) = i / F, in-frame position s(i) = i % F,
+ * F = Hs*Ws. Row block a covers [a*Bq, min(N, (a+1)*Bq)), column block c
+ * covers [c*Bk, min(N, (c+1)*Bk)); ragged last blocks keep their true sizes.
+ *
+ * Element types of input tensors: 0 = bf16 (uint16 bit patterns),
+ * 1 = fp32, 2 = fp64. Widening to fp64 is exact.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_BF16 0
+#define ORACLE_F32 1
+#define ORACLE_F64 2
+
+static double widen(const void* base, int dtype, int64_t off) {
+  if (dtype == ORACLE_BF16) {
+    uint32_t u = ((uint32_t)((const uint16_t*)base)[off]) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+  }
+  if (dtype == ORACLE_F32) return (double)((const float*)base)[off];
+  return ((const double*)base)[off];
+}
+
+/* ------------------------------------------------------------------------ */
+/* Radial window ([Radial]: attention weakens with spatial and temporal     */
+/* distance; each frame mostly attends to its nearest frames and the weight */
+/* falls off with frame distance by a fixed rule; the map is fixed ahead of */
+/* time; total cost grows as n log n).                                      */
+/*                                                                          */
+/* Reading taken: frame distance d falls in band r(d) = number of base-beta */
+/* digits of d (r(0) = 0). The spatial half-width halves per band:          */
+/* h_r = floor(h0 / beta^r). Once h_r would drop below half a key block     */
+/* (h_min = Bk/2), the window stays at h_min and instead only every         */
+/* beta^(r - r*)-th distance of band r is kept, r* = last band with         */
+/* h_r >= h_min. Token pair (i, j) is kept iff its distance is kept and     */
+/* |s(i) - s(j)| < h_eff(d).                                                */
+/* Returns 1 if distance d is kept and writes its half-width.               */
+/* ------------------------------------------------------------------------ */
+int oracle_radial_window(int64_t d, int64_t h0, int64_t beta, int64_t bk,
+                         int64_t* h_eff) {
+  int64_t r = 0, p = 1; /* p = beta^r(d) */
+  while (p <= d) { p *= beta; ++r; }
+  int64_t h_min = bk / 2;
+  /* r* = max{ r : floor(h0 / beta^r) >= h_min } */
+  int64_t rstar = 0, q = 1;
+  while (h0 / (q * beta) >= h_min) { q *= beta; ++rstar; }
+  if (r <= rstar) {
+    int64_t br = 1;
+    for (int64_t k = 0; k < r; ++k) br *= beta;
+    *h_eff = h0 / br;
+    return 1;
+  }
+  int64_t step = 1;
+  for (int64_t k = 0; k < r - rstar; ++k) step *= beta;
+  *h_eff = h_min;
+  return (d % step) == 0;
+}
+
+/* Brute-force count of kept token pairs (tiny grids only). */
+int64_t oracle_radial_count_pairs(int64_t T, int64_t Hs, int64_t Ws, int64_t h0,
+                                  int64_t beta, int64_t bk) {
+  int64_t F = Hs * Ws, N = T * F, cnt = 0;
+  for (int64_t i = 0; i < N; ++i)
+    for (int64_t j = 0; j < N; ++j) {
+      int64_t ti = i / F, tj = j / F, h;
+      int64_t d = ti > tj ? ti - tj : tj - ti;
+      if (!oracle_radial_window(d, h0, beta, bk, &h)) continue;
+      int64_t ds = (i % F) - (j % F);
+      if (ds < 0) ds = -ds;
+      if (ds < h) ++cnt;
+    }
+  return cnt;
+}
+
+/* Tile rule (binary keep/drop of whole blocks, [PSA]): tile (a, c) is kept
+ * iff some query token of row block a and some key token of column block c
+ * form a kept pair. For each query token the check is: in every frame that
+ * column block c touches, is there a key of the block whose in-frame position
+ * lies within the window of that frame distance. mask is [nQ][nK], head- and
+ * batch-independent. */
+void oracle_build_mask_radial(int64_t T, int64_t Hs, int64_t Ws, int64_t bq,
+                              int64_t bk, int64_t h0, int64_t beta,
+                              uint8_t* mask) {
+  int64_t F = Hs * Ws, N = T * F;
+  int64_t nQ = (N + bq - 1) / bq, nK = (N + bk - 1) / bk;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t a = 0; a < nQ; ++a) {
+    int64_t i0 = a * bq, i1 = (a + 1) * bq < N ? (a + 1) * bq : N;
+    for (int64_t c = 0; c < nK; ++c) {
+      int64_t j0 = c * bk, j1 = (c + 1) * bk < N ? (c + 1) * bk : N;
+      int keep = 0;
+      for (int64_t i = i0; i < i1 && !keep; ++i) {
+        int64_t ti = i / F, si = i % F;
+        for (int64_t tk = j0 / F; tk <= (j1 - 1) / F && !keep; ++tk) {
+          int64_t d = ti > tk ? ti - tk : tk - ti, h;
+          if (!oracle_radial_window(d, h0, beta, bk, &h)) continue;
+          /* keys of block c inside frame tk: in-frame positions [lo, hi] */
+          int64_t lo = (j0 > tk * F ? j0 : tk * F) - tk * F;
+          int64_t hi = ((j1 < (tk + 1) * F ? j1 : (tk + 1) * F) - 1) - tk * F;
+          int64_t dist = 0;
+          if (si < lo) dist = lo - si;
+          else if (si > hi) dist = si - hi;
+          if (dist < h) keep = 1;
+        }
+      }
+      mask[a * nK + c] = (uint8_t)keep;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Pooled block selection ([PSA]: keys are mean-pooled block by block;       */
+/* [VMoBA] sections 三 and 六: block relevance from pooled scores, number of */
+/* blocks per query set by a threshold that follows how concentrated the    */
+/* attention is; [PSA] ablation: threshold allocation beats quantiles).     */
+/*                                                                          */
+/* Steps, per (b, h):                                                       */
+/* 1. qbar_a = (sum over i in row block a of q_i, ascending i) / |R_a|;     */
+/*    kbar_c likewise over column block c.                                  */
+/* 2. S_ac = scale * (sum_k qbar_ak * kbar_ck), k ascending, each product   */
+/*    and sum rounded separately, then one multiply by scale.               */
+/* 3. Row a: order c by (S desc, c asc).                                    */
+/* 4. mode 0 (top-k): keep the first min(k, nK) of that order.              */
+/*    mode 1 (cumulative mass): e_c = exp(S_ac - max_c S_ac); Z = sum of e  */
+/*    in ascending c; p_c = e_c / Z; walk the order accumulating p and keep  */
+/*    the shortest prefix whose running sum is >= tau_p (all if never).     */
+/* margin_out[row] (optional) = distance of the running sum from tau_p at   */
+/* the last step inside the prefix and the step before it (mode 1).         */
+/* ------------------------------------------------------------------------ */
+typedef struct { double s; int64_t c; } scored;
+
+static int cmp_scored(const void* x, const void* y) {
+  const scored* a = (const scored*)x;
+  const scored* b = (const scored*)y;
+  if (a->s > b->s) return -1;
+  if (a->s < b->s) return 1;
+  return (a->c > b->c) - (a->c < b->c);
+}
+
+int oracle_build_mask_pooled(int64_t B, int64_t H, int64_t N, int64_t D,
+                             int64_t bq, int64_t bk, int dtype,
+                             const void* q, int64_t qsb, int64_t qsn, int64_t qsh,
+                             const void* k, int64_t ksb, int64_t ksn, int64_t ksh,
+                             double scale, int mode, double param,
+                             uint8_t* mask, double* scores_out,
+                             double* margin_out) {
+  int64_t nQ = (N + bq - 1) / bq, nK = (N + bk - 1) / bk;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < B * H; ++bh) {
+    int64_t b = bh / H, h = bh % H;
+    double* qbar = (double*)malloc(sizeof(double) * nQ * D);
+    double* kbar = (double*)malloc(sizeof(double) * nK * D);
+    double* S = (double*)malloc(sizeof(double) * nK);
+    scored* ord = (scored*)malloc(sizeof(scored) * nK);
+    if (!qbar || !kbar || !S || !ord) {
+#pragma omp atomic write
+      bad = 1;
+      free(qbar); free(kbar); free(S); free(ord);
+      continue;
+    }
+    for (int64_t a = 0; a < nQ; ++a) {
+      int64_t i0 = a * bq, i1 = (a + 1) * bq < N ? (a + 1) * bq : N;
+      for (int64_t x = 0; x < D; ++x) {
+        double acc = 0.0;
+        for (int64_t i = i0; i < i1; ++i)
+          acc = acc + widen(q, dtype, b * qsb + i * qsn + h * qsh + x);
+        qbar[a * D + x] = acc / (double)(i1 - i0);
+      }
+    }
+    for (int64_t c = 0; c < nK; ++c) {
+      int64_t j0 = c * bk, j1 = (c + 1) * bk < N ? (c + 1) * bk : N;
+      for (int64_t x = 0; x < D; ++x) {
+        double acc = 0.0;
+        for (int64_t j = j0; j < j1; ++j)
+          acc = acc + widen(k, dtype, b * ksb + j * ksn + h * ksh + x);
+        kbar[c * D + x] = acc / (double)(j1 - j0);
+      }
+    }
+    for (int64_t a = 0; a < nQ; ++a) {
+      int64_t row = bh * nQ + a;
+      for (int64_t c = 0; c < nK; ++c) {
+        double acc = 0.0;
+        for (int64_t x = 0; x < D; ++x) {
+          double pr = qbar[a * D + x] * kbar[c * D + x];
+          acc = acc + pr;
+        }
+        S[c] = scale * acc;
+        if (scores_out) scores_out[row * nK + c] = S[c];
+        ord[c].s = S[c];
+        ord[c].c = c;
+      }
+      qsort(ord, (size_t)nK, sizeof(scored), cmp_scored);
+      uint8_t* m = mask + row * nK;
+      memset(m, 0, (size_t)nK);
+      int64_t keep = nK;
+      double margin = INFINITY;
+      if (mode == 0) {
+        keep = (int64_t)param < nK ? (int64_t)param : nK;
+      } else {
+        double smax = ord[0].s, Z = 0.0;
+        for (int64_t c = 0; c < nK; ++c) Z = Z + exp(S[c] - smax);
+        double run = 0.0, prev = 0.0;
+        keep = nK;
+        for (int64_t t = 0; t < nK; ++t) {
+          prev = run;
+          run = run + exp(ord[t].s - smax) / Z;
+          if (run >= param) { keep = t + 1; break; }
+        }
+        margin = fabs(run - param);
+        if (keep > 1 && fabs(param - prev) < margin) margin = fabs(param - prev);
+      }
+      for (int64_t t = 0; t < keep; ++t) m[ord[t].c] = 1;
+      if (margin_out) margin_out[row] = margin;
+    }
+    free(qbar); free(kbar); free(S); free(ord);
+  }
+  return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Compaction ([Lite] sections 三 and 六: a skipped tile must cost no memory */
+/* transfer, so the loader walks only the kept tiles of each query block).   */
+/* Row r = (b*H + h)*nQ + a; element (r, c) of the mask lives at            */
+/* mask[(b*H + h)*mask_head_stride + a*nK + c] (stride 0: one mask for all  */
+/* heads). kv_idx lists, per row, the ascending c with mask = 1 and         */
+/* skip = 0; row_ptr is the exclusive prefix sum of the row lengths.        */
+/* Returns nnz.                                                             */
+/* ------------------------------------------------------------------------ */
+int64_t oracle_compact(int64_t B, int64_t H, int64_t nQ, int64_t nK,
+                       const uint8_t* mask, int64_t mask_head_stride,
+                       const uint8_t* skip, int32_t* row_ptr, int32_t* kv_idx) {
+  int64_t nnz = 0;
+  for (int64_t bh = 0; bh < B * H; ++bh)
+    for (int64_t a = 0; a < nQ; ++a) {
+      int64_t r = bh * nQ + a;
+      if (row_ptr) row_ptr[r] = (int32_t)nnz;
+      for (int64_t c = 0; c < nK; ++c) {
+        int on = mask[bh * mask_head_stride + a * nK + c] != 0;
+        if (skip && skip[r * nK + c]) on = 0;
+        if (on) {
+          if (kv_idx) kv_idx[nnz] = (int32_t)c;
+          ++nnz;
+        }
+      }
+    }
+  if (row_ptr) row_ptr[B * H * nQ] = (int32_t)nnz;
+  return nnz;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Masked softmax attention (the plain definition the kernels reach by an    */
+/* exact re-association; bidirectional, no causal mask). For query i of row  */
+/* block a of head (b, h), J_i is the union of the column blocks c with      */
+/* mask(b, h, a, c) = 1, and                                                 */
+/*   s_ij = scale * sum_x q_ix k_jx,  m_i = max_{j in J_i} s_ij,              */
+/*   l_i = sum_{j in J_i} exp(s_ij - m_i),                                   */
+/*   o_i = sum_{j in J_i} exp(s_ij - m_i) v_j / l_i,  lse_i = m_i + log l_i;  */
+/* empty J_i gives o_i = 0, lse_i = -inf.                                    */
+/*                                                                           */
+/* Tile gaps ([Lite] section 五: a tile whose local maximum lies far below   */
+/* the accumulated maximum contributes exponentially little; section 六:     */
+/* per-warp decisions combined across warps): visiting the kept column      */
+/* blocks of row block a in ascending order, with m_run(r) = -inf at start,  */
+/*   m_loc(r) = max_{j in C_c} s_rj,                                          */
+/*   gap(a, c) = max over valid rows r of (m_loc(r) - m_run(r)),              */
+/*   m_run(r) = max(m_run(r), m_loc(r)).                                      */
+/* Natural-log units of the scaled scores; +inf for the first visited tile.  */
+/*                                                                           */
+/* Only the requested rows are computed: rows[t] = (b*H + h)*nQ + a.         */
+/* Outputs: o_out [n_rows][bq][D], lse_out [n_rows][bq] (padding rows of a   */
+/* ragged last block are NaN), gap_out [n_rows][nK] (NaN where not kept),    */
+/* each optional.                                                            */
+/* ------------------------------------------------------------------------ */
+int oracle_attention(int64_t B, int64_t H, int64_t N, int64_t D, int64_t bq,
+                     int64_t bk, int dtype,
+                     const void* q, int64_t qsb, int64_t qsn, int64_t qsh,
+                     const void* k, int64_t ksb, int64_t ksn, int64_t ksh,
+                     const void* v, int64_t vsb, int64_t vsn, int64_t vsh,
+                     double scale, const uint8_t* mask, int64_t mask_head_stride,
+                     int64_t n_rows, const int64_t* rows,
+                     double* o_out, double* lse_out, double* gap_out) {
+  int64_t nQ = (N + bq - 1) / bq, nK = (N + bk - 1) / bk;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < n_rows; ++t) {
+    int64_t row = rows[t];
+    int64_t bh = row / nQ, a = row % nQ, b = bh / H, h = bh % H;
+    int64_t i0 = a * bq, i1 = (a + 1) * bq < N ? (a + 1) * bq : N;
+    const uint8_t* m = mask + bh * mask_head_stride + a * nK;
+    int64_t nJ = 0;
+    for (int64_t c = 0; c < nK; ++c)
+      if (m[c]) nJ += ((c + 1) * bk < N ? (c + 1) * bk : N) - c * bk;
+    double* s = (double*)malloc(sizeof(double) * (nJ > 0 ? nJ : 1));
+    double* qi = (double*)malloc(sizeof(double) * D);
+    double* acc = (double*)malloc(sizeof(double) * D);
+    double* mrun = (double*)malloc(sizeof(double) * bq);
+    if (!s || !qi || !acc || !mrun) {
+#pragma omp atomic write
+      bad = 1;
+      free(s); free(qi); free(acc); free(mrun);
+      continue;
+    }
+    for (int64_t r = 0; r < bq; ++r) mrun[r] = -INFINITY;
+    if (gap_out)
+      for (int64_t c = 0; c < nK; ++c) gap_out[t * nK + c] = NAN;
+    for (int64_t r = 0; r < bq; ++r) {
+      if (o_out) for (int64_t x = 0; x < D; ++x) o_out[(t * bq + r) * D + x] = NAN;
+      if (lse_out) lse_out[t * bq + r] = NAN;
+    }
+    for (int64_t i = i0; i < i1; ++i) {
+      int64_t r = i - i0;
+      for (int64_t x = 0; x < D; ++x) qi[x] = widen(q, dtype, b * qsb + i * qsn + h * qsh + x);
+      /* scores over J_i, in ascending j */
+      int64_t n = 0;
+      for (int64_t c = 0; c < nK; ++c) {
+        if (!m[c]) continue;
+        int64_t j0 = c * bk, j1 = (c + 1) * bk < N ? (c + 1) * bk : N;
+        double mloc = -INFINITY;
+        for (int64_t j = j0; j < j1; ++j) {
+          double dot = 0.0;
+          for (int64_t x = 0; x < D; ++x)
+            dot = dot + qi[x] * widen(k, dtype, b * ksb + j * ksn + h * ksh + x);
+          s[n++] = scale * dot;
+          if (s[n - 1] > mloc) mloc = s[n - 1];
+        }
+        if (gap_out) {
+          double g = mloc - mrun[r]; /* +inf on the first visited tile */
+          double* gp = &gap_out[t * nK + c];
+          if (isnan(*gp) || g > *gp) *gp = g;
+        }
+        if (mloc > mrun[r]) mrun[r] = mloc;
+      }
+      if (nJ == 0) {
+        if (o_out) for (int64_t x = 0; x < D; ++x) o_out[(t * bq + r) * D + x] = 0.0;
+        if (lse_out) lse_out[t * bq + r] = -INFINITY;
+        continue;
+      }
+      double mi = -INFINITY;
+      for (int64_t u = 0; u < nJ; ++u) if (s[u] > mi) mi = s[u];
+      double li = 0.0;
+      for (int64_t u = 0; u < nJ; ++u) li = li + exp(s[u] - mi);
+      for (int64_t x = 0; x < D; ++x) acc[x] = 0.0;
+      n = 0;
+      for (int64_t c = 0; c < nK; ++c) {
+        if (!m[c]) continue;
+        int64_t j0 = c * bk, j1 = (c + 1) * bk < N ? (c + 1) * bk : N;
+        for (int64_t j = j0; j < j1; ++j) {
+          double p = exp(s[n++] - mi);
+          for (int64_t x = 0; x < D; ++x)
+            acc[x] = acc[x] + p * widen(v, dtype, b * vsb + j * vsn + h * vsh + x);
+        }
+      }
+      if (o_out) for (int64_t x = 0; x < D; ++x) o_out[(t * bq + r) * D + x] = acc[x] / li;
+      if (lse_out) lse_out[t * bq + r] = mi + log(li);
+    }
+    free(s); free(qi); free(acc); free(mrun);
+  }
+  return bad ? -1 : 0;
+}

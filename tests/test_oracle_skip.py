@@ -1,0 +1,42 @@
+"""Pins for the oracle's carried skip mask over denoising steps (CPU only)."""
+import numpy as np
+
+import oracle
+import synth
+
+
+def small_workload():
+    # a few frames of a small video grid, ragged last blocks (N = 5*6*7 = 210)
+    return synth.Workload("skip_small", 1, 2, 32, 5, 6, 7, 16, 16, "bf16", "skip",
+                          77, True, tau=2.0, steps=4)
+
+
+def test_infinite_threshold_never_marks_and_equals_dense(oracle_lib):
+    w = small_workload()
+    x = synth.make_qkv(w, step=0)
+    skip = np.zeros((w.B, w.H, w.nQ, w.nK), np.uint8)
+    o, lse, gap, new = oracle.skip_step(x["q"], x["k"], x["v"], w.Bq, w.Bk, w.scale, skip, np.inf)
+    assert not new.any()
+    ones = np.ones((w.nQ, w.nK), np.uint8)
+    o2, lse2, _ = oracle.attention(x["q"], x["k"], x["v"], w.Bq, w.Bk, w.scale, ones, 0)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+def test_skip_set_grows_monotonically_and_rows_never_empty(oracle_lib):
+    w = small_workload()
+    v = synth.make_qkv(w, step=0, want=("v",))["v"]
+    skip = np.zeros((w.B, w.H, w.nQ, w.nK), np.uint8)
+    total = []
+    for s in range(w.steps):
+        qk = synth.make_step_qk(w, s)
+        _, _, gap, new = oracle.skip_step(qk["q"], qk["k"], v, w.Bq, w.Bk, w.scale, skip, w.tau)
+        assert np.all(new >= skip)                       # monotone OR
+        assert np.all((1 - new).sum(axis=-1) >= 1)       # never an empty row
+        # the first visited tile of each row has gap +inf
+        eff = (1 - skip).reshape(-1, w.nK)
+        first = eff.argmax(axis=1)
+        assert np.all(gap[np.arange(gap.shape[0]), first] == np.inf)
+        skip = new
+        total.append(int(skip.sum()))
+    assert total[-1] > 0
