@@ -1,0 +1,256 @@
+// api.cpp -- the C ABI of libbsa (declared in include/bsa.h): host-side
+// argument validation, then kernel launches on the caller's stream.
+// Validation touches no GPU state, so every error path is testable on a host
+// without a GPU.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "bsa.h"
+#include "bsa_internal.h"
+
+namespace bsa {
+int pooled_max_blocks();
+}
+
+namespace {
+
+thread_local char g_err[512];
+
+bsa_status fail(bsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bsa_status ok() {
+  g_err[0] = 0;
+  return BSA_OK;
+}
+
+bsa_status device(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(BSA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kI32Max = 2147483647;
+
+bsa_status make_geom(const bsa_shape* s, bsa::Geom* g) {
+  if (!s) return fail(BSA_ERR_INVALID, "shape is NULL");
+  if (s->batch < 0 || s->heads < 0 || s->frames < 0 || s->height < 0 || s->width < 0)
+    return fail(BSA_ERR_INVALID, "negative batch/heads/frames/height/width");
+  if (s->head_dim <= 0 || s->block_q <= 0 || s->block_k <= 0)
+    return fail(BSA_ERR_INVALID, "head_dim and block sizes must be positive");
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", s->head_dim);
+  if (s->block_q != 64 && s->block_q != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "block_q %d not in {64, 128}", s->block_q);
+  if (s->block_k != 64) return fail(BSA_ERR_UNSUPPORTED, "block_k %d is not 64", s->block_k);
+  const int64_t F = (int64_t)s->height * s->width;
+  const int64_t N = F * s->frames;
+  if (N > kI32Max) return fail(BSA_ERR_INVALID, "N = %lld tokens does not fit in int32", (long long)N);
+  g->B = s->batch; g->H = s->heads; g->D = s->head_dim;
+  g->T = s->frames; g->Hs = s->height; g->Ws = s->width;
+  g->Bq = s->block_q; g->Bk = s->block_k;
+  g->N = N; g->F = F;
+  g->nQ = (N + g->Bq - 1) / g->Bq;
+  g->nK = (N + g->Bk - 1) / g->Bk;
+  if ((int64_t)g->B * g->H * g->nQ > kI32Max)
+    return fail(BSA_ERR_INVALID, "batch*heads*row blocks does not fit in int32");
+  return BSA_OK;
+}
+
+bool empty(const bsa::Geom& g) { return g.N == 0 || g.B == 0 || g.H == 0; }
+
+bsa_status check_tensor(const char* name, const bsa_tensor& t, int elem_bytes) {
+  if (!t.ptr) return fail(BSA_ERR_INVALID, "%s.ptr is NULL", name);
+  if ((uintptr_t)t.ptr % 16) return fail(BSA_ERR_INVALID, "%s.ptr is not 16-byte aligned", name);
+  const int64_t q = 16 / elem_bytes;
+  if (t.stride_b < 0 || t.stride_n < 0 || t.stride_h < 0)
+    return fail(BSA_ERR_INVALID, "%s has a negative stride", name);
+  if (t.stride_b % q || t.stride_n % q || t.stride_h % q)
+    return fail(BSA_ERR_INVALID, "%s strides must be multiples of %lld elements", name,
+                (long long)q);
+  return BSA_OK;
+}
+
+bsa::TensorArg arg(const bsa_tensor& t) { return {t.ptr, t.stride_b, t.stride_n, t.stride_h}; }
+
+int elem_bytes(bsa_dtype dt) { return dt == BSA_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+const char* bsa_status_string(bsa_status st) {
+  switch (st) {
+    case BSA_OK: return "ok";
+    case BSA_ERR_INVALID: return "invalid argument";
+    case BSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case BSA_ERR_CAPACITY: return "kv_idx capacity too small";
+    case BSA_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* bsa_last_error(void) { return g_err; }
+
+bsa_status bsa_build_mask_radial(const bsa_shape* s, int32_t h0, int32_t decay_base,
+                                 uint8_t* mask, void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  if (decay_base < 2) return fail(BSA_ERR_INVALID, "decay_base %d < 2", decay_base);
+  if (h0 < g.Bk / 2 || h0 >= (1 << 30))
+    return fail(BSA_ERR_INVALID, "h0 %d outside [block_k/2, 2^30)", h0);
+  if (g.N == 0) return ok();
+  if (!mask) return fail(BSA_ERR_INVALID, "mask is NULL");
+  return device(bsa::launch_radial_mask(g, h0, decay_base, mask, (hipStream_t)stream),
+                "radial mask launch");
+}
+
+size_t bsa_pooled_workspace_bytes(const bsa_shape* s) {
+  bsa::Geom g;
+  if (make_geom(s, &g) != BSA_OK) return 0;
+  return bsa::pooled_workspace_bytes(g);
+}
+
+bsa_status bsa_build_mask_pooled(const bsa_shape* s, bsa_dtype dt, bsa_tensor q,
+                                 bsa_tensor k, double scale, int32_t mode, double param,
+                                 uint8_t* mask, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  if (dt != BSA_BF16 && dt != BSA_F32) return fail(BSA_ERR_UNSUPPORTED, "dtype %d", (int)dt);
+  if (!isfinite(scale)) return fail(BSA_ERR_INVALID, "scale is not finite");
+  if (mode == 0) {
+    if (!(param >= 1.0) || param != floor(param) || param > 2147483647.0)
+      return fail(BSA_ERR_INVALID, "top-k needs an integer k >= 1, got %g", param);
+  } else if (mode == 1) {
+    if (!(param > 0.0 && param <= 1.0))
+      return fail(BSA_ERR_INVALID, "cumulative mass tau_p must be in (0, 1], got %g", param);
+  } else {
+    return fail(BSA_ERR_INVALID, "mode %d not in {0, 1}", mode);
+  }
+  if (g.nK > bsa::pooled_max_blocks())
+    return fail(BSA_ERR_UNSUPPORTED, "pooled selection supports at most %d key blocks",
+                bsa::pooled_max_blocks());
+  if (empty(g)) return ok();
+  if ((st = check_tensor("q", q, elem_bytes(dt))) != BSA_OK) return st;
+  if ((st = check_tensor("k", k, elem_bytes(dt))) != BSA_OK) return st;
+  if (!mask) return fail(BSA_ERR_INVALID, "mask is NULL");
+  const size_t need = bsa::pooled_workspace_bytes(g);
+  if (!workspace || workspace_bytes < need)
+    return fail(BSA_ERR_INVALID, "workspace needs %zu bytes", need);
+  if ((uintptr_t)workspace % 256) return fail(BSA_ERR_INVALID, "workspace not 256-byte aligned");
+  return device(bsa::launch_pooled_mask(g, dt == BSA_BF16 ? 0 : 1, arg(q), arg(k), scale, mode,
+                                        param, mask, workspace, (hipStream_t)stream),
+                "pooled mask launch");
+}
+
+bsa_status bsa_compact_block_lists(const bsa_shape* s, const uint8_t* mask,
+                                   int64_t mask_head_stride, const uint8_t* skip,
+                                   int32_t* row_ptr, int32_t* kv_idx, int64_t kv_capacity,
+                                   int64_t* nnz_host, void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  const bool shared = mask_head_stride == 0 && skip == nullptr;
+  if (mask_head_stride != 0 && mask_head_stride < g.nQ * g.nK)
+    return fail(BSA_ERR_INVALID, "mask_head_stride must be 0 or >= nQ*nK");
+  if (kv_capacity < 0) return fail(BSA_ERR_INVALID, "kv_capacity < 0");
+  if (!row_ptr) return fail(BSA_ERR_INVALID, "row_ptr is NULL");
+  const int64_t R = shared ? g.nQ : (int64_t)g.B * g.H * g.nQ;
+  if (R * g.nK > kI32Max)
+    return fail(BSA_ERR_UNSUPPORTED, "list rows x key blocks exceeds int32 list offsets");
+  hipStream_t str = (hipStream_t)stream;
+  if (R == 0 || g.nK == 0) {
+    if (nnz_host) *nnz_host = 0;
+    return device(bsa::launch_zero_row_ptr(row_ptr, str), "compaction launch");
+  }
+  if (!mask) return fail(BSA_ERR_INVALID, "mask is NULL");
+  if (!kv_idx && kv_capacity > 0) return fail(BSA_ERR_INVALID, "kv_idx is NULL");
+  if (!nnz_host && kv_capacity < R * g.nK)
+    return fail(BSA_ERR_CAPACITY,
+                "without nnz_host, kv_capacity must cover every tile (%lld)",
+                (long long)(R * g.nK));
+  const int64_t mhs = mask_head_stride;
+  hipError_t e = bsa::launch_compact_count_scan(g, R, mask, mhs, skip, row_ptr, str);
+  if (e != hipSuccess) return device(e, "compaction count");
+  if (nnz_host) {
+    int32_t nnz = 0;
+    e = hipMemcpyAsync(&nnz, row_ptr + R, sizeof nnz, hipMemcpyDeviceToHost, str);
+    if (e == hipSuccess) e = hipStreamSynchronize(str);
+    if (e != hipSuccess) return device(e, "compaction count readback");
+    *nnz_host = nnz;
+    if (nnz > kv_capacity)
+      return fail(BSA_ERR_CAPACITY, "%d kept tiles exceed kv_capacity %lld", nnz,
+                  (long long)kv_capacity);
+    if (nnz > 0 && !kv_idx) return fail(BSA_ERR_INVALID, "kv_idx is NULL");
+  }
+  return device(bsa::launch_compact_scatter(g, R, mask, mhs, skip, row_ptr, kv_idx, str),
+                "compaction scatter");
+}
+
+bsa_status bsa_sparse_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, bsa_tensor k,
+                               bsa_tensor v, bsa_tensor o, float* lse, const int32_t* row_ptr,
+                               const int32_t* kv_idx, int32_t lists_shared, float scale,
+                               float* tile_gap, void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  if (dt != BSA_BF16 && dt != BSA_F32) return fail(BSA_ERR_UNSUPPORTED, "dtype %d", (int)dt);
+  if (!isfinite(scale) || scale < 0.f)
+    return fail(BSA_ERR_INVALID, "scale must be finite and >= 0");
+  if (lists_shared != 0 && lists_shared != 1)
+    return fail(BSA_ERR_INVALID, "lists_shared must be 0 or 1");
+  if ((row_ptr == nullptr) != (kv_idx == nullptr))
+    return fail(BSA_ERR_INVALID, "row_ptr and kv_idx must both be set or both be NULL");
+  if (tile_gap && !row_ptr) return fail(BSA_ERR_INVALID, "tile_gap needs block lists");
+  if (empty(g)) return ok();
+  const int eb = elem_bytes(dt);
+  if ((st = check_tensor("q", q, eb)) != BSA_OK) return st;
+  if ((st = check_tensor("k", k, eb)) != BSA_OK) return st;
+  if ((st = check_tensor("v", v, eb)) != BSA_OK) return st;
+  if ((st = check_tensor("o", o, eb)) != BSA_OK) return st;
+  if (o.ptr == q.ptr || o.ptr == k.ptr || o.ptr == v.ptr)
+    return fail(BSA_ERR_INVALID, "o must not alias q, k or v");
+  bsa::AttnArgs a;
+  a.q = arg(q); a.k = arg(k); a.v = arg(v);
+  a.o = o.ptr; a.osb = o.stride_b; a.osn = o.stride_n; a.osh = o.stride_h;
+  a.lse = lse;
+  a.row_ptr = row_ptr;
+  a.kv_idx = kv_idx;
+  a.lists_shared = lists_shared;
+  a.scale = scale;
+  a.tile_gap = tile_gap;
+  hipStream_t str = (hipStream_t)stream;
+  return device(dt == BSA_BF16 ? bsa::launch_attn_bf16(g, a, str) : bsa::launch_attn_f32(g, a, str),
+                "attention launch");
+}
+
+bsa_status bsa_update_skip_mask(const bsa_shape* s, const int32_t* row_ptr,
+                                const int32_t* kv_idx, const float* tile_gap, float tau,
+                                uint8_t* skip, void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  if (!(tau > 0.f)) return fail(BSA_ERR_INVALID, "tau must be > 0");
+  if ((int64_t)g.B * g.H * g.nQ * g.nK > kI32Max)
+    return fail(BSA_ERR_UNSUPPORTED, "list rows x key blocks exceeds int32 list offsets");
+  if (empty(g)) return ok();
+  if (!row_ptr || !kv_idx || !tile_gap || !skip)
+    return fail(BSA_ERR_INVALID, "row_ptr, kv_idx, tile_gap and skip are required");
+  const float tau2 = (float)((double)tau * 1.4426950408889634);
+  return device(bsa::launch_skip_update(g, row_ptr, kv_idx, tile_gap, tau2, skip,
+                                        (hipStream_t)stream),
+                "skip update launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// bsa_internal.h -- declarations shared by the C-ABI host layer and the HIP
+// kernel launchers of libbsa. Not installed; the public interface is bsa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+// Geometry derived once on the host from bsa_shape (all validated).
+struct Geom {
+  int32_t B, H, D, T, Hs, Ws, Bq, Bk;
+  int64_t N, F, nQ, nK;
+};
+
+struct TensorArg {
+  const void* ptr;
+  int64_t sb, sn, sh;  // element strides
+};
+
+// ---- masks and lists (mask_kernels.hip)
+hipError_t launch_radial_mask(const Geom& g, int32_t h0, int32_t beta, uint8_t* mask,
+                              hipStream_t st);
+
+size_t pooled_workspace_bytes(const Geom& g);
+hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k, double scale,
+                              int32_t mode, double param, uint8_t* mask, void* ws,
+                              hipStream_t st);
+
+// Counts kept tiles per list row into row_ptr[1..R] and row_ptr[0] = 0, then
+// turns row_ptr into its inclusive prefix sum.
+hipError_t launch_compact_count_scan(const Geom& g, int64_t R, const uint8_t* mask,
+                                     int64_t mask_head_stride, const uint8_t* skip,
+                                     int32_t* row_ptr, hipStream_t st);
+hipError_t launch_compact_scatter(const Geom& g, int64_t R, const uint8_t* mask,
+                                  int64_t mask_head_stride, const uint8_t* skip,
+                                  const int32_t* row_ptr, int32_t* kv_idx, hipStream_t st);
+hipError_t launch_zero_row_ptr(int32_t* row_ptr, hipStream_t st);
+
+hipError_t launch_skip_update(const Geom& g, const int32_t* row_ptr, const int32_t* kv_idx,
+                              const float* tile_gap, float tau2, uint8_t* skip,
+                              hipStream_t st);
+
+// ---- attention forward
+struct AttnArgs {
+  TensorArg q, k, v;
+  void* o;
+  int64_t osb, osn, osh;
+  float* lse;
+  const int32_t* row_ptr;  // NULL = dense
+  const int32_t* kv_idx;
+  int32_t lists_shared;
+  float scale;
+  float* tile_gap;
+};
+
+hipError_t launch_attn_bf16(const Geom& g, const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_f32(const Geom& g, const AttnArgs& a, hipStream_t st);
+
+}  // namespace bsa

@@ -1,0 +1,407 @@
+// mask_kernels.hip -- block-mask builders, list compaction and the skip-mask
+// update of libbsa (gfx950). These are small, latency- or HBM-bound kernels
+// around the attention forward; none of them is a dense contraction.
+//
+// Pages: [Radial] "MIT实验室推出Radial Attention：让视频AI生成快如闪电的神奇技术";
+// [PSA] "浙江大学突破视频AI瓶颈:金字塔方法提升视频AI效率10倍";
+// [VMoBA] VMoBA summary page (arXiv:2506.23858); [Lite] LiteAttention
+// summary page (arXiv:2511.11062).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "bsa_internal.h"
+
+namespace bsa {
+namespace {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ radial
+// Window of frame distance `dist` under the radial rule ([Radial]: weight
+// falls off with frame distance; a fixed map; n log n cost). The band of a
+// distance is its number of base-beta digits; the half-width is h0 divided
+// by beta once per band down to half a key block (bands 0..rstar); farther
+// bands keep that width and thin out the distances instead.
+__device__ inline bool radial_distance_kept(int64_t dist, int32_t h0, int32_t beta,
+                                            int32_t rstar, int32_t half_blk, int64_t* h) {
+  int band = 0;
+  for (int64_t x = dist; x > 0; x /= beta) ++band;
+  if (band <= rstar) {
+    int64_t w = h0;
+    for (int i = 0; i < band; ++i) w /= beta;
+    *h = w;
+    return true;
+  }
+  int64_t period = 1;
+  for (int i = rstar; i < band; ++i) period *= beta;
+  *h = half_blk;
+  return dist % period == 0;
+}
+
+// One thread per tile. For each pair of frames the two blocks touch, the
+// tile holds a kept token pair iff the distance is kept and the gap between
+// the blocks' in-frame position intervals is below the window.
+__global__ void radial_mask_kernel(int64_t N, int64_t F, int32_t Bq, int32_t Bk, int64_t nK,
+                                   int64_t tiles, int32_t h0, int32_t beta, int32_t rstar,
+                                   uint8_t* __restrict__ mask) {
+  const int64_t half_blk = Bk / 2;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < tiles;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t a = t / nK, c = t - a * nK;
+    const int64_t i0 = a * Bq, i1 = min(N, i0 + Bq);
+    const int64_t j0 = c * Bk, j1 = min(N, j0 + Bk);
+    bool keep = false;
+    for (int64_t tq = i0 / F; tq <= (i1 - 1) / F && !keep; ++tq) {
+      const int64_t qlo = max(i0, tq * F) - tq * F;
+      const int64_t qhi = min(i1, tq * F + F) - 1 - tq * F;
+      for (int64_t tk = j0 / F; tk <= (j1 - 1) / F && !keep; ++tk) {
+        const int64_t klo = max(j0, tk * F) - tk * F;
+        const int64_t khi = min(j1, tk * F + F) - 1 - tk * F;
+        const int64_t gap = max((int64_t)0, max(klo - qhi, qlo - khi));
+        int64_t h;
+        if (radial_distance_kept(tq > tk ? tq - tk : tk - tq, h0, beta, rstar,
+                                 (int32_t)half_blk, &h) &&
+            gap < h)
+          keep = true;
+      }
+    }
+    mask[t] = keep ? 1 : 0;
+  }
+}
+
+// ------------------------------------------------------------------ pooled
+// Input element widened to fp64 (exact).
+__device__ inline double widen(const void* p, int dtype, int64_t off) {
+  if (dtype == 0) {
+    const uint32_t u = (uint32_t)((const uint16_t*)p)[off] << 16;
+    return (double)__uint_as_float(u);
+  }
+  return (double)((const float*)p)[off];
+}
+
+// Block means of Q (row blocks) and K (column blocks): one thread per
+// (b*H + h, block, channel); tokens summed in ascending order, one division.
+__global__ void pool_mean_kernel(int64_t N, int32_t H, int32_t D, int32_t Bq, int32_t Bk,
+                                 int64_t nQ, int64_t nK, int64_t BH, int dtype, TensorArg q,
+                                 TensorArg k, double* __restrict__ qbar,
+                                 double* __restrict__ kbar) {
+  const int64_t per = (nQ + nK) * D;
+  const int64_t total = BH * per;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t bh = t / per;
+    const int64_t rem = t - bh * per;
+    const int64_t blk = rem / D;
+    const int32_t x = (int32_t)(rem - blk * D);
+    const int64_t b = bh / H, h = bh - b * H;
+    const bool isq = blk < nQ;
+    const int64_t bi = isq ? blk : blk - nQ;
+    const int32_t bs = isq ? Bq : Bk;
+    const TensorArg& in = isq ? q : k;
+    const int64_t i0 = bi * bs, i1 = min(N, i0 + bs);
+    double acc = 0.0;
+    const int64_t base = b * in.sb + h * in.sh + x;
+    for (int64_t i = i0; i < i1; ++i) acc = acc + widen(in.ptr, dtype, base + i * in.sn);
+    const double m = acc / (double)(i1 - i0);
+    if (isq)
+      qbar[(bh * nQ + bi) * D + x] = m;
+    else
+      kbar[(bh * nK + bi) * D + x] = m;
+  }
+}
+
+// Pooled scores S[bh][a][c] = scale * (sum over x ascending of qbar*kbar),
+// every product and sum rounded on its own (no fused multiply-add).
+constexpr int kScoreTile = 16;
+__global__ void pooled_scores_kernel(int32_t D, int64_t nQ, int64_t nK, double scale,
+                                     const double* __restrict__ qbar,
+                                     const double* __restrict__ kbar, double* __restrict__ S) {
+#pragma clang fp contract(off)
+  extern __shared__ double sm[];
+  const int ld = D + 1;
+  double* qs = sm;
+  double* ks = sm + kScoreTile * ld;
+  const int64_t bh = blockIdx.z;
+  const int64_t a0 = (int64_t)blockIdx.y * kScoreTile, c0 = (int64_t)blockIdx.x * kScoreTile;
+  const int tid = threadIdx.y * kScoreTile + threadIdx.x;
+  for (int e = tid; e < kScoreTile * D; e += kScoreTile * kScoreTile) {
+    const int r = e / D, x = e - r * D;
+    qs[r * ld + x] = (a0 + r < nQ) ? qbar[(bh * nQ + a0 + r) * D + x] : 0.0;
+    ks[r * ld + x] = (c0 + r < nK) ? kbar[(bh * nK + c0 + r) * D + x] : 0.0;
+  }
+  __syncthreads();
+  const int64_t a = a0 + threadIdx.y, c = c0 + threadIdx.x;
+  if (a < nQ && c < nK) {
+    double acc = 0.0;
+    for (int x = 0; x < D; ++x) {
+      const double pr = __dmul_rn(qs[threadIdx.y * ld + x], ks[threadIdx.x * ld + x]);
+      acc = __dadd_rn(acc, pr);
+    }
+    S[(bh * nQ + a) * nK + c] = __dmul_rn(scale, acc);
+  }
+}
+
+// Order a before b: higher score first, lower block index on ties.
+__device__ inline bool ranks_before(const double* s, int a, int b) {
+  if (b < 0) return a >= 0;
+  if (a < 0) return false;
+  return s[a] > s[b] || (s[a] == s[b] && a < b);
+}
+
+constexpr int kSelectThreads = 256;
+constexpr int kPooledMaxBlocks = 2048;  // keeps the select kernel under 64 KiB of LDS
+
+// One workgroup per (b, h, a): bitonic sort of the row's block indices by
+// (score desc, index asc), then top-k or the shortest prefix reaching the
+// cumulative softmax mass tau_p (sum Z in ascending block order, running sum
+// of p = e/Z in sorted order, both sequential).
+__global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double param,
+                                     const double* __restrict__ S, uint8_t* __restrict__ mask) {
+  extern __shared__ double smd[];
+  double* s = smd;                 // [nK] scores, block order
+  double* e = smd + nK;            // [nK] exp(S - max), block order
+  int32_t* idx = (int32_t*)(smd + 2 * nK);  // [P]
+  uint8_t* flag = (uint8_t*)(idx + P);      // [nK]
+  __shared__ int32_t keep_sh;
+  const int64_t row = blockIdx.x;
+  const double* srow = S + row * nK;
+  for (int c = threadIdx.x; c < P; c += blockDim.x) {
+    if (c < nK) {
+      s[c] = srow[c];
+      flag[c] = 0;
+    }
+    idx[c] = c < nK ? c : -1;
+  }
+  __syncthreads();
+  for (int kk = 2; kk <= P; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        const int l = i ^ j;
+        if (l > i) {
+          const int x = idx[i], y = idx[l];
+          const bool up = (i & kk) == 0;
+          const bool swap = up ? ranks_before(s, y, x) : ranks_before(s, x, y);
+          if (swap) {
+            idx[i] = y;
+            idx[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  int32_t keep;
+  if (mode == 0) {
+    keep = (int32_t)min((double)nK, param);
+  } else {
+    const double smax = s[idx[0]];
+    for (int c = threadIdx.x; c < nK; c += blockDim.x) e[c] = exp(s[c] - smax);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double Z = 0.0;
+      for (int64_t c = 0; c < nK; ++c) Z = Z + e[c];
+      double run = 0.0;
+      int32_t kp = (int32_t)nK;
+      for (int32_t t = 0; t < nK; ++t) {
+        run = run + e[idx[t]] / Z;
+        if (run >= param) {
+          kp = t + 1;
+          break;
+        }
+      }
+      keep_sh = kp;
+    }
+    __syncthreads();
+    keep = keep_sh;
+  }
+  for (int t = threadIdx.x; t < keep; t += blockDim.x) flag[idx[t]] = 1;
+  __syncthreads();
+  uint8_t* mrow = mask + row * nK;
+  for (int c = threadIdx.x; c < nK; c += blockDim.x) mrow[c] = flag[c];
+}
+
+// -------------------------------------------------------------- compaction
+__device__ inline bool tile_listed(const uint8_t* mask, int64_t mhs, const uint8_t* skip,
+                                   int64_t r, int64_t nQ, int64_t nK, int64_t c) {
+  const int64_t bh = r / nQ, a = r - bh * nQ;
+  bool on = mask[bh * mhs + a * nK + c] != 0;
+  if (skip && skip[r * nK + c]) on = false;
+  return on;
+}
+
+// One wave per list row: row_ptr[r + 1] = number of listed tiles.
+__global__ void compact_count_kernel(int64_t R, int64_t nQ, int64_t nK,
+                                     const uint8_t* __restrict__ mask, int64_t mhs,
+                                     const uint8_t* __restrict__ skip,
+                                     int32_t* __restrict__ row_ptr) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t r = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (blockIdx.x == 0 && threadIdx.x == 0) row_ptr[0] = 0;
+  if (r >= R) return;
+  int32_t cnt = 0;
+  for (int64_t c0 = 0; c0 < nK; c0 += kWave) {
+    const int64_t c = c0 + lane;
+    const bool on = c < nK && tile_listed(mask, mhs, skip, r, nQ, nK, c);
+    cnt += __popcll(__ballot(on));
+  }
+  if (lane == 0) row_ptr[r + 1] = cnt;
+}
+
+// Single workgroup: in-place inclusive scan of row_ptr[1..R].
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void compact_scan_kernel(int64_t R,
+                                                                    int32_t* __restrict__ row_ptr) {
+  __shared__ int32_t part[kScanThreads];
+  const int64_t chunk = (R + kScanThreads - 1) / kScanThreads;
+  const int64_t lo = 1 + threadIdx.x * chunk, hi = min(R + 1, lo + chunk);
+  int32_t sum = 0;
+  for (int64_t i = lo; i < hi; ++i) sum += row_ptr[i];
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const int32_t add = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += add;
+    __syncthreads();
+  }
+  int32_t run = threadIdx.x ? part[threadIdx.x - 1] : 0;
+  for (int64_t i = lo; i < hi; ++i) {
+    run += row_ptr[i];
+    row_ptr[i] = run;
+  }
+}
+
+// One wave per list row: write the listed key blocks in ascending order.
+__global__ void compact_scatter_kernel(int64_t R, int64_t nQ, int64_t nK,
+                                       const uint8_t* __restrict__ mask, int64_t mhs,
+                                       const uint8_t* __restrict__ skip,
+                                       const int32_t* __restrict__ row_ptr,
+                                       int32_t* __restrict__ kv_idx) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t r = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (r >= R) return;
+  int64_t out = row_ptr[r];
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int64_t c0 = 0; c0 < nK; c0 += kWave) {
+    const int64_t c = c0 + lane;
+    const bool on = c < nK && tile_listed(mask, mhs, skip, r, nQ, nK, c);
+    const uint64_t bal = __ballot(on);
+    if (on) kv_idx[out + __popcll(bal & below)] = (int32_t)c;
+    out += __popcll(bal);
+  }
+}
+
+__global__ void zero_row_ptr_kernel(int32_t* row_ptr) { row_ptr[0] = 0; }
+
+// ------------------------------------------------------------- skip update
+// One wave per list row: tiles whose gap lies at or below -tau2 join the
+// carried skip set ([Lite] sections 三 and 六).
+__global__ void skip_update_kernel(int64_t R, int64_t nK, const int32_t* __restrict__ row_ptr,
+                                   const int32_t* __restrict__ kv_idx,
+                                   const float* __restrict__ gap, float neg_tau2,
+                                   uint8_t* __restrict__ skip) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t r = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (r >= R) return;
+  const int32_t e1 = row_ptr[r + 1];
+  for (int32_t e = row_ptr[r] + lane; e < e1; e += kWave)
+    if (gap[e] <= neg_tau2) skip[r * nK + kv_idx[e]] = 1;
+}
+
+inline unsigned grid_for(int64_t work, int threads, int64_t cap = 1 << 20) {
+  int64_t g = (work + threads - 1) / threads;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+hipError_t launch_radial_mask(const Geom& g, int32_t h0, int32_t beta, uint8_t* mask,
+                              hipStream_t st) {
+  const int64_t tiles = g.nQ * g.nK;
+  if (tiles == 0) return hipSuccess;
+  int32_t rstar = 0;
+  for (int64_t w = h0 / beta; w >= g.Bk / 2; w /= beta) ++rstar;
+  hipLaunchKernelGGL(radial_mask_kernel, dim3(grid_for(tiles, 256)), dim3(256), 0, st, g.N,
+                     g.F, g.Bq, g.Bk, g.nK, tiles, h0, beta, rstar, mask);
+  return hipGetLastError();
+}
+
+size_t pooled_workspace_bytes(const Geom& g) {
+  const int64_t BH = (int64_t)g.B * g.H;
+  const int64_t n = BH * (g.nQ + g.nK) * g.D + BH * g.nQ * g.nK;
+  return (size_t)n * sizeof(double);
+}
+
+int pooled_max_blocks() { return kPooledMaxBlocks; }
+
+hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k, double scale,
+                              int32_t mode, double param, uint8_t* mask, void* ws,
+                              hipStream_t st) {
+  const int64_t BH = (int64_t)g.B * g.H;
+  if (BH == 0 || g.N == 0) return hipSuccess;
+  double* qbar = (double*)ws;
+  double* kbar = qbar + BH * g.nQ * g.D;
+  double* S = kbar + BH * g.nK * g.D;
+  const int64_t work = BH * (g.nQ + g.nK) * g.D;
+  hipLaunchKernelGGL(pool_mean_kernel, dim3(grid_for(work, 256)), dim3(256), 0, st, g.N, g.H,
+                     g.D, g.Bq, g.Bk, g.nQ, g.nK, BH, dtype, q, k, qbar, kbar);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  dim3 grid((unsigned)((g.nK + kScoreTile - 1) / kScoreTile),
+            (unsigned)((g.nQ + kScoreTile - 1) / kScoreTile), (unsigned)BH);
+  const size_t sh = sizeof(double) * 2 * kScoreTile * (g.D + 1);
+  hipLaunchKernelGGL(pooled_scores_kernel, grid, dim3(kScoreTile, kScoreTile), sh, st, g.D,
+                     g.nQ, g.nK, scale, qbar, kbar, S);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  int32_t P = 1;
+  while (P < g.nK) P <<= 1;
+  const size_t sh2 = sizeof(double) * 2 * g.nK + sizeof(int32_t) * P + g.nK + 16;
+  hipLaunchKernelGGL(pooled_select_kernel, dim3((unsigned)(BH * g.nQ)), dim3(kSelectThreads),
+                     sh2, st, g.nK, P, mode, param, S, mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_count_scan(const Geom& g, int64_t R, const uint8_t* mask,
+                                     int64_t mhs, const uint8_t* skip, int32_t* row_ptr,
+                                     hipStream_t st) {
+  const int waves = 4;
+  hipLaunchKernelGGL(compact_count_kernel, dim3(grid_for(R, waves, INT32_MAX)),
+                     dim3(waves * kWave), 0, st, R, g.nQ, g.nK, mask, mhs, skip, row_ptr);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, R, row_ptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_scatter(const Geom& g, int64_t R, const uint8_t* mask, int64_t mhs,
+                                  const uint8_t* skip, const int32_t* row_ptr, int32_t* kv_idx,
+                                  hipStream_t st) {
+  const int waves = 4;
+  hipLaunchKernelGGL(compact_scatter_kernel, dim3(grid_for(R, waves, INT32_MAX)),
+                     dim3(waves * kWave), 0, st, R, g.nQ, g.nK, mask, mhs, skip, row_ptr,
+                     kv_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_row_ptr(int32_t* row_ptr, hipStream_t st) {
+  hipLaunchKernelGGL(zero_row_ptr_kernel, dim3(1), dim3(1), 0, st, row_ptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_skip_update(const Geom& g, const int32_t* row_ptr, const int32_t* kv_idx,
+                              const float* tile_gap, float tau2, uint8_t* skip,
+                              hipStream_t st) {
+  const int64_t R = (int64_t)g.B * g.H * g.nQ;
+  if (R == 0) return hipSuccess;
+  const int waves = 4;
+  hipLaunchKernelGGL(skip_update_kernel, dim3(grid_for(R, waves, INT32_MAX)),
+                     dim3(waves * kWave), 0, st, R, g.nK, row_ptr, kv_idx, tile_gap, -tau2,
+                     skip);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,216 @@
+/*
+ * bsa.h -- C ABI of libbsa: block-sparse, bidirectional softmax attention over
+ * a flattened frames x height x width video token sequence, for MI355X (gfx950).
+ *
+ * Pages this interface follows (web pages that describe the method):
+ *   [Lite]   LiteAttention summary page (arXiv:2511.11062), numbered sections.
+ *   [VMoBA]  VMoBA summary page (arXiv:2506.23858), numbered sections.
+ *   [Radial] "MIT实验室推出Radial Attention：让视频AI生成快如闪电的神奇技术"
+ *            (arXiv:2506.19852).
+ *   [PARO]   PAROAttention summary page (arXiv:2506.16054), numbered sections.
+ *   [PSA]    "浙江大学突破视频AI瓶颈:金字塔方法提升视频AI效率10倍"
+ *            (arXiv:2512.04025).
+ * Every page presents its method as a drop-in replacement for dense attention
+ * ([Lite] section 六 extends an existing attention API with a persistent skip
+ * mask; [VMoBA] section 六 a standard replacement interface; [PSA] plug and
+ * play), so the calls below take the tensors a dense attention call takes,
+ * plus the block mask or block lists.
+ *
+ * Conventions shared by all calls
+ * -------------------------------
+ * Tokens: i = (t*height + y)*width + x, N = frames*height*width,
+ *   F = height*width tokens per frame. Row (query) block a covers tokens
+ *   [a*block_q, min(N, (a+1)*block_q)), column (key) block c covers
+ *   [c*block_k, min(N, (c+1)*block_k)); nQ = ceil(N/block_q),
+ *   nK = ceil(N/block_k). Ragged last blocks keep their true sizes: padding
+ *   tokens never enter a maximum, sum or mean.
+ * Tensors (bsa_tensor): element (b, i, h, x) of Q, K, V or O lives at
+ *   ptr + b*stride_b + i*stride_n + h*stride_h + x (strides in elements,
+ *   head_dim contiguous). The usual layout is [B][N][H][d].
+ * Masks: uint8, 0 = drop the tile, nonzero = keep. A per-head mask is
+ *   [B][H][nQ][nK]; a shared mask is [nQ][nK] (head stride 0).
+ * Block lists (CSR): list row r = (b*H + h)*nQ + a (or just a when one list
+ *   serves every (b, h)); kv_idx[row_ptr[r] .. row_ptr[r+1]) holds the kept
+ *   key blocks of that row in ascending order.
+ * Memory: every tensor, mask and list pointer is a DEVICE pointer owned by
+ *   the caller; the library allocates no device memory and keeps no state
+ *   besides its loaded kernels and a thread-local error string.
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = legacy default
+ *   stream). Calls validate their arguments on the host before touching the
+ *   GPU, enqueue their kernels on `stream` and return without synchronising
+ *   unless documented otherwise.
+ * Errors: no call throws; each returns a bsa_status. BSA_ERR_INVALID and
+ *   BSA_ERR_UNSUPPORTED are returned before anything is enqueued.
+ *   bsa_last_error() gives a thread-local text for the last failing call.
+ * Sizes: zero-sized shapes (B, H or N = 0) are valid and enqueue nothing
+ *   except the single row_ptr[0] = 0 of compaction.
+ */
+#ifndef BSA_H_
+#define BSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define BSA_API __attribute__((visibility("default")))
+#else
+#define BSA_API
+#endif
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID = 1,     /* null required pointer, bad size, misalignment, bad knob */
+  BSA_ERR_UNSUPPORTED = 2, /* head_dim, block size or dtype outside the compiled set */
+  BSA_ERR_CAPACITY = 3,    /* kv_capacity smaller than the number of kept tiles */
+  BSA_ERR_DEVICE = 4       /* a HIP call failed; see bsa_last_error() */
+} bsa_status;
+
+typedef enum { BSA_BF16 = 0, BSA_F32 = 1 } bsa_dtype;
+
+typedef struct {
+  int32_t batch, heads, head_dim; /* B, H, d (d in {64, 128}) */
+  int32_t frames, height, width;  /* T, Hs, Ws; N = T*Hs*Ws < 2^31 */
+  int32_t block_q, block_k;       /* block_q in {64, 128}; block_k = 64 */
+} bsa_shape;
+
+typedef struct {
+  void* ptr;                          /* device pointer, 16-byte aligned */
+  int64_t stride_b, stride_n, stride_h; /* in elements; multiples of 8 (bf16) or 4 (f32) */
+} bsa_tensor;
+
+/*
+ * Static radial mask ([Radial]: attention weakens with temporal and spatial
+ * distance, each frame attends mostly to its nearest frames with a weight that
+ * falls with frame distance, and the map is fixed ahead of time; cost grows as
+ * n log n).
+ * Frame distance dt = |t(i) - t(j)| falls in band r = number of base-
+ * `decay_base` digits of dt (r = 0 for dt = 0). The in-frame half-width is
+ * h_r = floor(h0 / decay_base^r) while h_r >= block_k/2 (bands 0..r*); beyond
+ * r*, the half-width stays block_k/2 and only every decay_base^(r - r*)-th
+ * distance of band r is kept. Token pair (i, j) is kept iff its distance is
+ * kept and |s(i) - s(j)| < h_eff, s = in-frame position. Tile (a, c) is kept
+ * iff any token pair of row block a and column block c is kept.
+ *   h0          window half-width at distance 0, tokens; block_k/2 <= h0 < 2^30
+ *   decay_base  >= 2
+ *   mask        out, [nQ][nK] (shared by all batches and heads)
+ * Integer only; the result is deterministic and exact.
+ */
+BSA_API bsa_status bsa_build_mask_radial(const bsa_shape* s, int32_t h0, int32_t decay_base,
+                                 uint8_t* mask, void* stream);
+
+/*
+ * Bytes of device workspace bsa_build_mask_pooled needs for shape s
+ * (pooled means of Q and K in fp64 and the per-row scores).
+ */
+BSA_API size_t bsa_pooled_workspace_bytes(const bsa_shape* s);
+
+/*
+ * Dynamic mask from mean-pooled block scores ([PSA]: average pooling of keys
+ * block by block; [VMoBA] sections 三 and 六: block relevance from pooled
+ * scores by matrix operations, and a threshold that sets how many blocks a
+ * query keeps according to how concentrated its attention is).
+ * Per (b, h), in fp64 with a fixed operation order:
+ *   qbar_a = (sum_{i in row block a} q_i) / |R_a|, sum in ascending i;
+ *   kbar_c likewise;
+ *   S_ac = scale * sum_x qbar_ax * kbar_cx, x ascending, no fused multiply-add;
+ *   row a orders c by (S desc, c asc) and keeps
+ *     mode 0: the first min(param, nK) blocks (param = k >= 1), or
+ *     mode 1: the shortest prefix whose running sum of p_c reaches param,
+ *             p_c = exp(S_ac - max S_a) / Z, Z summed in ascending c,
+ *             param = tau_p in (0, 1] (all blocks if the sum never reaches it).
+ *   q, k        inputs of dtype dt ([B][N][H][d] by strides)
+ *   mask        out, [B][H][nQ][nK]
+ *   workspace   device buffer of at least bsa_pooled_workspace_bytes(s)
+ *               bytes, 256-byte aligned; contents on return are unspecified.
+ * Supports nK <= 2048 key blocks (BSA_ERR_UNSUPPORTED beyond).
+ */
+BSA_API bsa_status bsa_build_mask_pooled(const bsa_shape* s, bsa_dtype dt, bsa_tensor q,
+                                 bsa_tensor k, double scale, int32_t mode, double param,
+                                 uint8_t* mask, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * Per-row lists of kept key blocks ([Lite] sections 三 and 六: a skipped tile
+ * must cost no softmax and no memory transfer, so the loader walks only the
+ * listed tiles).
+ * Tile (b, h, a, c) is listed iff mask[(b*H + h)*mask_head_stride + a*nK + c]
+ * != 0 and (skip == NULL or skip[((b*H + h)*nQ + a)*nK + c] == 0).
+ *   mask_head_stride  0 (one mask for every head) or >= nQ*nK
+ *   skip              nullable, [B][H][nQ][nK]
+ *   row_ptr           out, int32 [R+1], R = nQ if mask_head_stride == 0 and
+ *                     skip == NULL (one list for all (b, h)), else B*H*nQ
+ *   kv_idx            out, int32 [kv_capacity]
+ *   nnz_host          nullable host pointer. When given, the call counts the
+ *                     kept tiles, synchronises the stream, stores the count and
+ *                     returns BSA_ERR_CAPACITY without writing kv_idx if it
+ *                     exceeds kv_capacity. When NULL, kv_capacity must be at
+ *                     least R*nK (the worst case) or BSA_ERR_CAPACITY is
+ *                     returned before anything is enqueued.
+ * Exact integer work; lists are in ascending key-block order.
+ */
+BSA_API bsa_status bsa_compact_block_lists(const bsa_shape* s, const uint8_t* mask,
+                                   int64_t mask_head_stride, const uint8_t* skip,
+                                   int32_t* row_ptr, int32_t* kv_idx, int64_t kv_capacity,
+                                   int64_t* nnz_host, void* stream);
+
+/*
+ * Block-sparse attention forward ([PSA]: whole blocks are kept or dropped;
+ * [Lite] section 六: online softmax over the tiles of a persistent skip list;
+ * bidirectional, no causal mask). For query i of row block a of head (b, h),
+ * with J_i the union of the listed key blocks of that row:
+ *   s_ij = scale * q_i . k_j,  o_i = sum_{j in J_i} softmax_j(s_ij) v_j,
+ *   lse_i = log sum_{j in J_i} exp(s_ij)   (natural log).
+ * An empty list gives o_i = 0 and lse_i = -inf.
+ *   dt          BSA_BF16 (MFMA path, fp32 accumulation and softmax, O rounded
+ *               to bf16 nearest-even) or BSA_F32 (fp32 path)
+ *   q, k, v     inputs; o output, same dtype
+ *   lse         nullable, out fp32 [B][H][N]
+ *   row_ptr, kv_idx  lists as produced by bsa_compact_block_lists; both NULL
+ *               means every tile (dense attention)
+ *   lists_shared 1: one list row per a for every (b, h) (row_ptr [nQ+1]);
+ *               0: row_ptr [B*H*nQ+1]
+ *   tile_gap    nullable, out fp32, one value per list entry (per (b, h) and
+ *               list entry when lists_shared: index (b*H + h)*nnz + e):
+ *               with the listed tiles of a row visited in list order and
+ *               m_run(r) the running maximum of row r's scaled scores over
+ *               the tiles visited before, the maximum over valid rows r of
+ *               (max_{j in tile} s_rj - m_run(r)) in log2 units
+ *               (scores times log2(e)); +inf for the first tile of a row
+ *               ([Lite] section 五: a tile far below the accumulated maximum
+ *               contributes exponentially little).
+ * Q, K, V must not alias O.
+ */
+BSA_API bsa_status bsa_sparse_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, bsa_tensor k,
+                               bsa_tensor v, bsa_tensor o, float* lse, const int32_t* row_ptr,
+                               const int32_t* kv_idx, int32_t lists_shared, float scale,
+                               float* tile_gap, void* stream);
+
+/*
+ * Carry the skip decisions forward ([Lite] sections 二, 三 and 六: decide
+ * early, then reuse the decisions for every later denoising step; the skip
+ * set only grows). For every entry e of list row r = (b*H + h)*nQ + a:
+ *   skip[r*nK + kv_idx[e]] |= (tile_gap[e] <= -tau2),  tau2 = fp32(tau * log2(e)),
+ * with tau > 0 in natural-log units of the scaled scores.
+ *   row_ptr, kv_idx  per-head lists (B*H*nQ rows), as used by the forward call
+ *                    that produced tile_gap
+ *   skip             in/out, [B][H][nQ][nK]
+ */
+BSA_API bsa_status bsa_update_skip_mask(const bsa_shape* s, const int32_t* row_ptr,
+                                const int32_t* kv_idx, const float* tile_gap, float tau,
+                                uint8_t* skip, void* stream);
+
+/* Static text for a status code. */
+BSA_API const char* bsa_status_string(bsa_status st);
+
+/* Thread-local detail for the last non-OK return on this thread ("" if none). */
+BSA_API const char* bsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H_ */

@@ -1,0 +1,150 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/bsa.h declares, and rejects bad arguments with the documented status
+before anything is enqueued (no call here reaches a kernel launch)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_attention_flashattention_amd as bsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+INVALID, UNSUPPORTED, CAPACITY = 1, 2, 3
+P = 0x10000  # a 16-byte aligned stand-in address; validation never dereferences it
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"BSA_API\s+[\w\s\*]+?\b(bsa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bsa.LIB_PATH):
+        from block_sparse_attention_flashattention_amd import build
+        build.build()
+    return bsa.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) == 8
+    out = subprocess.run(["nm", "-D", "--defined-only", bsa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (bsa_\w+)", out))
+    assert set(names) <= exported
+    for n in names:
+        getattr(L, n)
+
+
+def T(ptr=P, sb=0, sn=128, sh=128):
+    return bsa.Tensor(ptr, sb, sn, sh)
+
+
+def S(**kw):
+    base = dict(batch=1, heads=2, head_dim=128, frames=3, height=5, width=7, block_q=128,
+                block_k=64)
+    base.update(kw)
+    return bsa.Shape(*[base[k] for k in ("batch", "heads", "head_dim", "frames", "height",
+                                          "width", "block_q", "block_k")])
+
+
+def fwd(L, s, q=None, k=None, v=None, o=None, dt=0, row_ptr=None, kv_idx=None, shared=0,
+        scale=0.1, gap=None):
+    return L.bsa_sparse_attn_fwd(C.byref(s), dt, q or T(), k or T(P + 256), v or T(P + 512),
+                                 o or T(P + 1024), None, row_ptr, kv_idx, shared, scale, gap,
+                                 None)
+
+
+def test_status_strings(L):
+    for st in range(5):
+        assert bsa.bsa_status_string(st)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), UNSUPPORTED), (dict(head_dim=0), INVALID), (dict(block_q=32), UNSUPPORTED),
+    (dict(block_k=128), UNSUPPORTED), (dict(batch=-1), INVALID), (dict(frames=-2), INVALID),
+    (dict(frames=100000, height=200, width=200), INVALID),
+])
+def test_shape_validation(L, kw, status):
+    assert fwd(L, S(**kw)) == status
+    assert bsa.bsa_last_error()
+
+
+def test_fwd_argument_validation(L):
+    s = S()
+    assert fwd(L, s, q=T(ptr=None)) == INVALID
+    assert fwd(L, s, q=T(ptr=P + 8)) == INVALID                 # misaligned
+    assert fwd(L, s, k=T(P + 256, sn=100)) == INVALID           # stride not a multiple of 8
+    assert fwd(L, s, v=T(P + 512, sh=-8)) == INVALID            # negative stride
+    assert fwd(L, s, o=T(P)) == INVALID                         # o aliases q
+    assert fwd(L, s, dt=7) == UNSUPPORTED
+    assert fwd(L, s, scale=-1.0) == INVALID
+    assert fwd(L, s, scale=float("nan")) == INVALID
+    assert fwd(L, s, row_ptr=P) == INVALID                      # lists half given
+    assert fwd(L, s, shared=2, row_ptr=P, kv_idx=P) == INVALID
+    assert fwd(L, s, gap=P) == INVALID                          # gaps need lists
+    # fp32: strides must be multiples of 4 elements
+    assert fwd(L, s, dt=1, q=T(sn=130)) == INVALID
+
+
+def test_empty_shapes_are_noops(L):
+    for kw in (dict(batch=0), dict(heads=0), dict(frames=0)):
+        assert fwd(L, S(**kw), q=T(ptr=None)) == 0
+
+
+def test_radial_validation(L):
+    s = S()
+    assert L.bsa_build_mask_radial(C.byref(s), 31, 2, P, None) == INVALID   # h0 < Bk/2
+    assert L.bsa_build_mask_radial(C.byref(s), 64, 1, P, None) == INVALID   # base < 2
+    assert L.bsa_build_mask_radial(C.byref(s), 64, 2, None, None) == INVALID
+    assert L.bsa_build_mask_radial(C.byref(S(head_dim=80)), 64, 2, P, None) == UNSUPPORTED
+
+
+def test_pooled_validation(L):
+    s = S()
+    need = L.bsa_pooled_workspace_bytes(C.byref(s))
+    B, H, D, nQ, nK = 1, 2, 128, 1, 2
+    assert need == 8 * (B * H * (nQ + nK) * D + B * H * nQ * nK)
+
+    def call(mode=1, param=0.5, ws=P, wsb=need, mask=P, dt=0, shape=s, scale=0.1):
+        return L.bsa_build_mask_pooled(C.byref(shape), dt, T(), T(P + 256), scale, mode, param,
+                                       mask, ws, wsb, None)
+    assert call(mode=2) == INVALID
+    assert call(mode=1, param=0.0) == INVALID
+    assert call(mode=1, param=1.5) == INVALID
+    assert call(mode=0, param=0.0) == INVALID
+    assert call(mode=0, param=2.5) == INVALID
+    assert call(wsb=need - 8) == INVALID
+    assert call(ws=None) == INVALID
+    assert call(ws=P + 64) == INVALID          # workspace alignment
+    assert call(mask=None) == INVALID
+    assert call(scale=float("inf")) == INVALID
+    assert call(dt=3) == UNSUPPORTED
+    big = S(frames=33, height=100, width=100)   # 330,000 tokens -> 5,157 key blocks
+    assert call(shape=big) == UNSUPPORTED
+
+
+def test_compaction_validation(L):
+    s = S()
+    nQ, nK = 1, 2
+    def call(mhs=0, skip=None, row_ptr=P, kv_idx=P, cap=4, nnz=None):
+        return L.bsa_compact_block_lists(C.byref(s), P, mhs, skip, row_ptr, kv_idx, cap, nnz, None)
+    assert call(mhs=1) == INVALID                 # 0 < stride < nQ*nK
+    assert call(row_ptr=None) == INVALID
+    assert call(cap=-1) == INVALID
+    assert call(cap=nQ * nK - 1) == CAPACITY      # shared list, worst case not covered
+    assert call(mhs=nQ * nK, skip=P, cap=2 * nQ * nK - 1) == CAPACITY
+
+
+def test_skip_update_validation(L):
+    s = S()
+    assert L.bsa_update_skip_mask(C.byref(s), P, P, P, 0.0, P, None) == INVALID
+    assert L.bsa_update_skip_mask(C.byref(s), P, P, P, float("nan"), P, None) == INVALID
+    assert L.bsa_update_skip_mask(C.byref(s), None, P, P, 10.0, P, None) == INVALID
+    assert L.bsa_update_skip_mask(C.byref(s), P, P, P, 10.0, None, None) == INVALID
