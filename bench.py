@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse video attention hot path on one MI355X.
+
+One step is one pass of the whole path over one synthetic layer input, with
+inputs already resident in HBM:
+  radial workloads: build_mask_radial -> compact_block_lists -> sparse_attn_fwd
+  pooled workload:  build_mask_pooled -> compact_block_lists -> sparse_attn_fwd
+  skip workload:    compact_block_lists (all tiles minus carried skips)
+                    -> sparse_attn_fwd (with tile gaps) -> update_skip_mask,
+                    one denoising step per bench step (cycling the 10 steps)
+Prints one JSON line: computed-tile TFLOP/s of the step, the forward kernel's
+ms per call and % of the bf16 MFMA peak, the roofline of the forward kernel
+(timed with HIP events on the stream it runs on) and the fp64 CPU oracle
+timed on a bounded sample of the same workload.
+
+    python bench.py [--steps 20] [--warmup 3] [--workload wan14b_720p]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse_attn_fwd ms/call + computed-tile TFLOPS as % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_flashattention_amd", "csrc",
+                          "attn_bf16.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def tile_flops(row_ptr: np.ndarray, kv_idx: np.ndarray, N: int, Bq: int, Bk: int, d: int,
+               nQ: int, reps: int) -> float:
+    """4 d |R_a| |C_c| summed over listed tiles (true ragged sizes), times reps
+    (the (b, h) pairs a shared list serves)."""
+    rows = np.repeat(np.arange(len(row_ptr) - 1), np.diff(row_ptr))
+    a = rows % nQ
+    ra = np.minimum(N, (a + 1) * Bq) - a * Bq
+    cc = np.minimum(N, (kv_idx.astype(np.int64) + 1) * Bk) - kv_idx.astype(np.int64) * Bk
+    return 4.0 * d * float(np.sum(ra * cc)) * reps
+
+
+def source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(workload: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_sha() or t.get("workload") != workload:
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan14b_720p")
+    ap.add_argument("--cpu-rows", type=int, default=192,
+                    help="row blocks in the CPU oracle sample (0 = skip)")
+    ap.add_argument("--no-dense", action="store_true", help="skip the all-tiles timing")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads would shard across GPUs with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_flashattention_amd as bsa
+    import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4}))
+        return
+
+    w = synth.workload(args.workload)
+    log(f"workload {w.name}: B={w.B} H={w.H} d={w.d} grid {w.T}x{w.Hs}x{w.Ws} N={w.N} "
+        f"Bq={w.Bq} Bk={w.Bk} mask={w.mask}")
+    t0 = time.time()
+    x = synth.make_qkv(w, step=0 if w.mask == "skip" else None)
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    s = bsa.shape(w.B, w.H, w.d, w.T, w.Hs, w.Ws, w.Bq, w.Bk)
+    nQ, nK, BH = s.nQ, s.nK, w.B * w.H
+    o = torch.empty_like(q)
+    lse = torch.empty(BH * w.N, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    shared = 1 if w.mask == "radial" else 0
+    R = nQ if shared else BH * nQ
+    mask = torch.empty((nQ * nK) if shared else (BH * nQ * nK), dtype=torch.uint8, device=dev)
+    row_ptr = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    kv_idx = torch.empty(R * nK, dtype=torch.int32, device=dev)
+    ws = None
+    step_inputs = None
+    skip = gap = ones = None
+    if w.mask == "pooled":
+        ws = torch.empty(bsa.bsa_pooled_workspace_bytes(s), dtype=torch.uint8, device=dev)
+    if w.mask == "skip":
+        ones = torch.ones(nQ * nK, dtype=torch.uint8, device=dev)
+        skip = torch.zeros(BH * nQ * nK, dtype=torch.uint8, device=dev)
+        gap = torch.empty(BH * nQ * nK, dtype=torch.float32, device=dev)
+        step_inputs = [(q, k)]
+        for st in range(1, w.steps):
+            y = synth.make_step_qk(w, st)
+            step_inputs.append((to_dev(y["q"]), to_dev(y["k"])))
+        log(f"{w.steps} denoising-step inputs resident")
+
+    fwd_events = []
+    state = {"i": 0}
+
+    def step(record: bool):
+        if w.mask == "radial":
+            bsa.bsa_build_mask_radial(s, w.h0, w.beta, mask)
+            bsa.bsa_compact_block_lists(s, mask, 0, None, row_ptr, kv_idx)
+            qq, kk_ = q, k
+        elif w.mask == "pooled":
+            bsa.bsa_build_mask_pooled(s, q, k, w.scale, w.pooled_mode, w.pooled_param, mask, ws)
+            bsa.bsa_compact_block_lists(s, mask, nQ * nK, None, row_ptr, kv_idx)
+            qq, kk_ = q, k
+        else:
+            si = state["i"] % w.steps
+            if si == 0:
+                skip.zero_()
+            qq, kk_ = step_inputs[si]
+            bsa.bsa_compact_block_lists(s, ones, 0, skip, row_ptr, kv_idx)
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        bsa.bsa_sparse_attn_fwd(s, qq, kk_, v, o, lse, row_ptr, kv_idx, shared, w.scale,
+                                gap if w.mask == "skip" else None)
+        if record:
+            e1.record(stream)
+            fwd_events.append((e0, e1, state["i"] % max(1, w.steps)))
+        if w.mask == "skip":
+            bsa.bsa_update_skip_mask(s, row_ptr, kv_idx, gap, w.tau, skip)
+        state["i"] += 1
+
+    # lists of one step, for the FLOP count (outside the timed region)
+    step(False)
+    torch.cuda.synchronize()
+    per_step_flops = []
+    nsteps_distinct = w.steps if w.mask == "skip" else 1
+    state["i"] = 0
+    for si in range(nsteps_distinct):
+        rp_before = None
+        if w.mask == "skip":
+            if si == 0:
+                skip.zero_()
+            bsa.bsa_compact_block_lists(s, ones, 0, skip, row_ptr, kv_idx)
+        else:
+            step(False)
+        torch.cuda.synchronize()
+        rp = row_ptr.cpu().numpy().astype(np.int64)
+        kvh = kv_idx[:int(rp[-1])].cpu().numpy()
+        per_step_flops.append(tile_flops(rp, kvh, w.N, w.Bq, w.Bk, w.d, nQ, BH if shared else 1))
+        if w.mask == "skip":
+            state["i"] = si
+            step(False)
+    state["i"] = 0
+    nnz_tiles = int(rp[-1]) if w.mask != "skip" else None
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    fwd_events.clear()
+    state["i"] = 0
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    fwd_ms_each = [e0.elapsed_time(e1) for e0, e1, _ in fwd_events]
+    fwd_ms = float(np.mean(fwd_ms_each))
+    flops_each = [per_step_flops[si % nsteps_distinct] for _, _, si in fwd_events]
+    flops_total = float(np.sum(flops_each))
+    step_tflops = flops_total / (ms_step * args.steps * 1e-3) / 1e12
+    fwd_tflops = flops_total / (np.sum(fwd_ms_each) * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms, forward {fwd_ms:.3f} ms/call "
+        f"({fwd_tflops:.1f} TFLOP/s, {100 * fwd_tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+
+    dense_speedup = None
+    dense_ms = None
+    if not args.no_dense and w.mask != "skip":
+        reps = 2
+        bsa.bsa_sparse_attn_fwd(s, q, k, v, o, lse, None, None, 0, w.scale)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            bsa.bsa_sparse_attn_fwd(s, q, k, v, o, lse, None, None, 0, w.scale)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / reps
+        dense_speedup = dense_ms / fwd_ms
+        log(f"all tiles: {dense_ms:.3f} ms/call, dense-equivalent speedup {dense_speedup:.2f}x")
+
+    # ---- CPU baseline: the fp64 oracle on a bounded sample of the same rows
+    cpu = None
+    if args.cpu_rows > 0:
+        import oracle
+        rng = np.random.default_rng(12345)
+        if w.mask == "radial":
+            mask_h = mask.cpu().numpy().reshape(nQ, nK)
+            mhs = 0
+        else:
+            if w.mask == "skip":
+                skip.zero_()
+                bsa.bsa_compact_block_lists(s, ones, 0, skip, row_ptr, kv_idx)
+                torch.cuda.synchronize()
+                mask_h = np.ones((BH, nQ, nK), np.uint8)
+            else:
+                step(False)
+                torch.cuda.synchronize()
+                mask_h = mask.cpu().numpy().reshape(BH, nQ, nK)
+            mhs = nQ * nK
+        rows = np.sort(rng.choice(BH * nQ, size=min(args.cpu_rows, BH * nQ), replace=False))
+        rr = rows % nQ
+        ra = np.minimum(w.N, (rr + 1) * w.Bq) - rr * w.Bq
+        per_row_keys = []
+        for r in rows:
+            bh, a = divmod(int(r), nQ)
+            mrow = mask_h[a] if mhs == 0 else mask_h[bh, a]
+            cs = np.nonzero(mrow)[0]
+            per_row_keys.append(int(np.sum(np.minimum(w.N, (cs + 1) * w.Bk) - cs * w.Bk)))
+        sample_flops = 4.0 * w.d * float(np.sum(ra * np.array(per_row_keys)))
+        log(f"CPU oracle on {len(rows)} row blocks ({sample_flops / 1e9:.1f} GFLOP), "
+            f"{oracle.num_threads()} threads")
+        t0 = time.time()
+        oracle.attention(x["q"], x["k"], x["v"], w.Bq, w.Bk, w.scale, mask_h, mhs, rows=rows)
+        cpu_s = time.time() - t0
+        cpu = {"value": sample_flops / cpu_s / 1e12, "unit": "TFLOP/s",
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"{len(rows)} of {BH * nQ} row blocks of {w.name} "
+                         f"(first step's mask), {sample_flops / 1e9:.1f} GFLOP fp64 in {cpu_s:.1f} s"}
+        log(f"CPU oracle: {cpu['value'] * 1e3:.3f} GFLOP/s")
+
+    traffic = traffic_for(w.name)
+    out = {
+        "metric": METRIC,
+        "value": step_tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "ms_per_call": fwd_ms,
+        "pct_of_bf16_peak": 100.0 * fwd_tflops / PEAK_BF16_TFLOPS,
+        "dense_equiv_speedup": dense_speedup,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "head_dim": w.d,
+            "grid_T_H_W": [w.T, w.Hs, w.Ws], "tokens": w.N, "block_q": w.Bq,
+            "block_k": w.Bk, "mask": w.mask,
+            "knobs": {"h0": w.h0, "decay_base": w.beta} if w.mask == "radial" else (
+                {"mode": w.pooled_mode, "tau_p": w.pooled_param} if w.mask == "pooled"
+                else {"tau": w.tau, "steps": w.steps}),
+            "kept_tiles": nnz_tiles,
+            "tile_sparsity": (1.0 - nnz_tiles / (R * nK)) if nnz_tiles is not None else None,
+            "computed_tflop_per_call": float(np.mean(per_step_flops)) / 1e12,
+            "dense_ms_per_call": dense_ms,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": fwd_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": fwd_tflops / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    if w.mask == "skip":
+        by = {}
+        for (e0, e1, si), ms in zip(fwd_events, fwd_ms_each):
+            by.setdefault(si, []).append(ms)
+        out["per_step"] = [{"step": si, "fwd_ms": float(np.mean(by[si])) if si in by else None,
+                            "computed_tflop": per_step_flops[si] / 1e12}
+                           for si in range(nsteps_distinct)]
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

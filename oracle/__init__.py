@@ -40,6 +40,8 @@ def lib():
             build(force=False)
         L = C.CDLL(_LIB)
         i64, p, d = C.c_int64, C.c_void_p, C.c_double
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = C.c_int
         L.oracle_radial_window.argtypes = [i64, i64, i64, i64, C.POINTER(i64)]
         L.oracle_radial_window.restype = C.c_int
         L.oracle_radial_count_pairs.argtypes = [i64] * 6
@@ -56,6 +58,11 @@ def lib():
         L.oracle_attention.restype = C.c_int
         _lib = L
     return _lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(lib().oracle_num_threads())
 
 
 def _ptr(a: np.ndarray):

@@ -33,10 +33,22 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_BF16 0
 #define ORACLE_F32 1
 #define ORACLE_F64 2
+
+/* Threads the OpenMP loops below run on (reported with timings). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 static double widen(const void* base, int dtype, int64_t off) {
   if (dtype == ORACLE_BF16) {
