@@ -221,6 +221,13 @@ bsa_status bsa_sparse_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, b
   if ((st = check_tensor("o", o, eb)) != BSA_OK) return st;
   if (o.ptr == q.ptr || o.ptr == k.ptr || o.ptr == v.ptr)
     return fail(BSA_ERR_INVALID, "o must not alias q, k or v");
+  // Key/value rows of a tile are addressed with 32-bit offsets from the tile's
+  // first row and bounds-checked by byte range, which needs rows that do not
+  // overlap and a 64-row tile span below 2^31 bytes.
+  if (g.N > 1 && (k.stride_n < g.D || v.stride_n < g.D))
+    return fail(BSA_ERR_INVALID, "k and v need stride_n >= head_dim");
+  if (k.stride_n > (int64_t)(1 << 23) || v.stride_n > (int64_t)(1 << 23))
+    return fail(BSA_ERR_UNSUPPORTED, "k/v stride_n above 2^23 elements");
   bsa::AttnArgs a;
   a.q = arg(q); a.k = arg(k); a.v = arg(v);
   a.o = o.ptr; a.osb = o.stride_b; a.osn = o.stride_n; a.osh = o.stride_h;

@@ -7,26 +7,31 @@
 // ([Lite] LiteAttention summary page, sections 三 and 六). Softmax is the
 // online form in log2 units; the per-tile gap (local max minus running max)
 // feeds the carried skip mask ([Lite] section 五), reduced across waves once
-// per tile on the barrier the pipeline already has ([Lite] section 六 defers
+// per tile on a barrier the pipeline already has ([Lite] section 六 defers
 // the cross-warp reduction for the same reason).
 //
 // gfx950 mapping (one workgroup per (b, h, row block); BQ/32 waves, each wave
 // owns 32 query rows):
-//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K tile rows from LDS,
-//    B = the wave's Q rows held in registers for the whole kernel. In the
+//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K tile rows read from
+//    LDS, B = the wave's Q rows held in registers for the whole kernel. In the
 //    32x32 accumulator a lane holds one query row (lane % 32) and 16 of the
-//    32 keys of a block, so a row max is 31 in-lane maxima plus one
-//    cross-half swap (v_permlane32_swap), and row sums stay per lane half
-//    until the epilogue.
-//  * O^T = V^T P^T: the score accumulator registers, rounded to bf16, are
-//    directly the B operand (same lane -> query row); the key order inside a
-//    16-key step is permuted identically in A and B, so no data moves across
-//    lanes. V is stored transposed in LDS (Vt[d][key]) so each A operand is
-//    two 8-byte reads; the transpose happens on the way in: each thread
-//    loads 8 key rows of one dword column and repacks them with v_perm.
-//  * K/V tiles are double-buffered in LDS with register staging: the global
-//    loads of tile i+1 are issued before the MFMAs of tile i; one barrier
-//    per tile.
+//    32 keys of a block, so a row max is in-lane maxima plus one cross-half
+//    swap (v_permlane32_swap) and row sums stay per lane half until the end.
+//  * O^T = V^T P^T: the score registers, rounded to bf16, are the B operand
+//    as they stand (same lane -> query row); the A operand V^T is gathered
+//    from the row-major V tile with ds_read_b64_tr_b16 (two per MFMA), whose
+//    16-lane transpose delivers exactly the keys the score layout holds.
+//  * K and V tiles go global -> LDS with 16-byte buffer loads that write LDS
+//    directly (no register staging). A per-tile buffer resource bounds the
+//    valid rows, so the ragged last key block reads zeros in hardware. The
+//    global side is XOR-swizzled per row so both LDS read patterns (b128 for
+//    K, b64 transpose for V) are free of bank conflicts without padding.
+//  * Two LDS stages: tile i+1 streams in while tile i is computed; explicit
+//    vmcnt waits and raw s_barrier keep the prefetch in flight across the
+//    barriers.
+//  * Rescaling of O is lazy: the exponent base moves only when the row max
+//    grows by more than 2^8, which keeps p <= 256 and leaves the result exact
+//    up to rounding (numerator and denominator share the base).
 //  * Workgroup ids are remapped so consecutive row blocks of a head land on
 //    the same XCD (hardware dispatch is round-robin over the 8 XCDs), which
 //    keeps the K/V tiles neighbouring row blocks share in that XCD's L2.
@@ -41,16 +46,22 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBk = 64;
 constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;   // log2 units
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
 
 struct Bf16Params {
   const uint16_t* q;
@@ -72,95 +83,122 @@ __device__ inline float other_half(float x) {
   // v_permlane32_swap: lanes 0-31 receive lanes 32-63 and vice versa.
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                                   false, false);
-  return __uint_as_float(threadIdx.x % 64 < 32 ? r[1] : r[0]);
+  return __uint_as_float((threadIdx.x & 63) < 32 ? r[1] : r[0]);
 }
+
+// Read of list data at a wave-uniform index through the constant address
+// space, so it becomes a scalar load (counted by lgkmcnt, not vmcnt).
+__device__ inline int32_t load_uniform(const int32_t* base, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)base)[i];
+}
+
+// Value of lane 0 (an SGPR) for quantities that are uniform across the wave.
+__device__ inline int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Wait until at most n vector-memory operations of this wave are in flight.
+template <int n>
+__device__ inline void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+}
+__device__ inline void barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ inline void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// LDS layout of a 64-row tile of D bf16 per row: rows of D*2 bytes, 16-byte
+// chunk c of row r stored at chunk c ^ f(r). K uses fK (conflict-free b128
+// reads of 16 consecutive rows), V uses fV (conflict-free transpose reads of
+// 4-row x 32-byte blocks).
+template <int D>
+struct Tile {
+  static constexpr int CPR = D / 8;        // chunks per row
+  static constexpr int RB = D * 2;         // bytes per row
+  static constexpr int BYTES = kBk * RB;   // bytes per tile
+  static constexpr int RPI = 1024 / RB;    // rows per 64-lane 16-byte load
+  static constexpr int IPT = kBk / RPI;    // loads per tile
+  __device__ static int fK(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static int fV(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+};
 
 template <int D, int BQ>
 struct Cfg {
-  static constexpr int NW = BQ / 32;        // waves
-  static constexpr int NT = NW * 64;        // threads
-  static constexpr int KS = D / 16;         // k-steps of Q K^T
-  static constexpr int DB = D / 32;         // 32-wide d blocks of O
-  static constexpr int KLD = D + 8;         // K tile row stride (elements)
-  static constexpr int VLD = kBk + 4;       // V^T tile row stride (elements)
-  static constexpr int KTILE = kBk * KLD;
-  static constexpr int VTILE = D * VLD;
-  static constexpr int KCH = kBk * (D / 8) / NT;  // 16-byte K chunks per thread
-  static constexpr int VIT = 8 * (D / 2) / NT;    // 8-row V column groups per thread
-  static_assert(KCH >= 1 && VIT >= 1, "tile loader split");
-  static_assert(BQ * (D + 8) <= 2 * KTILE, "O staging must fit in the K buffers");
+  static constexpr int NW = BQ / 32;                 // waves
+  static constexpr int NT = NW * 64;                 // threads
+  static constexpr int KS = D / 16;                  // k-steps of Q K^T
+  static constexpr int DB = D / 32;                  // 32-wide d blocks of O
+  static constexpr int LPW = Tile<D>::IPT / NW;      // loads per tile per wave, each of K and V
+  static constexpr int STAGE = 2 * Tile<D>::BYTES;   // K + V
+  static constexpr int SMEM = 2 * STAGE;             // two stages
+  static constexpr int OLD = D + 8;                  // O staging row stride (elements)
+  static_assert(LPW >= 1, "tile loader split");
+  static_assert(BQ * OLD * 2 <= SMEM, "O staging must fit in the stages");
+};
+
+// Per-lane constants of the direct loads of one tile: voffset of each of this
+// wave's LPW loads, for K (swizzle fK) and V (swizzle fV).
+template <int D, int BQ>
+struct LoadPlan {
+  uint32_t k[Cfg<D, BQ>::LPW];
+  uint32_t v[Cfg<D, BQ>::LPW];
 };
 
 template <int D, int BQ>
-struct Stage {
-  u32x4 k[Cfg<D, BQ>::KCH];
-  uint32_t v[Cfg<D, BQ>::VIT][8];
-};
-
-template <int D, int BQ>
-__device__ inline void load_tile(const Bf16Params& p, const uint16_t* kbase,
-                                 const uint16_t* vbase, int64_t c, int tid,
-                                 Stage<D, BQ>& st) {
+__device__ inline void make_plan(LoadPlan<D, BQ>& lp, int w, int lane, int64_t ksn, int64_t vsn) {
+  using T = Tile<D>;
   using C = Cfg<D, BQ>;
-  const int64_t j0 = c * kBk;
 #pragma unroll
-  for (int i = 0; i < C::KCH; ++i) {
-    const int id = tid + i * C::NT;
-    const int r = id / (D / 8), c8 = id % (D / 8);
-    const int64_t kv = j0 + r;
-    st.k[i] = kv < p.N ? *(const u32x4*)(kbase + kv * p.ksn + c8 * 8) : u32x4{0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int it = 0; it < C::VIT; ++it) {
-    const int id = tid + it * C::NT;
-    const int g8 = id / (D / 2), pc = id % (D / 2);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int64_t kv = j0 + g8 * 8 + r;
-      st.v[it][r] = kv < p.N ? *(const uint32_t*)(vbase + kv * p.vsn + 2 * pc) : 0u;
-    }
+  for (int i = 0; i < C::LPW; ++i) {
+    const int idx = w + C::NW * i;
+    const int r = T::RPI * idx + lane / T::CPR;
+    const int phys = lane % T::CPR;
+    lp.k[i] = (uint32_t)(r * ksn * 2 + (phys ^ T::fK(r)) * 16);
+    lp.v[i] = (uint32_t)(r * vsn * 2 + (phys ^ T::fV(r)) * 16);
   }
 }
 
 template <int D, int BQ>
-__device__ inline void store_tile(uint16_t* Ks, uint16_t* Vt, int tid, const Stage<D, BQ>& st) {
+__device__ inline void issue_tile(const LoadPlan<D, BQ>& lp, const uint16_t* kbase,
+                                  const uint16_t* vbase, int64_t ksn, int64_t vsn, int64_t c,
+                                  int64_t N, char* stage, int w) {
+  using T = Tile<D>;
   using C = Cfg<D, BQ>;
+  const int64_t j0 = c * kBk;
+  const int64_t rows = min((int64_t)kBk, N - j0);
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(kbase + j0 * ksn), 0, (int)(rows * ksn * 2), kRsrcWord3);
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(vbase + j0 * vsn), 0, (int)(rows * vsn * 2), kRsrcWord3);
 #pragma unroll
-  for (int i = 0; i < C::KCH; ++i) {
-    const int id = tid + i * C::NT;
-    const int r = id / (D / 8), c8 = id % (D / 8);
-    *(u32x4*)(Ks + r * C::KLD + c8 * 8) = st.k[i];
+  for (int i = 0; i < C::LPW; ++i) {
+    const int idx = w + C::NW * i;
+    const uint32_t off = lp.k[i];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + idx * 1024), 16, off, 0, 0,
+                                             0);
   }
 #pragma unroll
-  for (int it = 0; it < C::VIT; ++it) {
-    const int id = tid + it * C::NT;
-    const int g8 = id / (D / 2), pc = id % (D / 2);
-    u32x4 lo, hi;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t x = st.v[it][2 * w], y = st.v[it][2 * w + 1];
-      lo[w] = __builtin_amdgcn_perm(y, x, 0x05040100u);  // low halves: column 2*pc
-      hi[w] = __builtin_amdgcn_perm(y, x, 0x07060302u);  // high halves: column 2*pc+1
-    }
-    uint16_t* r0 = Vt + (2 * pc) * C::VLD + g8 * 8;
-    uint16_t* r1 = r0 + C::VLD;
-    *(u32x2*)(r0) = u32x2{lo[0], lo[1]};
-    *(u32x2*)(r0 + 4) = u32x2{lo[2], lo[3]};
-    *(u32x2*)(r1) = u32x2{hi[0], hi[1]};
-    *(u32x2*)(r1 + 4) = u32x2{hi[2], hi[3]};
+  for (int i = 0; i < C::LPW; ++i) {
+    const int idx = w + C::NW * i;
+    const uint32_t off = lp.v[i];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + T::BYTES + idx * 1024), 16,
+                                             off, 0, 0, 0);
   }
+}
+
+__device__ inline bf16x8 join(i16x4 lo, i16x4 hi) {
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
 }
 
 template <int D, int BQ, bool GAP>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p) {
   using C = Cfg<D, BQ>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::KTILE];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][C::VTILE];
+  using T = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
   __shared__ float gp[2][C::NW];
 
   const int tid = threadIdx.x;
-  const int lane = tid % 64, w = tid / 64;
-  const int n = lane % 32, hh = lane / 32;
+  const int lane = tid & 63;
+  const int w = wave_uniform(tid >> 6);
+  const int n = lane & 31, hh = lane >> 5;
 
   // XCD-aware remap: hardware sends workgroup x to XCD x % 8; give each XCD a
   // contiguous range of (head, row block) ids.
@@ -170,94 +208,127 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
   const int64_t bh = row / p.nQ, a = row - bh * p.nQ;
   const int64_t b = bh / p.H, h = bh - b * p.H;
 
-  // Q rows of this wave as MFMA B operands (k-slice hh*8..+7 of each 16-step).
-  const int64_t qrow = a * BQ + w * 32 + n;
-  const bool qvalid = qrow < p.N;
-  bf16x8 qf[C::KS];
-  {
-    const uint16_t* qp = p.q + b * p.qsb + qrow * p.qsn + h * p.qsh + hh * 8;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 raw = qvalid ? *(const u32x4*)(qp + ks * 16) : u32x4{0, 0, 0, 0};
-      qf[ks] = __builtin_bit_cast(bf16x8, raw);
-    }
-  }
-
   int64_t e0 = 0, e1 = p.nK, gbase = 0;
   if (p.row_ptr) {
     const int64_t lr = p.lists_shared ? a : row;
-    e0 = p.row_ptr[lr];
-    e1 = p.row_ptr[lr + 1];
-    if (GAP && p.lists_shared) gbase = bh * (int64_t)p.row_ptr[p.nQ];
+    e0 = load_uniform(p.row_ptr, lr);
+    e1 = load_uniform(p.row_ptr, lr + 1);
+    if (GAP && p.lists_shared) gbase = bh * (int64_t)load_uniform(p.row_ptr, p.nQ);
   }
   const int64_t L = e1 - e0;
   const uint16_t* kbase = p.k + b * p.ksb + h * p.ksh;
   const uint16_t* vbase = p.v + b * p.vsb + h * p.vsh;
 
+  // Key block of list entry e0 + i (uniform scalar loads).
+  auto block_of = [&](int64_t i) -> int64_t {
+    return p.row_ptr ? (int64_t)load_uniform(p.kv_idx, e0 + i) : e0 + i;
+  };
+  LoadPlan<D, BQ> lp;
+  make_plan<D, BQ>(lp, w, lane, p.ksn, p.vsn);
+  int64_t c_cur = L > 0 ? block_of(0) : 0;
+  int64_t c_nxt = L > 1 ? block_of(1) : 0;
+  if (L > 0) issue_tile<D, BQ>(lp, kbase, vbase, p.ksn, p.vsn, c_cur, p.N, smem, w);
+
+  // Q rows of this wave as MFMA B operands (k-slice hh*8..+7 of each 16-step).
+  const int64_t qrow = a * BQ + w * 32 + n;
+  const bool qvalid = qrow < p.N;
+  bf16x8 qf[C::KS];
+  {
+    const uint16_t* qp = p.q + b * p.qsb + (qvalid ? qrow : 0) * p.qsn + h * p.qsh + hh * 8;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4 raw = *(const u32x4*)(qp + ks * 16);
+      if (!qvalid) raw = u32x4{0, 0, 0, 0};
+      qf[ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  // LDS read offsets (bytes within a tile). K operand of key block kb at
+  // k-step ks: row kb*32 + n, logical chunk 2*ks + hh. V^T operand of d block
+  // db: lane group g = lane/16 reads rows 4*(g/2) + (lane%16)/4 (+ key base)
+  // and element column 32*db + 16*(g%2) + 4*(lane%4).
+  uint32_t koff[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = n * T::RB + (((2 * ks + hh) ^ T::fK(n)) * 16);
+  uint32_t voff[C::DB];
+  {
+    const int g = lane >> 4, s = lane & 15, kr = s >> 2, j = s & 3;
+    const int r = 4 * (g >> 1) + kr;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int colb = 2 * (32 * db + 16 * (g & 1) + 4 * j);
+      voff[db] = r * T::RB + (((colb >> 4) ^ T::fV(r)) * 16) + (colb & 15);
+    }
+  }
+
   f32x16 oacc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;  // log2 units
-  float l_lane = 0.f;       // this lane half's share of the row sum
-
-  Stage<D, BQ> stg;
-  if (L > 0) {
-    load_tile<D, BQ>(p, kbase, vbase, p.row_ptr ? p.kv_idx[e0] : e0, tid, stg);
-    store_tile<D, BQ>(Ks[0], Vt[0], tid, stg);
-  }
-  __syncthreads();
+  float m_use = -INFINITY;   // exponent base of p and l (log2 units)
+  float m_true = -INFINITY;  // running row max (log2 units), for the tile gaps
+  float l_lane = 0.f;        // this lane half's share of the row sum
 
   for (int64_t it = 0; it < L; ++it) {
-    const int buf = (int)(it & 1);
-    const int64_t c = p.row_ptr ? p.kv_idx[e0 + it] : e0 + it;
-    const bool has_next = it + 1 < L;
-    if (has_next)
-      load_tile<D, BQ>(p, kbase, vbase, p.row_ptr ? p.kv_idx[e0 + it + 1] : e0 + it + 1, tid,
-                       stg);
+    char* cur = smem + (it & 1) * C::STAGE;
+    const int64_t c = c_cur;
+    if (it + 1 < L) {
+      issue_tile<D, BQ>(lp, kbase, vbase, p.ksn, p.vsn, c_nxt, p.N,
+                        smem + ((it + 1) & 1) * C::STAGE, w);
+      wait_vmcnt<2 * C::LPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    c_cur = c_nxt;
+    if (it + 2 < L) c_nxt = block_of(it + 2);
+    barrier();  // every wave's loads of tile `it` have landed
 
     // ---- S^T = K Q^T for the 64 keys of the tile (two 32-key blocks).
-    const uint16_t* ks_ = Ks[buf];
+    const char* kt = cur;
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 av = *(const bf16x8*)(ks_ + (kb * 32 + n) * C::KLD + ks * 16 + hh * 8);
+        const bf16x8 av = *(const bf16x8*)(kt + koff[ks] + kb * 32 * T::RB);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sacc[kb], 0, 0, 0);
       }
     }
 
     // ---- online softmax. Lane value j of block kb is key
     // kb*32 + 8*(j/4) + 4*hh + j%4 of the tile.
-    const bool ragged = (c + 1) * kBk > p.N;
-    const int64_t jv = p.N - c * kBk;  // valid keys in this tile
-    float mloc = -INFINITY;
-    if (!ragged) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mloc = fmaxf(mloc, sacc[kb][j]);
-    } else {
+    const int jv = (int)min((int64_t)kBk, p.N - c * kBk);  // valid keys in this tile
+    if (jv < kBk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = kb * 32 + 8 * (j / 4) + 4 * hh + (j % 4);
-          if (key < jv) mloc = fmaxf(mloc, sacc[kb][j]);
+          if (key >= jv) sacc[kb][j] = -INFINITY;
         }
     }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mloc = fmaxf(mloc, sacc[kb][j]);
     mloc = fmaxf(mloc, other_half(mloc));
     const float m_loc2 = mloc * p.sl2;
     if (GAP) {
-      float g = qvalid ? m_loc2 - m_run : -INFINITY;
+      float g = qvalid ? m_loc2 - m_true : -INFINITY;
 #pragma unroll
       for (int off = 16; off >= 1; off >>= 1) g = fmaxf(g, __shfl_xor(g, off, 32));
-      if (lane == 0) gp[buf][w] = g;
+      if (lane == 0) gp[it & 1][w] = g;
+      m_true = fmaxf(m_true, m_loc2);
     }
-    const float m_new = fmaxf(m_run, m_loc2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float rs = 0.f;
+    if (__builtin_amdgcn_ballot_w64(m_loc2 > m_use + kRescaleSlack)) {
+      const float m_new = fmaxf(m_use, m_loc2);
+      const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
+      m_use = m_new;
+      l_lane *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+    }
+    const float neg_m = -m_use;
     bf16x8 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -265,50 +336,45 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
       for (int half = 0; half < 2; ++half) {
         f32x8 pv;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int j = half * 8 + t;
-          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j], p.sl2, -m_new));
-          if (ragged) {
-            const int key = kb * 32 + 8 * (j / 4) + 4 * hh + (j % 4);
-            pr = key < jv ? pr : 0.f;
-          }
-          rs += pr;
-          pv[t] = pr;
-        }
+        for (int t = 0; t < 8; ++t)
+          pv[t] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][half * 8 + t], p.sl2, neg_m));
         pb[kb][half] = __builtin_convertvector(pv, bf16x8);
+#pragma unroll
+        for (int t = 0; t < 8; t += 2)
+          l_lane = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[kb][half][t], pb[kb][half][t + 1]},
+                                                   bf16x2{(__bf16)1.0f, (__bf16)1.0f}, l_lane,
+                                                   false);
       }
     }
-    l_lane = l_lane * alpha + rs;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
 
     // ---- O^T += V^T P^T. For the 16-key step (kb, half) the B operand is
     // pb[kb][half]; element t of lane half hh is key
-    // kb*32 + 16*half + 8*(t/4) + 4*hh + t%4, so the A operand reads those
-    // keys of Vt row d: two runs of four.
-    const uint16_t* vt = Vt[buf];
+    // kb*32 + 16*half + 8*(t/4) + 4*hh + t%4, which two transpose reads of
+    // the V tile deliver in that order.
+    const char* vt = cur + T::BYTES;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int kbase_ = kb * 32 + 16 * half + 4 * hh;
+        const int kofs = (kb * 32 + 16 * half) * T::RB;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const uint16_t* rp = vt + (db * 32 + n) * C::VLD + kbase_;
-          const u32x2 lo = *(const u32x2*)(rp);
-          const u32x2 hi = *(const u32x2*)(rp + 8);
-          const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb][half], oacc[db], 0, 0, 0);
+          const i16x4 lo =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[db] + kofs));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vt + voff[db] + kofs + 8 * T::RB));
+          oacc[db] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(lo, hi), pb[kb][half], oacc[db], 0, 0, 0);
         }
       }
     }
 
-    if (has_next) store_tile<D, BQ>(Ks[buf ^ 1], Vt[buf ^ 1], tid, stg);
-    __syncthreads();
+    if (GAP) wait_lds();
+    barrier();  // every wave is done with this stage (it is refilled next iteration)
     if (GAP && tid == 0) {
-      float g = gp[buf][0];
+      float g = gp[it & 1][0];
 #pragma unroll
-      for (int x = 1; x < C::NW; ++x) g = fmaxf(g, gp[buf][x]);
+      for (int x = 1; x < C::NW; ++x) g = fmaxf(g, gp[it & 1][x]);
       p.tile_gap[gbase + e0 + it] = g;
     }
   }
@@ -316,9 +382,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
   // ---- epilogue: O = O^T / l through LDS for coalesced 16-byte stores.
   const float l_tot = l_lane + other_half(l_lane);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  __syncthreads();
-  uint16_t* Os = &Ks[0][0];
-  constexpr int OLD = D + 8;
+  uint16_t* Os = (uint16_t*)smem;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
@@ -327,20 +391,22 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
 #pragma unroll
       for (int t = 0; t < 4; ++t) tmp[t] = oacc[db][4 * j4 + t] * inv;
       const bf16x4 ov = __builtin_convertvector(tmp, bf16x4);
-      *(bf16x4*)(Os + (w * 32 + n) * OLD + db * 32 + 8 * j4 + 4 * hh) = ov;
+      *(bf16x4*)(Os + (w * 32 + n) * C::OLD + db * 32 + 8 * j4 + 4 * hh) = ov;
     }
   }
-  __syncthreads();
+  wait_lds();
+  barrier();
   uint16_t* obase = p.o + b * p.osb + h * p.osh;
 #pragma unroll
   for (int i = 0; i < BQ * (D / 8) / C::NT; ++i) {
     const int id = tid + i * C::NT;
     const int r = id / (D / 8), c8 = id % (D / 8);
     const int64_t orow = a * BQ + r;
-    if (orow < p.N) *(u32x4*)(obase + orow * p.osn + c8 * 8) = *(const u32x4*)(Os + r * OLD + c8 * 8);
+    if (orow < p.N)
+      *(u32x4*)(obase + orow * p.osn + c8 * 8) = *(const u32x4*)(Os + r * C::OLD + c8 * 8);
   }
   if (p.lse && hh == 0 && qvalid)
-    p.lse[bh * p.N + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    p.lse[bh * p.N + qrow] = l_tot > 0.f ? (m_use + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <int D, int BQ>

@@ -182,7 +182,7 @@ BSA_API bsa_status bsa_compact_block_lists(const bsa_shape* s, const uint8_t* ma
  *               (scores times log2(e)); +inf for the first tile of a row
  *               ([Lite] section 五: a tile far below the accumulated maximum
  *               contributes exponentially little).
- * Q, K, V must not alias O.
+ * Q, K, V must not alias O. K and V need head_dim <= stride_n <= 2^23.
  */
 BSA_API bsa_status bsa_sparse_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, bsa_tensor k,
                                bsa_tensor v, bsa_tensor o, float* lse, const int32_t* row_ptr,

@@ -83,6 +83,8 @@ def test_fwd_argument_validation(L):
     assert fwd(L, s, k=T(P + 256, sn=100)) == INVALID           # stride not a multiple of 8
     assert fwd(L, s, v=T(P + 512, sh=-8)) == INVALID            # negative stride
     assert fwd(L, s, o=T(P)) == INVALID                         # o aliases q
+    assert fwd(L, s, k=T(P + 256, sn=64)) == INVALID            # rows overlap
+    assert fwd(L, s, v=T(P + 512, sn=1 << 24)) == UNSUPPORTED   # tile span too large
     assert fwd(L, s, dt=7) == UNSUPPORTED
     assert fwd(L, s, scale=-1.0) == INVALID
     assert fwd(L, s, scale=float("nan")) == INVALID
