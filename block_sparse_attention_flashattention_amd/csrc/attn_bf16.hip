@@ -58,6 +58,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBk = 64;
 constexpr int kXcds = 8;
+constexpr int kBand = 2;  // row-block slots per position band
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
@@ -77,6 +78,8 @@ struct Bf16Params {
   float sl2;  // scale * log2(e)
   int64_t N, nQ, nK;
   int32_t H;
+  int32_t T, U;   // frames; row-block slots per frame (ceil(F / BQ))
+  int64_t F;      // tokens per frame
 };
 
 __device__ inline float other_half(float x) {
@@ -200,12 +203,32 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
   const int w = wave_uniform(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
 
-  // XCD-aware remap: hardware sends workgroup x to XCD x % 8; give each XCD a
-  // contiguous range of (head, row block) ids.
+  // Workgroup -> (head, row block). Hardware dispatch sends workgroup x to
+  // XCD x % 8; each XCD gets a contiguous range of the order below, so the
+  // row blocks it runs together share their K/V tiles in its L2. Within a
+  // head the order is position-major: bands of kBand row-block slots per
+  // frame, all frames of a band before the next band. Row blocks at the same
+  // in-frame position in different frames visit the same key frames in the
+  // same ascending order, so concurrently running ones reuse each other's
+  // tiles while they are still cached.
   const int64_t G = gridDim.x, wg = blockIdx.x;
   const int64_t xcd = wg % kXcds, kk = wg / kXcds, q8 = G / kXcds, r8 = G % kXcds;
-  const int64_t row = xcd * q8 + min(xcd, r8) + kk;  // (b*H + h)*nQ + a
-  const int64_t bh = row / p.nQ, a = row - bh * p.nQ;
+  const int64_t lid = xcd * q8 + min(xcd, r8) + kk;
+  const int64_t per_head = p.U ? (int64_t)p.T * p.U : p.nQ;
+  const int64_t bh = lid / per_head;
+  int64_t a = lid - bh * per_head;  // plain order when frames are tiny (U == 0)
+  if (p.U) {
+    const int64_t r = lid - bh * per_head;
+    const int64_t nb = (p.U + kBand - 1) / kBand;
+    const int64_t band = min(r / ((int64_t)p.T * kBand), nb - 1);
+    const int64_t r2 = r - band * p.T * kBand;
+    const int64_t bw = band == nb - 1 ? p.U - band * kBand : kBand;
+    const int64_t t = r2 / bw, u = band * kBand + (r2 - t * bw);
+    const int64_t f0 = (t * p.F + BQ - 1) / BQ, f1 = ((t + 1) * p.F + BQ - 1) / BQ;
+    if (u >= f1 - f0) return;  // this frame has fewer row blocks than slots
+    a = f0 + u;
+  }
+  const int64_t row = bh * p.nQ + a;  // list row when lists are per head
   const int64_t b = bh / p.H, h = bh - b * p.H;
 
   int64_t e0 = 0, e1 = p.nK, gbase = 0;
@@ -411,7 +434,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
 
 template <int D, int BQ>
 hipError_t launch(const Geom& g, const Bf16Params& p, hipStream_t st) {
-  const int64_t rows = (int64_t)g.B * g.H * g.nQ;
+  const int64_t rows = (int64_t)g.B * g.H * (p.U ? (int64_t)g.T * p.U : g.nQ);
   if (p.tile_gap)
     hipLaunchKernelGGL((attn_bf16_kernel<D, BQ, true>), dim3((unsigned)rows),
                        dim3(Cfg<D, BQ>::NT), 0, st, p);
@@ -441,6 +464,8 @@ hipError_t launch_attn_bf16(const Geom& g, const AttnArgs& a, hipStream_t st) {
   p.lists_shared = a.lists_shared;
   p.sl2 = a.scale * kLog2e;
   p.N = g.N; p.nQ = g.nQ; p.nK = g.nK; p.H = g.H;
+  p.T = g.T; p.F = g.F; p.U = (int32_t)((g.F + g.Bq - 1) / g.Bq);
+  if ((int64_t)g.T * p.U > g.nQ + g.nQ / 4) p.U = 0;  // tiny frames: plain row order
   if (g.D == 64) return g.Bq == 64 ? launch<64, 64>(g, p, st) : launch<64, 128>(g, p, st);
   return g.Bq == 64 ? launch<128, 64>(g, p, st) : launch<128, 128>(g, p, st);
 }
