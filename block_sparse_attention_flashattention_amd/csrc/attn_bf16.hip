@@ -6,9 +6,10 @@
 // block, so a dropped tile costs no load, no softmax and no MFMA
 // ([Lite] LiteAttention summary page, sections 三 and 六). Softmax is the
 // online form in log2 units; the per-tile gap (local max minus running max)
-// feeds the carried skip mask ([Lite] section 五), reduced across waves once
-// per tile on a barrier the pipeline already has ([Lite] section 六 defers
-// the cross-warp reduction for the same reason).
+// feeds the carried skip mask ([Lite] section 五); the cross-wave part of
+// that reduction is an order-independent atomic max per tile, so no wave
+// waits on another for it ([Lite] section 六 defers the cross-warp
+// reduction for the same reason).
 //
 // gfx950 mapping (one workgroup per (b, h, row block); BQ/32 waves, each wave
 // owns 32 query rows):
@@ -26,15 +27,17 @@
 //    valid rows, so the ragged last key block reads zeros in hardware. The
 //    global side is XOR-swizzled per row so both LDS read patterns (b128 for
 //    K, b64 transpose for V) are free of bank conflicts without padding.
-//  * Two LDS stages: tile i+1 streams in while tile i is computed; explicit
-//    vmcnt waits and raw s_barrier keep the prefetch in flight across the
-//    barriers.
+//  * Software pipeline, one barrier per tile. While the exponentials of tile
+//    i run on the VALU, the matrix core computes the scores of tile i+1;
+//    while it accumulates P_i V_i, the VALU reduces the row maxima of tile
+//    i+1. K is three LDS stages deep (tile i+3 is requested while tile i+1
+//    is read), V two (tile i+1 is requested while tile i is read): 80 KiB,
+//    two workgroups per CU.
 //  * Rescaling of O is lazy: the exponent base moves only when the row max
 //    grows by more than 2^8, which keeps p <= 256 and leaves the result exact
 //    up to rounding (numerator and denominator share the base).
-//  * Workgroup ids are remapped so consecutive row blocks of a head land on
-//    the same XCD (hardware dispatch is round-robin over the 8 XCDs), which
-//    keeps the K/V tiles neighbouring row blocks share in that XCD's L2.
+//  * Workgroup ids are remapped so the row blocks an XCD runs together share
+//    K/V tiles in its L2 (see the mapping in the kernel).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -59,6 +62,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kBk = 64;
 constexpr int kXcds = 8;
 constexpr int kBand = 2;  // row-block slots per position band
+constexpr int kKStages = 3;
+constexpr int kVStages = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
@@ -78,8 +83,8 @@ struct Bf16Params {
   float sl2;  // scale * log2(e)
   int64_t N, nQ, nK;
   int32_t H;
-  int32_t T, U;   // frames; row-block slots per frame (ceil(F / BQ))
-  int64_t F;      // tokens per frame
+  int32_t T, U;  // frames; row-block slots per frame (ceil(F / BQ)), 0 = plain order
+  int64_t F;     // tokens per frame
 };
 
 __device__ inline float other_half(float x) {
@@ -107,6 +112,15 @@ __device__ inline void wait_vmcnt() {
 __device__ inline void barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ inline void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Float max into global memory, independent of arrival order: non-negative
+// values order like signed ints, negative ones inversely like unsigned ints.
+__device__ inline void atomic_max_float(float* addr, float v) {
+  if (__float_as_int(v) >= 0)
+    atomicMax((int*)addr, __float_as_int(v));
+  else
+    atomicMin((unsigned int*)addr, __float_as_uint(v));
+}
+
 // LDS layout of a 64-row tile of D bf16 per row: rows of D*2 bytes, 16-byte
 // chunk c of row r stored at chunk c ^ f(r). K uses fK (conflict-free b128
 // reads of 16 consecutive rows), V uses fV (conflict-free transpose reads of
@@ -124,20 +138,20 @@ struct Tile {
 
 template <int D, int BQ>
 struct Cfg {
-  static constexpr int NW = BQ / 32;                 // waves
-  static constexpr int NT = NW * 64;                 // threads
-  static constexpr int KS = D / 16;                  // k-steps of Q K^T
-  static constexpr int DB = D / 32;                  // 32-wide d blocks of O
-  static constexpr int LPW = Tile<D>::IPT / NW;      // loads per tile per wave, each of K and V
-  static constexpr int STAGE = 2 * Tile<D>::BYTES;   // K + V
-  static constexpr int SMEM = 2 * STAGE;             // two stages
-  static constexpr int OLD = D + 8;                  // O staging row stride (elements)
+  static constexpr int NW = BQ / 32;                      // waves
+  static constexpr int NT = NW * 64;                      // threads
+  static constexpr int KS = D / 16;                       // k-steps of Q K^T
+  static constexpr int DB = D / 32;                       // 32-wide d blocks of O
+  static constexpr int LPW = Tile<D>::IPT / NW;           // loads per tile per wave (K or V)
+  static constexpr int VOFF = kKStages * Tile<D>::BYTES;  // V stages follow the K stages
+  static constexpr int SMEM = (kKStages + kVStages) * Tile<D>::BYTES;
+  static constexpr int OLD = D + 8;                       // O staging row stride (elements)
   static_assert(LPW >= 1, "tile loader split");
   static_assert(BQ * OLD * 2 <= SMEM, "O staging must fit in the stages");
 };
 
-// Per-lane constants of the direct loads of one tile: voffset of each of this
-// wave's LPW loads, for K (swizzle fK) and V (swizzle fV).
+// Per-lane voffsets of this wave's LPW direct loads of one K tile and one V
+// tile (swizzles fK and fV applied on the global side).
 template <int D, int BQ>
 struct LoadPlan {
   uint32_t k[Cfg<D, BQ>::LPW];
@@ -158,31 +172,20 @@ __device__ inline void make_plan(LoadPlan<D, BQ>& lp, int w, int lane, int64_t k
   }
 }
 
+// This wave's share of the direct global -> LDS loads of one 64-row tile.
 template <int D, int BQ>
-__device__ inline void issue_tile(const LoadPlan<D, BQ>& lp, const uint16_t* kbase,
-                                  const uint16_t* vbase, int64_t ksn, int64_t vsn, int64_t c,
-                                  int64_t N, char* stage, int w) {
-  using T = Tile<D>;
+__device__ inline void issue_rows(const uint32_t* off, const uint16_t* base, int64_t sn,
+                                  int64_t c, int64_t N, char* stage, int w) {
   using C = Cfg<D, BQ>;
   const int64_t j0 = c * kBk;
   const int64_t rows = min((int64_t)kBk, N - j0);
-  const auto rk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(kbase + j0 * ksn), 0, (int)(rows * ksn * 2), kRsrcWord3);
-  const auto rv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(vbase + j0 * vsn), 0, (int)(rows * vsn * 2), kRsrcWord3);
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(base + j0 * sn), 0,
+                                                    (int)(rows * sn * 2), kRsrcWord3);
 #pragma unroll
   for (int i = 0; i < C::LPW; ++i) {
     const int idx = w + C::NW * i;
-    const uint32_t off = lp.k[i];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + idx * 1024), 16, off, 0, 0,
-                                             0);
-  }
-#pragma unroll
-  for (int i = 0; i < C::LPW; ++i) {
-    const int idx = w + C::NW * i;
-    const uint32_t off = lp.v[i];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + T::BYTES + idx * 1024), 16,
-                                             off, 0, 0, 0);
+    const uint32_t o = off[i];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(stage + idx * 1024), 16, o, 0, 0, 0);
   }
 }
 
@@ -191,12 +194,14 @@ __device__ inline bf16x8 join(i16x4 lo, i16x4 hi) {
   return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
 }
 
+// Key of lane value j (0..15) of 32-key block kb: kb*32 + 8*(j/4) + 4*hh + j%4.
+__device__ inline int key_of(int kb, int j, int hh) { return kb * 32 + 8 * (j / 4) + 4 * hh + (j % 4); }
+
 template <int D, int BQ, bool GAP>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p) {
   using C = Cfg<D, BQ>;
   using T = Tile<D>;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
-  __shared__ float gp[2][C::NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -241,16 +246,38 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
   const int64_t L = e1 - e0;
   const uint16_t* kbase = p.k + b * p.ksb + h * p.ksh;
   const uint16_t* vbase = p.v + b * p.vsb + h * p.vsh;
-
-  // Key block of list entry e0 + i (uniform scalar loads).
   auto block_of = [&](int64_t i) -> int64_t {
     return p.row_ptr ? (int64_t)load_uniform(p.kv_idx, e0 + i) : e0 + i;
   };
+  auto valid_keys = [&](int64_t c) -> int { return (int)min((int64_t)kBk, p.N - c * kBk); };
+
   LoadPlan<D, BQ> lp;
   make_plan<D, BQ>(lp, w, lane, p.ksn, p.vsn);
-  int64_t c_cur = L > 0 ? block_of(0) : 0;
-  int64_t c_nxt = L > 1 ? block_of(1) : 0;
-  if (L > 0) issue_tile<D, BQ>(lp, kbase, vbase, p.ksn, p.vsn, c_cur, p.N, smem, w);
+  char* kst = smem;
+  char* vst = smem + C::VOFF;
+  auto issue_k = [&](int64_t i, int64_t c) {
+    issue_rows<D, BQ>(lp.k, kbase, p.ksn, c, p.N, kst + (int)(i % kKStages) * T::BYTES, w);
+  };
+  auto issue_v = [&](int64_t i, int64_t c) {
+    issue_rows<D, BQ>(lp.v, vbase, p.vsn, c, p.N, vst + (int)(i % kVStages) * T::BYTES, w);
+  };
+
+  // Key-block indices of list entries it, it+1, it+2, it+3 (rolling).
+  int64_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+  if (L > 0) {
+    c0 = block_of(0);
+    issue_k(0, c0);
+    issue_v(0, c0);
+  }
+  if (L > 1) {
+    c1 = block_of(1);
+    issue_k(1, c1);
+  }
+  if (L > 2) {
+    c2 = block_of(2);
+    issue_k(2, c2);
+  }
+  if (L > 3) c3 = block_of(3);
 
   // Q rows of this wave as MFMA B operands (k-slice hh*8..+7 of each 16-step).
   const int64_t qrow = a * BQ + w * 32 + n;
@@ -291,23 +318,11 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
   float m_true = -INFINITY;  // running row max (log2 units), for the tile gaps
   float l_lane = 0.f;        // this lane half's share of the row sum
 
-  for (int64_t it = 0; it < L; ++it) {
-    char* cur = smem + (it & 1) * C::STAGE;
-    const int64_t c = c_cur;
-    if (it + 1 < L) {
-      issue_tile<D, BQ>(lp, kbase, vbase, p.ksn, p.vsn, c_nxt, p.N,
-                        smem + ((it + 1) & 1) * C::STAGE, w);
-      wait_vmcnt<2 * C::LPW>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    c_cur = c_nxt;
-    if (it + 2 < L) c_nxt = block_of(it + 2);
-    barrier();  // every wave's loads of tile `it` have landed
-
-    // ---- S^T = K Q^T for the 64 keys of the tile (two 32-key blocks).
-    const char* kt = cur;
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  // ---- pipeline pieces
+  // Scores of one K stage: two 32-key blocks.
+  auto scores = [&](const char* kt, f32x16(&sacc)[2]) {
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
@@ -316,18 +331,17 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sacc[kb], 0, 0, 0);
       }
     }
-
-    // ---- online softmax. Lane value j of block kb is key
-    // kb*32 + 8*(j/4) + 4*hh + j%4 of the tile.
-    const int jv = (int)min((int64_t)kBk, p.N - c * kBk);  // valid keys in this tile
+  };
+  // Row max of a tile's scores (valid keys only), in log2 units, then the
+  // tile gap and the exponent-base update. O must already hold every earlier
+  // tile when this runs (it may be rescaled).
+  auto absorb_max = [&](f32x16(&sacc)[2], int jv, int64_t entry) {
     if (jv < kBk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = kb * 32 + 8 * (j / 4) + 4 * hh + (j % 4);
-          if (key >= jv) sacc[kb][j] = -INFINITY;
-        }
+        for (int j = 0; j < 16; ++j)
+          if (key_of(kb, j, hh) >= jv) sacc[kb][j] = -INFINITY;
     }
     float mloc = -INFINITY;
 #pragma unroll
@@ -340,7 +354,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
       float g = qvalid ? m_loc2 - m_true : -INFINITY;
 #pragma unroll
       for (int off = 16; off >= 1; off >>= 1) g = fmaxf(g, __shfl_xor(g, off, 32));
-      if (lane == 0) gp[it & 1][w] = g;
+      if (lane == 0) atomic_max_float(p.tile_gap + gbase + e0 + entry, g);
       m_true = fmaxf(m_true, m_loc2);
     }
     if (__builtin_amdgcn_ballot_w64(m_loc2 > m_use + kRescaleSlack)) {
@@ -351,8 +365,11 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
     }
+  };
+  // p = 2^(s*scale*log2e - m) rounded to bf16, and its row sum. Masked keys
+  // hold -inf and give 0.
+  auto probs = [&](const f32x16(&sacc)[2], bf16x8(&pb)[2][2]) {
     const float neg_m = -m_use;
-    bf16x8 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -369,12 +386,12 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
                                                    false);
       }
     }
-
-    // ---- O^T += V^T P^T. For the 16-key step (kb, half) the B operand is
-    // pb[kb][half]; element t of lane half hh is key
-    // kb*32 + 16*half + 8*(t/4) + 4*hh + t%4, which two transpose reads of
-    // the V tile deliver in that order.
-    const char* vt = cur + T::BYTES;
+  };
+  // O^T += V^T P^T over one V stage. For the 16-key step (kb, half) the B
+  // operand is pb[kb][half]; element t of lane half hh is key
+  // kb*32 + 16*half + 8*(t/4) + 4*hh + t%4, which two transpose reads of the
+  // V tile deliver in that order.
+  auto accumulate = [&](const char* vt, const bf16x8(&pb)[2][2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -391,20 +408,63 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
         }
       }
     }
+  };
 
-    if (GAP) wait_lds();
-    barrier();  // every wave is done with this stage (it is refilled next iteration)
-    if (GAP && tid == 0) {
-      float g = gp[it & 1][0];
-#pragma unroll
-      for (int x = 1; x < C::NW; ++x) g = fmaxf(g, gp[it & 1][x]);
-      p.tile_gap[gbase + e0 + it] = g;
+  // Loads in flight are always, oldest first: ..., V(it), K(it+2). V(j+1)
+  // and K(j+3) are issued right after the barrier of iteration j, into
+  // stages last read before that barrier.
+  f32x16 sA[2], sB[2];
+  if (L > 0) {
+    // prologue: scores and max of tile 0
+    if (L > 2) wait_vmcnt<3 * C::LPW>();  // K0 done; V0, K1, K2 may fly
+    else if (L > 1) wait_vmcnt<2 * C::LPW>();
+    else wait_vmcnt<C::LPW>();
+    barrier();
+    scores(kst, sA);
+    absorb_max(sA, valid_keys(c0), 0);
+  }
+  // One pipeline step: tile `it` has scores in `cur`; when `has_next`, the
+  // scores of tile it+1 are computed into `nxt` meanwhile.
+  auto step = [&](int64_t it, f32x16(&cur)[2], f32x16(&nxt)[2], bool has_next) {
+    if (it + 2 < L) wait_vmcnt<C::LPW>();  // V(it) and K(it+1) done; K(it+2) may fly
+    else wait_vmcnt<0>();
+    barrier();
+    if (it + 1 < L) issue_v(it + 1, c1);
+    if (it + 3 < L) issue_k(it + 3, c3);
+    bf16x8 pb[2][2];
+    if (has_next) {
+      // phase A: exponentials of tile it with the score MFMAs of tile it+1
+      scores(kst + (int)((it + 1) % kKStages) * T::BYTES, nxt);
+      probs(cur, pb);
+      // phase B: P V of tile it with the row max of tile it+1
+      accumulate(vst + (int)(it % kVStages) * T::BYTES, pb);
+      absorb_max(nxt, valid_keys(c1), it + 1);
+    } else {
+      probs(cur, pb);
+      accumulate(vst + (int)(it % kVStages) * T::BYTES, pb);
     }
+    c0 = c1;
+    c1 = c2;
+    c2 = c3;
+    if (it + 4 < L) c3 = block_of(it + 4);
+  };
+  int64_t it = 0;
+  for (; it + 2 < L; it += 2) {
+    step(it, sA, sB, true);
+    step(it + 1, sB, sA, true);
+  }
+  if (it + 1 < L) {
+    step(it, sA, sB, true);
+    step(it + 1, sB, sA, false);
+  } else if (it < L) {
+    step(it, sA, sB, false);
   }
 
   // ---- epilogue: O = O^T / l through LDS for coalesced 16-byte stores.
   const float l_tot = l_lane + other_half(l_lane);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  wait_lds();
+  barrier();  // every wave is done reading the stages
   uint16_t* Os = (uint16_t*)smem;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) {
@@ -432,15 +492,29 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
     p.lse[bh * p.N + qrow] = l_tot > 0.f ? (m_use + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
+// tile_gap[0 .. count) = -inf, count = row_ptr[R] * mult (read on the device).
+__global__ void gap_init_kernel(float* gap, const int32_t* row_ptr, int64_t R, int64_t mult) {
+  const int64_t count = (int64_t)row_ptr[R] * mult;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * blockDim.x)
+    gap[i] = -INFINITY;
+}
+
 template <int D, int BQ>
 hipError_t launch(const Geom& g, const Bf16Params& p, hipStream_t st) {
   const int64_t rows = (int64_t)g.B * g.H * (p.U ? (int64_t)g.T * p.U : g.nQ);
-  if (p.tile_gap)
+  if (p.tile_gap) {
+    // per-wave gaps are folded in with an atomic max starting from -inf
+    const int64_t R = p.lists_shared ? g.nQ : (int64_t)g.B * g.H * g.nQ;
+    const int64_t mult = p.lists_shared ? (int64_t)g.B * g.H : 1;
+    hipLaunchKernelGGL(gap_init_kernel, dim3(1024), dim3(256), 0, st, p.tile_gap, p.row_ptr, R,
+                       mult);
     hipLaunchKernelGGL((attn_bf16_kernel<D, BQ, true>), dim3((unsigned)rows),
                        dim3(Cfg<D, BQ>::NT), 0, st, p);
-  else
+  } else {
     hipLaunchKernelGGL((attn_bf16_kernel<D, BQ, false>), dim3((unsigned)rows),
                        dim3(Cfg<D, BQ>::NT), 0, st, p);
+  }
   return hipGetLastError();
 }
 
