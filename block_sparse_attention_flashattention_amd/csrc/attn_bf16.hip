@@ -55,6 +55,7 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -172,21 +173,30 @@ __device__ inline void make_plan(LoadPlan<D, BQ>& lp, int w, int lane, int64_t k
   }
 }
 
-// This wave's share of the direct global -> LDS loads of one 64-row tile.
+// 16 bytes per lane from global memory straight into LDS; lane l's bytes
+// land at M0 + 16*l. Written as inline assembly on purpose: the compiler's
+// wait-count pass cannot tell LDS stages apart and would otherwise drain every
+// outstanding load before each LDS read, which defeats prefetching. The
+// kernel orders these loads itself (explicit vmcnt waits and barriers). Rows
+// at or beyond the descriptor's num_records read as zero.
+__device__ inline void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
+// This wave's share of the direct global -> LDS loads of one 64-row tile
+// (`stage` is an LDS byte address).
 template <int D, int BQ>
 __device__ inline void issue_rows(const uint32_t* off, const uint16_t* base, int64_t sn,
-                                  int64_t c, int64_t N, char* stage, int w) {
+                                  int64_t c, int64_t N, uint32_t stage, int w) {
   using C = Cfg<D, BQ>;
   const int64_t j0 = c * kBk;
   const int64_t rows = min((int64_t)kBk, N - j0);
-  const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(base + j0 * sn), 0,
-                                                    (int)(rows * sn * 2), kRsrcWord3);
+  const uint64_t a = (uint64_t)(base + j0 * sn);
+  const i32x4 rs = {(int32_t)(uint32_t)a, (int32_t)((a >> 32) & 0xffff), (int32_t)(rows * sn * 2),
+                    kRsrcWord3};
 #pragma unroll
-  for (int i = 0; i < C::LPW; ++i) {
-    const int idx = w + C::NW * i;
-    const uint32_t o = off[i];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(stage + idx * 1024), 16, o, 0, 0, 0);
-  }
+  for (int i = 0; i < C::LPW; ++i) dma16(rs, stage + (uint32_t)(w + C::NW * i) * 1024, off[i]);
 }
 
 __device__ inline bf16x8 join(i16x4 lo, i16x4 hi) {
@@ -253,29 +263,32 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
 
   LoadPlan<D, BQ> lp;
   make_plan<D, BQ>(lp, w, lane, p.ksn, p.vsn);
-  char* kst = smem;
-  char* vst = smem + C::VOFF;
-  auto issue_k = [&](int64_t i, int64_t c) {
-    issue_rows<D, BQ>(lp.k, kbase, p.ksn, c, p.N, kst + (int)(i % kKStages) * T::BYTES, w);
+  // Stage byte offsets, rotated every tile: K stages of tiles it, it+1, it+2
+  // (tile it+3 reuses it's), V stages of tiles it, it+1.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  int kso0 = 0, kso1 = T::BYTES, kso2 = 2 * T::BYTES;
+  int vso0 = C::VOFF, vso1 = C::VOFF + T::BYTES;
+  auto issue_k = [&](int so, int64_t c) {
+    issue_rows<D, BQ>(lp.k, kbase, p.ksn, c, p.N, lds0 + so, w);
   };
-  auto issue_v = [&](int64_t i, int64_t c) {
-    issue_rows<D, BQ>(lp.v, vbase, p.vsn, c, p.N, vst + (int)(i % kVStages) * T::BYTES, w);
+  auto issue_v = [&](int so, int64_t c) {
+    issue_rows<D, BQ>(lp.v, vbase, p.vsn, c, p.N, lds0 + so, w);
   };
 
   // Key-block indices of list entries it, it+1, it+2, it+3 (rolling).
   int64_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
   if (L > 0) {
     c0 = block_of(0);
-    issue_k(0, c0);
-    issue_v(0, c0);
+    issue_k(kso0, c0);
+    issue_v(vso0, c0);
   }
   if (L > 1) {
     c1 = block_of(1);
-    issue_k(1, c1);
+    issue_k(kso1, c1);
   }
   if (L > 2) {
     c2 = block_of(2);
-    issue_k(2, c2);
+    issue_k(kso2, c2);
   }
   if (L > 3) c3 = block_of(3);
 
@@ -420,33 +433,44 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
     else if (L > 1) wait_vmcnt<2 * C::LPW>();
     else wait_vmcnt<C::LPW>();
     barrier();
-    scores(kst, sA);
+    scores(smem + kso0, sA);
     absorb_max(sA, valid_keys(c0), 0);
   }
   // One pipeline step: tile `it` has scores in `cur`; when `has_next`, the
-  // scores of tile it+1 are computed into `nxt` meanwhile.
+  // scores of tile it+1 are computed into `nxt` meanwhile. Every LDS read of
+  // the previous step has completed before the barrier (lgkmcnt(0)), so the
+  // stages it read may be refilled right after it.
   auto step = [&](int64_t it, f32x16(&cur)[2], f32x16(&nxt)[2], bool has_next) {
     if (it + 2 < L) wait_vmcnt<C::LPW>();  // V(it) and K(it+1) done; K(it+2) may fly
     else wait_vmcnt<0>();
+    wait_lds();
     barrier();
-    if (it + 1 < L) issue_v(it + 1, c1);
-    if (it + 3 < L) issue_k(it + 3, c3);
+    if (it + 1 < L) issue_v(vso1, c1);
+    if (it + 3 < L) issue_k(kso0, c3);
+    const int64_t c4 = it + 4 < L ? block_of(it + 4) : 0;
     bf16x8 pb[2][2];
     if (has_next) {
       // phase A: exponentials of tile it with the score MFMAs of tile it+1
-      scores(kst + (int)((it + 1) % kKStages) * T::BYTES, nxt);
+      scores(smem + kso1, nxt);
       probs(cur, pb);
       // phase B: P V of tile it with the row max of tile it+1
-      accumulate(vst + (int)(it % kVStages) * T::BYTES, pb);
+      accumulate(smem + vso0, pb);
       absorb_max(nxt, valid_keys(c1), it + 1);
     } else {
       probs(cur, pb);
-      accumulate(vst + (int)(it % kVStages) * T::BYTES, pb);
+      accumulate(smem + vso0, pb);
     }
     c0 = c1;
     c1 = c2;
     c2 = c3;
-    if (it + 4 < L) c3 = block_of(it + 4);
+    c3 = c4;
+    const int kt = kso0;
+    kso0 = kso1;
+    kso1 = kso2;
+    kso2 = kt;
+    const int vt = vso0;
+    vso0 = vso1;
+    vso1 = vt;
   };
   int64_t it = 0;
   for (; it + 2 < L; it += 2) {
