@@ -30,9 +30,10 @@
 //  * Software pipeline, one barrier per tile. While the exponentials of tile
 //    i run on the VALU, the matrix core computes the scores of tile i+1;
 //    while it accumulates P_i V_i, the VALU reduces the row maxima of tile
-//    i+1. K is three LDS stages deep (tile i+3 is requested while tile i+1
-//    is read), V two (tile i+1 is requested while tile i is read): 80 KiB,
-//    two workgroups per CU.
+//    i+1. K and V have two LDS stages each (tiles i+2 and i+1 are requested
+//    right after the barrier of step i): 64 KiB, two workgroups per CU. The
+//    loop is unrolled by two so that every stage address is a constant
+//    offset of the LDS read instructions.
 //  * Rescaling of O is lazy: the exponent base moves only when the row max
 //    grows by more than 2^8, which keeps p <= 256 and leaves the result exact
 //    up to rounding (numerator and denominator share the base).
@@ -41,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "bsa_internal.h"
 
@@ -63,7 +66,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kBk = 64;
 constexpr int kXcds = 8;
 constexpr int kBand = 2;  // row-block slots per position band
-constexpr int kKStages = 3;
+constexpr int kKStages = 2;
 constexpr int kVStages = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -177,10 +180,12 @@ __device__ inline void make_plan(LoadPlan<D, BQ>& lp, int w, int lane, int64_t k
 // land at M0 + 16*l. Written as inline assembly on purpose: the compiler's
 // wait-count pass cannot tell LDS stages apart and would otherwise drain every
 // outstanding load before each LDS read, which defeats prefetching. The
-// kernel orders these loads itself (explicit vmcnt waits and barriers). Rows
-// at or beyond the descriptor's num_records read as zero.
+// kernel orders these loads itself (explicit vmcnt waits and barriers). The
+// s_nop is the one wait state required between an M0 write and an LDS DMA
+// load that reads it. Rows at or beyond the descriptor's num_records read as
+// zero.
 __device__ inline void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 
@@ -263,11 +268,10 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
 
   LoadPlan<D, BQ> lp;
   make_plan<D, BQ>(lp, w, lane, p.ksn, p.vsn);
-  // Stage byte offsets, rotated every tile: K stages of tiles it, it+1, it+2
-  // (tile it+3 reuses it's), V stages of tiles it, it+1.
+  // Stage byte offsets: tile i uses K stage i % 2 and V stage i % 2.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
-  int kso0 = 0, kso1 = T::BYTES, kso2 = 2 * T::BYTES;
-  int vso0 = C::VOFF, vso1 = C::VOFF + T::BYTES;
+  constexpr int kso[2] = {0, T::BYTES};
+  constexpr int vso[2] = {C::VOFF, C::VOFF + T::BYTES};
   auto issue_k = [&](int so, int64_t c) {
     issue_rows<D, BQ>(lp.k, kbase, p.ksn, c, p.N, lds0 + so, w);
   };
@@ -275,22 +279,18 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
     issue_rows<D, BQ>(lp.v, vbase, p.vsn, c, p.N, lds0 + so, w);
   };
 
-  // Key-block indices of list entries it, it+1, it+2, it+3 (rolling).
-  int64_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+  // Key-block indices of list entries it, it+1, it+2 (rolling).
+  int64_t c0 = 0, c1 = 0, c2 = 0;
   if (L > 0) {
     c0 = block_of(0);
-    issue_k(kso0, c0);
-    issue_v(vso0, c0);
+    issue_k(kso[0], c0);
+    issue_v(vso[0], c0);
   }
   if (L > 1) {
     c1 = block_of(1);
-    issue_k(kso1, c1);
+    issue_k(kso[1], c1);
   }
-  if (L > 2) {
-    c2 = block_of(2);
-    issue_k(kso2, c2);
-  }
-  if (L > 3) c3 = block_of(3);
+  if (L > 2) c2 = block_of(2);
 
   // Q rows of this wave as MFMA B operands (k-slice hh*8..+7 of each 16-step).
   const int64_t qrow = a * BQ + w * 32 + n;
@@ -345,11 +345,11 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
       }
     }
   };
-  // Row max of a tile's scores (valid keys only), in log2 units, then the
-  // tile gap and the exponent-base update. O must already hold every earlier
-  // tile when this runs (it may be rescaled).
-  auto absorb_max = [&](f32x16(&sacc)[2], int jv, int64_t entry) {
-    if (jv < kBk) {
+  // Row max of a tile's scores in log2 units. When `masked`, keys at or
+  // beyond jv (only the last key block can be ragged) are set to -inf first,
+  // which also makes their probabilities 0.
+  auto tile_max = [&](f32x16(&sacc)[2], bool masked, int jv) -> float {
+    if (masked) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -362,7 +362,11 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
 #pragma unroll
       for (int j = 0; j < 16; ++j) mloc = fmaxf(mloc, sacc[kb][j]);
     mloc = fmaxf(mloc, other_half(mloc));
-    const float m_loc2 = mloc * p.sl2;
+    return mloc * p.sl2;
+  };
+  // Tile gap and exponent-base update for a tile whose row max is m_loc2. O
+  // must already hold every earlier tile when this runs (it may be rescaled).
+  auto apply_max = [&](float m_loc2, int64_t entry) {
     if (GAP) {
       float g = qvalid ? m_loc2 - m_true : -INFINITY;
 #pragma unroll
@@ -423,65 +427,59 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
     }
   };
 
-  // Loads in flight are always, oldest first: ..., V(it), K(it+2). V(j+1)
-  // and K(j+3) are issued right after the barrier of iteration j, into
-  // stages last read before that barrier.
+  // V(j+1) and K(j+2) are issued right after the barrier of step j, into
+  // stages last read before that barrier, and waited for at the start of
+  // step j+1.
   f32x16 sA[2], sB[2];
   if (L > 0) {
     // prologue: scores and max of tile 0
-    if (L > 2) wait_vmcnt<3 * C::LPW>();  // K0 done; V0, K1, K2 may fly
-    else if (L > 1) wait_vmcnt<2 * C::LPW>();
+    if (L > 1) wait_vmcnt<2 * C::LPW>();  // K0 done; V0, K1 may fly
     else wait_vmcnt<C::LPW>();
     barrier();
-    scores(smem + kso0, sA);
-    absorb_max(sA, valid_keys(c0), 0);
+    scores(smem + kso[0], sA);
+    apply_max(tile_max(sA, true, valid_keys(c0)), 0);
   }
   // One pipeline step: tile `it` has scores in `cur`; when `has_next`, the
   // scores of tile it+1 are computed into `nxt` meanwhile. Every LDS read of
   // the previous step has completed before the barrier (lgkmcnt(0)), so the
   // stages it read may be refilled right after it.
-  auto step = [&](int64_t it, f32x16(&cur)[2], f32x16(&nxt)[2], bool has_next) {
-    if (it + 2 < L) wait_vmcnt<C::LPW>();  // V(it) and K(it+1) done; K(it+2) may fly
-    else wait_vmcnt<0>();
+  auto step = [&](int64_t it, f32x16(&cur)[2], f32x16(&nxt)[2], bool has_next, auto par_c) {
+    constexpr int par = decltype(par_c)::value;
+    wait_vmcnt<0>();  // V(it) and K(it+1) done
     wait_lds();
     barrier();
-    if (it + 1 < L) issue_v(vso1, c1);
-    if (it + 3 < L) issue_k(kso0, c3);
-    const int64_t c4 = it + 4 < L ? block_of(it + 4) : 0;
+    if (it + 1 < L) issue_v(vso[1 - par], c1);
+    if (it + 2 < L) issue_k(kso[par], c2);
+    const int64_t c3 = it + 3 < L ? block_of(it + 3) : 0;
     bf16x8 pb[2][2];
     if (has_next) {
       // phase A: exponentials of tile it with the score MFMAs of tile it+1
-      scores(smem + kso1, nxt);
+      scores(smem + kso[1 - par], nxt);
       probs(cur, pb);
       // phase B: P V of tile it with the row max of tile it+1
-      accumulate(smem + vso0, pb);
-      absorb_max(nxt, valid_keys(c1), it + 1);
+      accumulate(smem + vso[par], pb);
+      const int jv = valid_keys(c1);
+      apply_max(tile_max(nxt, jv < kBk, jv), it + 1);
     } else {
       probs(cur, pb);
-      accumulate(smem + vso0, pb);
+      accumulate(smem + vso[par], pb);
     }
     c0 = c1;
     c1 = c2;
     c2 = c3;
-    c3 = c4;
-    const int kt = kso0;
-    kso0 = kso1;
-    kso1 = kso2;
-    kso2 = kt;
-    const int vt = vso0;
-    vso0 = vso1;
-    vso1 = vt;
   };
   int64_t it = 0;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   for (; it + 2 < L; it += 2) {
-    step(it, sA, sB, true);
-    step(it + 1, sB, sA, true);
+    step(it, sA, sB, true, P0{});
+    step(it + 1, sB, sA, true, P1{});
   }
   if (it + 1 < L) {
-    step(it, sA, sB, true);
-    step(it + 1, sB, sA, false);
+    step(it, sA, sB, true, P0{});
+    step(it + 1, sB, sA, false, P1{});
   } else if (it < L) {
-    step(it, sA, sB, false);
+    step(it, sA, sB, false, P0{});
   }
 
   // ---- epilogue: O = O^T / l through LDS for coalesced 16-byte stores.
