@@ -74,6 +74,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan14b_720p")
+    ap.add_argument("--tau", type=float, default=None,
+                    help="skip-carry threshold override (natural-log units; default: the "
+                         "workload's)")
     ap.add_argument("--cpu-rows", type=int, default=192,
                     help="row blocks in the CPU oracle sample (0 = skip)")
     ap.add_argument("--no-dense", action="store_true", help="skip the all-tiles timing")
@@ -105,6 +108,9 @@ def main():
         return
 
     w = synth.workload(args.workload)
+    if args.tau is not None:
+        import dataclasses
+        w = dataclasses.replace(w, tau=args.tau)
     log(f"workload {w.name}: B={w.B} H={w.H} d={w.d} grid {w.T}x{w.Hs}x{w.Ws} N={w.N} "
         f"Bq={w.Bq} Bk={w.Bk} mask={w.mask}")
     t0 = time.time()

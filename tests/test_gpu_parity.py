@@ -179,3 +179,18 @@ def _full_radial(name, per_head, seed):
 
 def test_fwd_wan14b_720p_radial_sampled():
     _full_radial("wan14b_720p", per_head=4, seed=3)
+
+
+def test_fwd_all_rows_empty():
+    """Every list empty: O = 0 and LSE = -inf everywhere, for both row-block sizes."""
+    for Bq in (64, 128):
+        w = small(128, Bq, T=2, Hs=5, Ws=7, B=1, H=2)
+        x = synth.make_qkv(w)
+        s = shape_of(w)
+        R = w.B * w.H * w.nQ
+        rp = torch.zeros(R + 1, dtype=torch.int32, device=DEV)
+        kv = torch.zeros(1, dtype=torch.int32, device=DEV)
+        o, lse, gap = run_fwd(s, dev(x["q"]), dev(x["k"]), dev(x["v"]), rp, kv, 0, w.scale,
+                              gap_len=1)
+        assert torch.count_nonzero(o.float()).item() == 0
+        assert bool(torch.all(torch.isneginf(lse)))

@@ -1,0 +1,214 @@
+"""GPU parity for the dynamic mask builders and the step carry, through the C ABI.
+
+Pooled masks are decided by comparisons on fp64 pooled scores that both sides
+compute in the same fixed order, so the masks must match bit for bit. The
+skip carry is checked per denoising step: outputs within the attention bounds,
+tile gaps within 1e-3 of the oracle's, the update's decisions bit-exact
+against the rule applied to the GPU's own gaps in the kernel's precision
+(fp32, log2 units), and the skip set only grows. Where the oracle's fp64
+decision differs, the gap must sit within the gap tolerance of the threshold.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_flashattention_amd as bsa
+import oracle
+import synth
+from _gpu_util import (DEV, GAP_ABS, compare, dev, gather_rows, host, note, run_fwd,
+                       sample_rows, shape_of)
+
+pytestmark = pytest.mark.gpu
+
+LOG2E = 1.4426950408889634
+
+
+def _pooled_gpu(w, x, mode, param):
+    s = shape_of(w)
+    ws = torch.empty(bsa.bsa_pooled_workspace_bytes(s), dtype=torch.uint8, device=DEV)
+    mask = torch.empty(w.B * w.H * w.nQ * w.nK, dtype=torch.uint8, device=DEV)
+    bsa.bsa_build_mask_pooled(s, dev(x["q"]), dev(x["k"]), w.scale, mode, param, mask, ws)
+    torch.cuda.synchronize()
+    return host(mask).reshape(w.B, w.H, w.nQ, w.nK)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Bq", [64, 128])
+@pytest.mark.parametrize("mode,param", [(0, 1.0), (0, 4.0), (1, 0.5), (1, 0.9), (1, 1.0)])
+def test_pooled_mask_small_bit_exact(dtype, Bq, mode, param):
+    w = synth.Workload("pooled_small", 2, 3, 128, 5, 12, 17, Bq, 64, dtype, "pooled", 610, True)
+    note(f"pooled small {dtype} Bq={Bq} mode={mode} param={param} N={w.N}")
+    x = synth.make_qkv(w)
+    got = _pooled_gpu(w, x, mode, param)
+    ref, _, _ = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, mode, param)
+    np.testing.assert_array_equal(got, ref)
+    if mode == 0:
+        assert np.all(got.sum(-1) == min(int(param), w.nK))
+
+
+def test_pooled_mask_d64_bit_exact():
+    w = synth.Workload("pooled_d64", 1, 2, 64, 4, 9, 14, 64, 64, "bf16", "pooled", 611, True)
+    x = synth.make_qkv(w)
+    got = _pooled_gpu(w, x, 1, 0.7)
+    ref, _, _ = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, 1, 0.7)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_pooled_mask_wan13b_480p_full():
+    w = synth.workload("wan13b_480p")
+    note(f"{w.name}: generating inputs")
+    x = synth.make_qkv(w)
+    got = _pooled_gpu(w, x, w.pooled_mode, w.pooled_param)
+    ref, _, margin = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale,
+                                              w.pooled_mode, w.pooled_param)
+    diff = int(np.sum(got != ref))
+    note(f"{w.name}: {ref.sum()} kept tiles ({100 * (1 - ref.mean()):.1f}% sparse), "
+         f"{diff} differ; smallest selection margin {margin.min():.3e}")
+    np.testing.assert_array_equal(got, ref)
+    assert 0.80 < 1 - ref.mean() < 0.90
+
+
+def test_pooled_then_forward_wan13b_480p_sampled():
+    """The pooled builder feeding compaction and the Bq = 64 forward, end to end."""
+    w = synth.workload("wan13b_480p")
+    x = synth.make_qkv(w)
+    s = shape_of(w)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    ws = torch.empty(bsa.bsa_pooled_workspace_bytes(s), dtype=torch.uint8, device=DEV)
+    R = w.B * w.H * w.nQ
+    mask = torch.empty(R * w.nK, dtype=torch.uint8, device=DEV)
+    bsa.bsa_build_mask_pooled(s, q, k, w.scale, w.pooled_mode, w.pooled_param, mask, ws)
+    rp = torch.empty(R + 1, dtype=torch.int32, device=DEV)
+    kv = torch.empty(R * w.nK, dtype=torch.int32, device=DEV)
+    bsa.bsa_compact_block_lists(s, mask, w.nQ * w.nK, None, rp, kv)
+    o, lse, _ = run_fwd(s, q, k, v, rp, kv, 0, w.scale)
+    mask_h = host(mask).reshape(w.B, w.H, w.nQ, w.nK)
+    rows = sample_rows(w.B, w.H, w.nQ, 3, 21, heads=[0, 5, w.H - 1])
+    o_ref, lse_ref, _ = oracle.attention(x["q"], x["k"], x["v"], w.Bq, w.Bk, w.scale, mask_h,
+                                         w.nQ * w.nK, rows=rows)
+    og, lg = gather_rows(host(o), host(lse), rows, w.B, w.H, w.N, w.Bq)
+    compare(og, lg, o_ref, lse_ref, f"{w.name} pooled sampled")
+
+
+# ---------------------------------------------------------------- skip carry
+def _gap_matrix(gap_list, rp, kv, R, nK):
+    """List-ordered gaps -> [R][nK] (NaN where no tile was listed)."""
+    out = np.full((R, nK), np.nan)
+    for r in range(R):
+        e0, e1 = rp[r], rp[r + 1]
+        out[r, kv[e0:e1]] = gap_list[e0:e1]
+    return out
+
+
+def _skip_carry(w, steps, tau, rows=None):
+    s = shape_of(w)
+    R = w.B * w.H * w.nQ
+    nK = w.nK
+    x0 = synth.make_qkv(w, step=0)
+    v_np = x0["v"]
+    v = dev(v_np)
+    ones = torch.ones(w.nQ * nK, dtype=torch.uint8, device=DEV)
+    skip = torch.zeros(R * nK, dtype=torch.uint8, device=DEV)
+    rp = torch.empty(R + 1, dtype=torch.int32, device=DEV)
+    kv = torch.empty(R * nK, dtype=torch.int32, device=DEV)
+    gap = torch.empty(R * nK, dtype=torch.float32, device=DEV)
+    tau2 = np.float32(np.float64(tau) * LOG2E)
+    for st in range(steps):
+        x = x0 if st == 0 else synth.make_step_qk(w, st)
+        q, k = dev(x["q"]), dev(x["k"])
+        skip_prev = host(skip).reshape(R, nK).copy()
+        nnz = bsa.bsa_compact_block_lists(s, ones, 0, skip, rp, kv, want_nnz=True)
+        o = torch.empty_like(q)
+        lse = torch.empty(w.B * w.H * w.N, dtype=torch.float32, device=DEV)
+        bsa.bsa_sparse_attn_fwd(s, q, k, v, o, lse, rp, kv, 0, w.scale, gap)
+        bsa.bsa_update_skip_mask(s, rp, kv, gap, tau, skip)
+        torch.cuda.synchronize()
+        rp_h, kv_h = host(rp).astype(np.int64), host(kv)[:nnz]
+        gap_h = host(gap)[:nnz].astype(np.float32)
+        skip_new = host(skip).reshape(R, nK)
+        # lists are the complement of the carried set
+        rp_ref, kv_ref = oracle.compact(np.ones((w.nQ, nK), np.uint8), w.B, w.H, w.nQ, nK, 0,
+                                        skip_prev.reshape(w.B, w.H, w.nQ, nK))
+        np.testing.assert_array_equal(rp_h, rp_ref)
+        np.testing.assert_array_equal(kv_h, kv_ref)
+        # update rule, bit-exact on the GPU's own gaps in fp32 / log2 units
+        gm = _gap_matrix(gap_h, rp_h, kv_h, R, nK)
+        expect = skip_prev | (np.nan_to_num(gm, nan=np.inf) <= -tau2).astype(np.uint8)
+        np.testing.assert_array_equal(skip_new, expect)
+        assert np.all(skip_new >= skip_prev), "skip set must only grow"
+        # against the oracle (fp64): outputs, gaps, decisions
+        sel = np.arange(R) if rows is None else rows
+        o_ref, lse_ref, gap_ref, skip_ref = oracle.skip_step(
+            x["q"], x["k"], v_np, w.Bq, w.Bk, w.scale, skip_prev.reshape(w.B, w.H, w.nQ, nK),
+            tau, rows=sel)
+        og, lg = gather_rows(host(o), host(lse), sel, w.B, w.H, w.N, w.Bq)
+        compare(og, lg, o_ref, lse_ref, f"{w.name} step {st}")
+        g_gpu = gm[sel] * math.log(2.0)
+        fin = np.isfinite(gap_ref) & np.isfinite(g_gpu)
+        assert np.array_equal(np.isnan(gap_ref), np.isnan(gm[sel])), "visited tiles differ"
+        assert np.array_equal(np.isposinf(gap_ref), np.isposinf(g_gpu)), "first-tile pattern"
+        gerr = float(np.abs(g_gpu[fin] - gap_ref[fin]).max()) if fin.any() else 0.0
+        dec_gpu = skip_new[sel]
+        dec_ref = skip_ref.reshape(R, nK)[sel]
+        flips = np.argwhere(dec_gpu != dec_ref)
+        for r_, c_ in flips:
+            assert abs(gap_ref[r_, c_] + tau) <= GAP_ABS, "decision differs away from the threshold"
+        note(f"{w.name} step {st}: {nnz} tiles, {int(skip_new.sum())} skipped, gap max err "
+             f"{gerr:.2e}, {len(flips)} threshold-edge flips")
+        assert gerr <= GAP_ABS
+    return int(skip_new.sum())
+
+
+# Thresholds here are set from these inputs' gap distribution (most gaps lie
+# in [-4, 0] natural-log units) so that tiles are actually marked and carried;
+# at the workload's own tau = 10 nothing is marked (checked last).
+def test_skip_carry_small_steps():
+    w = synth.Workload("skip_small", 1, 3, 128, 6, 10, 14, 64, 64, "bf16", "skip", 620, True,
+                       tau=1.0, steps=5)
+    _skip_carry(w, w.steps, w.tau)
+
+
+def test_skip_carry_small_bq128_ragged():
+    w = synth.Workload("skip_small128", 2, 2, 64, 5, 9, 13, 128, 64, "bf16", "skip", 621, True,
+                       tau=0.25, steps=4)
+    _skip_carry(w, w.steps, w.tau)
+
+
+def test_skip_carry_480p_sampled():
+    w = synth.workload("skip_carry_480p")
+    rows = sample_rows(w.B, w.H, w.nQ, 2, 23, heads=[0, w.H - 1])
+    _skip_carry(w, 4, 2.0, rows=rows)
+
+
+def test_skip_carry_480p_workload_tau_marks_nothing():
+    w = synth.workload("skip_carry_480p")
+    rows = sample_rows(w.B, w.H, w.nQ, 1, 24, heads=[3])
+    marked = _skip_carry(w, 2, w.tau, rows=rows)
+    assert marked == 0
+
+
+# ------------------------------------------------------------ long video
+def test_fwd_hunyuan_4x_radial_sampled():
+    w = synth.workload("hunyuan_4x")
+    note(f"{w.name}: generating {w.B}x{w.N}x{w.H}x{w.d} bf16 inputs")
+    x = synth.make_qkv(w)
+    s = shape_of(w)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    mask = torch.empty(s.nQ * s.nK, dtype=torch.uint8, device=DEV)
+    bsa.bsa_build_mask_radial(s, w.h0, w.beta, mask)
+    rp = torch.empty(s.nQ + 1, dtype=torch.int32, device=DEV)
+    kv = torch.empty(s.nQ * s.nK, dtype=torch.int32, device=DEV)
+    bsa.bsa_compact_block_lists(s, mask, 0, None, rp, kv)
+    o, lse, _ = run_fwd(s, q, k, v, rp, kv, 1, w.scale)
+    ref_mask = oracle.build_mask_radial(w.T, w.Hs, w.Ws, w.Bq, w.Bk, w.h0, w.beta)
+    np.testing.assert_array_equal(host(mask).reshape(w.nQ, w.nK), ref_mask)
+    heads = [0, w.H - 1]
+    F_blocks = [a for a in range(1, w.nQ) if (a * w.Bq) // w.F != ((a + 1) * w.Bq - 1) // w.F]
+    rows = sample_rows(w.B, w.H, w.nQ, 3, 9, heads=heads, extra=F_blocks[:1])
+    note(f"{w.name}: oracle on {len(rows)} sampled row blocks")
+    o_ref, lse_ref, _ = oracle.attention(x["q"], x["k"], x["v"], w.Bq, w.Bk, w.scale, ref_mask,
+                                         0, rows=rows)
+    og, lg = gather_rows(host(o), host(lse), rows, w.B, w.H, w.N, w.Bq)
+    compare(og, lg, o_ref, lse_ref, f"{w.name} sampled")
