@@ -129,46 +129,50 @@ __device__ inline void atomic_max_float(float* addr, float v) {
 // chunk c of row r stored at chunk c ^ f(r). K uses fK (conflict-free b128
 // reads of 16 consecutive rows), V uses fV (conflict-free transpose reads of
 // 4-row x 32-byte blocks).
-template <int D>
+template <int D, int ROWS = kBk>
 struct Tile {
   static constexpr int CPR = D / 8;        // chunks per row
   static constexpr int RB = D * 2;         // bytes per row
-  static constexpr int BYTES = kBk * RB;   // bytes per tile
+  static constexpr int BYTES = ROWS * RB;  // bytes per stage
   static constexpr int RPI = 1024 / RB;    // rows per 64-lane 16-byte load
-  static constexpr int IPT = kBk / RPI;    // loads per tile
+  static constexpr int IPT = ROWS / RPI;   // loads per stage
   __device__ static int fK(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
   __device__ static int fV(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
-template <int D, int BQ>
+// BQ rows per workgroup (32 per wave); SUB keys per pipeline step (a whole
+// 64-key block, or half of one so that two-wave workgroups fit four per CU).
+template <int D, int BQ, int SUB>
 struct Cfg {
-  static constexpr int NW = BQ / 32;                      // waves
-  static constexpr int NT = NW * 64;                      // threads
-  static constexpr int KS = D / 16;                       // k-steps of Q K^T
-  static constexpr int DB = D / 32;                       // 32-wide d blocks of O
-  static constexpr int LPW = Tile<D>::IPT / NW;           // loads per tile per wave (K or V)
-  static constexpr int VOFF = kKStages * Tile<D>::BYTES;  // V stages follow the K stages
-  static constexpr int SMEM = (kKStages + kVStages) * Tile<D>::BYTES;
-  static constexpr int OLD = D + 8;                       // O staging row stride (elements)
+  using T = Tile<D, SUB>;
+  static constexpr int NW = BQ / 32;                // waves
+  static constexpr int NT = NW * 64;                // threads
+  static constexpr int KS = D / 16;                 // k-steps of Q K^T
+  static constexpr int DB = D / 32;                 // 32-wide d blocks of O
+  static constexpr int KB = SUB / 32;               // 32-key blocks per step
+  static constexpr int NSUB = kBk / SUB;            // steps per key block
+  static constexpr int LPW = T::IPT / NW;           // loads per stage per wave (K or V)
+  static constexpr int VOFF = kKStages * T::BYTES;  // V stages follow the K stages
+  static constexpr int SMEM = (kKStages + kVStages) * T::BYTES;
+  static constexpr int OLD = D + 8;                 // O staging row stride (elements)
   static_assert(LPW >= 1, "tile loader split");
   static_assert(BQ * OLD * 2 <= SMEM, "O staging must fit in the stages");
 };
 
-// Per-lane voffsets of this wave's LPW direct loads of one K tile and one V
-// tile (swizzles fK and fV applied on the global side).
-template <int D, int BQ>
+// Per-lane voffsets of this wave's LPW direct loads of one K stage and one V
+// stage (swizzles fK and fV applied on the global side).
+template <int LPW>
 struct LoadPlan {
-  uint32_t k[Cfg<D, BQ>::LPW];
-  uint32_t v[Cfg<D, BQ>::LPW];
+  uint32_t k[LPW];
+  uint32_t v[LPW];
 };
 
-template <int D, int BQ>
-__device__ inline void make_plan(LoadPlan<D, BQ>& lp, int w, int lane, int64_t ksn, int64_t vsn) {
+template <int D, int NW, int LPW>
+__device__ inline void make_plan(LoadPlan<LPW>& lp, int w, int lane, int64_t ksn, int64_t vsn) {
   using T = Tile<D>;
-  using C = Cfg<D, BQ>;
 #pragma unroll
-  for (int i = 0; i < C::LPW; ++i) {
-    const int idx = w + C::NW * i;
+  for (int i = 0; i < LPW; ++i) {
+    const int idx = w + NW * i;
     const int r = T::RPI * idx + lane / T::CPR;
     const int phys = lane % T::CPR;
     lp.k[i] = (uint32_t)(r * ksn * 2 + (phys ^ T::fK(r)) * 16);
@@ -189,19 +193,16 @@ __device__ inline void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
                :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 
-// This wave's share of the direct global -> LDS loads of one 64-row tile
-// (`stage` is an LDS byte address).
-template <int D, int BQ>
+// This wave's share of the direct global -> LDS loads of `rows` (0..SUB)
+// key rows starting at j0 (`stage` is an LDS byte address).
+template <int NW, int LPW>
 __device__ inline void issue_rows(const uint32_t* off, const uint16_t* base, int64_t sn,
-                                  int64_t c, int64_t N, uint32_t stage, int w) {
-  using C = Cfg<D, BQ>;
-  const int64_t j0 = c * kBk;
-  const int64_t rows = min((int64_t)kBk, N - j0);
+                                  int64_t j0, int64_t rows, uint32_t stage, int w) {
   const uint64_t a = (uint64_t)(base + j0 * sn);
   const i32x4 rs = {(int32_t)(uint32_t)a, (int32_t)((a >> 32) & 0xffff), (int32_t)(rows * sn * 2),
                     kRsrcWord3};
 #pragma unroll
-  for (int i = 0; i < C::LPW; ++i) dma16(rs, stage + (uint32_t)(w + C::NW * i) * 1024, off[i]);
+  for (int i = 0; i < LPW; ++i) dma16(rs, stage + (uint32_t)(w + NW * i) * 1024, off[i]);
 }
 
 __device__ inline bf16x8 join(i16x4 lo, i16x4 hi) {
@@ -212,10 +213,12 @@ __device__ inline bf16x8 join(i16x4 lo, i16x4 hi) {
 // Key of lane value j (0..15) of 32-key block kb: kb*32 + 8*(j/4) + 4*hh + j%4.
 __device__ inline int key_of(int kb, int j, int hh) { return kb * 32 + 8 * (j / 4) + 4 * hh + (j % 4); }
 
-template <int D, int BQ, bool GAP>
-__global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p) {
-  using C = Cfg<D, BQ>;
-  using T = Tile<D>;
+template <int D, int BQ, int SUB, bool GAP>
+__global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bf16_kernel(const Bf16Params p) {
+  using C = Cfg<D, BQ, SUB>;
+  using T = typename C::T;
+  constexpr int KB = C::KB, NSUB = C::NSUB;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
 
   const int tid = threadIdx.x;
@@ -258,39 +261,50 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
     e1 = load_uniform(p.row_ptr, lr + 1);
     if (GAP && p.lists_shared) gbase = bh * (int64_t)load_uniform(p.row_ptr, p.nQ);
   }
-  const int64_t L = e1 - e0;
+  const int64_t L = e1 - e0;     // listed key blocks
+  const int64_t LS = L * NSUB;   // pipeline steps (SUB keys each)
   const uint16_t* kbase = p.k + b * p.ksb + h * p.ksh;
   const uint16_t* vbase = p.v + b * p.vsb + h * p.vsh;
-  auto block_of = [&](int64_t i) -> int64_t {
+  // Step u covers keys [j0, j0 + SUB) with j0 = 64 * (key block of list
+  // entry u / NSUB) + SUB * (u % NSUB); part = u % NSUB is static in the
+  // unrolled loop below.
+  auto block_of = [&](int64_t u) -> int64_t {
+    const int64_t i = u / NSUB;
     return p.row_ptr ? (int64_t)load_uniform(p.kv_idx, e0 + i) : e0 + i;
   };
-  auto valid_keys = [&](int64_t c) -> int { return (int)min((int64_t)kBk, p.N - c * kBk); };
+  auto first_key = [&](int64_t c, int part) -> int64_t { return c * kBk + part * SUB; };
+  auto valid_keys = [&](int64_t c, int part) -> int {
+    return (int)max((int64_t)0, min((int64_t)SUB, p.N - first_key(c, part)));
+  };
 
-  LoadPlan<D, BQ> lp;
-  make_plan<D, BQ>(lp, w, lane, p.ksn, p.vsn);
-  // Stage byte offsets: tile i uses K stage i % 2 and V stage i % 2.
+  LoadPlan<C::LPW> lp;
+  make_plan<D, C::NW, C::LPW>(lp, w, lane, p.ksn, p.vsn);
+  // Stage byte offsets: step u uses K stage u % 2 and V stage u % 2.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   constexpr int kso[2] = {0, T::BYTES};
   constexpr int vso[2] = {C::VOFF, C::VOFF + T::BYTES};
-  auto issue_k = [&](int so, int64_t c) {
-    issue_rows<D, BQ>(lp.k, kbase, p.ksn, c, p.N, lds0 + so, w);
+  auto issue_k = [&](int so, int64_t c, int part) {
+    issue_rows<C::NW, C::LPW>(lp.k, kbase, p.ksn, first_key(c, part), valid_keys(c, part),
+                              lds0 + so, w);
   };
-  auto issue_v = [&](int so, int64_t c) {
-    issue_rows<D, BQ>(lp.v, vbase, p.vsn, c, p.N, lds0 + so, w);
+  auto issue_v = [&](int so, int64_t c, int part) {
+    issue_rows<C::NW, C::LPW>(lp.v, vbase, p.vsn, first_key(c, part), valid_keys(c, part),
+                              lds0 + so, w);
   };
+  constexpr int PART1 = NSUB == 2 ? 1 : 0;  // part of step 1 (and of every odd step)
 
-  // Key-block indices of list entries it, it+1, it+2 (rolling).
+  // Key blocks of steps it, it+1, it+2 (rolling).
   int64_t c0 = 0, c1 = 0, c2 = 0;
-  if (L > 0) {
+  if (LS > 0) {
     c0 = block_of(0);
-    issue_k(kso[0], c0);
-    issue_v(vso[0], c0);
+    issue_k(kso[0], c0, 0);
+    issue_v(vso[0], c0, 0);
   }
-  if (L > 1) {
+  if (LS > 1) {
     c1 = block_of(1);
-    issue_k(kso[1], c1);
+    issue_k(kso[1], c1, PART1);
   }
-  if (L > 2) c2 = block_of(2);
+  if (LS > 2) c2 = block_of(2);
 
   // Q rows of this wave as MFMA B operands (k-slice hh*8..+7 of each 16-step).
   const int64_t qrow = a * BQ + w * 32 + n;
@@ -329,50 +343,56 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
   for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
   float m_use = -INFINITY;   // exponent base of p and l (log2 units)
   float m_true = -INFINITY;  // running row max (log2 units), for the tile gaps
+  float m_blk = -INFINITY;   // row max of the current key block's steps so far
   float l_lane = 0.f;        // this lane half's share of the row sum
 
   // ---- pipeline pieces
-  // Scores of one K stage: two 32-key blocks.
-  auto scores = [&](const char* kt, f32x16(&sacc)[2]) {
-    sacc[0] = f32x16{};
-    sacc[1] = f32x16{};
+  // Scores of one K stage: KB 32-key blocks.
+  auto scores = [&](const char* kt, f32x16(&sacc)[KB]) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         const bf16x8 av = *(const bf16x8*)(kt + koff[ks] + kb * 32 * T::RB);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sacc[kb], 0, 0, 0);
       }
     }
   };
-  // Row max of a tile's scores in log2 units. When `masked`, keys at or
+  // Row max of a step's scores in log2 units. When `masked`, keys at or
   // beyond jv (only the last key block can be ragged) are set to -inf first,
-  // which also makes their probabilities 0.
-  auto tile_max = [&](f32x16(&sacc)[2], bool masked, int jv) -> float {
+  // which also makes their probabilities 0. A step with no valid key (second
+  // half of a short last block) has max -inf.
+  auto tile_max = [&](f32x16(&sacc)[KB], bool masked, int jv) -> float {
     if (masked) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
           if (key_of(kb, j, hh) >= jv) sacc[kb][j] = -INFINITY;
     }
     float mloc = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mloc = fmaxf(mloc, sacc[kb][j]);
     mloc = fmaxf(mloc, other_half(mloc));
     return mloc * p.sl2;
   };
-  // Tile gap and exponent-base update for a tile whose row max is m_loc2. O
-  // must already hold every earlier tile when this runs (it may be rescaled).
-  auto apply_max = [&](float m_loc2, int64_t entry) {
+  // Tile gap (once the key block's last step is in) and exponent-base update
+  // for a step whose row max is m_loc2. O must already hold every earlier
+  // step when this runs (it may be rescaled).
+  auto apply_max = [&](float m_loc2, int64_t u, int part) {
     if (GAP) {
-      float g = qvalid ? m_loc2 - m_true : -INFINITY;
+      m_blk = part == 0 ? m_loc2 : fmaxf(m_blk, m_loc2);
+      if (part == NSUB - 1) {
+        float g = qvalid ? m_blk - m_true : -INFINITY;
 #pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) g = fmaxf(g, __shfl_xor(g, off, 32));
-      if (lane == 0) atomic_max_float(p.tile_gap + gbase + e0 + entry, g);
-      m_true = fmaxf(m_true, m_loc2);
+        for (int off = 16; off >= 1; off >>= 1) g = fmaxf(g, __shfl_xor(g, off, 32));
+        if (lane == 0) atomic_max_float(p.tile_gap + gbase + e0 + u / NSUB, g);
+        m_true = fmaxf(m_true, m_blk);
+      }
     }
     if (__builtin_amdgcn_ballot_w64(m_loc2 > m_use + kRescaleSlack)) {
       const float m_new = fmaxf(m_use, m_loc2);
@@ -384,11 +404,11 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
     }
   };
   // p = 2^(s*scale*log2e - m) rounded to bf16, and its row sum. Masked keys
-  // hold -inf and give 0.
-  auto probs = [&](const f32x16(&sacc)[2], bf16x8(&pb)[2][2]) {
+  // hold -inf and give 0 (sl2 > 0 always, see launch_attn_bf16).
+  auto probs = [&](const f32x16(&sacc)[KB], bf16x8(&pb)[KB][2]) {
     const float neg_m = -m_use;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         f32x8 pv;
@@ -408,9 +428,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
   // operand is pb[kb][half]; element t of lane half hh is key
   // kb*32 + 16*half + 8*(t/4) + 4*hh + t%4, which two transpose reads of the
   // V tile deliver in that order.
-  auto accumulate = [&](const char* vt, const bf16x8(&pb)[2][2]) {
+  auto accumulate = [&](const char* vt, const bf16x8(&pb)[KB][2]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int kofs = (kb * 32 + 16 * half) * T::RB;
@@ -430,36 +450,38 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
   // V(j+1) and K(j+2) are issued right after the barrier of step j, into
   // stages last read before that barrier, and waited for at the start of
   // step j+1.
-  f32x16 sA[2], sB[2];
-  if (L > 0) {
-    // prologue: scores and max of tile 0
-    if (L > 1) wait_vmcnt<2 * C::LPW>();  // K0 done; V0, K1 may fly
+  f32x16 sA[KB], sB[KB];
+  if (LS > 0) {
+    // prologue: scores and max of step 0
+    if (LS > 1) wait_vmcnt<2 * C::LPW>();  // K0 done; V0, K1 may fly
     else wait_vmcnt<C::LPW>();
     barrier();
     scores(smem + kso[0], sA);
-    apply_max(tile_max(sA, true, valid_keys(c0)), 0);
+    const int jv = valid_keys(c0, 0);
+    apply_max(tile_max(sA, jv < SUB, jv), 0, 0);
   }
-  // One pipeline step: tile `it` has scores in `cur`; when `has_next`, the
-  // scores of tile it+1 are computed into `nxt` meanwhile. Every LDS read of
+  // One pipeline step: step `it` has scores in `cur`; when `has_next`, the
+  // scores of step it+1 are computed into `nxt` meanwhile. Every LDS read of
   // the previous step has completed before the barrier (lgkmcnt(0)), so the
-  // stages it read may be refilled right after it.
-  auto step = [&](int64_t it, f32x16(&cur)[2], f32x16(&nxt)[2], bool has_next, auto par_c) {
+  // stages it read may be refilled right after it. `par` = it % 2.
+  auto step = [&](int64_t it, f32x16(&cur)[KB], f32x16(&nxt)[KB], bool has_next, auto par_c) {
     constexpr int par = decltype(par_c)::value;
+    constexpr int part0 = NSUB == 2 ? par : 0, part1 = NSUB == 2 ? 1 - par : 0;
     wait_vmcnt<0>();  // V(it) and K(it+1) done
     wait_lds();
     barrier();
-    if (it + 1 < L) issue_v(vso[1 - par], c1);
-    if (it + 2 < L) issue_k(kso[par], c2);
-    const int64_t c3 = it + 3 < L ? block_of(it + 3) : 0;
-    bf16x8 pb[2][2];
+    if (it + 1 < LS) issue_v(vso[1 - par], c1, part1);
+    if (it + 2 < LS) issue_k(kso[par], c2, part0);
+    const int64_t c3 = it + 3 < LS ? block_of(it + 3) : 0;
+    bf16x8 pb[KB][2];
     if (has_next) {
-      // phase A: exponentials of tile it with the score MFMAs of tile it+1
+      // phase A: exponentials of step it with the score MFMAs of step it+1
       scores(smem + kso[1 - par], nxt);
       probs(cur, pb);
-      // phase B: P V of tile it with the row max of tile it+1
+      // phase B: P V of step it with the row max of step it+1
       accumulate(smem + vso[par], pb);
-      const int jv = valid_keys(c1);
-      apply_max(tile_max(nxt, jv < kBk, jv), it + 1);
+      const int jv = valid_keys(c1, part1);
+      apply_max(tile_max(nxt, jv < SUB, jv), it + 1, part1);
     } else {
       probs(cur, pb);
       accumulate(smem + vso[par], pb);
@@ -471,14 +493,14 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(const Bf16Params p
   int64_t it = 0;
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  for (; it + 2 < L; it += 2) {
+  for (; it + 2 < LS; it += 2) {
     step(it, sA, sB, true, P0{});
     step(it + 1, sB, sA, true, P1{});
   }
-  if (it + 1 < L) {
+  if (it + 1 < LS) {
     step(it, sA, sB, true, P0{});
     step(it + 1, sB, sA, false, P1{});
-  } else if (it < L) {
+  } else if (it < LS) {
     step(it, sA, sB, false, P0{});
   }
 
@@ -524,6 +546,10 @@ __global__ void gap_init_kernel(float* gap, const int32_t* row_ptr, int64_t R, i
 
 template <int D, int BQ>
 hipError_t launch(const Geom& g, const Bf16Params& p, hipStream_t st) {
+  // Two-wave workgroups step through half key blocks (32 KiB of LDS, four
+  // workgroups per CU); four-wave ones through whole blocks.
+  constexpr int SUB = BQ == 64 ? 32 : 64;
+  using C = Cfg<D, BQ, SUB>;
   const int64_t rows = (int64_t)g.B * g.H * (p.U ? (int64_t)g.T * p.U : g.nQ);
   if (p.tile_gap) {
     // per-wave gaps are folded in with an atomic max starting from -inf
@@ -531,11 +557,11 @@ hipError_t launch(const Geom& g, const Bf16Params& p, hipStream_t st) {
     const int64_t mult = p.lists_shared ? (int64_t)g.B * g.H : 1;
     hipLaunchKernelGGL(gap_init_kernel, dim3(1024), dim3(256), 0, st, p.tile_gap, p.row_ptr, R,
                        mult);
-    hipLaunchKernelGGL((attn_bf16_kernel<D, BQ, true>), dim3((unsigned)rows),
-                       dim3(Cfg<D, BQ>::NT), 0, st, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BQ, SUB, true>), dim3((unsigned)rows), dim3(C::NT),
+                       0, st, p);
   } else {
-    hipLaunchKernelGGL((attn_bf16_kernel<D, BQ, false>), dim3((unsigned)rows),
-                       dim3(Cfg<D, BQ>::NT), 0, st, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BQ, SUB, false>), dim3((unsigned)rows), dim3(C::NT),
+                       0, st, p);
   }
   return hipGetLastError();
 }
@@ -558,7 +584,11 @@ hipError_t launch_attn_bf16(const Geom& g, const AttnArgs& a, hipStream_t st) {
   p.kv_idx = a.kv_idx;
   p.tile_gap = a.tile_gap;
   p.lists_shared = a.lists_shared;
-  p.sl2 = a.scale * kLog2e;
+  // Scores enter every exponent as s * sl2. A zero scale is taken as the
+  // smallest normal float instead: finite scores then still contribute
+  // 2^(~0) (off by far less than bf16 rounding) while masked keys (-inf)
+  // keep probability 0 instead of turning into NaN.
+  p.sl2 = fmaxf(a.scale * kLog2e, 1.17549435e-38f);
   p.N = g.N; p.nQ = g.nQ; p.nK = g.nK; p.H = g.H;
   p.T = g.T; p.F = g.F; p.U = (int32_t)((g.F + g.Bq - 1) / g.Bq);
   if ((int64_t)g.T * p.U > g.nQ + g.nQ / 4) p.U = 0;  // tiny frames: plain row order

@@ -194,3 +194,21 @@ def test_fwd_all_rows_empty():
                               gap_len=1)
         assert torch.count_nonzero(o.float()).item() == 0
         assert bool(torch.all(torch.isneginf(lse)))
+
+
+@pytest.mark.parametrize("Bq", [64, 128])
+def test_fwd_zero_scale_ragged(Bq):
+    """scale = 0: uniform weights over each row's listed keys, ragged last block included."""
+    w = small(128, Bq, T=3, Hs=7, Ws=9, B=1, H=2)
+    x = synth.make_qkv(w)
+    s = shape_of(w)
+    mask_np = _random_lists(w, 11)
+    mask_np[..., w.nK - 1] = 1
+    rp = torch.empty(w.B * w.H * w.nQ + 1, dtype=torch.int32, device=DEV)
+    kv = torch.empty(w.B * w.H * w.nQ * w.nK, dtype=torch.int32, device=DEV)
+    bsa.bsa_compact_block_lists(s, dev(mask_np), w.nQ * w.nK, None, rp, kv)
+    o, lse, _ = run_fwd(s, dev(x["q"]), dev(x["k"]), dev(x["v"]), rp, kv, 0, 0.0)
+    o_ref, lse_ref, _ = oracle.attention(x["q"], x["k"], x["v"], w.Bq, w.Bk, 0.0, mask_np,
+                                         w.nQ * w.nK)
+    og, lg = gather_rows(host(o), host(lse), np.arange(w.B * w.H * w.nQ), w.B, w.H, w.N, w.Bq)
+    compare(og, lg, o_ref, lse_ref, f"zero scale Bq={Bq}")
