@@ -68,6 +68,44 @@ def traffic_for(workload: str):
     return t.get("traffic_bytes_per_launch")
 
 
+def _counter_mean(folder: str, kernel_substr: str, counter: str) -> tuple[float, int]:
+    """Mean per-dispatch value of a rocprofv3 counter over the dispatches of a kernel."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                    vals[(f, r["Dispatch_Id"])] = vals.get((f, r["Dispatch_Id"]), 0.0) + \
+                        float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {kernel_substr!r} in {folder}")
+    return float(np.mean(list(vals.values()))), len(vals)
+
+
+def ingest_counters(workload: str, fetch_dir: str, write_dir: str, copy_f: str, copy_w: str):
+    """HBM bytes per forward launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
+    scaled by what the same counter reads for a device copy of 1 GiB each way."""
+    fetch, nf = _counter_mean(fetch_dir, "attn_bf16_kernel", "FETCH_SIZE")
+    write, nw = _counter_mean(write_dir, "attn_bf16_kernel", "WRITE_SIZE")
+    cf, _ = _counter_mean(copy_f, "copyBuffer", "FETCH_SIZE")
+    cw, _ = _counter_mean(copy_w, "copyBuffer", "WRITE_SIZE")
+    kib = float(1 << 20)  # 1 GiB in KiB, each way
+    f_fetch, f_write = kib / cf, kib / cw
+    traffic = (fetch * f_fetch + write * f_write) * 1024.0
+    out = {"workload": workload, "source_sha256": source_sha(),
+           "kernel": "attn_bf16_kernel", "dispatches": [nf, nw],
+           "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+           "copy_fetch_kib_per_gib": cf, "copy_write_kib_per_gib": cw,
+           "fetch_scale": f_fetch, "write_scale": f_write,
+           "traffic_bytes_per_launch": traffic}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -77,12 +115,20 @@ def main():
     ap.add_argument("--tau", type=float, default=None,
                     help="skip-carry threshold override (natural-log units; default: the "
                          "workload's)")
-    ap.add_argument("--cpu-rows", type=int, default=192,
+    ap.add_argument("--cpu-rows", type=int, default=800,
                     help="row blocks in the CPU oracle sample (0 = skip)")
     ap.add_argument("--no-dense", action="store_true", help="skip the all-tiles timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
+                                                          "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn four rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE "
+                         "of this workload's bench run and of --calibrate-copy-mib 1024) into "
+                         "profiles/traffic.json; no GPU work")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(args.workload, *args.ingest_counters)
+        return
 
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
