@@ -188,21 +188,30 @@ __device__ inline void make_plan(LoadPlan<LPW>& lp, int w, int lane, int64_t ksn
 // s_nop is the one wait state required between an M0 write and an LDS DMA
 // load that reads it. Rows at or beyond the descriptor's num_records read as
 // zero.
-__device__ inline void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+template <uint32_t OFS>
+__device__ inline void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_base), "v"(voff), "s"(rsrc), "n"(OFS) : "memory", "m0", "scc");
 }
 
 // This wave's share of the direct global -> LDS loads of `rows` (0..SUB)
-// key rows starting at j0 (`stage` is an LDS byte address).
-template <int NW, int LPW>
-__device__ inline void issue_rows(const uint32_t* off, const uint16_t* base, int64_t sn,
-                                  int64_t j0, int64_t rows, uint32_t stage, int w) {
-  const uint64_t a = (uint64_t)(base + j0 * sn);
-  const i32x4 rs = {(int32_t)(uint32_t)a, (int32_t)((a >> 32) & 0xffff), (int32_t)(rows * sn * 2),
-                    kRsrcWord3};
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) dma16(rs, stage + (uint32_t)(w + NW * i) * 1024, off[i]);
+// key rows starting at j0 into the stage at byte offset SO; `wave_lds` is the
+// LDS address of this wave's first 1 KiB slot (LDS base + 1024 * wave).
+template <int NW, int LPW, uint32_t SO, int I = 0>
+__device__ inline void issue_rows(const uint32_t* off, const i32x4& rs, uint32_t wave_lds) {
+  if constexpr (I < LPW) {
+    dma16<SO + NW * I * 1024>(rs, wave_lds, off[I]);
+    issue_rows<NW, LPW, SO, I + 1>(off, rs, wave_lds);
+  }
+}
+
+// Buffer descriptor for `rows` key rows from row j0 of a (b, h) slice with
+// row stride sn elements; reads at or beyond the last row return zero.
+__device__ inline i32x4 rows_rsrc(const uint16_t* base, int64_t sn, int j0, int rows) {
+  const uint64_t a = (uint64_t)(base + (int64_t)j0 * sn);
+  // wave-uniform by construction; readfirstlane keeps the descriptor in SGPRs
+  return i32x4{wave_uniform((int32_t)(uint32_t)a), wave_uniform((int32_t)((a >> 32) & 0xffff)),
+               wave_uniform(rows * (int32_t)sn * 2), kRsrcWord3};
 }
 
 __device__ inline bf16x8 join(i16x4 lo, i16x4 hi) {
@@ -254,55 +263,67 @@ void attn_bf16_kernel(const Bf16Params p) {
   const int64_t row = bh * p.nQ + a;  // list row when lists are per head
   const int64_t b = bh / p.H, h = bh - b * p.H;
 
-  int64_t e0 = 0, e1 = p.nK, gbase = 0;
+  // List entries, steps and key rows fit in 32 bits (row_ptr is int32 and
+  // N < 2^31); 32-bit scalar arithmetic keeps the loop's index math on the
+  // scalar unit.
+  int e0 = 0, e1 = (int)p.nK;
+  int64_t gbase = 0;
   if (p.row_ptr) {
     const int64_t lr = p.lists_shared ? a : row;
     e0 = load_uniform(p.row_ptr, lr);
     e1 = load_uniform(p.row_ptr, lr + 1);
     if (GAP && p.lists_shared) gbase = bh * (int64_t)load_uniform(p.row_ptr, p.nQ);
   }
-  const int64_t L = e1 - e0;     // listed key blocks
-  const int64_t LS = L * NSUB;   // pipeline steps (SUB keys each)
+  const int L = e1 - e0;      // listed key blocks
+  const int LS = L * NSUB;    // pipeline steps (SUB keys each)
+  const int N32 = (int)p.N;
   const uint16_t* kbase = p.k + b * p.ksb + h * p.ksh;
   const uint16_t* vbase = p.v + b * p.vsb + h * p.vsh;
   // Step u covers keys [j0, j0 + SUB) with j0 = 64 * (key block of list
   // entry u / NSUB) + SUB * (u % NSUB); part = u % NSUB is static in the
   // unrolled loop below.
-  auto block_of = [&](int64_t u) -> int64_t {
-    const int64_t i = u / NSUB;
-    return p.row_ptr ? (int64_t)load_uniform(p.kv_idx, e0 + i) : e0 + i;
+  auto block_of = [&](int u) -> int {
+    const int i = u / NSUB;
+    return p.row_ptr ? load_uniform(p.kv_idx, e0 + i) : e0 + i;
   };
-  auto first_key = [&](int64_t c, int part) -> int64_t { return c * kBk + part * SUB; };
-  auto valid_keys = [&](int64_t c, int part) -> int {
-    return (int)max((int64_t)0, min((int64_t)SUB, p.N - first_key(c, part)));
+  auto first_key = [&](int c, int part) -> int { return c * kBk + part * SUB; };
+  auto valid_keys = [&](int c, int part) -> int {
+    return max(0, min(SUB, N32 - first_key(c, part)));
   };
 
   LoadPlan<C::LPW> lp;
   make_plan<D, C::NW, C::LPW>(lp, w, lane, p.ksn, p.vsn);
   // Stage byte offsets: step u uses K stage u % 2 and V stage u % 2.
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  const uint32_t wave_lds =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem + (uint32_t)w * 1024;
   constexpr int kso[2] = {0, T::BYTES};
   constexpr int vso[2] = {C::VOFF, C::VOFF + T::BYTES};
-  auto issue_k = [&](int so, int64_t c, int part) {
-    issue_rows<C::NW, C::LPW>(lp.k, kbase, p.ksn, first_key(c, part), valid_keys(c, part),
-                              lds0 + so, w);
+  auto issue_k = [&](auto so_c, int c, int part) {
+    const int j0 = first_key(c, part);
+    issue_rows<C::NW, C::LPW, decltype(so_c)::value>(
+        lp.k, rows_rsrc(kbase, p.ksn, j0, max(0, min(SUB, N32 - j0))), wave_lds);
   };
-  auto issue_v = [&](int so, int64_t c, int part) {
-    issue_rows<C::NW, C::LPW>(lp.v, vbase, p.vsn, first_key(c, part), valid_keys(c, part),
-                              lds0 + so, w);
+  auto issue_v = [&](auto so_c, int c, int part) {
+    const int j0 = first_key(c, part);
+    issue_rows<C::NW, C::LPW, decltype(so_c)::value>(
+        lp.v, rows_rsrc(vbase, p.vsn, j0, max(0, min(SUB, N32 - j0))), wave_lds);
   };
+  using K0 = std::integral_constant<uint32_t, kso[0]>;
+  using K1 = std::integral_constant<uint32_t, kso[1]>;
+  using V0 = std::integral_constant<uint32_t, vso[0]>;
+  using V1 = std::integral_constant<uint32_t, vso[1]>;
   constexpr int PART1 = NSUB == 2 ? 1 : 0;  // part of step 1 (and of every odd step)
 
   // Key blocks of steps it, it+1, it+2 (rolling).
-  int64_t c0 = 0, c1 = 0, c2 = 0;
+  int c0 = 0, c1 = 0, c2 = 0;
   if (LS > 0) {
     c0 = block_of(0);
-    issue_k(kso[0], c0, 0);
-    issue_v(vso[0], c0, 0);
+    issue_k(K0{}, c0, 0);
+    issue_v(V0{}, c0, 0);
   }
   if (LS > 1) {
     c1 = block_of(1);
-    issue_k(kso[1], c1, PART1);
+    issue_k(K1{}, c1, PART1);
   }
   if (LS > 2) c2 = block_of(2);
 
@@ -383,7 +404,7 @@ void attn_bf16_kernel(const Bf16Params p) {
   // Tile gap (once the key block's last step is in) and exponent-base update
   // for a step whose row max is m_loc2. O must already hold every earlier
   // step when this runs (it may be rescaled).
-  auto apply_max = [&](float m_loc2, int64_t u, int part) {
+  auto apply_max = [&](float m_loc2, int u, int part) {
     if (GAP) {
       m_blk = part == 0 ? m_loc2 : fmaxf(m_blk, m_loc2);
       if (part == NSUB - 1) {
@@ -464,15 +485,17 @@ void attn_bf16_kernel(const Bf16Params p) {
   // scores of step it+1 are computed into `nxt` meanwhile. Every LDS read of
   // the previous step has completed before the barrier (lgkmcnt(0)), so the
   // stages it read may be refilled right after it. `par` = it % 2.
-  auto step = [&](int64_t it, f32x16(&cur)[KB], f32x16(&nxt)[KB], bool has_next, auto par_c) {
+  auto step = [&](int it, f32x16(&cur)[KB], f32x16(&nxt)[KB], bool has_next, auto par_c) {
     constexpr int par = decltype(par_c)::value;
     constexpr int part0 = NSUB == 2 ? par : 0, part1 = NSUB == 2 ? 1 - par : 0;
+    using KS_ = std::integral_constant<uint32_t, kso[par]>;
+    using VS_ = std::integral_constant<uint32_t, vso[1 - par]>;
     wait_vmcnt<0>();  // V(it) and K(it+1) done
     wait_lds();
     barrier();
-    if (it + 1 < LS) issue_v(vso[1 - par], c1, part1);
-    if (it + 2 < LS) issue_k(kso[par], c2, part0);
-    const int64_t c3 = it + 3 < LS ? block_of(it + 3) : 0;
+    if (it + 1 < LS) issue_v(VS_{}, c1, part1);
+    if (it + 2 < LS) issue_k(KS_{}, c2, part0);
+    const int c3 = it + 3 < LS ? block_of(it + 3) : 0;
     bf16x8 pb[KB][2];
     if (has_next) {
       // phase A: exponentials of step it with the score MFMAs of step it+1
@@ -490,7 +513,7 @@ void attn_bf16_kernel(const Bf16Params p) {
     c1 = c2;
     c2 = c3;
   };
-  int64_t it = 0;
+  int it = 0;
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   for (; it + 2 < LS; it += 2) {
