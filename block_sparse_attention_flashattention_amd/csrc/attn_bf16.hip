@@ -30,10 +30,13 @@
 //  * Software pipeline, one barrier per tile. While the exponentials of tile
 //    i run on the VALU, the matrix core computes the scores of tile i+1;
 //    while it accumulates P_i V_i, the VALU reduces the row maxima of tile
-//    i+1. K and V have two LDS stages each (tiles i+2 and i+1 are requested
-//    right after the barrier of step i): 64 KiB, two workgroups per CU. The
-//    loop is unrolled by two so that every stage address is a constant
-//    offset of the LDS read instructions.
+//    i+1. Each of the two phases is laid out slot by slot: one MFMA per slot,
+//    its share of the VALU work, and the LDS fragment reads for the MFMA
+//    three slots ahead, with a scheduling fence between slots so that the
+//    compiler keeps this interleave. K and V have two LDS stages each (tiles
+//    i+2 and i+1 are requested right after the barrier of step i): 64 KiB,
+//    two workgroups per CU. The loop is unrolled by two so that every stage
+//    address is a constant offset of the LDS read instructions.
 //  * Rescaling of O is lazy: the exponent base moves only when the row max
 //    grows by more than 2^8, which keeps p <= 256 and leaves the result exact
 //    up to rounding (numerator and denominator share the base).
@@ -56,6 +59,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -72,6 +76,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
+constexpr int kPfK = 3;  // K fragment reads issued ahead of their score MFMA (slots)
+constexpr int kPfV = 3;  // V fragment reads issued ahead of their P V MFMA (slots)
 
 struct Bf16Params {
   const uint16_t* q;
@@ -155,7 +161,14 @@ struct Cfg {
   static constexpr int VOFF = kKStages * T::BYTES;  // V stages follow the K stages
   static constexpr int SMEM = (kKStages + kVStages) * T::BYTES;
   static constexpr int OLD = D + 8;                 // O staging row stride (elements)
+  static constexpr int NA = KS * KB;                // score MFMAs per step
+  static constexpr int NB = KB * 2 * DB;            // P V MFMAs per step
+  static constexpr int EPS = 16 * KB / NA;          // probabilities per score MFMA (per lane)
+  static constexpr int MPS = 16 * KB / NB;          // max inputs per P V MFMA (per lane)
   static_assert(LPW >= 1, "tile loader split");
+  static_assert(EPS % 2 == 0 && MPS % 2 == 0 && EPS * NA == 16 * KB && MPS * NB == 16 * KB,
+                "softmax work splits evenly over the MFMA slots");
+  static_assert(kPfK < NA && kPfV < NB, "fragment prefetch depth");
   static_assert(BQ * OLD * 2 <= SMEM, "O staging must fit in the stages");
 };
 
@@ -498,13 +511,85 @@ void attn_bf16_kernel(const Bf16Params p) {
     const int c3 = it + 3 < LS ? block_of(it + 3) : 0;
     bf16x8 pb[KB][2];
     if (has_next) {
-      // phase A: exponentials of step it with the score MFMAs of step it+1
-      scores(smem + kso[1 - par], nxt);
-      probs(cur, pb);
-      // phase B: P V of step it with the row max of step it+1
-      accumulate(smem + vso[par], pb);
+      const char* kt = smem + kso[1 - par];
+      const char* vt = smem + vso[par];
+      // K fragment of score MFMA i (k-step i / KB, key block i % KB) and V^T
+      // fragment of P V MFMA i (key block, 16-key half, d block).
+      auto kread = [&](int i) -> bf16x8 {
+        return *(const bf16x8*)(kt + koff[i / KB] + (i % KB) * 32 * T::RB);
+      };
+      auto vread = [&](int i) -> bf16x8 {
+        const int kb = i / (2 * C::DB), half = (i / C::DB) % 2, db = i % C::DB;
+        const int kofs = (kb * 32 + 16 * half) * T::RB;
+        const i16x4 lo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[db] + kofs));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vt + voff[db] + kofs + 8 * T::RB));
+        return join(lo, hi);
+      };
+      bf16x8 kbuf[kPfK + 1];
+      bf16x8 vbuf[kPfV + 1];
+      uint32_t pw[KB][2][4];  // probabilities as packed bf16 pairs
+      // Phase A: slot i issues score MFMA i of step it+1 and forms EPS
+      // probabilities of step it (exp2, bf16 pair, row-sum dot).
+      const float neg_m = -m_use;
+#pragma unroll
+      for (int i = 0; i < kPfK; ++i) kbuf[i] = kread(i);
+#pragma unroll
+      for (int i = 0; i < C::NA; ++i) {
+        if (i + kPfK < C::NA) kbuf[(i + kPfK) % (kPfK + 1)] = kread(i + kPfK);
+        if (i >= C::NA - kPfV) vbuf[i - (C::NA - kPfV)] = vread(i - (C::NA - kPfV));
+        const int ks = i / KB, kb = i % KB;
+        nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbuf[i % (kPfK + 1)], qf[ks],
+                                                          ks == 0 ? f32x16{} : nxt[kb], 0, 0, 0);
+#pragma unroll
+        for (int e2 = 0; e2 < C::EPS; e2 += 2) {
+          const int e = i * C::EPS + e2, kb2 = e / 16, j = e % 16;
+          const float x0 = __builtin_amdgcn_exp2f(fmaf(cur[kb2][j], p.sl2, neg_m));
+          const float x1 = __builtin_amdgcn_exp2f(fmaf(cur[kb2][j + 1], p.sl2, neg_m));
+          const bf16x2 pr = __builtin_convertvector((f32x2{x0, x1}), bf16x2);
+          pw[kb2][j / 8][(j % 8) / 2] = __builtin_bit_cast(uint32_t, pr);
+          l_lane = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, l_lane,
+                                                   false);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          pb[kb][half] = __builtin_bit_cast(
+              bf16x8, (u32x4{pw[kb][half][0], pw[kb][half][1], pw[kb][half][2], pw[kb][half][3]}));
+          // the probabilities stay in phase A (not sunk past the branch below)
+          asm volatile("" ::"v"(pb[kb][half]));
+        }
+      asm volatile("" ::"v"(l_lane));
       const int jv = valid_keys(c1, part1);
-      apply_max(tile_max(nxt, jv < SUB, jv), it + 1, part1);
+      if (jv < SUB) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (key_of(kb, j, hh) >= jv) nxt[kb][j] = -INFINITY;
+      }
+      // Phase B: slot i issues P V MFMA i of step it and folds MPS scores of
+      // step it+1 into the row max.
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < C::NB; ++i) {
+        if (i + kPfV < C::NB) vbuf[(i + kPfV) % (kPfV + 1)] = vread(i + kPfV);
+        const int kb = i / (2 * C::DB), half = (i / C::DB) % 2, db = i % C::DB;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vbuf[i % (kPfV + 1)], pb[kb][half],
+                                                           oacc[db], 0, 0, 0);
+#pragma unroll
+        for (int e2 = 0; e2 < C::MPS; e2 += 2) {
+          const int e = i * C::MPS + e2, kb2 = e / 16, j = e % 16;
+          mloc = fmaxf(mloc, fmaxf(nxt[kb2][j], nxt[kb2][j + 1]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mloc = fmaxf(mloc, other_half(mloc));
+      apply_max(mloc * p.sl2, it + 1, part1);
     } else {
       probs(cur, pb);
       accumulate(smem + vso[par], pb);
@@ -530,6 +615,7 @@ void attn_bf16_kernel(const Bf16Params p) {
   // ---- epilogue: O = O^T / l through LDS for coalesced 16-byte stores.
   const float l_tot = l_lane + other_half(l_lane);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  wait_vmcnt<0>();
   wait_lds();
   barrier();  // every wave is done reading the stages
   uint16_t* Os = (uint16_t*)smem;
