@@ -54,8 +54,10 @@ def lib():
         L.oracle_compact.argtypes = [i64] * 4 + [p, i64, p, p, p]
         L.oracle_compact.restype = i64
         L.oracle_attention.argtypes = ([i64] * 6 + [C.c_int] + [p, i64, i64, i64] * 3
-                                       + [d, p, i64, i64, p, p, p, p])
+                                       + [d, p, i64, i64, p, p, p, p, C.c_int])
         L.oracle_attention.restype = C.c_int
+        L.oracle_order_lists.argtypes = [i64] * 5 + [C.c_int, p, p, p]
+        L.oracle_order_lists.restype = None
         _lib = L
     return _lib
 
@@ -144,11 +146,29 @@ def compact(mask: np.ndarray, B: int, H: int, nQ: int, nK: int,
     return row_ptr, kv_idx[:nnz]
 
 
+ORDER_ASCENDING, ORDER_RADIAL = 0, 1
+
+
+def order_lists(row_ptr: np.ndarray, kv_idx: np.ndarray, N: int, bq: int, bk: int,
+                order: int) -> np.ndarray:
+    """Each CSR row's key blocks in visiting order (LiteAttention summary page,
+    section 五: radial-centric order; see oracle_order_lists)."""
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    kv_in = np.ascontiguousarray(kv_idx, dtype=np.int32)
+    nQ = -(-N // bq)
+    out = np.empty_like(kv_in)
+    if kv_in.size:
+        lib().oracle_order_lists(N, bq, bk, nQ, row_ptr.size - 1, int(order), _ptr(row_ptr),
+                                 _ptr(kv_in), _ptr(out))
+    return out
+
+
 # ---------------------------------------------------------------- attention
 def attention(q, k, v, bq: int, bk: int, scale: float, mask: np.ndarray,
-              mask_head_stride: int, rows=None, want_gap=False):
+              mask_head_stride: int, rows=None, want_gap=False, order: int = ORDER_ASCENDING):
     """Masked attention for the given rows ((b*H + h)*nQ + a); all rows if None.
 
+    Tile gaps visit each row's kept blocks in `order` (ascending or radial).
     Returns (o [n][bq][D] fp64, lse [n][bq] fp64, gap [n][nK] fp64 or None).
     """
     B, N, H, D = q.shape
@@ -166,7 +186,7 @@ def attention(q, k, v, bq: int, bk: int, scale: float, mask: np.ndarray,
     rc = lib().oracle_attention(
         B, H, N, D, bq, bk, dt, _ptr(q), *_strides(q), _ptr(k), *_strides(k),
         _ptr(v), *_strides(v), float(scale), _ptr(mask), mask_head_stride,
-        n, _ptr(rows), _ptr(o), _ptr(lse), _ptr(gap) if gap is not None else None)
+        n, _ptr(rows), _ptr(o), _ptr(lse), _ptr(gap) if gap is not None else None, int(order))
     if rc != 0:
         raise MemoryError("oracle_attention failed to allocate")
     return o, lse, gap
@@ -174,15 +194,15 @@ def attention(q, k, v, bq: int, bk: int, scale: float, mask: np.ndarray,
 
 # ---------------------------------------------------------------- skip carry
 def skip_step(q, k, v, bq: int, bk: int, scale: float, skip_prev: np.ndarray,
-              tau: float, rows=None):
+              tau: float, rows=None, order: int = ORDER_ASCENDING):
     """One denoising step of the carried skip mask, decided in fp64.
 
     LiteAttention summary page, sections 二, 三, 五 and 六: the effective mask of
     step s is (all tiles) minus the tiles skipped so far; attention runs over it
     while each visited tile's gap (local max minus running max, in ascending
-    key-block order) is measured; tiles with gap <= -tau (natural-log units)
-    join the skip set, which only grows. Tiles marked at step s are still
-    computed at step s.
+    key-block order, or radial-centric order as in section 五) is measured;
+    tiles with gap <= -tau (natural-log units) join the skip set, which only
+    grows. Tiles marked at step s are still computed at step s.
 
     Returns (o, lse, gap, skip_new) with o/lse/gap as in attention() for the
     given rows (all rows if None) and skip_new [B][H][nQ][nK].
@@ -190,7 +210,8 @@ def skip_step(q, k, v, bq: int, bk: int, scale: float, skip_prev: np.ndarray,
     B, N, H, D = q.shape
     nQ, nK = -(-N // bq), -(-N // bk)
     eff = (1 - np.asarray(skip_prev, dtype=np.uint8)).reshape(B, H, nQ, nK)
-    o, lse, gap = attention(q, k, v, bq, bk, scale, eff, nQ * nK, rows=rows, want_gap=True)
+    o, lse, gap = attention(q, k, v, bq, bk, scale, eff, nQ * nK, rows=rows, want_gap=True,
+                            order=order)
     if rows is None:
         rows = np.arange(B * H * nQ)
     new = np.array(skip_prev, dtype=np.uint8).reshape(B * H * nQ, nK).copy()

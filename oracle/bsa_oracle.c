@@ -289,6 +289,55 @@ int64_t oracle_compact(int64_t B, int64_t H, int64_t nQ, int64_t nK,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Visiting order of the kept key blocks of a row ([Lite] section 五: a      */
+/* radial-centric order of the blocks reaches the row's maximum sooner, so   */
+/* the running-maximum test can skip more; section 十 expects more sparsity */
+/* from a better order).                                                    */
+/* Reading taken: blocks are visited by increasing distance between the     */
+/* token midpoints of the key block and of the row block, ties to the lower */
+/* block index. In integers, with the true (ragged) block bounds:           */
+/*   cq2(a) = a*bq + min(N, (a+1)*bq) - 1   (twice the row-block midpoint)  */
+/*   ck2(c) = c*bk + min(N, (c+1)*bk) - 1   (twice the key-block midpoint)  */
+/*   key(c) = (|ck2(c) - cq2(a)|, c), ascending.                            */
+/* order 0 keeps the ascending order. Lists are CSR rows r (R of them);     */
+/* row r belongs to row block a = r % nQ.                                   */
+/* ------------------------------------------------------------------------ */
+static int64_t block_mid2(int64_t c, int64_t bk, int64_t N) {
+  int64_t e = (c + 1) * bk < N ? (c + 1) * bk : N;
+  return c * bk + e - 1;
+}
+
+/* 1 if key block x comes before key block y around twice-midpoint cq2. */
+static int radial_before(int32_t x, int32_t y, int64_t cq2, int64_t bk, int64_t N) {
+  int64_t dx = llabs(block_mid2(x, bk, N) - cq2);
+  int64_t dy = llabs(block_mid2(y, bk, N) - cq2);
+  return dx < dy || (dx == dy && x < y);
+}
+
+/* Insertion sort of n key blocks into radial-centric order. */
+static void radial_sort(int32_t* v, int64_t n, int64_t cq2, int64_t bk, int64_t N) {
+  for (int64_t i = 1; i < n; ++i) {
+    int32_t x = v[i];
+    int64_t j = i;
+    while (j > 0 && radial_before(x, v[j - 1], cq2, bk, N)) {
+      v[j] = v[j - 1];
+      --j;
+    }
+    v[j] = x;
+  }
+}
+
+void oracle_order_lists(int64_t N, int64_t bq, int64_t bk, int64_t nQ, int64_t R,
+                        int order, const int32_t* row_ptr, const int32_t* kv_in,
+                        int32_t* kv_out) {
+  for (int64_t r = 0; r < R; ++r) {
+    int64_t e0 = row_ptr[r], e1 = row_ptr[r + 1];
+    for (int64_t e = e0; e < e1; ++e) kv_out[e] = kv_in[e];
+    if (order == 1) radial_sort(kv_out + e0, e1 - e0, block_mid2(r % nQ, bq, N), bk, N);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Masked softmax attention (the plain definition the kernels reach by an    */
 /* exact re-association; bidirectional, no causal mask). For query i of row  */
 /* block a of head (b, h), J_i is the union of the column blocks c with      */
@@ -301,7 +350,9 @@ int64_t oracle_compact(int64_t B, int64_t H, int64_t nQ, int64_t nK,
 /* Tile gaps ([Lite] section 五: a tile whose local maximum lies far below   */
 /* the accumulated maximum contributes exponentially little; section 六:     */
 /* per-warp decisions combined across warps): visiting the kept column      */
-/* blocks of row block a in ascending order, with m_run(r) = -inf at start,  */
+/* blocks of row block a in ascending order (order 0) or in the radial-     */
+/* centric order of oracle_order_lists (order 1), with m_run(r) = -inf at   */
+/* start,                                                                    */
 /*   m_loc(r) = max_{j in C_c} s_rj,                                          */
 /*   gap(a, c) = max over valid rows r of (m_loc(r) - m_run(r)),              */
 /*   m_run(r) = max(m_run(r), m_loc(r)).                                      */
@@ -319,7 +370,7 @@ int oracle_attention(int64_t B, int64_t H, int64_t N, int64_t D, int64_t bq,
                      const void* v, int64_t vsb, int64_t vsn, int64_t vsh,
                      double scale, const uint8_t* mask, int64_t mask_head_stride,
                      int64_t n_rows, const int64_t* rows,
-                     double* o_out, double* lse_out, double* gap_out) {
+                     double* o_out, double* lse_out, double* gap_out, int order) {
   int64_t nQ = (N + bq - 1) / bq, nK = (N + bk - 1) / bk;
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -335,12 +386,19 @@ int oracle_attention(int64_t B, int64_t H, int64_t N, int64_t D, int64_t bq,
     double* qi = (double*)malloc(sizeof(double) * D);
     double* acc = (double*)malloc(sizeof(double) * D);
     double* mrun = (double*)malloc(sizeof(double) * bq);
-    if (!s || !qi || !acc || !mrun) {
+    double* mblk = (double*)malloc(sizeof(double) * nK);
+    int32_t* visit = (int32_t*)malloc(sizeof(int32_t) * (nK > 0 ? nK : 1));
+    if (!s || !qi || !acc || !mrun || !mblk || !visit) {
 #pragma omp atomic write
       bad = 1;
-      free(s); free(qi); free(acc); free(mrun);
+      free(s); free(qi); free(acc); free(mrun); free(mblk); free(visit);
       continue;
     }
+    /* the kept blocks of this row in visiting order */
+    int64_t n_visit = 0;
+    for (int64_t c = 0; c < nK; ++c)
+      if (m[c]) visit[n_visit++] = (int32_t)c;
+    if (order == 1) radial_sort(visit, n_visit, block_mid2(a, bq, N), bk, N);
     for (int64_t r = 0; r < bq; ++r) mrun[r] = -INFINITY;
     if (gap_out)
       for (int64_t c = 0; c < nK; ++c) gap_out[t * nK + c] = NAN;
@@ -364,12 +422,17 @@ int oracle_attention(int64_t B, int64_t H, int64_t N, int64_t D, int64_t bq,
           s[n++] = scale * dot;
           if (s[n - 1] > mloc) mloc = s[n - 1];
         }
+        mblk[c] = mloc;
+      }
+      /* gaps: the kept blocks in visiting order against the running max */
+      for (int64_t u = 0; u < n_visit; ++u) {
+        int64_t c = visit[u];
         if (gap_out) {
-          double g = mloc - mrun[r]; /* +inf on the first visited tile */
+          double g = mblk[c] - mrun[r]; /* +inf on the first visited tile */
           double* gp = &gap_out[t * nK + c];
           if (isnan(*gp) || g > *gp) *gp = g;
         }
-        if (mloc > mrun[r]) mrun[r] = mloc;
+        if (mblk[c] > mrun[r]) mrun[r] = mblk[c];
       }
       if (nJ == 0) {
         if (o_out) for (int64_t x = 0; x < D; ++x) o_out[(t * bq + r) * D + x] = 0.0;
@@ -394,7 +457,7 @@ int oracle_attention(int64_t B, int64_t H, int64_t N, int64_t D, int64_t bq,
       if (o_out) for (int64_t x = 0; x < D; ++x) o_out[(t * bq + r) * D + x] = acc[x] / li;
       if (lse_out) lse_out[t * bq + r] = mi + log(li);
     }
-    free(s); free(qi); free(acc); free(mrun);
+    free(s); free(qi); free(acc); free(mrun); free(mblk); free(visit);
   }
   return bad ? -1 : 0;
 }

@@ -1,5 +1,6 @@
 """Pins for the oracle's carried skip mask over denoising steps (CPU only)."""
 import numpy as np
+import pytest
 
 import oracle
 import synth
@@ -23,19 +24,23 @@ def test_infinite_threshold_never_marks_and_equals_dense(oracle_lib):
     np.testing.assert_array_equal(lse, lse2)
 
 
-def test_skip_set_grows_monotonically_and_rows_never_empty(oracle_lib):
+@pytest.mark.parametrize("order", [oracle.ORDER_ASCENDING, oracle.ORDER_RADIAL])
+def test_skip_set_grows_monotonically_and_rows_never_empty(oracle_lib, order):
     w = small_workload()
     v = synth.make_qkv(w, step=0, want=("v",))["v"]
     skip = np.zeros((w.B, w.H, w.nQ, w.nK), np.uint8)
     total = []
     for s in range(w.steps):
         qk = synth.make_step_qk(w, s)
-        _, _, gap, new = oracle.skip_step(qk["q"], qk["k"], v, w.Bq, w.Bk, w.scale, skip, w.tau)
+        _, _, gap, new = oracle.skip_step(qk["q"], qk["k"], v, w.Bq, w.Bk, w.scale, skip, w.tau,
+                                          order=order)
         assert np.all(new >= skip)                       # monotone OR
         assert np.all((1 - new).sum(axis=-1) >= 1)       # never an empty row
-        # the first visited tile of each row has gap +inf
+        # the first visited tile of each row has gap +inf and is never marked
         eff = (1 - skip).reshape(-1, w.nK)
-        first = eff.argmax(axis=1)
+        row_ptr = np.concatenate([[0], np.cumsum(eff.sum(axis=1))]).astype(np.int32)
+        kv = np.concatenate([np.nonzero(e)[0] for e in eff]).astype(np.int32)
+        first = oracle.order_lists(row_ptr, kv, w.N, w.Bq, w.Bk, order)[row_ptr[:-1]]
         assert np.all(gap[np.arange(gap.shape[0]), first] == np.inf)
         skip = new
         total.append(int(skip.sum()))
