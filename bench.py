@@ -115,6 +115,15 @@ def main():
     ap.add_argument("--tau", type=float, default=None,
                     help="skip-carry threshold override (natural-log units; default: the "
                          "workload's)")
+    ap.add_argument("--order", choices=("ascending", "radial"), default="ascending",
+                    help="skip carry: visiting order of each row's key blocks (radial = "
+                         "centre-out, the order the skip rule reaches the row max soonest in)")
+    ap.add_argument("--tau-schedule", default=None, metavar="START:END",
+                    help="skip carry: threshold per step, linear from START (step 0) to END "
+                         "(last step), natural-log units; overrides --tau")
+    ap.add_argument("--share-after", type=int, default=None, metavar="K",
+                    help="skip carry: steps >= K share the skip set reached after step K-1 "
+                         "(no tile gaps, no update, lists built once)")
     ap.add_argument("--cpu-rows", type=int, default=800,
                     help="row blocks in the CPU oracle sample (0 = skip)")
     ap.add_argument("--no-dense", action="store_true", help="skip the all-tiles timing")
@@ -185,10 +194,20 @@ def main():
     skip = gap = ones = None
     if w.mask == "pooled":
         ws = torch.empty(bsa.bsa_pooled_workspace_bytes(s), dtype=torch.uint8, device=dev)
+    order = bsa.ORDER_RADIAL if args.order == "radial" else bsa.ORDER_ASCENDING
+    taus = None
+    kv_asc = None
     if w.mask == "skip":
         ones = torch.ones(nQ * nK, dtype=torch.uint8, device=dev)
         skip = torch.zeros(BH * nQ * nK, dtype=torch.uint8, device=dev)
         gap = torch.empty(BH * nQ * nK, dtype=torch.float32, device=dev)
+        if order != bsa.ORDER_ASCENDING:
+            kv_asc = torch.empty(R * nK, dtype=torch.int32, device=dev)
+        if args.tau_schedule:
+            t_a, t_b = (float(x) for x in args.tau_schedule.split(":"))
+            taus = [t_a + (t_b - t_a) * si / max(1, w.steps - 1) for si in range(w.steps)]
+        else:
+            taus = [w.tau] * w.steps
         step_inputs = [(q, k)]
         for st in range(1, w.steps):
             y = synth.make_step_qk(w, st)
@@ -196,7 +215,7 @@ def main():
         log(f"{w.steps} denoising-step inputs resident")
 
     fwd_events = []
-    state = {"i": 0}
+    state = {"i": 0, "capture": None}
 
     def step(record: bool):
         if w.mask == "radial":
@@ -212,41 +231,43 @@ def main():
             if si == 0:
                 skip.zero_()
             qq, kk_ = step_inputs[si]
-            bsa.bsa_compact_block_lists(s, ones, 0, skip, row_ptr, kv_idx)
+            frozen = args.share_after is not None and si >= args.share_after
+            if not frozen or si == args.share_after:
+                if kv_asc is None:
+                    bsa.bsa_compact_block_lists(s, ones, 0, skip, row_ptr, kv_idx)
+                else:
+                    bsa.bsa_compact_block_lists(s, ones, 0, skip, row_ptr, kv_asc)
+                    bsa.bsa_order_block_lists(s, order, row_ptr, 0, kv_asc, kv_idx)
+        if state["capture"] is not None:
+            torch.cuda.synchronize()
+            rp_c = row_ptr.cpu().numpy().astype(np.int64)
+            state["capture"].append((rp_c, kv_idx[:int(rp_c[-1])].cpu().numpy()))
+        use_gap = w.mask == "skip" and not frozen
         if record:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
         bsa.bsa_sparse_attn_fwd(s, qq, kk_, v, o, lse, row_ptr, kv_idx, shared, w.scale,
-                                gap if w.mask == "skip" else None)
+                                gap if use_gap else None)
         if record:
             e1.record(stream)
             fwd_events.append((e0, e1, state["i"] % max(1, w.steps)))
-        if w.mask == "skip":
-            bsa.bsa_update_skip_mask(s, row_ptr, kv_idx, gap, w.tau, skip)
+        if use_gap:
+            bsa.bsa_update_skip_mask(s, row_ptr, kv_idx, gap, taus[si], skip)
         state["i"] += 1
 
-    # lists of one step, for the FLOP count (outside the timed region)
-    step(False)
-    torch.cuda.synchronize()
-    per_step_flops = []
+    # lists of every distinct step, for the FLOP count (outside the timed region)
     nsteps_distinct = w.steps if w.mask == "skip" else 1
     state["i"] = 0
-    for si in range(nsteps_distinct):
-        rp_before = None
-        if w.mask == "skip":
-            if si == 0:
-                skip.zero_()
-            bsa.bsa_compact_block_lists(s, ones, 0, skip, row_ptr, kv_idx)
-        else:
-            step(False)
-        torch.cuda.synchronize()
-        rp = row_ptr.cpu().numpy().astype(np.int64)
-        kvh = kv_idx[:int(rp[-1])].cpu().numpy()
-        per_step_flops.append(tile_flops(rp, kvh, w.N, w.Bq, w.Bk, w.d, nQ, BH if shared else 1))
-        if w.mask == "skip":
-            state["i"] = si
-            step(False)
+    state["capture"] = []
+    for _ in range(nsteps_distinct):
+        step(False)
+    torch.cuda.synchronize()
+    captured, state["capture"] = state["capture"], None
+    per_step_flops = [tile_flops(rp, kvh, w.N, w.Bq, w.Bk, w.d, nQ, BH if shared else 1)
+                      for rp, kvh in captured]
+    per_step_tiles = [int(rp[-1]) for rp, _ in captured]
+    rp = captured[-1][0]
     state["i"] = 0
     nnz_tiles = int(rp[-1]) if w.mask != "skip" else None
     torch.cuda.synchronize()
@@ -354,7 +375,8 @@ def main():
             "block_k": w.Bk, "mask": w.mask,
             "knobs": {"h0": w.h0, "decay_base": w.beta} if w.mask == "radial" else (
                 {"mode": w.pooled_mode, "tau_p": w.pooled_param} if w.mask == "pooled"
-                else {"tau": w.tau, "steps": w.steps}),
+                else {"tau": taus, "steps": w.steps, "order": args.order,
+                      "share_after": args.share_after}),
             "kept_tiles": nnz_tiles,
             "tile_sparsity": (1.0 - nnz_tiles / (R * nK)) if nnz_tiles is not None else None,
             "computed_tflop_per_call": float(np.mean(per_step_flops)) / 1e12,
@@ -375,8 +397,12 @@ def main():
         for (e0, e1, si), ms in zip(fwd_events, fwd_ms_each):
             by.setdefault(si, []).append(ms)
         out["per_step"] = [{"step": si, "fwd_ms": float(np.mean(by[si])) if si in by else None,
-                            "computed_tflop": per_step_flops[si] / 1e12}
+                            "computed_tflop": per_step_flops[si] / 1e12,
+                            "listed_tiles": per_step_tiles[si],
+                            "tile_sparsity": 1.0 - per_step_tiles[si] / (R * nK)}
                            for si in range(nsteps_distinct)]
+        log("per step (sparsity, fwd ms): " + ", ".join(
+            f"{p['tile_sparsity']:.3f}/{p['fwd_ms']:.2f}" for p in out["per_step"]))
     print(json.dumps(out))
 
 

@@ -16,7 +16,8 @@ import os
 __all__ = [
     "BsaError", "Shape", "shape", "lib", "BSA_BF16", "BSA_F32",
     "bsa_build_mask_radial", "bsa_pooled_workspace_bytes", "bsa_build_mask_pooled",
-    "bsa_compact_block_lists", "bsa_sparse_attn_fwd", "bsa_update_skip_mask",
+    "bsa_compact_block_lists", "bsa_order_block_lists", "bsa_sparse_attn_fwd",
+    "bsa_update_skip_mask", "ORDER_ASCENDING", "ORDER_RADIAL",
     "bsa_status_string", "bsa_last_error",
 ]
 
@@ -25,6 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libbsa.so")
 
 BSA_OK, BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED, BSA_ERR_CAPACITY, BSA_ERR_DEVICE = range(5)
 BSA_BF16, BSA_F32 = 0, 1
+ORDER_ASCENDING, ORDER_RADIAL = 0, 1
 
 
 class BsaError(RuntimeError):
@@ -79,6 +81,7 @@ def lib() -> C.CDLL:
             "bsa_pooled_workspace_bytes": (sz, [SP]),
             "bsa_build_mask_pooled": (i32, [SP, i32, Tensor, Tensor, f64, i32, f64, p, p, sz, p]),
             "bsa_compact_block_lists": (i32, [SP, p, i64, p, p, p, i64, C.POINTER(i64), p]),
+            "bsa_order_block_lists": (i32, [SP, i32, p, i32, p, p, p]),
             "bsa_sparse_attn_fwd": (i32, [SP, i32, Tensor, Tensor, Tensor, Tensor, p, p, p, i32,
                                           f32, p, p]),
             "bsa_update_skip_mask": (i32, [SP, p, p, p, f32, p, p]),
@@ -168,6 +171,13 @@ def bsa_compact_block_lists(s: Shape, mask, mask_head_stride: int, skip, row_ptr
                                          _ptr(row_ptr), _ptr(kv_idx), kv_capacity,
                                          C.byref(nnz) if want_nnz else None, _stream(stream)))
     return int(nnz.value) if want_nnz else None
+
+
+def bsa_order_block_lists(s: Shape, order: int, row_ptr, lists_shared: int, kv_in, kv_out,
+                          stream=None):
+    _check("bsa_order_block_lists",
+           lib().bsa_order_block_lists(C.byref(s), order, _ptr(row_ptr), lists_shared,
+                                       _ptr(kv_in), _ptr(kv_out), _stream(stream)))
 
 
 def bsa_sparse_attn_fwd(s: Shape, q, k, v, o, lse=None, row_ptr=None, kv_idx=None,

@@ -198,6 +198,26 @@ bsa_status bsa_compact_block_lists(const bsa_shape* s, const uint8_t* mask,
                 "compaction scatter");
 }
 
+bsa_status bsa_order_block_lists(const bsa_shape* s, int32_t order, const int32_t* row_ptr,
+                                 int32_t lists_shared, const int32_t* kv_in, int32_t* kv_out,
+                                 void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  if (order != 0 && order != 1) return fail(BSA_ERR_INVALID, "order %d not in {0, 1}", order);
+  if (lists_shared != 0 && lists_shared != 1)
+    return fail(BSA_ERR_INVALID, "lists_shared must be 0 or 1");
+  const int64_t R = lists_shared ? g.nQ : (int64_t)g.B * g.H * g.nQ;
+  if (R * g.nK > kI32Max)
+    return fail(BSA_ERR_UNSUPPORTED, "list rows x key blocks exceeds int32 list offsets");
+  if (R == 0 || g.nK == 0) return ok();
+  if (!row_ptr || !kv_in || !kv_out)
+    return fail(BSA_ERR_INVALID, "row_ptr, kv_in and kv_out are required");
+  if (kv_in == kv_out) return fail(BSA_ERR_INVALID, "kv_out must not alias kv_in");
+  return device(bsa::launch_order_lists(g, R, order, row_ptr, kv_in, kv_out, (hipStream_t)stream),
+                "list order launch");
+}
+
 bsa_status bsa_sparse_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, bsa_tensor k,
                                bsa_tensor v, bsa_tensor o, float* lse, const int32_t* row_ptr,
                                const int32_t* kv_idx, int32_t lists_shared, float scale,

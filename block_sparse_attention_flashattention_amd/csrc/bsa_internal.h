@@ -36,6 +36,8 @@ hipError_t launch_compact_scatter(const Geom& g, int64_t R, const uint8_t* mask,
                                   int64_t mask_head_stride, const uint8_t* skip,
                                   const int32_t* row_ptr, int32_t* kv_idx, hipStream_t st);
 hipError_t launch_zero_row_ptr(int32_t* row_ptr, hipStream_t st);
+hipError_t launch_order_lists(const Geom& g, int64_t R, int32_t order, const int32_t* row_ptr,
+                              const int32_t* kv_in, int32_t* kv_out, hipStream_t st);
 
 hipError_t launch_skip_update(const Geom& g, const int32_t* row_ptr, const int32_t* kv_idx,
                               const float* tile_gap, float tau2, uint8_t* skip,

@@ -1,5 +1,5 @@
-// mask_kernels.hip -- block-mask builders, list compaction and the skip-mask
-// update of libbsa (gfx950). These are small, latency- or HBM-bound kernels
+// mask_kernels.hip -- block-mask builders, list compaction and ordering and
+// the skip-mask update of libbsa (gfx950). These are small, latency- or HBM-bound kernels
 // around the attention forward; none of them is a dense contraction.
 //
 // Pages: [Radial] "MIT实验室推出Radial Attention：让视频AI生成快如闪电的神奇技术";
@@ -309,6 +309,70 @@ __global__ void skip_update_kernel(int64_t R, int64_t nK, const int32_t* __restr
     if (gap[e] <= neg_tau2) skip[r * nK + kv_idx[e]] = 1;
 }
 
+// ------------------------------------------------------------ list order
+// Radial-centric visiting order of each list row ([Lite] section 五: visiting
+// key blocks outward from the row's own position reaches the row maximum
+// sooner, so the running-maximum test can skip more). Key blocks are ordered
+// by the distance between token midpoints of key block and row block (twice
+// the midpoints, in integers), ties to the lower block index.
+// The ascending input splits at the row's midpoint into a left run whose
+// distances fall and a right run whose distances rise; the output position
+// of an entry is its rank in its own run plus the number of entries of the
+// other run that precede it, found by binary search. One wave per list row,
+// lanes over its entries. order 0 copies. Every write lands inside the row.
+__device__ inline int64_t mid2(int64_t c, int64_t blk, int64_t N) {
+  return c * blk + min(N, (c + 1) * blk) - 1;
+}
+
+__global__ void order_lists_kernel(int64_t R, int64_t nQ, int64_t N, int32_t Bq, int32_t Bk,
+                                   int32_t order, const int32_t* __restrict__ row_ptr,
+                                   const int32_t* __restrict__ kv_in,
+                                   int32_t* __restrict__ kv_out) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t r = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (r >= R) return;
+  const int32_t e0 = row_ptr[r], e1 = row_ptr[r + 1];
+  const int32_t n = e1 - e0;
+  if (order == 0) {
+    for (int32_t e = lane; e < n; e += kWave) kv_out[e0 + e] = kv_in[e0 + e];
+    return;
+  }
+  const int32_t* in = kv_in + e0;
+  const int64_t cq2 = mid2(r % nQ, Bq, N);
+  // p = number of entries left of the row midpoint (mid2 < cq2)
+  int32_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int32_t m = (lo + hi) / 2;
+    if (mid2(in[m], Bk, N) < cq2) lo = m + 1;
+    else hi = m;
+  }
+  const int32_t p = lo;
+  for (int32_t e = lane; e < n; e += kWave) {
+    const int64_t d = mid2(in[e], Bk, N) - cq2;
+    int32_t rank;
+    if (e < p) {
+      // left run, distance -d falls with e; right entries strictly nearer come first
+      int32_t l2 = p, h2 = n;
+      while (l2 < h2) {
+        const int32_t m = (l2 + h2) / 2;
+        if (mid2(in[m], Bk, N) - cq2 < -d) l2 = m + 1;
+        else h2 = m;
+      }
+      rank = (p - 1 - e) + (l2 - p);
+    } else {
+      // right run, distance d rises with e; left entries as near or nearer come first
+      int32_t l2 = 0, h2 = p;
+      while (l2 < h2) {
+        const int32_t m = (l2 + h2) / 2;
+        if (cq2 - mid2(in[m], Bk, N) > d) l2 = m + 1;
+        else h2 = m;
+      }
+      rank = (e - p) + (p - l2);
+    }
+    kv_out[e0 + rank] = in[e];
+  }
+}
+
 inline unsigned grid_for(int64_t work, int threads, int64_t cap = 1 << 20) {
   int64_t g = (work + threads - 1) / threads;
   if (g < 1) g = 1;
@@ -389,6 +453,15 @@ hipError_t launch_compact_scatter(const Geom& g, int64_t R, const uint8_t* mask,
 
 hipError_t launch_zero_row_ptr(int32_t* row_ptr, hipStream_t st) {
   hipLaunchKernelGGL(zero_row_ptr_kernel, dim3(1), dim3(1), 0, st, row_ptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_order_lists(const Geom& g, int64_t R, int32_t order, const int32_t* row_ptr,
+                              const int32_t* kv_in, int32_t* kv_out, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  const int waves = 4;
+  hipLaunchKernelGGL(order_lists_kernel, dim3(grid_for(R, waves, INT32_MAX)), dim3(waves * kWave),
+                     0, st, R, g.nQ, g.N, g.Bq, g.Bk, order, row_ptr, kv_in, kv_out);
   return hipGetLastError();
 }
 

@@ -31,7 +31,8 @@
  *   [B][H][nQ][nK]; a shared mask is [nQ][nK] (head stride 0).
  * Block lists (CSR): list row r = (b*H + h)*nQ + a (or just a when one list
  *   serves every (b, h)); kv_idx[row_ptr[r] .. row_ptr[r+1]) holds the kept
- *   key blocks of that row in ascending order.
+ *   key blocks of that row, in ascending order as compaction writes them or
+ *   in the visiting order bsa_order_block_lists gives them.
  * Memory: every tensor, mask and list pointer is a DEVICE pointer owned by
  *   the caller; the library allocates no device memory and keeps no state
  *   besides its loaded kernels and a thread-local error string.
@@ -156,6 +157,30 @@ BSA_API bsa_status bsa_compact_block_lists(const bsa_shape* s, const uint8_t* ma
                                    int64_t mask_head_stride, const uint8_t* skip,
                                    int32_t* row_ptr, int32_t* kv_idx, int64_t kv_capacity,
                                    int64_t* nnz_host, void* stream);
+
+/*
+ * Visiting order of the listed key blocks ([Lite] section 五: a radial-centric
+ * order of the tiles reaches a row's maximum sooner, which lets the
+ * running-maximum skip test mark more tiles; section 十 expects 10-20% more
+ * sparsity from a better order). The forward pass visits each row's list in
+ * the order it is stored, so reordering a list changes the tile gaps (and
+ * with them the skip decisions), never the attention result beyond rounding.
+ *   order       0: ascending key-block order (a copy); 1: radial-centric:
+ *               key blocks by increasing |ck2 - cq2| with ck2 = c*block_k +
+ *               min(N, (c+1)*block_k) - 1 and cq2 = a*block_q + min(N,
+ *               (a+1)*block_q) - 1 (twice the token midpoints of key block c
+ *               and of the row's block a), ties to the lower c.
+ *   row_ptr     the lists' row pointers ([R+1], R = nQ when lists_shared,
+ *               else B*H*nQ); row r belongs to row block a = r % nQ
+ *   kv_in       lists in ascending order, as bsa_compact_block_lists writes
+ *               them (other inputs give an unspecified arrangement of each
+ *               row's entries, still written inside that row)
+ *   kv_out      out, same row_ptr; must not alias kv_in
+ * Exact integer work; deterministic.
+ */
+BSA_API bsa_status bsa_order_block_lists(const bsa_shape* s, int32_t order, const int32_t* row_ptr,
+                                 int32_t lists_shared, const int32_t* kv_in, int32_t* kv_out,
+                                 void* stream);
 
 /*
  * Block-sparse attention forward ([PSA]: whole blocks are kept or dropped;

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     out = subprocess.run(["nm", "-D", "--defined-only", bsa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (bsa_\w+)", out))
@@ -150,3 +150,19 @@ def test_skip_update_validation(L):
     assert L.bsa_update_skip_mask(C.byref(s), P, P, P, float("nan"), P, None) == INVALID
     assert L.bsa_update_skip_mask(C.byref(s), None, P, P, 10.0, P, None) == INVALID
     assert L.bsa_update_skip_mask(C.byref(s), P, P, P, 10.0, None, None) == INVALID
+
+
+def test_order_lists_validation(L):
+    s = S()
+    def call(order=1, row_ptr=P, shared=1, kv_in=P, kv_out=P + 4096):
+        return L.bsa_order_block_lists(C.byref(s), order, row_ptr, shared, kv_in, kv_out, None)
+    assert call(order=2) == INVALID
+    assert call(order=-1) == INVALID
+    assert call(shared=2) == INVALID
+    assert call(row_ptr=None) == INVALID
+    assert call(kv_in=None) == INVALID
+    assert call(kv_out=None) == INVALID
+    assert call(kv_out=P) == INVALID                  # in place is refused
+    assert L.bsa_order_block_lists(C.byref(S(head_dim=96)), 1, P, 1, P, P + 64, None) == UNSUPPORTED
+    # empty shapes enqueue nothing and need no pointers
+    assert L.bsa_order_block_lists(C.byref(S(frames=0)), 1, None, 1, None, None, None) == 0

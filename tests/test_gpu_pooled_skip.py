@@ -17,8 +17,8 @@ import torch
 import block_sparse_attention_flashattention_amd as bsa
 import oracle
 import synth
-from _gpu_util import (DEV, GAP_ABS, compare, dev, gather_rows, host, note, run_fwd,
-                       sample_rows, shape_of)
+from _gpu_util import (DEV, GAP_ABS, compare, dev, gather_rows, host, note, radial_lists,
+                       run_fwd, sample_rows, shape_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -102,7 +102,11 @@ def _gap_matrix(gap_list, rp, kv, R, nK):
     return out
 
 
-def _skip_carry(w, steps, tau, rows=None):
+def _skip_carry(w, steps, tau, rows=None, order=bsa.ORDER_ASCENDING, freeze_after=None):
+    """Run `steps` denoising steps of the carried skip mask on the GPU and check
+    each against the oracle. `tau` is one threshold or one per step; `order`
+    the visiting order of each row's list; from step `freeze_after` on, the
+    skip set is shared unchanged (no gaps, no update)."""
     s = shape_of(w)
     R = w.B * w.H * w.nQ
     nK = w.nK
@@ -112,37 +116,52 @@ def _skip_carry(w, steps, tau, rows=None):
     ones = torch.ones(w.nQ * nK, dtype=torch.uint8, device=DEV)
     skip = torch.zeros(R * nK, dtype=torch.uint8, device=DEV)
     rp = torch.empty(R + 1, dtype=torch.int32, device=DEV)
+    kv_asc = torch.empty(R * nK, dtype=torch.int32, device=DEV)
     kv = torch.empty(R * nK, dtype=torch.int32, device=DEV)
     gap = torch.empty(R * nK, dtype=torch.float32, device=DEV)
-    tau2 = np.float32(np.float64(tau) * LOG2E)
+    taus = list(tau) if isinstance(tau, (list, tuple)) else [tau] * steps
     for st in range(steps):
+        frozen = freeze_after is not None and st >= freeze_after
+        tau_s = taus[st]
+        tau2 = np.float32(np.float64(tau_s) * LOG2E)
         x = x0 if st == 0 else synth.make_step_qk(w, st)
         q, k = dev(x["q"]), dev(x["k"])
         skip_prev = host(skip).reshape(R, nK).copy()
-        nnz = bsa.bsa_compact_block_lists(s, ones, 0, skip, rp, kv, want_nnz=True)
+        nnz = bsa.bsa_compact_block_lists(s, ones, 0, skip, rp, kv_asc, want_nnz=True)
+        bsa.bsa_order_block_lists(s, order, rp, 0, kv_asc, kv)
         o = torch.empty_like(q)
         lse = torch.empty(w.B * w.H * w.N, dtype=torch.float32, device=DEV)
-        bsa.bsa_sparse_attn_fwd(s, q, k, v, o, lse, rp, kv, 0, w.scale, gap)
-        bsa.bsa_update_skip_mask(s, rp, kv, gap, tau, skip)
+        bsa.bsa_sparse_attn_fwd(s, q, k, v, o, lse, rp, kv, 0, w.scale, None if frozen else gap)
+        if not frozen:
+            bsa.bsa_update_skip_mask(s, rp, kv, gap, tau_s, skip)
         torch.cuda.synchronize()
         rp_h, kv_h = host(rp).astype(np.int64), host(kv)[:nnz]
-        gap_h = host(gap)[:nnz].astype(np.float32)
         skip_new = host(skip).reshape(R, nK)
-        # lists are the complement of the carried set
+        # lists are the complement of the carried set, in the requested order
         rp_ref, kv_ref = oracle.compact(np.ones((w.nQ, nK), np.uint8), w.B, w.H, w.nQ, nK, 0,
                                         skip_prev.reshape(w.B, w.H, w.nQ, nK))
         np.testing.assert_array_equal(rp_h, rp_ref)
-        np.testing.assert_array_equal(kv_h, kv_ref)
+        np.testing.assert_array_equal(kv_h, oracle.order_lists(rp_ref, kv_ref, w.N, w.Bq, w.Bk,
+                                                               order))
+        sel = np.arange(R) if rows is None else rows
+        if frozen:
+            np.testing.assert_array_equal(skip_new, skip_prev)
+            eff = (1 - skip_prev).reshape(w.B, w.H, w.nQ, nK)
+            o_ref, lse_ref, _ = oracle.attention(x["q"], x["k"], v_np, w.Bq, w.Bk, w.scale, eff,
+                                                 w.nQ * nK, rows=sel)
+            og, lg = gather_rows(host(o), host(lse), sel, w.B, w.H, w.N, w.Bq)
+            compare(og, lg, o_ref, lse_ref, f"{w.name} step {st} (shared mask)")
+            continue
+        gap_h = host(gap)[:nnz].astype(np.float32)
         # update rule, bit-exact on the GPU's own gaps in fp32 / log2 units
         gm = _gap_matrix(gap_h, rp_h, kv_h, R, nK)
         expect = skip_prev | (np.nan_to_num(gm, nan=np.inf) <= -tau2).astype(np.uint8)
         np.testing.assert_array_equal(skip_new, expect)
         assert np.all(skip_new >= skip_prev), "skip set must only grow"
         # against the oracle (fp64): outputs, gaps, decisions
-        sel = np.arange(R) if rows is None else rows
         o_ref, lse_ref, gap_ref, skip_ref = oracle.skip_step(
             x["q"], x["k"], v_np, w.Bq, w.Bk, w.scale, skip_prev.reshape(w.B, w.H, w.nQ, nK),
-            tau, rows=sel)
+            tau_s, rows=sel, order=order)
         og, lg = gather_rows(host(o), host(lse), sel, w.B, w.H, w.N, w.Bq)
         compare(og, lg, o_ref, lse_ref, f"{w.name} step {st}")
         g_gpu = gm[sel] * math.log(2.0)
@@ -154,9 +173,11 @@ def _skip_carry(w, steps, tau, rows=None):
         dec_ref = skip_ref.reshape(R, nK)[sel]
         flips = np.argwhere(dec_gpu != dec_ref)
         for r_, c_ in flips:
-            assert abs(gap_ref[r_, c_] + tau) <= GAP_ABS, "decision differs away from the threshold"
-        note(f"{w.name} step {st}: {nnz} tiles, {int(skip_new.sum())} skipped, gap max err "
-             f"{gerr:.2e}, {len(flips)} threshold-edge flips")
+            assert abs(gap_ref[r_, c_] + tau_s) <= GAP_ABS, \
+                "decision differs away from the threshold"
+        note(f"{w.name} step {st} (order {order}, tau {tau_s}): {nnz} tiles, "
+             f"{int(skip_new.sum())} skipped, gap max err {gerr:.2e}, "
+             f"{len(flips)} threshold-edge flips")
         assert gerr <= GAP_ABS
     return int(skip_new.sum())
 
@@ -187,6 +208,83 @@ def test_skip_carry_480p_workload_tau_marks_nothing():
     rows = sample_rows(w.B, w.H, w.nQ, 1, 24, heads=[3])
     marked = _skip_carry(w, 2, w.tau, rows=rows)
     assert marked == 0
+
+
+# ------------------------------------------- visiting order and schedules
+def test_skip_carry_small_radial_order():
+    w = synth.Workload("skip_small", 1, 3, 128, 6, 10, 14, 64, 64, "bf16", "skip", 620, True,
+                       tau=1.0, steps=5)
+    _skip_carry(w, w.steps, w.tau, order=bsa.ORDER_RADIAL)
+
+
+def test_skip_carry_small_bq128_ragged_radial_order():
+    w = synth.Workload("skip_small128", 2, 2, 64, 5, 9, 13, 128, 64, "bf16", "skip", 621, True,
+                       tau=0.25, steps=4)
+    _skip_carry(w, w.steps, w.tau, order=bsa.ORDER_RADIAL)
+
+
+def test_skip_carry_480p_sampled_radial_order():
+    w = synth.workload("skip_carry_480p")
+    rows = sample_rows(w.B, w.H, w.nQ, 2, 25, heads=[0, w.H - 1])
+    _skip_carry(w, 3, 2.0, rows=rows, order=bsa.ORDER_RADIAL)
+
+
+def test_skip_carry_tau_schedule_then_shared_mask():
+    """Stricter threshold early (larger tau), looser later; the second half of
+    the steps shares the skip set reached at the half-way point."""
+    w = synth.Workload("skip_sched", 1, 2, 128, 6, 10, 14, 64, 64, "bf16", "skip", 622, True,
+                       tau=1.0, steps=6)
+    taus = [2.0, 1.5, 1.0, 1.0, 1.0, 1.0]
+    _skip_carry(w, w.steps, taus, order=bsa.ORDER_RADIAL, freeze_after=3)
+
+
+def test_order_lists_bit_exact():
+    # shared radial lists of the 720p shape, and per-head ragged lists
+    w = synth.workload("wan14b_720p")
+    s = shape_of(w)
+    mask, rp, kv = radial_lists(s, w.h0, w.beta)
+    nnz = int(host(rp)[-1])
+    out = torch.empty_like(kv)
+    for order in (bsa.ORDER_ASCENDING, bsa.ORDER_RADIAL):
+        bsa.bsa_order_block_lists(s, order, rp, 1, kv, out)
+        torch.cuda.synchronize()
+        ref = oracle.order_lists(host(rp), host(kv)[:nnz], w.N, w.Bq, w.Bk, order)
+        np.testing.assert_array_equal(host(out)[:nnz], ref)
+        note(f"720p shared lists, order {order}: {nnz} entries bit-exact")
+    r = np.random.default_rng(7)
+    for (T, Hs, Ws, bq) in ((5, 9, 13, 128), (7, 11, 17, 64)):
+        s2 = bsa.shape(2, 3, 128, T, Hs, Ws, bq)
+        R = 6 * s2.nQ
+        m = (r.random((R, s2.nK)) < 0.3).astype(np.uint8)
+        m[:, 0] = 0
+        m[::7] = 0                                   # some empty rows
+        rp_ref, kv_ref = oracle.compact(m.reshape(2, 3, s2.nQ, s2.nK), 2, 3, s2.nQ, s2.nK,
+                                        s2.nQ * s2.nK)
+        rp_d, kv_d = dev(rp_ref), dev(kv_ref.astype(np.int32))
+        out = torch.full_like(kv_d, -1)
+        bsa.bsa_order_block_lists(s2, bsa.ORDER_RADIAL, rp_d, 0, kv_d, out)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(
+            host(out), oracle.order_lists(rp_ref, kv_ref, s2.N, bq, 64, bsa.ORDER_RADIAL))
+
+
+def test_fwd_wan14b_720p_radial_order_sampled():
+    """Forward over radially ordered lists: the visiting order changes only
+    rounding, so the outputs stay within the bounds of the oracle."""
+    w = synth.workload("wan14b_720p")
+    s = shape_of(w)
+    x = synth.make_qkv(w)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    mask, rp, kv = radial_lists(s, w.h0, w.beta)
+    kv2 = torch.empty_like(kv)
+    bsa.bsa_order_block_lists(s, bsa.ORDER_RADIAL, rp, 1, kv, kv2)
+    o, lse, _ = run_fwd(s, q, k, v, rp, kv2, 1, w.scale)
+    rows = sample_rows(w.B, w.H, w.nQ, 2, 26, heads=[0, 17, w.H - 1])
+    mask_h = host(mask).reshape(w.nQ, w.nK)
+    o_ref, lse_ref, _ = oracle.attention(x["q"], x["k"], x["v"], w.Bq, w.Bk, w.scale, mask_h, 0,
+                                         rows=rows)
+    og, lg = gather_rows(host(o), host(lse), rows, w.B, w.H, w.N, w.Bq)
+    compare(og, lg, o_ref, lse_ref, "720p radial order")
 
 
 # ------------------------------------------------------------ long video
