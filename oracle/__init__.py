@@ -112,7 +112,12 @@ def build_mask_radial(T, Hs, Ws, bq, bk, h0, beta) -> np.ndarray:
 # ------------------------------------------------------------------- pooled
 def build_mask_pooled(q: np.ndarray, k: np.ndarray, bq: int, bk: int, scale: float,
                       mode: int, param: float, want_scores=False):
-    """Returns (mask [B][H][nQ][nK] uint8, scores or None, margin [B][H][nQ])."""
+    """Returns (mask [B][H][nQ][nK] uint8, scores or None, margin [B][H][nQ]).
+
+    mode 0: per-row top-k (param = k); 1: per-row cumulative mass (param =
+    tau_p); 2: head-wide top-k over all (row, block) pairs (param = k);
+    3: head-wide cumulative mass reaching tau_p * nQ (param = tau_p). In the
+    head-wide modes every row also keeps its best block."""
     B, N, H, D = q.shape
     nQ, nK = -(-N // bq), -(-N // bk)
     dt = _dtype_code(q)

@@ -166,6 +166,19 @@ void oracle_build_mask_radial(int64_t T, int64_t Hs, int64_t Ws, int64_t bq,
 /*    the shortest prefix whose running sum is >= tau_p (all if never).     */
 /* margin_out[row] (optional) = distance of the running sum from tau_p at   */
 /* the last step inside the prefix and the step before it (mode 1).         */
+/*                                                                          */
+/* Global modes ([VMoBA] section 三: rank the relevance of every query with */
+/* every block and serve the strongest combinations first, instead of the   */
+/* same number of blocks per query; the number of blocks a head keeps       */
+/* follows how concentrated its attention is). Per (b, h), all nQ*nK pairs  */
+/* are ordered together by (key desc, a*nK + c asc) and                     */
+/*    mode 2 (global top-k): the first min(k, nQ*nK) pairs are kept, key S; */
+/*    mode 3 (global cumulative mass): key p_ac = e_ac / Z_a with e and Z   */
+/*      of row a as in mode 1; the shortest prefix whose running sum of p   */
+/*      reaches tau_p * nQ is kept (all pairs if never).                    */
+/* In both, every row also keeps its own first block in (S desc, c asc)     */
+/* order, so that no row is left empty. margin_out[bh*nQ] holds the head's  */
+/* margin for mode 3 (as in mode 1, against tau_p * nQ); other rows inf.    */
 /* ------------------------------------------------------------------------ */
 typedef struct { double s; int64_t c; } scored;
 
@@ -191,12 +204,14 @@ int oracle_build_mask_pooled(int64_t B, int64_t H, int64_t N, int64_t D,
     int64_t b = bh / H, h = bh % H;
     double* qbar = (double*)malloc(sizeof(double) * nQ * D);
     double* kbar = (double*)malloc(sizeof(double) * nK * D);
-    double* S = (double*)malloc(sizeof(double) * nK);
+    double* S = (double*)malloc(sizeof(double) * nQ * nK);
     scored* ord = (scored*)malloc(sizeof(scored) * nK);
-    if (!qbar || !kbar || !S || !ord) {
+    double* P = mode == 3 ? (double*)malloc(sizeof(double) * nQ * nK) : NULL;
+    scored* gord = mode >= 2 ? (scored*)malloc(sizeof(scored) * nQ * nK) : NULL;
+    if (!qbar || !kbar || !S || !ord || (mode == 3 && !P) || (mode >= 2 && !gord)) {
 #pragma omp atomic write
       bad = 1;
-      free(qbar); free(kbar); free(S); free(ord);
+      free(qbar); free(kbar); free(S); free(ord); free(P); free(gord);
       continue;
     }
     for (int64_t a = 0; a < nQ; ++a) {
@@ -225,21 +240,26 @@ int oracle_build_mask_pooled(int64_t B, int64_t H, int64_t N, int64_t D,
           double pr = qbar[a * D + x] * kbar[c * D + x];
           acc = acc + pr;
         }
-        S[c] = scale * acc;
-        if (scores_out) scores_out[row * nK + c] = S[c];
-        ord[c].s = S[c];
+        S[a * nK + c] = scale * acc;
+        if (scores_out) scores_out[row * nK + c] = S[a * nK + c];
+      }
+    }
+    memset(mask + bh * nQ * nK, 0, (size_t)(nQ * nK));
+    for (int64_t a = 0; a < nQ; ++a) {
+      int64_t row = bh * nQ + a;
+      for (int64_t c = 0; c < nK; ++c) {
+        ord[c].s = S[a * nK + c];
         ord[c].c = c;
       }
       qsort(ord, (size_t)nK, sizeof(scored), cmp_scored);
       uint8_t* m = mask + row * nK;
-      memset(m, 0, (size_t)nK);
       int64_t keep = nK;
       double margin = INFINITY;
       if (mode == 0) {
         keep = (int64_t)param < nK ? (int64_t)param : nK;
-      } else {
+      } else if (mode == 1) {
         double smax = ord[0].s, Z = 0.0;
-        for (int64_t c = 0; c < nK; ++c) Z = Z + exp(S[c] - smax);
+        for (int64_t c = 0; c < nK; ++c) Z = Z + exp(S[a * nK + c] - smax);
         double run = 0.0, prev = 0.0;
         keep = nK;
         for (int64_t t = 0; t < nK; ++t) {
@@ -249,11 +269,43 @@ int oracle_build_mask_pooled(int64_t B, int64_t H, int64_t N, int64_t D,
         }
         margin = fabs(run - param);
         if (keep > 1 && fabs(param - prev) < margin) margin = fabs(param - prev);
+      } else {
+        /* global modes: the row keeps its best block; p of the row for mode 3 */
+        keep = 1;
+        if (mode == 3) {
+          double smax = ord[0].s, Z = 0.0;
+          for (int64_t c = 0; c < nK; ++c) Z = Z + exp(S[a * nK + c] - smax);
+          for (int64_t c = 0; c < nK; ++c) P[a * nK + c] = exp(S[a * nK + c] - smax) / Z;
+        }
       }
       for (int64_t t = 0; t < keep; ++t) m[ord[t].c] = 1;
       if (margin_out) margin_out[row] = margin;
     }
-    free(qbar); free(kbar); free(S); free(ord);
+    if (mode >= 2) {
+      int64_t n = nQ * nK;
+      for (int64_t u = 0; u < n; ++u) {
+        gord[u].s = mode == 2 ? S[u] : P[u];
+        gord[u].c = u;
+      }
+      qsort(gord, (size_t)n, sizeof(scored), cmp_scored);
+      int64_t keep = n;
+      double margin = INFINITY;
+      if (mode == 2) {
+        keep = (int64_t)param < n ? (int64_t)param : n;
+      } else {
+        double target = param * (double)nQ, run = 0.0, prev = 0.0;
+        for (int64_t t = 0; t < n; ++t) {
+          prev = run;
+          run = run + gord[t].s;
+          if (run >= target) { keep = t + 1; break; }
+        }
+        margin = fabs(run - target);
+        if (keep > 1 && fabs(target - prev) < margin) margin = fabs(target - prev);
+      }
+      for (int64_t t = 0; t < keep; ++t) mask[bh * n + gord[t].c] = 1;
+      if (margin_out) margin_out[bh * nQ] = margin;
+    }
+    free(qbar); free(kbar); free(S); free(ord); free(P); free(gord);
   }
   return bad ? -1 : 0;
 }

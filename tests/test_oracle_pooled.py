@@ -138,3 +138,95 @@ def test_compaction_matches_nonzero_scan(oracle_lib, shared):
         for row in range(B * H * nQ):
             np.testing.assert_array_equal(kv_idx[row_ptr[row]:row_ptr[row + 1]],
                                           np.nonzero(eff[row])[0])
+
+
+# ------------------------------------------------------ global selection
+def _row_argmax_mask(S):
+    m = np.zeros(S.shape, np.uint8)
+    np.put_along_axis(m, S.argmax(axis=-1)[..., None], 1, axis=-1)
+    return m
+
+
+def test_global_topk_full_budget_and_top1(oracle_lib):
+    q, k = rand_qk(1, 150, 2, 8, seed=12)
+    nQ, nK = -(-150 // 32), -(-150 // 16)
+    m, _, _ = oracle.build_mask_pooled(q, k, 32, 16, 0.3, 2, nQ * nK)
+    assert np.all(m == 1)
+    # one pair per head plus every row's best block is the per-row top-1 mask
+    # (the head's best pair is its row's best block)
+    m1, _, _ = oracle.build_mask_pooled(q, k, 32, 16, 0.3, 2, 1)
+    r1, _, _ = oracle.build_mask_pooled(q, k, 32, 16, 0.3, 0, 1)
+    np.testing.assert_array_equal(m1, r1)
+
+
+@pytest.mark.parametrize("kk", [3, 17, 40])
+def test_global_topk_is_head_wide_stable_sort_prefix_plus_row_best(oracle_lib, kk):
+    q, k = rand_qk(2, 190, 2, 8, seed=13 + kk)
+    S = numpy_scores(q, k, 32, 16, 0.5)
+    B, H, nQ, nK = S.shape
+    m, _, _ = oracle.build_mask_pooled(q, k, 32, 16, 0.5, 2, kk)
+    flat = S.reshape(B, H, nQ * nK)
+    order = np.argsort(-flat, axis=-1, kind="stable")[..., :kk]
+    ref = np.zeros(flat.shape, np.uint8)
+    np.put_along_axis(ref, order, 1, axis=-1)
+    ref = ref.reshape(S.shape) | _row_argmax_mask(S)
+    np.testing.assert_array_equal(m, ref)
+
+
+def test_global_topk_ties_break_to_lower_pair_index(oracle_lib):
+    # identical key blocks: every pair of a row scores the same
+    B, N, H, D = 1, 64, 1, 4
+    r = np.random.default_rng(14)
+    q = np.tile(r.standard_normal((1, D)), (N, 1))[None, :, None, :].copy()
+    k = np.tile(r.standard_normal((16, D)), (4, 1))[None, :, None, :].copy()
+    m, S, _ = oracle.build_mask_pooled(q, k, 16, 16, 1.0, 2, 6, want_scores=True)
+    assert np.all(S == S.flat[0])
+    # pairs 0..5 in row-major order, plus block 0 of every row
+    ref = np.zeros(16, np.uint8)
+    ref[:6] = 1
+    ref = ref.reshape(4, 4)
+    ref[:, 0] = 1
+    np.testing.assert_array_equal(m[0, 0], ref)
+
+
+@pytest.mark.parametrize("tau", [0.2, 0.45, 0.7, 0.9])
+def test_global_cumulative_mass_is_minimal_pair_set(oracle_lib, tau):
+    """Exhaustive over all 12 pairs of a 3x4 head: the kept pairs minus the
+    rows' best blocks form a smallest set of pairs whose mass (each row's
+    softmax over its blocks) reaches tau * nQ, with the largest mass among
+    sets of that size; the rows' best blocks are added on top."""
+    B, N, H, D, bq, bk = 1, 48, 2, 6, 16, 12
+    q, k = rand_qk(B, N, H, D, seed=int(tau * 1000))
+    m, S, margin = oracle.build_mask_pooled(q, k, bq, bk, 2.0, 3, tau, want_scores=True)
+    nQ, nK = 3, 4
+    for h in range(H):
+        s = S[0, h]
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p = (p / p.sum(axis=1, keepdims=True)).ravel()
+        best = None
+        for size in range(1, nQ * nK + 1):
+            cands = [(p[list(c)].sum(), c) for c in itertools.combinations(range(nQ * nK), size)]
+            ok = [x for x in cands if x[0] >= tau * nQ]
+            if ok:
+                best = max(ok)
+                break
+        ref = np.zeros(nQ * nK, np.uint8)
+        if best is None:
+            ref[:] = 1
+        else:
+            ref[list(best[1])] = 1
+        ref = ref.reshape(nQ, nK) | _row_argmax_mask(s)
+        np.testing.assert_array_equal(m[0, h], ref)
+        assert margin[0, h, 0] >= 0
+
+
+def test_global_cumulative_mass_monotone_in_tau_and_rows_nonempty(oracle_lib):
+    q, k = rand_qk(1, 300, 3, 8, seed=15)
+    prev = None
+    for tau in (0.05, 0.2, 0.5, 0.8, 0.95, 1.0):
+        m, _, _ = oracle.build_mask_pooled(q, k, 32, 16, 0.4, 3, tau)
+        assert np.all(m.sum(axis=-1) >= 1)
+        if prev is not None:
+            assert np.all(m >= prev)          # larger tau keeps a superset
+        prev = m
+    assert prev.mean() > 0.9
