@@ -124,6 +124,12 @@ def main():
     ap.add_argument("--share-after", type=int, default=None, metavar="K",
                     help="skip carry: steps >= K share the skip set reached after step K-1 "
                          "(no tile gaps, no update, lists built once)")
+    ap.add_argument("--pooled-mode", type=int, default=None, choices=(0, 1, 2, 3),
+                    help="pooled workloads: selection rule (0 row top-k, 1 row cumulative mass, "
+                         "2 head-wide top-k, 3 head-wide cumulative mass); default: the "
+                         "workload's")
+    ap.add_argument("--pooled-param", type=float, default=None,
+                    help="pooled workloads: k or tau_p for --pooled-mode")
     ap.add_argument("--cpu-rows", type=int, default=800,
                     help="row blocks in the CPU oracle sample (0 = skip)")
     ap.add_argument("--no-dense", action="store_true", help="skip the all-tiles timing")
@@ -163,9 +169,13 @@ def main():
         return
 
     w = synth.workload(args.workload)
+    import dataclasses
     if args.tau is not None:
-        import dataclasses
         w = dataclasses.replace(w, tau=args.tau)
+    if args.pooled_mode is not None:
+        if args.pooled_param is None:
+            sys.exit("--pooled-mode needs --pooled-param")
+        w = dataclasses.replace(w, pooled_mode=args.pooled_mode, pooled_param=args.pooled_param)
     log(f"workload {w.name}: B={w.B} H={w.H} d={w.d} grid {w.T}x{w.Hs}x{w.Ws} N={w.N} "
         f"Bq={w.Bq} Bk={w.Bk} mask={w.mask}")
     t0 = time.time()

@@ -129,14 +129,14 @@ bsa_status bsa_build_mask_pooled(const bsa_shape* s, bsa_dtype dt, bsa_tensor q,
   if (st != BSA_OK) return st;
   if (dt != BSA_BF16 && dt != BSA_F32) return fail(BSA_ERR_UNSUPPORTED, "dtype %d", (int)dt);
   if (!isfinite(scale)) return fail(BSA_ERR_INVALID, "scale is not finite");
-  if (mode == 0) {
+  if (mode == 0 || mode == 2) {
     if (!(param >= 1.0) || param != floor(param) || param > 2147483647.0)
       return fail(BSA_ERR_INVALID, "top-k needs an integer k >= 1, got %g", param);
-  } else if (mode == 1) {
+  } else if (mode == 1 || mode == 3) {
     if (!(param > 0.0 && param <= 1.0))
       return fail(BSA_ERR_INVALID, "cumulative mass tau_p must be in (0, 1], got %g", param);
   } else {
-    return fail(BSA_ERR_INVALID, "mode %d not in {0, 1}", mode);
+    return fail(BSA_ERR_INVALID, "mode %d not in {0, 1, 2, 3}", mode);
   }
   if (g.nK > bsa::pooled_max_blocks())
     return fail(BSA_ERR_UNSUPPORTED, "pooled selection supports at most %d key blocks",

@@ -26,6 +26,8 @@ size_t pooled_workspace_bytes(const Geom& g);
 hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k, double scale,
                               int32_t mode, double param, uint8_t* mask, void* ws,
                               hipStream_t st);
+hipError_t launch_pooled_global(const Geom& g, int32_t mode, double param, uint8_t* mask,
+                                void* ws, hipStream_t st);
 
 // Counts kept tiles per list row into row_ptr[1..R] and row_ptr[0] = 0, then
 // turns row_ptr into its inclusive prefix sum.

@@ -221,6 +221,224 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
   for (int c = threadIdx.x; c < nK; c += blockDim.x) mrow[c] = flag[c];
 }
 
+// ------------------------------------------------------- global selection
+// Head-wide selection over every (row block, key block) pair ([VMoBA]
+// section 三: rank all query/block relevances together and serve the
+// strongest first; the number of blocks a head keeps follows how
+// concentrated its attention is). Mode 2 ranks pairs by S, mode 3 by the row
+// softmax p = exp(S - max_row S) / Z_row (Z summed in ascending block order,
+// as in mode 1), ties to the lower pair index a*nK + c. Mode 2 keeps the
+// first k pairs, mode 3 the shortest prefix whose mass reaches tau_p * nQ
+// (all pairs when tau_p = 1 or the total falls short). Every row also keeps
+// its best block (S desc, c asc).
+
+// One wave per row: best block, and for mode 3 the row's probabilities
+// (exponentials in parallel, Z summed sequentially in ascending block order
+// as in mode 1, then one division each).
+__global__ __launch_bounds__(kWave) void pooled_rowstats_kernel(int64_t nK, int32_t mode,
+                                                               const double* __restrict__ S,
+                                                               double* __restrict__ P,
+                                                               int32_t* __restrict__ best) {
+  __shared__ double ex[kPooledMaxBlocks];
+  __shared__ double zsh;
+  const int lane = threadIdx.x;
+  const int64_t r = blockIdx.x;
+  const double* s = S + r * nK;
+  double m = -INFINITY;
+  int32_t arg = INT32_MAX;
+  for (int64_t c = lane; c < nK; c += kWave) {
+    if (s[c] > m || (s[c] == m && c < arg)) {
+      m = s[c];
+      arg = (int32_t)c;
+    }
+  }
+  for (int off = kWave / 2; off >= 1; off >>= 1) {
+    const double m2 = __shfl_xor(m, off);
+    const int32_t a2 = __shfl_xor(arg, off);
+    if (m2 > m || (m2 == m && a2 < arg)) {
+      m = m2;
+      arg = a2;
+    }
+  }
+  if (lane == 0) best[r] = arg;
+  if (mode != 3) return;
+  for (int64_t c = lane; c < nK; c += kWave) ex[c] = exp(s[c] - m);
+  __syncthreads();
+  if (lane == 0) {
+    double Z = 0.0;
+    for (int64_t c = 0; c < nK; ++c) Z = Z + ex[c];
+    zsh = Z;
+  }
+  __syncthreads();
+  const double Z = zsh;
+  double* pr = P + r * nK;
+  for (int64_t c = lane; c < nK; c += kWave) pr[c] = ex[c] / Z;
+}
+
+// Order-preserving map of a double to 64 bits (larger value -> larger key;
+// -0 and +0 map alike).
+__device__ inline uint64_t order_key(double v) {
+  if (v == 0.0) v = 0.0;
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  return (b >> 63) ? ~b : (b | (1ull << 63));
+}
+
+// The cut of one head, found 4 bits at a time from the top (radix select in
+// (key desc, index asc) order). `need_c` / `need_m` are the pairs / mass
+// still to take below the keys already fixed as larger.
+struct HeadCut {
+  uint64_t prefix;  // key bits fixed so far
+  double need_m;
+  int64_t need_c;
+  int64_t ties;     // pairs whose key equals the final prefix
+  int64_t last;     // tied pairs with index <= last are kept
+  int32_t all;      // every pair is kept
+  int32_t pad;
+};
+
+constexpr int kGselThreads = 256;
+constexpr int kGselGroups = 32;  // workgroups per head in a histogram pass
+
+__global__ void gsel_init_kernel(int64_t BH, int64_t nQ, int64_t nK, int32_t mode, double param,
+                                 HeadCut* __restrict__ cut) {
+  const int64_t bh = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (bh >= BH) return;
+  const int64_t n = nQ * nK;
+  HeadCut c;
+  c.prefix = 0;
+  c.need_m = param * (double)nQ;
+  c.need_c = mode == 2 ? (int64_t)param : 0;
+  c.ties = 0;
+  c.last = n;
+  c.all = (mode == 2 ? param >= (double)n : param >= 1.0) ? 1 : 0;
+  c.pad = 0;
+  cut[bh] = c;
+}
+
+// One histogram pass: per (head, group of pairs) the count and mass of the
+// pairs matching the prefix, by the 4-bit digit at `shift`. Each thread
+// walks its pairs in a fixed order into its own LDS slots; slots are then
+// summed in a fixed tree, so the masses are deterministic.
+__global__ __launch_bounds__(kGselThreads) void gsel_hist_kernel(
+    int64_t nQ, int64_t nK, int32_t mode, int32_t shift, const double* __restrict__ S,
+    const double* __restrict__ P, const HeadCut* __restrict__ cut, int64_t* __restrict__ pc,
+    double* __restrict__ pm) {
+  __shared__ double hm[16][kGselThreads];
+  __shared__ int32_t hc[16][kGselThreads];
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.y, g = blockIdx.x, n = nQ * nK;
+  const HeadCut c = cut[bh];
+  if (c.all) return;
+  for (int b = 0; b < 16; ++b) {
+    hm[b][tid] = 0.0;
+    hc[b][tid] = 0;
+  }
+  const uint64_t pmask = shift >= 60 ? 0 : (~0ull << (shift + 4));
+  const int64_t per = (n + kGselGroups - 1) / kGselGroups;
+  const int64_t e0 = g * per, e1 = min(n, e0 + per);
+  const double* keys = (mode == 2 ? S : P) + bh * n;
+  const double* mass = P + bh * n;
+  for (int64_t e = e0 + tid; e < e1; e += kGselThreads) {
+    const uint64_t u = order_key(keys[e]);
+    if ((u & pmask) != c.prefix) continue;
+    const int b = (int)((u >> shift) & 15);
+    hc[b][tid] += 1;
+    if (mode == 3) hm[b][tid] = hm[b][tid] + mass[e];
+  }
+  __syncthreads();
+  for (int off = kGselThreads / 2; off >= 1; off >>= 1) {
+    if (tid < off)
+      for (int b = 0; b < 16; ++b) {
+        hc[b][tid] += hc[b][tid + off];
+        hm[b][tid] = hm[b][tid] + hm[b][tid + off];
+      }
+    __syncthreads();
+  }
+  if (tid < 16) {
+    pc[(bh * kGselGroups + g) * 16 + tid] = hc[tid][0];
+    pm[(bh * kGselGroups + g) * 16 + tid] = hm[tid][0];
+  }
+}
+
+// One thread per head: add the groups' histograms in group order and fix the
+// next digit: the highest bucket in which the remaining count (mode 2) or
+// mass (mode 3) is reached. When the mass is never reached the walk ends in
+// the lowest bucket with the rest counted above it, which keeps every pair.
+__global__ void gsel_choose_kernel(int64_t BH, int32_t mode, int32_t shift,
+                                   const int64_t* __restrict__ pc, const double* __restrict__ pm,
+                                   HeadCut* __restrict__ cut) {
+  const int64_t bh = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (bh >= BH) return;
+  HeadCut c = cut[bh];
+  if (c.all) return;
+  int chosen = 0;
+  for (int b = 15; b >= 0; --b) {
+    int64_t cb = 0;
+    double mb = 0.0;
+    for (int g = 0; g < kGselGroups; ++g) {
+      cb += pc[(bh * kGselGroups + g) * 16 + b];
+      mb = mb + pm[(bh * kGselGroups + g) * 16 + b];
+    }
+    const bool here = mode == 2 ? cb >= c.need_c : (cb > 0 && mb >= c.need_m);
+    if (here || b == 0) {
+      chosen = b;
+      c.ties = cb;
+      break;
+    }
+    c.need_c -= cb;
+    c.need_m = c.need_m - mb;
+  }
+  c.prefix |= (uint64_t)chosen << shift;
+  cut[bh] = c;
+}
+
+// One thread per head: among several pairs with the cut key, the ones taken
+// come first in index order (rare: equal keys).
+__global__ void gsel_ties_kernel(int64_t BH, int64_t n, int32_t mode, const double* __restrict__ S,
+                                 const double* __restrict__ P, HeadCut* __restrict__ cut) {
+  const int64_t bh = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (bh >= BH) return;
+  HeadCut c = cut[bh];
+  if (c.all || c.ties <= 1) return;
+  const double* keys = (mode == 2 ? S : P) + bh * n;
+  const double* mass = P + bh * n;
+  int64_t need = c.need_c;
+  double acc = 0.0;
+  for (int64_t e = 0; e < n; ++e) {
+    if (order_key(keys[e]) != c.prefix) continue;
+    if (mode == 2) {
+      if (--need == 0) {
+        c.last = e;
+        break;
+      }
+    } else {
+      acc = acc + mass[e];
+      if (acc >= c.need_m) {
+        c.last = e;
+        break;
+      }
+    }
+  }
+  cut[bh] = c;
+}
+
+// One thread per pair: keep the pairs before the cut and every row's best block.
+__global__ void gsel_mark_kernel(int64_t BH, int64_t nQ, int64_t nK, int32_t mode,
+                                 const double* __restrict__ S, const double* __restrict__ P,
+                                 const int32_t* __restrict__ best,
+                                 const HeadCut* __restrict__ cut, uint8_t* __restrict__ mask) {
+  const int64_t n = nQ * nK, total = BH * n;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t bh = t / n, e = t - bh * n, a = e / nK, c = e - a * nK;
+    const HeadCut h = cut[bh];
+    const uint64_t u = order_key((mode == 2 ? S : P)[t]);
+    const bool keep = h.all || u > h.prefix || (u == h.prefix && e <= h.last) ||
+                      best[bh * nQ + a] == (int32_t)c;
+    mask[t] = keep ? 1 : 0;
+  }
+}
+
 // -------------------------------------------------------------- compaction
 __device__ inline bool tile_listed(const uint8_t* mask, int64_t mhs, const uint8_t* skip,
                                    int64_t r, int64_t nQ, int64_t nK, int64_t c) {
@@ -394,9 +612,15 @@ hipError_t launch_radial_mask(const Geom& g, int32_t h0, int32_t beta, uint8_t* 
 }
 
 size_t pooled_workspace_bytes(const Geom& g) {
+  // qbar, kbar, scores; then for the head-wide modes: probabilities, per-group
+  // histogram partials (counts and masses), one cut per head, best blocks
   const int64_t BH = (int64_t)g.B * g.H;
-  const int64_t n = BH * (g.nQ + g.nK) * g.D + BH * g.nQ * g.nK;
-  return (size_t)n * sizeof(double);
+  const int64_t n = BH * (g.nQ + g.nK) * g.D + 2 * BH * g.nQ * g.nK;
+  size_t bytes = (size_t)n * sizeof(double);
+  bytes += (size_t)BH * kGselGroups * 16 * (sizeof(int64_t) + sizeof(double));
+  bytes += (size_t)BH * sizeof(HeadCut);
+  bytes += (size_t)BH * g.nQ * sizeof(int32_t);
+  return (bytes + 255) / 256 * 256;
 }
 
 int pooled_max_blocks() { return kPooledMaxBlocks; }
@@ -421,11 +645,40 @@ hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k
                      g.nQ, g.nK, scale, qbar, kbar, S);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (mode >= 2) return launch_pooled_global(g, mode, param, mask, ws, st);
   int32_t P = 1;
   while (P < g.nK) P <<= 1;
   const size_t sh2 = sizeof(double) * 2 * g.nK + sizeof(int32_t) * P + g.nK + 16;
   hipLaunchKernelGGL(pooled_select_kernel, dim3((unsigned)(BH * g.nQ)), dim3(kSelectThreads),
                      sh2, st, g.nK, P, mode, param, S, mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_pooled_global(const Geom& g, int32_t mode, double param, uint8_t* mask,
+                                void* ws, hipStream_t st) {
+  const int64_t BH = (int64_t)g.B * g.H;
+  if (BH == 0 || g.N == 0) return hipSuccess;
+  const int64_t n = g.nQ * g.nK;
+  double* S = (double*)ws + BH * (g.nQ + g.nK) * g.D;
+  double* P = S + BH * n;
+  int64_t* pc = (int64_t*)(P + BH * n);
+  double* pm = (double*)(pc + BH * kGselGroups * 16);
+  HeadCut* cut = (HeadCut*)(pm + BH * kGselGroups * 16);
+  int32_t* best = (int32_t*)(cut + BH);
+  hipLaunchKernelGGL(pooled_rowstats_kernel, dim3((unsigned)(BH * g.nQ)), dim3(kWave), 0, st,
+                     g.nK, mode, S, P, best);
+  hipLaunchKernelGGL(gsel_init_kernel, dim3(grid_for(BH, 64)), dim3(64), 0, st, BH, g.nQ, g.nK,
+                     mode, param, cut);
+  for (int shift = 60; shift >= 0; shift -= 4) {
+    hipLaunchKernelGGL(gsel_hist_kernel, dim3(kGselGroups, (unsigned)BH), dim3(kGselThreads), 0,
+                       st, g.nQ, g.nK, mode, shift, S, P, cut, pc, pm);
+    hipLaunchKernelGGL(gsel_choose_kernel, dim3(grid_for(BH, 64)), dim3(64), 0, st, BH, mode,
+                       shift, pc, pm, cut);
+  }
+  hipLaunchKernelGGL(gsel_ties_kernel, dim3(grid_for(BH, 64)), dim3(64), 0, st, BH, n, mode, S, P,
+                     cut);
+  hipLaunchKernelGGL(gsel_mark_kernel, dim3(grid_for(BH * n, 256)), dim3(256), 0, st, BH, g.nQ,
+                     g.nK, mode, S, P, best, cut, mask);
   return hipGetLastError();
 }
 

@@ -104,8 +104,10 @@ BSA_API bsa_status bsa_build_mask_radial(const bsa_shape* s, int32_t h0, int32_t
                                  uint8_t* mask, void* stream);
 
 /*
- * Bytes of device workspace bsa_build_mask_pooled needs for shape s
- * (pooled means of Q and K in fp64 and the per-row scores).
+ * Bytes of device workspace bsa_build_mask_pooled needs for shape s, any
+ * mode (pooled means of Q and K and the scores in fp64; for the head-wide
+ * modes also the row probabilities and the selection's per-head state);
+ * a multiple of 256.
  */
 BSA_API size_t bsa_pooled_workspace_bytes(const bsa_shape* s);
 
@@ -123,6 +125,20 @@ BSA_API size_t bsa_pooled_workspace_bytes(const bsa_shape* s);
  *     mode 1: the shortest prefix whose running sum of p_c reaches param,
  *             p_c = exp(S_ac - max S_a) / Z, Z summed in ascending c,
  *             param = tau_p in (0, 1] (all blocks if the sum never reaches it).
+ *   Head-wide modes ([VMoBA] section 三: rank every query block against every
+ *   key block together and serve the strongest pairs first; a head keeps as
+ *   many blocks as its attention concentration calls for): all nQ*nK pairs
+ *   of (b, h) are ordered by (key desc, a*nK + c asc) and
+ *     mode 2: the first min(param, nQ*nK) pairs are kept, key S_ac
+ *             (param = k >= 1), or
+ *     mode 3: key p_ac (the row softmax of mode 1); the shortest prefix whose
+ *             running mass reaches param * nQ is kept (param = tau_p in
+ *             (0, 1]; all pairs for tau_p = 1 or if the mass falls short).
+ *             The mass is summed in a fixed parallel order, so a pair whose
+ *             prefix sum lies within rounding (~1e-12 relative) of the target
+ *             can differ from a sequential sum.
+ *   In modes 2 and 3 every row also keeps its best block (S desc, c asc), so
+ *   no row is empty.
  *   q, k        inputs of dtype dt ([B][N][H][d] by strides)
  *   mask        out, [B][H][nQ][nK]
  *   workspace   device buffer of at least bsa_pooled_workspace_bytes(s)

@@ -175,7 +175,7 @@ void oracle_build_mask_radial(int64_t T, int64_t Hs, int64_t Ws, int64_t bq,
 /*    mode 2 (global top-k): the first min(k, nQ*nK) pairs are kept, key S; */
 /*    mode 3 (global cumulative mass): key p_ac = e_ac / Z_a with e and Z   */
 /*      of row a as in mode 1; the shortest prefix whose running sum of p   */
-/*      reaches tau_p * nQ is kept (all pairs if never).                    */
+/*      reaches tau_p * nQ is kept (all pairs if never, or if tau_p = 1).   */
 /* In both, every row also keeps its own first block in (S desc, c asc)     */
 /* order, so that no row is left empty. margin_out[bh*nQ] holds the head's  */
 /* margin for mode 3 (as in mode 1, against tau_p * nQ); other rows inf.    */
@@ -292,6 +292,8 @@ int oracle_build_mask_pooled(int64_t B, int64_t H, int64_t N, int64_t D,
       double margin = INFINITY;
       if (mode == 2) {
         keep = (int64_t)param < n ? (int64_t)param : n;
+      } else if (param >= 1.0) {
+        keep = n; /* the whole mass: every pair, however the sum rounds */
       } else {
         double target = param * (double)nQ, run = 0.0, prev = 0.0;
         for (int64_t t = 0; t < n; ++t) {

@@ -112,12 +112,18 @@ def test_pooled_validation(L):
     s = S()
     need = L.bsa_pooled_workspace_bytes(C.byref(s))
     B, H, D, nQ, nK = 1, 2, 128, 1, 2
-    assert need == 8 * (B * H * (nQ + nK) * D + B * H * nQ * nK)
+    # pooled means and scores, plus the head-wide modes' probabilities
+    assert need >= 8 * (B * H * (nQ + nK) * D + 2 * B * H * nQ * nK)
+    assert need % 256 == 0
 
     def call(mode=1, param=0.5, ws=P, wsb=need, mask=P, dt=0, shape=s, scale=0.1):
         return L.bsa_build_mask_pooled(C.byref(shape), dt, T(), T(P + 256), scale, mode, param,
                                        mask, ws, wsb, None)
-    assert call(mode=2) == INVALID
+    assert call(mode=4) == INVALID
+    assert call(mode=-1) == INVALID
+    assert call(mode=2, param=0.5) == INVALID     # head-wide top-k needs an integer k
+    assert call(mode=3, param=0.0) == INVALID
+    assert call(mode=3, param=1.01) == INVALID
     assert call(mode=1, param=0.0) == INVALID
     assert call(mode=1, param=1.5) == INVALID
     assert call(mode=0, param=0.0) == INVALID
