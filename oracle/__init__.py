@@ -58,6 +58,8 @@ def lib():
         L.oracle_attention.restype = C.c_int
         L.oracle_order_lists.argtypes = [i64] * 5 + [C.c_int, p, p, p]
         L.oracle_order_lists.restype = None
+        L.oracle_make_permutation.argtypes = [i64, i64, i64, C.c_int, p, p]
+        L.oracle_make_permutation.restype = None
         _lib = L
     return _lib
 
@@ -165,6 +167,41 @@ def order_lists(row_ptr: np.ndarray, kv_idx: np.ndarray, N: int, bq: int, bk: in
     if kv_in.size:
         lib().oracle_order_lists(N, bq, bk, nQ, row_ptr.size - 1, int(order), _ptr(row_ptr),
                                  _ptr(kv_in), _ptr(out))
+    return out
+
+
+# ------------------------------------------------------- token permutation
+PERM_AXES, PERM_BOXES = 0, 1
+
+
+def make_permutation(T: int, Hs: int, Ws: int, kind: int, axes) -> np.ndarray:
+    """perm[i'] = original token of new position i' (PAROAttention summary page,
+    section 二: one of the six axis orders; VMoBA summary page, section 三:
+    temporal chunks, spatial patches or cubes). kind 0: axes = (slowest,
+    middle, fastest) axis ids (0 frame, 1 row, 2 column); kind 1: axes =
+    box extent (frames, rows, columns)."""
+    if kind == PERM_AXES and sorted(axes) != [0, 1, 2]:
+        raise ValueError("axis order must be a permutation of (0, 1, 2)")
+    if kind == PERM_BOXES and min(axes) < 1:
+        raise ValueError("box extents must be >= 1")
+    ax = np.ascontiguousarray(axes, dtype=np.int64)
+    perm = np.empty(T * Hs * Ws, dtype=np.int32)
+    lib().oracle_make_permutation(T, Hs, Ws, int(kind), _ptr(ax), _ptr(perm))
+    return perm
+
+
+def permute_tokens(x: np.ndarray, perm: np.ndarray, scatter: bool = False) -> np.ndarray:
+    """Gather (out[:, i'] = x[:, perm[i']]) or scatter (out[:, perm[i']] = x[:, i'])
+    of the token axis of a [B][N][H][d] array; perm is [N] (every head) or
+    [H][N] (one per head)."""
+    out = np.empty_like(x)
+    P = np.asarray(perm)
+    for h in range(x.shape[2]):
+        ph = P if P.ndim == 1 else P[h]
+        if scatter:
+            out[:, ph, h, :] = x[:, :, h, :]
+        else:
+            out[:, :, h, :] = x[:, ph, h, :]
     return out
 
 

@@ -392,6 +392,45 @@ void oracle_order_lists(int64_t N, int64_t bq, int64_t bk, int64_t nQ, int64_t R
 }
 
 /* ------------------------------------------------------------------------ */
+/* Token orders before blocking. [PARO] section 二: flattening the video to  */
+/* one sequence scatters tokens that attend to each other; reordering them  */
+/* (one of the 6 orders of the frame, height and width axes, chosen per     */
+/* head) gathers them into block-shaped patterns. [VMoBA] section 三: blocks */
+/* made of temporal chunks (about 3 frames), spatial patches, or            */
+/* spatio-temporal cubes, cycled across layers.                             */
+/* perm[i'] = original token index of new position i' (i = (t*Hs + y)*Ws+x).*/
+/* kind 0: axis order; axes[0..2] name the slowest, middle and fastest axis */
+/*         (0 = frame t, 1 = row y, 2 = column x).                          */
+/* kind 1: box partition: boxes of axes[0] frames x axes[1] rows x axes[2]  */
+/*         columns (smaller at the far edges), boxes in (t, y, x) order and */
+/*         tokens inside a box in (t, y, x) order. Boxes of one frame's     */
+/*         whole plane are temporal chunks, boxes of one frame are spatial  */
+/*         patches, boxes spanning several frames are cubes.                */
+/* Plain enumeration in the stated order.                                   */
+/* ------------------------------------------------------------------------ */
+void oracle_make_permutation(int64_t T, int64_t Hs, int64_t Ws, int kind,
+                             const int64_t* axes, int32_t* perm) {
+  int64_t n = 0;
+  if (kind == 0) {
+    int64_t ext[3] = {T, Hs, Ws};
+    int64_t co[3];
+    for (co[axes[0]] = 0; co[axes[0]] < ext[axes[0]]; ++co[axes[0]])
+      for (co[axes[1]] = 0; co[axes[1]] < ext[axes[1]]; ++co[axes[1]])
+        for (co[axes[2]] = 0; co[axes[2]] < ext[axes[2]]; ++co[axes[2]])
+          perm[n++] = (int32_t)((co[0] * Hs + co[1]) * Ws + co[2]);
+    return;
+  }
+  int64_t ct = axes[0], cy = axes[1], cx = axes[2];
+  for (int64_t t0 = 0; t0 < T; t0 += ct)
+    for (int64_t y0 = 0; y0 < Hs; y0 += cy)
+      for (int64_t x0 = 0; x0 < Ws; x0 += cx)
+        for (int64_t t = t0; t < t0 + ct && t < T; ++t)
+          for (int64_t y = y0; y < y0 + cy && y < Hs; ++y)
+            for (int64_t x = x0; x < x0 + cx && x < Ws; ++x)
+              perm[n++] = (int32_t)((t * Hs + y) * Ws + x);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Masked softmax attention (the plain definition the kernels reach by an    */
 /* exact re-association; bidirectional, no causal mask). For query i of row  */
 /* block a of head (b, h), J_i is the union of the column blocks c with      */
