@@ -130,6 +130,11 @@ def main():
                          "workload's")
     ap.add_argument("--pooled-param", type=float, default=None,
                     help="pooled workloads: k or tau_p for --pooled-mode")
+    ap.add_argument("--token-order", default=None, metavar="SPEC",
+                    help="pooled workloads: gather Q/K/V into a token order before blocking "
+                         "and scatter O back, inside the step: axes:A,B,C (slowest..fastest, "
+                         "0 frame 1 row 2 column), boxes:T,H,W (box extent), or paro (head h "
+                         "takes axis order h mod 6)")
     ap.add_argument("--cpu-rows", type=int, default=800,
                     help="row blocks in the CPU oracle sample (0 = skip)")
     ap.add_argument("--no-dense", action="store_true", help="skip the all-tiles timing")
@@ -224,6 +229,28 @@ def main():
             step_inputs.append((to_dev(y["q"]), to_dev(y["k"])))
         log(f"{w.steps} denoising-step inputs resident")
 
+    perm = None
+    vv = v
+    if args.token_order:
+        if w.mask != "pooled":
+            sys.exit("--token-order applies to pooled workloads (radial masks are defined on "
+                     "the (t, y, x) order)")
+        import itertools
+        orders = list(itertools.permutations(range(3)))
+        perm = torch.empty(w.H * w.N, dtype=torch.int32, device=dev)   # one order per head
+        spec = args.token_order
+        for h in range(w.H):
+            sl = perm[h * w.N:(h + 1) * w.N]
+            if spec == "paro":
+                bsa.bsa_make_token_permutation(s, bsa.PERM_AXES, orders[h % 6], sl)
+            else:
+                kind, vals = spec.split(":")
+                ax = [int(z) for z in vals.split(",")]
+                bsa.bsa_make_token_permutation(
+                    s, bsa.PERM_AXES if kind == "axes" else bsa.PERM_BOXES, ax, sl)
+        qp, kp, vp, op = (torch.empty_like(q) for _ in range(4))
+        vv = vp
+
     fwd_events = []
     state = {"i": 0, "capture": None}
 
@@ -233,9 +260,14 @@ def main():
             bsa.bsa_compact_block_lists(s, mask, 0, None, row_ptr, kv_idx)
             qq, kk_ = q, k
         elif w.mask == "pooled":
-            bsa.bsa_build_mask_pooled(s, q, k, w.scale, w.pooled_mode, w.pooled_param, mask, ws)
-            bsa.bsa_compact_block_lists(s, mask, nQ * nK, None, row_ptr, kv_idx)
             qq, kk_ = q, k
+            if perm is not None:
+                for a, b in ((q, qp), (k, kp), (v, vp)):
+                    bsa.bsa_permute_tokens(s, perm, w.N, 0, a, b)
+                qq, kk_ = qp, kp
+            bsa.bsa_build_mask_pooled(s, qq, kk_, w.scale, w.pooled_mode, w.pooled_param, mask,
+                                      ws)
+            bsa.bsa_compact_block_lists(s, mask, nQ * nK, None, row_ptr, kv_idx)
         else:
             si = state["i"] % w.steps
             if si == 0:
@@ -257,11 +289,13 @@ def main():
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        bsa.bsa_sparse_attn_fwd(s, qq, kk_, v, o, lse, row_ptr, kv_idx, shared, w.scale,
-                                gap if use_gap else None)
+        bsa.bsa_sparse_attn_fwd(s, qq, kk_, vv, op if perm is not None else o, lse, row_ptr,
+                                kv_idx, shared, w.scale, gap if use_gap else None)
         if record:
             e1.record(stream)
             fwd_events.append((e0, e1, state["i"] % max(1, w.steps)))
+        if perm is not None:
+            bsa.bsa_permute_tokens(s, perm, w.N, 1, op, o)
         if use_gap:
             bsa.bsa_update_skip_mask(s, row_ptr, kv_idx, gap, taus[si], skip)
         state["i"] += 1
@@ -387,6 +421,7 @@ def main():
                 {"mode": w.pooled_mode, "tau_p": w.pooled_param} if w.mask == "pooled"
                 else {"tau": taus, "steps": w.steps, "order": args.order,
                       "share_after": args.share_after}),
+            "token_order": args.token_order,
             "kept_tiles": nnz_tiles,
             "tile_sparsity": (1.0 - nnz_tiles / (R * nK)) if nnz_tiles is not None else None,
             "computed_tflop_per_call": float(np.mean(per_step_flops)) / 1e12,

@@ -18,6 +18,7 @@ __all__ = [
     "bsa_build_mask_radial", "bsa_pooled_workspace_bytes", "bsa_build_mask_pooled",
     "bsa_compact_block_lists", "bsa_order_block_lists", "bsa_sparse_attn_fwd",
     "bsa_update_skip_mask", "ORDER_ASCENDING", "ORDER_RADIAL",
+    "bsa_make_token_permutation", "bsa_permute_tokens", "PERM_AXES", "PERM_BOXES",
     "bsa_status_string", "bsa_last_error",
 ]
 
@@ -27,6 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libbsa.so")
 BSA_OK, BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED, BSA_ERR_CAPACITY, BSA_ERR_DEVICE = range(5)
 BSA_BF16, BSA_F32 = 0, 1
 ORDER_ASCENDING, ORDER_RADIAL = 0, 1
+PERM_AXES, PERM_BOXES = 0, 1
 
 
 class BsaError(RuntimeError):
@@ -82,6 +84,8 @@ def lib() -> C.CDLL:
             "bsa_build_mask_pooled": (i32, [SP, i32, Tensor, Tensor, f64, i32, f64, p, p, sz, p]),
             "bsa_compact_block_lists": (i32, [SP, p, i64, p, p, p, i64, C.POINTER(i64), p]),
             "bsa_order_block_lists": (i32, [SP, i32, p, i32, p, p, p]),
+            "bsa_make_token_permutation": (i32, [SP, i32, C.POINTER(i32), p, p]),
+            "bsa_permute_tokens": (i32, [SP, i32, p, i64, i32, Tensor, Tensor, p]),
             "bsa_sparse_attn_fwd": (i32, [SP, i32, Tensor, Tensor, Tensor, Tensor, p, p, p, i32,
                                           f32, p, p]),
             "bsa_update_skip_mask": (i32, [SP, p, p, p, f32, p, p]),
@@ -178,6 +182,19 @@ def bsa_order_block_lists(s: Shape, order: int, row_ptr, lists_shared: int, kv_i
     _check("bsa_order_block_lists",
            lib().bsa_order_block_lists(C.byref(s), order, _ptr(row_ptr), lists_shared,
                                        _ptr(kv_in), _ptr(kv_out), _stream(stream)))
+
+
+def bsa_make_token_permutation(s: Shape, kind: int, axes, perm, stream=None):
+    ax = (C.c_int32 * 3)(*[int(a) for a in axes])
+    _check("bsa_make_token_permutation",
+           lib().bsa_make_token_permutation(C.byref(s), kind, ax, _ptr(perm), _stream(stream)))
+
+
+def bsa_permute_tokens(s: Shape, perm, perm_head_stride: int, scatter: int, x, out,
+                       stream=None):
+    _check("bsa_permute_tokens",
+           lib().bsa_permute_tokens(C.byref(s), _dtype(x), _ptr(perm), perm_head_stride, scatter,
+                                    _tensor(x), _tensor(out), _stream(stream)))
 
 
 def bsa_sparse_attn_fwd(s: Shape, q, k, v, o, lse=None, row_ptr=None, kv_idx=None,

@@ -218,6 +218,51 @@ bsa_status bsa_order_block_lists(const bsa_shape* s, int32_t order, const int32_
                 "list order launch");
 }
 
+bsa_status bsa_make_token_permutation(const bsa_shape* s, int32_t kind, const int32_t* axes,
+                                      int32_t* perm, void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  if (!axes) return fail(BSA_ERR_INVALID, "axes is NULL");
+  if (kind == 0) {
+    const int32_t a = axes[0], b = axes[1], c = axes[2];
+    if (a < 0 || b < 0 || c < 0 || a > 2 || b > 2 || c > 2 || a == b || b == c || a == c)
+      return fail(BSA_ERR_INVALID, "axis order (%d, %d, %d) is not a permutation of (0, 1, 2)",
+                  a, b, c);
+  } else if (kind == 1) {
+    if (axes[0] < 1 || axes[1] < 1 || axes[2] < 1)
+      return fail(BSA_ERR_INVALID, "box extents (%d, %d, %d) must be >= 1", axes[0], axes[1],
+                  axes[2]);
+  } else {
+    return fail(BSA_ERR_INVALID, "kind %d not in {0, 1}", kind);
+  }
+  if (g.N == 0) return ok();
+  if (!perm) return fail(BSA_ERR_INVALID, "perm is NULL");
+  return device(bsa::launch_make_permutation(g, kind, axes, perm, (hipStream_t)stream),
+                "permutation launch");
+}
+
+bsa_status bsa_permute_tokens(const bsa_shape* s, bsa_dtype dt, const int32_t* perm,
+                              int64_t perm_head_stride, int32_t scatter, bsa_tensor in,
+                              bsa_tensor out, void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  if (dt != BSA_BF16 && dt != BSA_F32) return fail(BSA_ERR_UNSUPPORTED, "dtype %d", (int)dt);
+  if (scatter != 0 && scatter != 1) return fail(BSA_ERR_INVALID, "scatter must be 0 or 1");
+  if (perm_head_stride != 0 && perm_head_stride < g.N)
+    return fail(BSA_ERR_INVALID, "perm_head_stride must be 0 or >= N");
+  if (empty(g)) return ok();
+  if (!perm) return fail(BSA_ERR_INVALID, "perm is NULL");
+  const int eb = elem_bytes(dt);
+  if ((st = check_tensor("in", in, eb)) != BSA_OK) return st;
+  if ((st = check_tensor("out", out, eb)) != BSA_OK) return st;
+  if (in.ptr == out.ptr) return fail(BSA_ERR_INVALID, "out must not alias in");
+  return device(bsa::launch_permute_tokens(g, eb, perm, perm_head_stride, scatter, arg(in),
+                                           arg(out), (hipStream_t)stream),
+                "permute launch");
+}
+
 bsa_status bsa_sparse_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, bsa_tensor k,
                                bsa_tensor v, bsa_tensor o, float* lse, const int32_t* row_ptr,
                                const int32_t* kv_idx, int32_t lists_shared, float scale,

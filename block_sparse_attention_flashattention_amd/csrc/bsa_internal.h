@@ -45,6 +45,13 @@ hipError_t launch_skip_update(const Geom& g, const int32_t* row_ptr, const int32
                               const float* tile_gap, float tau2, uint8_t* skip,
                               hipStream_t st);
 
+// ---- token orders (permute_kernels.hip)
+hipError_t launch_make_permutation(const Geom& g, int32_t kind, const int32_t* axes,
+                                   int32_t* perm, hipStream_t st);
+hipError_t launch_permute_tokens(const Geom& g, int elem_bytes, const int32_t* perm,
+                                 int64_t perm_head_stride, int32_t scatter, TensorArg in,
+                                 TensorArg out, hipStream_t st);
+
 // ---- attention forward
 struct AttnArgs {
   TensorArg q, k, v;

@@ -199,6 +199,45 @@ BSA_API bsa_status bsa_order_block_lists(const bsa_shape* s, int32_t order, cons
                                  void* stream);
 
 /*
+ * Token order before blocking ([PARO] section 二: flattening the video to one
+ * sequence separates tokens that attend to each other; reordering by one of
+ * the six orders of the frame, row and column axes, chosen per head, makes
+ * the attention block-shaped. [VMoBA] section 三: blocks made of temporal
+ * chunks, spatial patches or spatio-temporal cubes).
+ * Writes perm[i'] = the original token (i = (t*height + y)*width + x) that
+ * new position i' holds:
+ *   kind 0: axes = (slowest, middle, fastest) axis, a permutation of
+ *           (0 = frame, 1 = row, 2 = column); (0, 1, 2) is the identity.
+ *   kind 1: axes = box extent (frames, rows, columns), each >= 1: boxes in
+ *           (frame, row, column) order, tokens inside a box in (frame, row,
+ *           column) order, boxes at the far edges smaller. Boxes covering
+ *           whole frames are temporal chunks (the identity order); boxes of
+ *           one frame are spatial patches; deeper boxes are cubes.
+ *   perm        out, int32 [N] (device)
+ * Exact integer work. One call per order; per-head orders are built into
+ * consecutive [N] slices of one [H][N] array.
+ */
+BSA_API bsa_status bsa_make_token_permutation(const bsa_shape* s, int32_t kind,
+                                      const int32_t* axes /* host, [3] */, int32_t* perm,
+                                      void* stream);
+
+/*
+ * Moves the tokens of a [B][N][H][d] tensor into or out of a token order
+ * (pure data movement; bytes are copied as they are):
+ *   scatter 0 (gather):  out[b][i'][h] = in[b][perm_h[i']][h]
+ *   scatter 1 (scatter): out[b][perm_h[i']][h] = in[b][i'][h]
+ * with perm_h = perm + h*perm_head_stride (0: one order for every head, else
+ * >= N). Q, K and V are gathered before masks, lists and the forward call,
+ * and the forward's O is scattered back; attention over the new order
+ * differs from the original only through which tiles the mask keeps.
+ * perm should hold each of 0..N-1 once; an entry outside [0, N) moves
+ * nothing. out must not alias in.
+ */
+BSA_API bsa_status bsa_permute_tokens(const bsa_shape* s, bsa_dtype dt, const int32_t* perm,
+                              int64_t perm_head_stride, int32_t scatter, bsa_tensor in,
+                              bsa_tensor out, void* stream);
+
+/*
  * Block-sparse attention forward ([PSA]: whole blocks are kept or dropped;
  * [Lite] section 六: online softmax over the tiles of a persistent skip list;
  * bidirectional, no causal mask). For query i of row block a of head (b, h),

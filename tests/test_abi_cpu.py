@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     out = subprocess.run(["nm", "-D", "--defined-only", bsa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (bsa_\w+)", out))
@@ -172,3 +172,25 @@ def test_order_lists_validation(L):
     assert L.bsa_order_block_lists(C.byref(S(head_dim=96)), 1, P, 1, P, P + 64, None) == UNSUPPORTED
     # empty shapes enqueue nothing and need no pointers
     assert L.bsa_order_block_lists(C.byref(S(frames=0)), 1, None, 1, None, None, None) == 0
+
+
+def test_permutation_validation(L):
+    s = S()
+    def mk(kind, axes, perm=P):
+        return L.bsa_make_token_permutation(C.byref(s), kind, (C.c_int32 * 3)(*axes), perm, None)
+    assert mk(0, (0, 1, 1)) == INVALID               # not a permutation of the axes
+    assert mk(0, (0, 1, 3)) == INVALID
+    assert mk(1, (1, 0, 2)) == INVALID               # empty box
+    assert mk(2, (1, 1, 1)) == INVALID
+    assert mk(0, (2, 0, 1), perm=None) == INVALID
+    assert L.bsa_make_token_permutation(C.byref(s), 0, None, P, None) == INVALID
+    N = 3 * 5 * 7
+    def pt(perm=P, phs=0, scatter=0, x=None, out=None, dt=0):
+        return L.bsa_permute_tokens(C.byref(s), dt, perm, phs, scatter, x or T(), out or T(P + 4096),
+                                    None)
+    assert pt(phs=N - 1) == INVALID
+    assert pt(scatter=2) == INVALID
+    assert pt(perm=None) == INVALID
+    assert pt(out=T()) == INVALID                    # in place is refused
+    assert pt(x=T(P + 8)) == INVALID                 # misaligned
+    assert pt(dt=5) == UNSUPPORTED

@@ -1,0 +1,120 @@
+"""GPU parity for token orders before blocking, through the C ABI.
+
+PAROAttention summary page, section 二 (six axis orders, per head); VMoBA
+summary page, section 三 (chunks, patches, cubes). The orders and the
+gather/scatter are integer work and data movement, so they must match the
+oracle bit for bit; the pooled path over a permuted sequence is checked end
+to end (mask bit-exact, outputs within the attention bounds).
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_flashattention_amd as bsa
+import oracle
+import synth
+from _gpu_util import (DEV, compare, dev, gather_rows, host, note, run_fwd, sample_rows,
+                       shape_of)
+
+pytestmark = pytest.mark.gpu
+
+ORDERS = list(itertools.permutations(range(3)))
+BOXES = [(1, 2, 2), (3, 4, 4), (2, 5, 8), (1, 15, 26), (3, 30, 52), (4, 7, 9)]
+
+
+def gpu_perm(s, kind, axes):
+    perm = torch.full((s.N,), -1, dtype=torch.int32, device=DEV)
+    bsa.bsa_make_token_permutation(s, kind, axes, perm)
+    torch.cuda.synchronize()
+    return host(perm)
+
+
+@pytest.mark.parametrize("grid", [(21, 30, 52), (21, 45, 80), (5, 7, 9), (1, 1, 3)])
+def test_make_permutation_bit_exact(grid):
+    T, Hs, Ws = grid
+    s = bsa.shape(1, 1, 128, T, Hs, Ws, 64)
+    for axes in ORDERS:
+        np.testing.assert_array_equal(gpu_perm(s, bsa.PERM_AXES, axes),
+                                      oracle.make_permutation(T, Hs, Ws, 0, axes))
+    for box in BOXES:
+        np.testing.assert_array_equal(gpu_perm(s, bsa.PERM_BOXES, box),
+                                      oracle.make_permutation(T, Hs, Ws, 1, box))
+    note(f"grid {grid}: 6 axis orders and {len(BOXES)} box partitions bit-exact")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("per_head", [False, True])
+def test_permute_tokens_bit_exact(dtype, per_head):
+    w = synth.Workload("perm_small", 2, 3, 128, 5, 7, 9, 64, 64, dtype, "pooled", 630, True)
+    s = shape_of(w)
+    x = synth.make_qkv(w)
+    if per_head:
+        P = np.stack([oracle.make_permutation(w.T, w.Hs, w.Ws, 0, ORDERS[h + 1])
+                      for h in range(w.H)])
+        phs = w.N
+    else:
+        P = oracle.make_permutation(w.T, w.Hs, w.Ws, 1, (2, 3, 4))
+        phs = 0
+    pd = dev(P.astype(np.int32).ravel())
+    for name in ("q", "v"):
+        a = dev(x[name])
+        g = torch.empty_like(a)
+        bsa.bsa_permute_tokens(s, pd, phs, 0, a, g)
+        back = torch.empty_like(a)
+        bsa.bsa_permute_tokens(s, pd, phs, 1, g, back)
+        torch.cuda.synchronize()
+        want = oracle.permute_tokens(x[name], P)
+        gh = g.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" \
+            else g.cpu().numpy()
+        np.testing.assert_array_equal(gh, want)
+        assert torch.equal(back, a)
+
+
+def test_permuted_pooled_path_wan13b_480p_sampled():
+    """Per-head axis orders (head h takes order h mod 6), Q/K/V gathered, the
+    pooled mask and lists built over the new order, the forward run and O
+    scattered back; against the same steps on the CPU."""
+    w = synth.workload("wan13b_480p")
+    s = shape_of(w)
+    x = synth.make_qkv(w)
+    P = np.stack([oracle.make_permutation(w.T, w.Hs, w.Ws, 0, ORDERS[h % 6])
+                  for h in range(w.H)])
+    pd = torch.empty(w.H * w.N, dtype=torch.int32, device=DEV)
+    for h in range(w.H):
+        bsa.bsa_make_token_permutation(s, bsa.PERM_AXES, ORDERS[h % 6], pd[h * w.N:(h + 1) * w.N])
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    qp, kp, vp = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    for a, b in ((q, qp), (k, kp), (v, vp)):
+        bsa.bsa_permute_tokens(s, pd, w.N, 0, a, b)
+    ws = torch.empty(bsa.bsa_pooled_workspace_bytes(s), dtype=torch.uint8, device=DEV)
+    R = w.B * w.H * w.nQ
+    mask = torch.empty(R * w.nK, dtype=torch.uint8, device=DEV)
+    bsa.bsa_build_mask_pooled(s, qp, kp, w.scale, w.pooled_mode, w.pooled_param, mask, ws)
+    rp = torch.empty(R + 1, dtype=torch.int32, device=DEV)
+    kv = torch.empty(R * w.nK, dtype=torch.int32, device=DEV)
+    bsa.bsa_compact_block_lists(s, mask, w.nQ * w.nK, None, rp, kv)
+    op, lsep, _ = run_fwd(s, qp, kp, vp, rp, kv, 0, w.scale)
+    o = torch.empty_like(op)
+    bsa.bsa_permute_tokens(s, pd, w.N, 1, op, o)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(pd).reshape(w.H, w.N), P)
+    xq, xk, xv = (oracle.permute_tokens(x[n], P) for n in ("q", "k", "v"))
+    mref, _, margin = oracle.build_mask_pooled(xq, xk, w.Bq, w.Bk, w.scale, w.pooled_mode,
+                                               w.pooled_param)
+    mgpu = host(mask).reshape(w.B, w.H, w.nQ, w.nK)
+    np.testing.assert_array_equal(mgpu, mref)
+    rows = sample_rows(w.B, w.H, w.nQ, 3, 31, heads=[0, 1, 5, w.H - 1])
+    o_ref, lse_ref, _ = oracle.attention(xq, xk, xv, w.Bq, w.Bk, w.scale, mref, w.nQ * w.nK,
+                                         rows=rows)
+    og, lg = gather_rows(host(op), host(lsep), rows, w.B, w.H, w.N, w.Bq)
+    compare(og, lg, o_ref, lse_ref, "480p permuted pooled")
+    # the scatter returns every row to its original token
+    back = oracle.permute_tokens(host(op).astype(np.float32), P, scatter=True)
+    np.testing.assert_array_equal(host(o).astype(np.float32), back)
+    dense = 1 - mref.mean()
+    plain, _, _ = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, w.pooled_mode,
+                                           w.pooled_param)
+    note(f"480p pooled at tau_p {w.pooled_param:.4f}: {100 * dense:.1f}% sparse over per-head "
+         f"orders vs {100 * (1 - plain.mean()):.1f}% in (t, y, x) order")
