@@ -49,7 +49,7 @@ def lib():
         L.oracle_build_mask_radial.argtypes = [i64] * 7 + [p]
         L.oracle_build_mask_radial.restype = None
         L.oracle_build_mask_pooled.argtypes = ([i64] * 6 + [C.c_int] + [p, i64, i64, i64] * 2
-                                               + [d, C.c_int, d, p, p, p])
+                                               + [d, C.c_int, d, p, p, p, p, i64])
         L.oracle_build_mask_pooled.restype = C.c_int
         L.oracle_compact.argtypes = [i64] * 4 + [p, i64, p, p, p]
         L.oracle_compact.restype = i64
@@ -60,6 +60,13 @@ def lib():
         L.oracle_order_lists.restype = None
         L.oracle_make_permutation.argtypes = [i64, i64, i64, C.c_int, p, p]
         L.oracle_make_permutation.restype = None
+        L.oracle_pyramid_attention.argtypes = ([i64] * 6 + [C.c_int] + [p, i64, i64, i64] * 3
+                                               + [d, p, i64, i64, p, p, p])
+        L.oracle_pyramid_attention.restype = C.c_int
+        L.oracle_pyramid_regions.argtypes = [i64, i64, i64, p, p]
+        L.oracle_pyramid_regions.restype = None
+        L.oracle_compact_pyramid.argtypes = [i64] * 7 + [p, i64, p, p, p]
+        L.oracle_compact_pyramid.restype = i64
         _lib = L
     return _lib
 
@@ -113,13 +120,15 @@ def build_mask_radial(T, Hs, Ws, bq, bk, h0, beta) -> np.ndarray:
 
 # ------------------------------------------------------------------- pooled
 def build_mask_pooled(q: np.ndarray, k: np.ndarray, bq: int, bk: int, scale: float,
-                      mode: int, param: float, want_scores=False):
+                      mode: int, param: float, want_scores=False, levels_tau=None):
     """Returns (mask [B][H][nQ][nK] uint8, scores or None, margin [B][H][nQ]).
 
     mode 0: per-row top-k (param = k); 1: per-row cumulative mass (param =
     tau_p); 2: head-wide top-k over all (row, block) pairs (param = k);
     3: head-wide cumulative mass reaching tau_p * nQ (param = tau_p). In the
-    head-wide modes every row also keeps its best block."""
+    head-wide modes every row also keeps its best block. 4: pyramid levels
+    (Pyramid Sparse Attention page): mask = 1 + level by the thresholds
+    levels_tau (non-decreasing), 0 = dropped."""
     B, N, H, D = q.shape
     nQ, nK = -(-N // bq), -(-N // bk)
     dt = _dtype_code(q)
@@ -127,10 +136,14 @@ def build_mask_pooled(q: np.ndarray, k: np.ndarray, bq: int, bk: int, scale: flo
     mask = np.zeros((B, H, nQ, nK), dtype=np.uint8)
     scores = np.zeros((B, H, nQ, nK), dtype=np.float64) if want_scores else None
     margin = np.zeros((B, H, nQ), dtype=np.float64)
+    lt = np.ascontiguousarray(levels_tau if levels_tau is not None else [], dtype=np.float64)
+    if mode == 4 and not (1 <= lt.size <= 3 and np.all(np.diff(lt) >= 0)):
+        raise ValueError("pyramid levels need 1..3 non-decreasing thresholds")
     rc = lib().oracle_build_mask_pooled(
         B, H, N, D, bq, bk, dt, _ptr(q), *_strides(q), _ptr(k), *_strides(k),
         float(scale), int(mode), float(param), _ptr(mask),
-        _ptr(scores) if scores is not None else None, _ptr(margin))
+        _ptr(scores) if scores is not None else None, _ptr(margin),
+        _ptr(lt) if lt.size else None, int(lt.size))
     if rc != 0:
         raise MemoryError("oracle_build_mask_pooled failed to allocate")
     return mask, scores, margin
@@ -203,6 +216,56 @@ def permute_tokens(x: np.ndarray, perm: np.ndarray, scatter: bool = False) -> np
         else:
             out[:, :, h, :] = x[:, ph, h, :]
     return out
+
+
+# ------------------------------------------------------------------ pyramid
+def pyramid_regions(N: int, bk: int, n_levels: int):
+    """(first augmented block of each level's region + total, rows per level)."""
+    rb = np.zeros(n_levels + 1, np.int64)
+    rr = np.zeros(n_levels + 1, np.int64)
+    lib().oracle_pyramid_regions(N, bk, n_levels, _ptr(rb), _ptr(rr))
+    return rb, rr[:n_levels]
+
+
+def compact_pyramid(mask: np.ndarray, B: int, H: int, nQ: int, nK: int, N: int, bk: int,
+                    n_levels: int, mask_head_stride: int):
+    """Augmented-tile lists of a pyramid mask: (row_ptr, kv_idx, kv_quarters)."""
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    L = lib()
+    nnz = L.oracle_compact_pyramid(B, H, nQ, nK, N, bk, n_levels, _ptr(mask), mask_head_stride,
+                                   None, None, None)
+    row_ptr = np.zeros(B * H * nQ + 1, np.int32)
+    kv = np.zeros(max(nnz, 1), np.int32)
+    qm = np.zeros(max(nnz, 1), np.uint8)
+    L.oracle_compact_pyramid(B, H, nQ, nK, N, bk, n_levels, _ptr(mask), mask_head_stride,
+                             _ptr(row_ptr), _ptr(kv), _ptr(qm))
+    return row_ptr, kv[:nnz], qm[:nnz]
+
+
+def pyramid_attention(q, k, v, bq: int, bk: int, scale: float, mask: np.ndarray,
+                      mask_head_stride: int, rows=None):
+    """Attention where key block c attends at level mask-1 (Pyramid Sparse
+    Attention page): pooled keys/values of 2^level tokens with score +
+    level*ln 2. Returns (o [n][bq][D], lse [n][bq])."""
+    B, N, H, D = q.shape
+    nQ = -(-N // bq)
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    top = int(mask.max()) - 1 if mask.size else 0
+    if top >= 1 and N % (1 << top):
+        raise ValueError(f"level {top} needs N divisible by {1 << top}")
+    dt = _dtype_code(q)
+    if rows is None:
+        rows = np.arange(B * H * nQ, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    o = np.empty((rows.size, bq, D), np.float64)
+    lse = np.empty((rows.size, bq), np.float64)
+    rc = lib().oracle_pyramid_attention(
+        B, H, N, D, bq, bk, dt, _ptr(q), *_strides(q), _ptr(k), *_strides(k), _ptr(v),
+        *_strides(v), float(scale), _ptr(mask), mask_head_stride, rows.size, _ptr(rows),
+        _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise MemoryError("oracle_pyramid_attention failed to allocate")
+    return o, lse
 
 
 # ---------------------------------------------------------------- attention

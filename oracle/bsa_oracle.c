@@ -176,6 +176,14 @@ void oracle_build_mask_radial(int64_t T, int64_t Hs, int64_t Ws, int64_t bq,
 /*    mode 3 (global cumulative mass): key p_ac = e_ac / Z_a with e and Z   */
 /*      of row a as in mode 1; the shortest prefix whose running sum of p   */
 /*      reaches tau_p * nQ is kept (all pairs if never, or if tau_p = 1).   */
+/* Pyramid levels (mode 4; [PSA]: each query-block/key-block pair gets a    */
+/* resolution level by its importance, with thresholds rather than          */
+/* quantiles): row a walks its blocks in (S desc, c asc) order accumulating */
+/* the mode-1 softmax mass; a block whose running sum (including itself)    */
+/* first reaches levels_tau[l] or is still below it joins level l, for      */
+/* l = 0 .. n_levels-1 with levels_tau non-decreasing; later blocks are     */
+/* dropped. mask = 1 + level (0 = dropped). The row's first block is always */
+/* at level 0.                                                              */
 /* In both, every row also keeps its own first block in (S desc, c asc)     */
 /* order, so that no row is left empty. margin_out[bh*nQ] holds the head's  */
 /* margin for mode 3 (as in mode 1, against tau_p * nQ); other rows inf.    */
@@ -196,7 +204,8 @@ int oracle_build_mask_pooled(int64_t B, int64_t H, int64_t N, int64_t D,
                              const void* k, int64_t ksb, int64_t ksn, int64_t ksh,
                              double scale, int mode, double param,
                              uint8_t* mask, double* scores_out,
-                             double* margin_out) {
+                             double* margin_out, const double* levels_tau,
+                             int64_t n_levels) {
   int64_t nQ = (N + bq - 1) / bq, nK = (N + bk - 1) / bk;
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -207,8 +216,9 @@ int oracle_build_mask_pooled(int64_t B, int64_t H, int64_t N, int64_t D,
     double* S = (double*)malloc(sizeof(double) * nQ * nK);
     scored* ord = (scored*)malloc(sizeof(scored) * nK);
     double* P = mode == 3 ? (double*)malloc(sizeof(double) * nQ * nK) : NULL;
-    scored* gord = mode >= 2 ? (scored*)malloc(sizeof(scored) * nQ * nK) : NULL;
-    if (!qbar || !kbar || !S || !ord || (mode == 3 && !P) || (mode >= 2 && !gord)) {
+    int global = mode == 2 || mode == 3;
+    scored* gord = global ? (scored*)malloc(sizeof(scored) * nQ * nK) : NULL;
+    if (!qbar || !kbar || !S || !ord || (mode == 3 && !P) || (global && !gord)) {
 #pragma omp atomic write
       bad = 1;
       free(qbar); free(kbar); free(S); free(ord); free(P); free(gord);
@@ -269,6 +279,17 @@ int oracle_build_mask_pooled(int64_t B, int64_t H, int64_t N, int64_t D,
         }
         margin = fabs(run - param);
         if (keep > 1 && fabs(param - prev) < margin) margin = fabs(param - prev);
+      } else if (mode == 4) {
+        double smax = ord[0].s, Z = 0.0;
+        for (int64_t c = 0; c < nK; ++c) Z = Z + exp(S[a * nK + c] - smax);
+        double run = 0.0;
+        int64_t lvl = 0;
+        for (int64_t t = 0; t < nK && lvl < n_levels; ++t) {
+          m[ord[t].c] = (uint8_t)(1 + lvl);
+          run = run + exp(ord[t].s - smax) / Z;
+          while (lvl < n_levels && run >= levels_tau[lvl]) ++lvl;
+        }
+        keep = 0; /* levels written above */
       } else {
         /* global modes: the row keeps its best block; p of the row for mode 3 */
         keep = 1;
@@ -281,7 +302,7 @@ int oracle_build_mask_pooled(int64_t B, int64_t H, int64_t N, int64_t D,
       for (int64_t t = 0; t < keep; ++t) m[ord[t].c] = 1;
       if (margin_out) margin_out[row] = margin;
     }
-    if (mode >= 2) {
+    if (global) {
       int64_t n = nQ * nK;
       for (int64_t u = 0; u < n; ++u) {
         gord[u].s = mode == 2 ? S[u] : P[u];
@@ -428,6 +449,161 @@ void oracle_make_permutation(int64_t T, int64_t Hs, int64_t Ws, int kind,
           for (int64_t y = y0; y < y0 + cy && y < Hs; ++y)
             for (int64_t x = x0; x < x0 + cx && x < Ws; ++x)
               perm[n++] = (int32_t)((t * Hs + y) * Ws + x);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Pyramid attention ([PSA]: key/value blocks kept at several resolutions,  */
+/* each coarser level the average of the finer one; each pair of query and */
+/* key block attends at its assigned level; the probabilities stay          */
+/* consistent across levels).                                               */
+/* Reading: level l of key block c holds bk / 2^l pooled keys, each the     */
+/* mean of 2^l consecutive tokens of K (and of V); a pooled key stands for  */
+/* its 2^l tokens, so its weight is 2^l exp(s): its score gets + l ln 2.    */
+/* With equal scores inside every group the result equals level 0. N must  */
+/* be a multiple of 2^l for the levels used. For query i of row block a,    */
+/* the keys are: the tokens of blocks with mask = 1 (level 0) and the       */
+/* pooled keys of blocks with mask = 1 + l; softmax over all of them.       */
+/* Outputs as in oracle_attention (rows requested; NaN padding).            */
+/* ------------------------------------------------------------------------ */
+int oracle_pyramid_attention(int64_t B, int64_t H, int64_t N, int64_t D, int64_t bq,
+                             int64_t bk, int dtype,
+                             const void* q, int64_t qsb, int64_t qsn, int64_t qsh,
+                             const void* k, int64_t ksb, int64_t ksn, int64_t ksh,
+                             const void* v, int64_t vsb, int64_t vsn, int64_t vsh,
+                             double scale, const uint8_t* mask, int64_t mask_head_stride,
+                             int64_t n_rows, const int64_t* rows,
+                             double* o_out, double* lse_out) {
+  int64_t nQ = (N + bq - 1) / bq, nK = (N + bk - 1) / bk;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < n_rows; ++t) {
+    int64_t row = rows[t];
+    int64_t bh = row / nQ, a = row % nQ, b = bh / H, h = bh % H;
+    int64_t i0 = a * bq, i1 = (a + 1) * bq < N ? (a + 1) * bq : N;
+    const uint8_t* m = mask + bh * mask_head_stride + a * nK;
+    /* the row's keys: (pooled) key vectors, value vectors, log-weights */
+    int64_t nkeys = 0;
+    for (int64_t c = 0; c < nK; ++c) {
+      if (!m[c]) continue;
+      int64_t len = ((c + 1) * bk < N ? (c + 1) * bk : N) - c * bk;
+      nkeys += len >> (m[c] - 1);
+    }
+    double* kk = (double*)malloc(sizeof(double) * (nkeys > 0 ? nkeys : 1) * D);
+    double* vv = (double*)malloc(sizeof(double) * (nkeys > 0 ? nkeys : 1) * D);
+    double* lw = (double*)malloc(sizeof(double) * (nkeys > 0 ? nkeys : 1));
+    double* sc = (double*)malloc(sizeof(double) * (nkeys > 0 ? nkeys : 1));
+    double* qi = (double*)malloc(sizeof(double) * D);
+    double* acc = (double*)malloc(sizeof(double) * D);
+    if (!kk || !vv || !lw || !sc || !qi || !acc) {
+#pragma omp atomic write
+      bad = 1;
+      free(kk); free(vv); free(lw); free(sc); free(qi); free(acc);
+      continue;
+    }
+    int64_t u = 0;
+    for (int64_t c = 0; c < nK; ++c) {
+      if (!m[c]) continue;
+      int64_t lev = m[c] - 1, g = (int64_t)1 << lev;
+      int64_t j0 = c * bk, j1 = (c + 1) * bk < N ? (c + 1) * bk : N;
+      for (int64_t j = j0; j < j1; j += g, ++u) {
+        for (int64_t x = 0; x < D; ++x) {
+          double sk = 0.0, sv = 0.0;
+          for (int64_t jj = j; jj < j + g; ++jj) {
+            sk = sk + widen(k, dtype, b * ksb + jj * ksn + h * ksh + x);
+            sv = sv + widen(v, dtype, b * vsb + jj * vsn + h * vsh + x);
+          }
+          kk[u * D + x] = sk / (double)g;
+          vv[u * D + x] = sv / (double)g;
+        }
+        lw[u] = log((double)g);
+      }
+    }
+    for (int64_t r = 0; r < bq; ++r) {
+      if (o_out) for (int64_t x = 0; x < D; ++x) o_out[(t * bq + r) * D + x] = NAN;
+      if (lse_out) lse_out[t * bq + r] = NAN;
+    }
+    for (int64_t i = i0; i < i1; ++i) {
+      int64_t r = i - i0;
+      if (nkeys == 0) {
+        if (o_out) for (int64_t x = 0; x < D; ++x) o_out[(t * bq + r) * D + x] = 0.0;
+        if (lse_out) lse_out[t * bq + r] = -INFINITY;
+        continue;
+      }
+      for (int64_t x = 0; x < D; ++x) qi[x] = widen(q, dtype, b * qsb + i * qsn + h * qsh + x);
+      double mi = -INFINITY;
+      for (int64_t w = 0; w < nkeys; ++w) {
+        double dot = 0.0;
+        for (int64_t x = 0; x < D; ++x) dot = dot + qi[x] * kk[w * D + x];
+        sc[w] = scale * dot + lw[w];
+        if (sc[w] > mi) mi = sc[w];
+      }
+      double li = 0.0;
+      for (int64_t x = 0; x < D; ++x) acc[x] = 0.0;
+      for (int64_t w = 0; w < nkeys; ++w) {
+        double p = exp(sc[w] - mi);
+        li = li + p;
+        for (int64_t x = 0; x < D; ++x) acc[x] = acc[x] + p * vv[w * D + x];
+      }
+      if (o_out) for (int64_t x = 0; x < D; ++x) o_out[(t * bq + r) * D + x] = acc[x] / li;
+      if (lse_out) lse_out[t * bq + r] = mi + log(li);
+    }
+    free(kk); free(vv); free(lw); free(sc); free(qi); free(acc);
+  }
+  return bad ? -1 : 0;
+}
+
+/* Rows of the level-l region of the augmented key array: level l holds     */
+/* N / 2^l pooled rows, each region padded to a multiple of bk rows, levels */
+/* in order. region_block[l] = first block of region l.                     */
+void oracle_pyramid_regions(int64_t N, int64_t bk, int64_t n_levels, int64_t* region_block,
+                            int64_t* region_rows) {
+  int64_t blk = 0;
+  for (int64_t l = 0; l < n_levels; ++l) {
+    region_block[l] = blk;
+    region_rows[l] = N >> l;
+    blk += ((N >> l) + bk - 1) / bk;
+  }
+  region_block[n_levels] = blk;
+}
+
+/* Lists of augmented tiles for a pyramid mask ([PSA]: the logical block    */
+/* size is decoupled from the hardware tile). Logical block c at level l    */
+/* covers pooled rows [c*bk/2^l, (c+1)*bk/2^l) of region l, i.e. quarters   */
+/* (bk/4 rows each) of augmented block region_block[l] + c*bk/2^l / bk.     */
+/* Per row: every augmented block with at least one selected quarter, in    */
+/* ascending block order, with the bit mask of its selected quarters.       */
+int64_t oracle_compact_pyramid(int64_t B, int64_t H, int64_t nQ, int64_t nK, int64_t N,
+                               int64_t bk, int64_t n_levels, const uint8_t* mask,
+                               int64_t mask_head_stride, int32_t* row_ptr, int32_t* kv_idx,
+                               uint8_t* kv_quarters) {
+  int64_t rb[4], rr[4];
+  oracle_pyramid_regions(N, bk, n_levels, rb, rr);
+  int64_t nA = rb[n_levels];
+  uint8_t* qm = (uint8_t*)calloc((size_t)(nA > 0 ? nA : 1), 1);
+  int64_t nnz = 0;
+  for (int64_t bh = 0; bh < B * H; ++bh)
+    for (int64_t a = 0; a < nQ; ++a) {
+      int64_t r = bh * nQ + a;
+      if (row_ptr) row_ptr[r] = (int32_t)nnz;
+      memset(qm, 0, (size_t)nA);
+      for (int64_t c = 0; c < nK; ++c) {
+        int v = mask[bh * mask_head_stride + a * nK + c];
+        if (!v) continue;
+        int64_t l = v - 1, per = bk >> l;          /* pooled rows of the block */
+        int64_t row0 = c * per;                      /* first pooled row in region */
+        for (int64_t rr0 = row0; rr0 < row0 + per; rr0 += bk / 4)
+          qm[rb[l] + rr0 / bk] |= (uint8_t)(1u << ((rr0 % bk) / (bk / 4)));
+      }
+      for (int64_t ab = 0; ab < nA; ++ab)
+        if (qm[ab]) {
+          if (kv_idx) kv_idx[nnz] = (int32_t)ab;
+          if (kv_quarters) kv_quarters[nnz] = qm[ab];
+          ++nnz;
+        }
+    }
+  if (row_ptr) row_ptr[B * H * nQ] = (int32_t)nnz;
+  free(qm);
+  return nnz;
 }
 
 /* ------------------------------------------------------------------------ */
