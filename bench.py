@@ -52,6 +52,23 @@ def tile_flops(row_ptr: np.ndarray, kv_idx: np.ndarray, N: int, Bq: int, Bk: int
     return 4.0 * d * float(np.sum(ra * cc)) * reps
 
 
+def pyramid_flops(row_ptr, kv_idx, kv_q, N, Bq, Bk, d, nQ, rb) -> float:
+    """4 d |R_a| (keys of the selected quarters) summed over pyramid tiles; a
+    level-l tile's keys are pooled rows, N >> l of them in level l."""
+    rows = np.repeat(np.arange(len(row_ptr) - 1), np.diff(row_ptr))
+    a = rows % nQ
+    ra = np.minimum(N, (a + 1) * Bq) - a * Bq
+    ab = kv_idx.astype(np.int64)
+    lev = np.searchsorted(np.asarray(rb[1:]), ab, side="right")
+    start = (ab - np.asarray(rb)[lev]) * Bk
+    valid = np.clip((N >> lev) - start, 0, Bk)
+    keys = np.zeros_like(ab)
+    for qd in range(4):
+        on = (kv_q.astype(np.int64) >> qd) & 1
+        keys += on * np.clip(valid - 16 * qd, 0, 16)
+    return 4.0 * d * float(np.sum(ra * keys))
+
+
 def source_sha() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
@@ -135,6 +152,10 @@ def main():
                          "and scatter O back, inside the step: axes:A,B,C (slowest..fastest, "
                          "0 frame 1 row 2 column), boxes:T,H,W (box extent), or paro (head h "
                          "takes axis order h mod 6)")
+    ap.add_argument("--pyramid", default=None, metavar="T0[,T1[,T2]]",
+                    help="pooled workloads: pyramid attention with these level thresholds "
+                         "(cumulative mass; level l pools 2^l tokens); the step builds the "
+                         "K/V levels, the level mask and the tile lists, then runs the forward")
     ap.add_argument("--cpu-rows", type=int, default=800,
                     help="row blocks in the CPU oracle sample (0 = skip)")
     ap.add_argument("--no-dense", action="store_true", help="skip the all-tiles timing")
@@ -251,6 +272,22 @@ def main():
         qp, kp, vp, op = (torch.empty_like(q) for _ in range(4))
         vv = vp
 
+    taus_pyr = None
+    if args.pyramid:
+        if w.mask != "pooled" or args.token_order:
+            sys.exit("--pyramid applies to pooled workloads in (t, y, x) order")
+        taus_pyr = [float(z) for z in args.pyramid.split(",")]
+        n_lev = len(taus_pyr)
+        prow = bsa.bsa_pyramid_rows(s, n_lev)
+        kpyr = torch.empty((w.B, max(prow, 1), w.H, w.d), dtype=q.dtype, device=dev)
+        vpyr = torch.empty_like(kpyr)
+        rb_p = [0]
+        for l in range(1, n_lev + 1):
+            rb_p.append(rb_p[-1] + -(-(w.N >> (l - 1)) // w.Bk))
+        cap_p = BH * nQ * rb_p[-1]
+        kv_idx = torch.empty(cap_p, dtype=torch.int32, device=dev)
+        kv_q = torch.empty(cap_p, dtype=torch.int32, device=dev)
+
     fwd_events = []
     state = {"i": 0, "capture": None}
 
@@ -259,6 +296,11 @@ def main():
             bsa.bsa_build_mask_radial(s, w.h0, w.beta, mask)
             bsa.bsa_compact_block_lists(s, mask, 0, None, row_ptr, kv_idx)
             qq, kk_ = q, k
+        elif w.mask == "pooled" and taus_pyr is not None:
+            qq, kk_ = q, k
+            bsa.bsa_build_kv_pyramid(s, n_lev, k, v, kpyr, vpyr)
+            bsa.bsa_build_mask_pyramid(s, q, k, w.scale, taus_pyr, mask, ws)
+            bsa.bsa_compact_pyramid_lists(s, n_lev, mask, nQ * nK, row_ptr, kv_idx, kv_q)
         elif w.mask == "pooled":
             qq, kk_ = q, k
             if perm is not None:
@@ -283,14 +325,20 @@ def main():
         if state["capture"] is not None:
             torch.cuda.synchronize()
             rp_c = row_ptr.cpu().numpy().astype(np.int64)
-            state["capture"].append((rp_c, kv_idx[:int(rp_c[-1])].cpu().numpy()))
+            nz = int(rp_c[-1])
+            state["capture"].append((rp_c, kv_idx[:nz].cpu().numpy(),
+                                     kv_q[:nz].cpu().numpy() if taus_pyr is not None else None))
         use_gap = w.mask == "skip" and not frozen
         if record:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        bsa.bsa_sparse_attn_fwd(s, qq, kk_, vv, op if perm is not None else o, lse, row_ptr,
-                                kv_idx, shared, w.scale, gap if use_gap else None)
+        if taus_pyr is not None:
+            bsa.bsa_pyramid_attn_fwd(s, q, k, v, kpyr, vpyr, n_lev, o, lse, row_ptr, kv_idx,
+                                     kv_q, w.scale)
+        else:
+            bsa.bsa_sparse_attn_fwd(s, qq, kk_, vv, op if perm is not None else o, lse, row_ptr,
+                                    kv_idx, shared, w.scale, gap if use_gap else None)
         if record:
             e1.record(stream)
             fwd_events.append((e0, e1, state["i"] % max(1, w.steps)))
@@ -308,9 +356,13 @@ def main():
         step(False)
     torch.cuda.synchronize()
     captured, state["capture"] = state["capture"], None
-    per_step_flops = [tile_flops(rp, kvh, w.N, w.Bq, w.Bk, w.d, nQ, BH if shared else 1)
-                      for rp, kvh in captured]
-    per_step_tiles = [int(rp[-1]) for rp, _ in captured]
+    if taus_pyr is not None:
+        per_step_flops = [pyramid_flops(rp, kvh, qmh, w.N, w.Bq, w.Bk, w.d, nQ, rb_p)
+                          for rp, kvh, qmh in captured]
+    else:
+        per_step_flops = [tile_flops(rp, kvh, w.N, w.Bq, w.Bk, w.d, nQ, BH if shared else 1)
+                          for rp, kvh, _ in captured]
+    per_step_tiles = [int(rp[-1]) for rp, _, _ in captured]
     rp = captured[-1][0]
     state["i"] = 0
     nnz_tiles = int(rp[-1]) if w.mask != "skip" else None
@@ -422,6 +474,7 @@ def main():
                 else {"tau": taus, "steps": w.steps, "order": args.order,
                       "share_after": args.share_after}),
             "token_order": args.token_order,
+            "pyramid_levels_tau": taus_pyr,
             "kept_tiles": nnz_tiles,
             "tile_sparsity": (1.0 - nnz_tiles / (R * nK)) if nnz_tiles is not None else None,
             "computed_tflop_per_call": float(np.mean(per_step_flops)) / 1e12,

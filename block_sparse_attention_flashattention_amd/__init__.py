@@ -19,6 +19,8 @@ __all__ = [
     "bsa_compact_block_lists", "bsa_order_block_lists", "bsa_sparse_attn_fwd",
     "bsa_update_skip_mask", "ORDER_ASCENDING", "ORDER_RADIAL",
     "bsa_make_token_permutation", "bsa_permute_tokens", "PERM_AXES", "PERM_BOXES",
+    "bsa_pyramid_rows", "bsa_build_kv_pyramid", "bsa_build_mask_pyramid",
+    "bsa_compact_pyramid_lists", "bsa_pyramid_attn_fwd",
     "bsa_status_string", "bsa_last_error",
 ]
 
@@ -86,6 +88,14 @@ def lib() -> C.CDLL:
             "bsa_order_block_lists": (i32, [SP, i32, p, i32, p, p, p]),
             "bsa_make_token_permutation": (i32, [SP, i32, C.POINTER(i32), p, p]),
             "bsa_permute_tokens": (i32, [SP, i32, p, i64, i32, Tensor, Tensor, p]),
+            "bsa_pyramid_rows": (i64, [SP, i32]),
+            "bsa_build_kv_pyramid": (i32, [SP, i32, i32, Tensor, Tensor, Tensor, Tensor, p]),
+            "bsa_build_mask_pyramid": (i32, [SP, i32, Tensor, Tensor, f64, i32,
+                                             C.POINTER(f64), p, p, sz, p]),
+            "bsa_compact_pyramid_lists": (i32, [SP, i32, p, i64, p, p, p, i64, C.POINTER(i64),
+                                                p]),
+            "bsa_pyramid_attn_fwd": (i32, [SP, i32, Tensor, Tensor, Tensor, Tensor, Tensor, i32,
+                                           Tensor, p, p, p, p, f32, p]),
             "bsa_sparse_attn_fwd": (i32, [SP, i32, Tensor, Tensor, Tensor, Tensor, p, p, p, i32,
                                           f32, p, p]),
             "bsa_update_skip_mask": (i32, [SP, p, p, p, f32, p, p]),
@@ -195,6 +205,51 @@ def bsa_permute_tokens(s: Shape, perm, perm_head_stride: int, scatter: int, x, o
     _check("bsa_permute_tokens",
            lib().bsa_permute_tokens(C.byref(s), _dtype(x), _ptr(perm), perm_head_stride, scatter,
                                     _tensor(x), _tensor(out), _stream(stream)))
+
+
+def bsa_pyramid_rows(s: Shape, n_levels: int) -> int:
+    return int(lib().bsa_pyramid_rows(C.byref(s), n_levels))
+
+
+def bsa_build_kv_pyramid(s: Shape, n_levels: int, k, v, k_pyr, v_pyr, stream=None):
+    _check("bsa_build_kv_pyramid",
+           lib().bsa_build_kv_pyramid(C.byref(s), _dtype(k), n_levels, _tensor(k), _tensor(v),
+                                      _tensor(k_pyr), _tensor(v_pyr), _stream(stream)))
+
+
+def bsa_build_mask_pyramid(s: Shape, q, k, scale: float, levels_tau, mask, workspace,
+                           stream=None):
+    taus = (C.c_double * len(levels_tau))(*[float(t) for t in levels_tau])
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("bsa_build_mask_pyramid",
+           lib().bsa_build_mask_pyramid(C.byref(s), _dtype(q), _tensor(q), _tensor(k), scale,
+                                        len(levels_tau), taus, _ptr(mask), _ptr(workspace),
+                                        nbytes, _stream(stream)))
+
+
+def bsa_compact_pyramid_lists(s: Shape, n_levels: int, mask, mask_head_stride: int, row_ptr,
+                              kv_idx, kv_quarters, kv_capacity: int | None = None,
+                              want_nnz: bool = False, stream=None):
+    if kv_capacity is None:
+        kv_capacity = kv_idx.numel() if kv_idx is not None else 0
+    nnz = C.c_int64(-1)
+    _check("bsa_compact_pyramid_lists",
+           lib().bsa_compact_pyramid_lists(C.byref(s), n_levels, _ptr(mask), mask_head_stride,
+                                           _ptr(row_ptr), _ptr(kv_idx), _ptr(kv_quarters),
+                                           kv_capacity, C.byref(nnz) if want_nnz else None,
+                                           _stream(stream)))
+    return int(nnz.value) if want_nnz else None
+
+
+def bsa_pyramid_attn_fwd(s: Shape, q, k, v, k_pyr, v_pyr, n_levels: int, o, lse, row_ptr,
+                         kv_idx, kv_quarters, scale: float | None = None, stream=None):
+    if scale is None:
+        scale = 1.0 / float(s.head_dim) ** 0.5
+    _check("bsa_pyramid_attn_fwd",
+           lib().bsa_pyramid_attn_fwd(C.byref(s), _dtype(q), _tensor(q), _tensor(k), _tensor(v),
+                                      _tensor(k_pyr), _tensor(v_pyr), n_levels, _tensor(o),
+                                      _ptr(lse), _ptr(row_ptr), _ptr(kv_idx), _ptr(kv_quarters),
+                                      scale, _stream(stream)))
 
 
 def bsa_sparse_attn_fwd(s: Shape, q, k, v, o, lse=None, row_ptr=None, kv_idx=None,

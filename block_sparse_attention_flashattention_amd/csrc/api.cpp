@@ -263,6 +263,180 @@ bsa_status bsa_permute_tokens(const bsa_shape* s, bsa_dtype dt, const int32_t* p
                 "permute launch");
 }
 
+// Level regions of pyramid lists: rb[l] = first augmented key block of level
+// l (each level's N >> l pooled rows padded to whole 64-row blocks).
+static void pyramid_regions(const bsa::Geom& g, int32_t n_levels, int64_t rb[4]) {
+  rb[0] = 0;
+  for (int l = 1; l <= 3; ++l)
+    rb[l] = l <= n_levels ? rb[l - 1] + (((g.N >> (l - 1)) + g.Bk - 1) / g.Bk) : rb[l - 1];
+}
+
+static bsa_status check_levels(const bsa::Geom& g, int32_t n_levels) {
+  if (n_levels < 1 || n_levels > 3) return fail(BSA_ERR_INVALID, "n_levels %d not in 1..3", n_levels);
+  if (g.N % (int64_t(1) << (n_levels - 1)))
+    return fail(BSA_ERR_UNSUPPORTED, "N = %lld is not a multiple of %d (pooling groups)",
+                (long long)g.N, 1 << (n_levels - 1));
+  return BSA_OK;
+}
+
+int64_t bsa_pyramid_rows(const bsa_shape* s, int32_t n_levels) {
+  bsa::Geom g;
+  if (make_geom(s, &g) != BSA_OK || n_levels < 1 || n_levels > 3) return -1;
+  int64_t rb[4];
+  pyramid_regions(g, n_levels, rb);
+  return (rb[n_levels] - rb[1 < n_levels ? 1 : n_levels]) * g.Bk;
+}
+
+bsa_status bsa_build_kv_pyramid(const bsa_shape* s, bsa_dtype dt, int32_t n_levels, bsa_tensor k,
+                                bsa_tensor v, bsa_tensor k_pyr, bsa_tensor v_pyr, void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  if (dt != BSA_BF16 && dt != BSA_F32) return fail(BSA_ERR_UNSUPPORTED, "dtype %d", (int)dt);
+  if ((st = check_levels(g, n_levels)) != BSA_OK) return st;
+  if (empty(g) || n_levels == 1) return ok();
+  const int eb = elem_bytes(dt);
+  if ((st = check_tensor("k", k, eb)) != BSA_OK) return st;
+  if ((st = check_tensor("v", v, eb)) != BSA_OK) return st;
+  if ((st = check_tensor("k_pyr", k_pyr, eb)) != BSA_OK) return st;
+  if ((st = check_tensor("v_pyr", v_pyr, eb)) != BSA_OK) return st;
+  int64_t rb[4];
+  pyramid_regions(g, n_levels, rb);
+  return device(bsa::launch_kv_pyramid(g, eb, n_levels, rb, arg(k), arg(v), arg(k_pyr),
+                                       arg(v_pyr), (hipStream_t)stream),
+                "key/value pyramid launch");
+}
+
+bsa_status bsa_build_mask_pyramid(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, bsa_tensor k,
+                                  double scale, int32_t n_levels, const double* levels_tau,
+                                  uint8_t* mask, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  if (dt != BSA_BF16 && dt != BSA_F32) return fail(BSA_ERR_UNSUPPORTED, "dtype %d", (int)dt);
+  if (!isfinite(scale)) return fail(BSA_ERR_INVALID, "scale is not finite");
+  if (n_levels < 1 || n_levels > 3) return fail(BSA_ERR_INVALID, "n_levels %d not in 1..3", n_levels);
+  if (!levels_tau) return fail(BSA_ERR_INVALID, "levels_tau is NULL");
+  double taus[3] = {0, 0, 0};
+  for (int l = 0; l < n_levels; ++l) {
+    taus[l] = levels_tau[l];
+    if (!(taus[l] > 0.0 && taus[l] <= 1.0) || (l > 0 && taus[l] < taus[l - 1]))
+      return fail(BSA_ERR_INVALID, "level thresholds must be non-decreasing in (0, 1]");
+  }
+  if (g.nK > bsa::pooled_max_blocks())
+    return fail(BSA_ERR_UNSUPPORTED, "pooled selection supports at most %d key blocks",
+                bsa::pooled_max_blocks());
+  if (empty(g)) return ok();
+  if ((st = check_tensor("q", q, elem_bytes(dt))) != BSA_OK) return st;
+  if ((st = check_tensor("k", k, elem_bytes(dt))) != BSA_OK) return st;
+  if (!mask) return fail(BSA_ERR_INVALID, "mask is NULL");
+  const size_t need = bsa::pooled_workspace_bytes(g);
+  if (!workspace || workspace_bytes < need)
+    return fail(BSA_ERR_INVALID, "workspace needs %zu bytes", need);
+  if ((uintptr_t)workspace % 256) return fail(BSA_ERR_INVALID, "workspace not 256-byte aligned");
+  return device(bsa::launch_pooled_mask(g, dt == BSA_BF16 ? 0 : 1, arg(q), arg(k), scale, 4,
+                                        taus[0], mask, workspace, (hipStream_t)stream, taus,
+                                        n_levels),
+                "pyramid mask launch");
+}
+
+bsa_status bsa_compact_pyramid_lists(const bsa_shape* s, int32_t n_levels, const uint8_t* mask,
+                                     int64_t mask_head_stride, int32_t* row_ptr, int32_t* kv_idx,
+                                     int32_t* kv_quarters, int64_t kv_capacity,
+                                     int64_t* nnz_host, void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  if (n_levels < 1 || n_levels > 3) return fail(BSA_ERR_INVALID, "n_levels %d not in 1..3", n_levels);
+  if (mask_head_stride != 0 && mask_head_stride < g.nQ * g.nK)
+    return fail(BSA_ERR_INVALID, "mask_head_stride must be 0 or >= nQ*nK");
+  if (kv_capacity < 0) return fail(BSA_ERR_INVALID, "kv_capacity < 0");
+  if (!row_ptr) return fail(BSA_ERR_INVALID, "row_ptr is NULL");
+  int64_t rb[4];
+  pyramid_regions(g, n_levels, rb);
+  const int64_t R = (int64_t)g.B * g.H * g.nQ, nA = rb[n_levels];
+  if (R * nA > kI32Max)
+    return fail(BSA_ERR_UNSUPPORTED, "list rows x augmented blocks exceeds int32 list offsets");
+  hipStream_t str = (hipStream_t)stream;
+  if (R == 0 || g.nK == 0) {
+    if (nnz_host) *nnz_host = 0;
+    return device(bsa::launch_zero_row_ptr(row_ptr, str), "pyramid lists launch");
+  }
+  if (!mask) return fail(BSA_ERR_INVALID, "mask is NULL");
+  if ((!kv_idx || !kv_quarters) && kv_capacity > 0)
+    return fail(BSA_ERR_INVALID, "kv_idx and kv_quarters are required");
+  if (!nnz_host && kv_capacity < R * nA)
+    return fail(BSA_ERR_CAPACITY, "without nnz_host, kv_capacity must cover every tile (%lld)",
+                (long long)(R * nA));
+  hipError_t e = bsa::launch_pyramid_lists(g, n_levels, rb, mask, mask_head_stride, row_ptr,
+                                           nullptr, nullptr, true, str);
+  if (e != hipSuccess) return device(e, "pyramid list count");
+  if (nnz_host) {
+    int32_t nnz = 0;
+    e = hipMemcpyAsync(&nnz, row_ptr + R, sizeof nnz, hipMemcpyDeviceToHost, str);
+    if (e == hipSuccess) e = hipStreamSynchronize(str);
+    if (e != hipSuccess) return device(e, "pyramid list count readback");
+    *nnz_host = nnz;
+    if (nnz > kv_capacity)
+      return fail(BSA_ERR_CAPACITY, "%d tiles exceed kv_capacity %lld", nnz,
+                  (long long)kv_capacity);
+    if (nnz > 0 && (!kv_idx || !kv_quarters))
+      return fail(BSA_ERR_INVALID, "kv_idx and kv_quarters are required");
+  }
+  return device(bsa::launch_pyramid_lists(g, n_levels, rb, mask, mask_head_stride, row_ptr,
+                                          kv_idx, kv_quarters, false, str),
+                "pyramid list scatter");
+}
+
+bsa_status bsa_pyramid_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, bsa_tensor k,
+                                bsa_tensor v, bsa_tensor k_pyr, bsa_tensor v_pyr,
+                                int32_t n_levels, bsa_tensor o, float* lse,
+                                const int32_t* row_ptr, const int32_t* kv_idx,
+                                const int32_t* kv_quarters, float scale, void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  if (dt != BSA_BF16) return fail(BSA_ERR_UNSUPPORTED, "pyramid attention runs on bf16 inputs");
+  if ((st = check_levels(g, n_levels)) != BSA_OK) return st;
+  if (!isfinite(scale) || scale < 0.f)
+    return fail(BSA_ERR_INVALID, "scale must be finite and >= 0");
+  if (!row_ptr || !kv_idx || !kv_quarters)
+    return fail(BSA_ERR_INVALID, "row_ptr, kv_idx and kv_quarters are required");
+  if (empty(g)) return ok();
+  const int eb = 2;
+  if ((st = check_tensor("q", q, eb)) != BSA_OK) return st;
+  if ((st = check_tensor("k", k, eb)) != BSA_OK) return st;
+  if ((st = check_tensor("v", v, eb)) != BSA_OK) return st;
+  if ((st = check_tensor("o", o, eb)) != BSA_OK) return st;
+  if (o.ptr == q.ptr || o.ptr == k.ptr || o.ptr == v.ptr)
+    return fail(BSA_ERR_INVALID, "o must not alias q, k or v");
+  if (g.N > 1 && (k.stride_n < g.D || v.stride_n < g.D))
+    return fail(BSA_ERR_INVALID, "k and v need stride_n >= head_dim");
+  if (k.stride_n > (int64_t)(1 << 23) || v.stride_n > (int64_t)(1 << 23))
+    return fail(BSA_ERR_UNSUPPORTED, "k/v stride_n above 2^23 elements");
+  if (n_levels > 1) {
+    if ((st = check_tensor("k_pyr", k_pyr, eb)) != BSA_OK) return st;
+    if ((st = check_tensor("v_pyr", v_pyr, eb)) != BSA_OK) return st;
+    if (k_pyr.stride_n != k.stride_n || v_pyr.stride_n != v.stride_n)
+      return fail(BSA_ERR_INVALID, "k_pyr / v_pyr need the row stride of k / v");
+  }
+  bsa::AttnArgs a;
+  a.q = arg(q); a.k = arg(k); a.v = arg(v);
+  a.o = o.ptr; a.osb = o.stride_b; a.osn = o.stride_n; a.osh = o.stride_h;
+  a.lse = lse;
+  a.row_ptr = row_ptr;
+  a.kv_idx = kv_idx;
+  a.lists_shared = 0;
+  a.scale = scale;
+  a.tile_gap = nullptr;
+  a.kp = n_levels > 1 ? arg(k_pyr) : arg(k);
+  a.vp = n_levels > 1 ? arg(v_pyr) : arg(v);
+  a.kv_quarters = kv_quarters;
+  pyramid_regions(g, n_levels, a.pyr_rb);
+  return device(bsa::launch_attn_bf16(g, a, (hipStream_t)stream), "pyramid attention launch");
+}
+
 bsa_status bsa_sparse_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, bsa_tensor k,
                                bsa_tensor v, bsa_tensor o, float* lse, const int32_t* row_ptr,
                                const int32_t* kv_idx, int32_t lists_shared, float scale,

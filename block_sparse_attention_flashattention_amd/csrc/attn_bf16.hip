@@ -95,6 +95,14 @@ struct Bf16Params {
   int32_t H;
   int32_t T, U;  // frames; row-block slots per frame (ceil(F / BQ)), 0 = plain order
   int64_t F;     // tokens per frame
+  // pyramid attention: key blocks >= rb1 are pooled levels held in kp / vp
+  // (same row strides as k / v); level l region = blocks [rb_l, rb_{l+1}),
+  // N >> l valid rows; kv_quarters = selected 16-row quarters per entry
+  const uint16_t* kp;
+  const uint16_t* vp;
+  int64_t kpsb, kpsh, vpsb, vpsh;
+  const int32_t* kv_quarters;
+  int32_t rb1, rb2, rb3;
 };
 
 __device__ inline float other_half(float x) {
@@ -235,9 +243,10 @@ __device__ inline bf16x8 join(i16x4 lo, i16x4 hi) {
 // Key of lane value j (0..15) of 32-key block kb: kb*32 + 8*(j/4) + 4*hh + j%4.
 __device__ inline int key_of(int kb, int j, int hh) { return kb * 32 + 8 * (j / 4) + 4 * hh + (j % 4); }
 
-template <int D, int BQ, int SUB, bool GAP>
+template <int D, int BQ, int SUB, bool GAP, bool PYR>
 __global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(const Bf16Params p) {
+  static_assert(!(GAP && PYR), "tile gaps are defined on single-level lists");
   using C = Cfg<D, BQ, SUB>;
   using T = typename C::T;
   constexpr int KB = C::KB, NSUB = C::NSUB;
@@ -292,6 +301,8 @@ void attn_bf16_kernel(const Bf16Params p) {
   const int N32 = (int)p.N;
   const uint16_t* kbase = p.k + b * p.ksb + h * p.ksh;
   const uint16_t* vbase = p.v + b * p.vsb + h * p.vsh;
+  const uint16_t* kpbase = PYR ? p.kp + b * p.kpsb + h * p.kpsh : nullptr;
+  const uint16_t* vpbase = PYR ? p.vp + b * p.vpsb + h * p.vpsh : nullptr;
   // Step u covers keys [j0, j0 + SUB) with j0 = 64 * (key block of list
   // entry u / NSUB) + SUB * (u % NSUB); part = u % NSUB is static in the
   // unrolled loop below.
@@ -299,9 +310,33 @@ void attn_bf16_kernel(const Bf16Params p) {
     const int i = u / NSUB;
     return p.row_ptr ? load_uniform(p.kv_idx, e0 + i) : e0 + i;
   };
-  auto first_key = [&](int c, int part) -> int { return c * kBk + part * SUB; };
+  // Pyramid level of a key block (0 outside pyramid lists), the first row of
+  // the step in its source tensor (k or kp), and the valid rows of the step
+  // (level l region holds N >> l rows).
+  auto level_of = [&](int c) -> int {
+    if constexpr (!PYR) return 0;
+    return c < p.rb1 ? 0 : (c < p.rb2 ? 1 : 2);
+  };
+  auto first_key = [&](int c, int part) -> int {
+    if constexpr (PYR)
+      if (c >= p.rb1) return (c - p.rb1) * kBk + part * SUB;
+    return c * kBk + part * SUB;
+  };
   auto valid_keys = [&](int c, int part) -> int {
+    if constexpr (PYR) {
+      if (c < 0 || c >= p.rb3) return 0;  // not an augmented block: nothing read
+      const int l = level_of(c);
+      const int rb_l = l == 0 ? 0 : (l == 1 ? p.rb1 : p.rb2);
+      return max(0, min(SUB, (N32 >> l) - ((c - rb_l) * kBk + part * SUB)));
+    }
     return max(0, min(SUB, N32 - first_key(c, part)));
+  };
+  // Selected quarters of step u's keys, as a 4-bit mask over the step's
+  // (up to) four 16-key quarters (all set outside pyramid lists).
+  auto quarters_of = [&](int u) -> int {
+    if constexpr (!PYR) return 0xF;
+    const int q = load_uniform(p.kv_quarters, e0 + u / NSUB);
+    return NSUB == 2 ? ((q >> (2 * (u % NSUB))) & 3) | 0xC : q;
   };
 
   LoadPlan<C::LPW> lp;
@@ -313,13 +348,15 @@ void attn_bf16_kernel(const Bf16Params p) {
   constexpr int vso[2] = {C::VOFF, C::VOFF + T::BYTES};
   auto issue_k = [&](auto so_c, int c, int part) {
     const int j0 = first_key(c, part);
+    const uint16_t* base = (PYR && c >= p.rb1) ? kpbase : kbase;
     issue_rows<C::NW, C::LPW, decltype(so_c)::value>(
-        lp.k, rows_rsrc(kbase, p.ksn, j0, max(0, min(SUB, N32 - j0))), wave_lds);
+        lp.k, rows_rsrc(base, p.ksn, j0, valid_keys(c, part)), wave_lds);
   };
   auto issue_v = [&](auto so_c, int c, int part) {
     const int j0 = first_key(c, part);
+    const uint16_t* base = (PYR && c >= p.rb1) ? vpbase : vbase;
     issue_rows<C::NW, C::LPW, decltype(so_c)::value>(
-        lp.v, rows_rsrc(vbase, p.vsn, j0, max(0, min(SUB, N32 - j0))), wave_lds);
+        lp.v, rows_rsrc(base, p.vsn, j0, valid_keys(c, part)), wave_lds);
   };
   using K0 = std::integral_constant<uint32_t, kso[0]>;
   using K1 = std::integral_constant<uint32_t, kso[1]>;
@@ -329,16 +366,22 @@ void attn_bf16_kernel(const Bf16Params p) {
 
   // Key blocks of steps it, it+1, it+2 (rolling).
   int c0 = 0, c1 = 0, c2 = 0;
+  int q0 = 0xF, q1 = 0xF, q2 = 0xF;  // quarter masks of those steps
   if (LS > 0) {
     c0 = block_of(0);
+    q0 = quarters_of(0);
     issue_k(K0{}, c0, 0);
     issue_v(V0{}, c0, 0);
   }
   if (LS > 1) {
     c1 = block_of(1);
+    q1 = quarters_of(1);
     issue_k(K1{}, c1, PART1);
   }
-  if (LS > 2) c2 = block_of(2);
+  if (LS > 2) {
+    c2 = block_of(2);
+    q2 = quarters_of(2);
+  }
 
   // Q rows of this wave as MFMA B operands (k-slice hh*8..+7 of each 16-step).
   const int64_t qrow = a * BQ + w * 32 + n;
@@ -398,14 +441,18 @@ void attn_bf16_kernel(const Bf16Params p) {
   // beyond jv (only the last key block can be ragged) are set to -inf first,
   // which also makes their probabilities 0. A step with no valid key (second
   // half of a short last block) has max -inf.
-  auto tile_max = [&](f32x16(&sacc)[KB], bool masked, int jv) -> float {
-    if (masked) {
+  // Keys at or beyond jv, and keys in quarters outside qm (pyramid lists),
+  // are set to -inf: they take no part in the max and get probability 0.
+  auto mask_keys = [&](f32x16(&sacc)[KB], int jv, int qm) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (key_of(kb, j, hh) >= jv) sacc[kb][j] = -INFINITY;
-    }
+      for (int j = 0; j < 16; ++j)
+        if (key_of(kb, j, hh) >= jv || !((qm >> (2 * kb + (j >= 8))) & 1))
+          sacc[kb][j] = -INFINITY;
+  };
+  auto tile_max = [&](f32x16(&sacc)[KB], bool masked, int jv, int qm = 0xF) -> float {
+    if (masked) mask_keys(sacc, jv, qm);
     float mloc = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -439,8 +486,8 @@ void attn_bf16_kernel(const Bf16Params p) {
   };
   // p = 2^(s*scale*log2e - m) rounded to bf16, and its row sum. Masked keys
   // hold -inf and give 0 (sl2 > 0 always, see launch_attn_bf16).
-  auto probs = [&](const f32x16(&sacc)[KB], bf16x8(&pb)[KB][2]) {
-    const float neg_m = -m_use;
+  auto probs = [&](const f32x16(&sacc)[KB], bf16x8(&pb)[KB][2], float bias) {
+    const float neg_m = bias - m_use;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -492,7 +539,7 @@ void attn_bf16_kernel(const Bf16Params p) {
     barrier();
     scores(smem + kso[0], sA);
     const int jv = valid_keys(c0, 0);
-    apply_max(tile_max(sA, jv < SUB, jv), 0, 0);
+    apply_max(tile_max(sA, jv < SUB || q0 != 0xF, jv, q0) + (float)level_of(c0), 0, 0);
   }
   // One pipeline step: step `it` has scores in `cur`; when `has_next`, the
   // scores of step it+1 are computed into `nxt` meanwhile. Every LDS read of
@@ -509,6 +556,7 @@ void attn_bf16_kernel(const Bf16Params p) {
     if (it + 1 < LS) issue_v(VS_{}, c1, part1);
     if (it + 2 < LS) issue_k(KS_{}, c2, part0);
     const int c3 = it + 3 < LS ? block_of(it + 3) : 0;
+    const int q3 = (PYR && it + 3 < LS) ? quarters_of(it + 3) : 0xF;
     bf16x8 pb[KB][2];
     if (has_next) {
       const char* kt = smem + kso[1 - par];
@@ -532,7 +580,9 @@ void attn_bf16_kernel(const Bf16Params p) {
       uint32_t pw[KB][2][4];  // probabilities as packed bf16 pairs
       // Phase A: slot i issues score MFMA i of step it+1 and forms EPS
       // probabilities of step it (exp2, bf16 pair, row-sum dot).
-      const float neg_m = -m_use;
+      // a pooled key stands for 2^level tokens: its weight 2^level p, i.e.
+      // + level in the log2 exponent
+      const float neg_m = (float)level_of(c0) - m_use;
 #pragma unroll
       for (int i = 0; i < kPfK; ++i) kbuf[i] = kread(i);
 #pragma unroll
@@ -565,13 +615,7 @@ void attn_bf16_kernel(const Bf16Params p) {
         }
       asm volatile("" ::"v"(l_lane));
       const int jv = valid_keys(c1, part1);
-      if (jv < SUB) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (key_of(kb, j, hh) >= jv) nxt[kb][j] = -INFINITY;
-      }
+      if (jv < SUB || q1 != 0xF) mask_keys(nxt, jv, q1);
       // Phase B: slot i issues P V MFMA i of step it and folds MPS scores of
       // step it+1 into the row max.
       float mloc = -INFINITY;
@@ -589,14 +633,17 @@ void attn_bf16_kernel(const Bf16Params p) {
         __builtin_amdgcn_sched_barrier(0);
       }
       mloc = fmaxf(mloc, other_half(mloc));
-      apply_max(mloc * p.sl2, it + 1, part1);
+      apply_max(mloc * p.sl2 + (float)level_of(c1), it + 1, part1);
     } else {
-      probs(cur, pb);
+      probs(cur, pb, (float)level_of(c0));
       accumulate(smem + vso[par], pb);
     }
     c0 = c1;
     c1 = c2;
     c2 = c3;
+    q0 = q1;
+    q1 = q2;
+    q2 = q3;
   };
   int it = 0;
   using P0 = std::integral_constant<int, 0>;
@@ -666,11 +713,14 @@ hipError_t launch(const Geom& g, const Bf16Params& p, hipStream_t st) {
     const int64_t mult = p.lists_shared ? (int64_t)g.B * g.H : 1;
     hipLaunchKernelGGL(gap_init_kernel, dim3(1024), dim3(256), 0, st, p.tile_gap, p.row_ptr, R,
                        mult);
-    hipLaunchKernelGGL((attn_bf16_kernel<D, BQ, SUB, true>), dim3((unsigned)rows), dim3(C::NT),
-                       0, st, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BQ, SUB, true, false>), dim3((unsigned)rows),
+                       dim3(C::NT), 0, st, p);
+  } else if (p.kv_quarters) {
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BQ, SUB, false, true>), dim3((unsigned)rows),
+                       dim3(C::NT), 0, st, p);
   } else {
-    hipLaunchKernelGGL((attn_bf16_kernel<D, BQ, SUB, false>), dim3((unsigned)rows), dim3(C::NT),
-                       0, st, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BQ, SUB, false, false>), dim3((unsigned)rows),
+                       dim3(C::NT), 0, st, p);
   }
   return hipGetLastError();
 }
@@ -693,6 +743,14 @@ hipError_t launch_attn_bf16(const Geom& g, const AttnArgs& a, hipStream_t st) {
   p.kv_idx = a.kv_idx;
   p.tile_gap = a.tile_gap;
   p.lists_shared = a.lists_shared;
+  p.kp = (const uint16_t*)a.kp.ptr;
+  p.vp = (const uint16_t*)a.vp.ptr;
+  p.kpsb = a.kp.sb; p.kpsh = a.kp.sh;
+  p.vpsb = a.vp.sb; p.vpsh = a.vp.sh;
+  p.kv_quarters = a.kv_quarters;
+  p.rb1 = (int32_t)a.pyr_rb[1];
+  p.rb2 = (int32_t)a.pyr_rb[2];
+  p.rb3 = (int32_t)a.pyr_rb[3];
   // Scores enter every exponent as s * sl2. A zero scale is taken as the
   // smallest normal float instead: finite scores then still contribute
   // 2^(~0) (off by far less than bf16 rounding) while masked keys (-inf)

@@ -25,7 +25,8 @@ hipError_t launch_radial_mask(const Geom& g, int32_t h0, int32_t beta, uint8_t* 
 size_t pooled_workspace_bytes(const Geom& g);
 hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k, double scale,
                               int32_t mode, double param, uint8_t* mask, void* ws,
-                              hipStream_t st);
+                              hipStream_t st, const double* levels = nullptr,
+                              int32_t n_levels = 0);
 hipError_t launch_pooled_global(const Geom& g, int32_t mode, double param, uint8_t* mask,
                                 void* ws, hipStream_t st);
 
@@ -38,6 +39,16 @@ hipError_t launch_compact_scatter(const Geom& g, int64_t R, const uint8_t* mask,
                                   int64_t mask_head_stride, const uint8_t* skip,
                                   const int32_t* row_ptr, int32_t* kv_idx, hipStream_t st);
 hipError_t launch_zero_row_ptr(int32_t* row_ptr, hipStream_t st);
+// Pyramid lists: count + scan into row_ptr (count_only), or scatter.
+// rb[0..n_levels] = first augmented block of each level region, then the end.
+hipError_t launch_pyramid_lists(const Geom& g, int32_t n_levels, const int64_t* rb,
+                                const uint8_t* mask, int64_t mhs, int32_t* row_ptr,
+                                int32_t* kv_idx, int32_t* kv_quarters, bool count_only,
+                                hipStream_t st);
+// Pooled key/value levels 1..n_levels-1 (means of 2^l tokens) into k_pyr/v_pyr.
+hipError_t launch_kv_pyramid(const Geom& g, int elem_bytes, int32_t n_levels, const int64_t* rb,
+                             TensorArg k, TensorArg v, TensorArg kp, TensorArg vp,
+                             hipStream_t st);
 hipError_t launch_order_lists(const Geom& g, int64_t R, int32_t order, const int32_t* row_ptr,
                               const int32_t* kv_in, int32_t* kv_out, hipStream_t st);
 
@@ -63,6 +74,10 @@ struct AttnArgs {
   int32_t lists_shared;
   float scale;
   float* tile_gap;
+  // pyramid attention (kv_quarters non-NULL): pooled levels and region starts
+  TensorArg kp{}, vp{};
+  const int32_t* kv_quarters = nullptr;
+  int64_t pyr_rb[4] = {0, 0, 0, 0};
 };
 
 hipError_t launch_attn_bf16(const Geom& g, const AttnArgs& a, hipStream_t st);

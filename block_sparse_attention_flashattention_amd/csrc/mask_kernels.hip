@@ -157,6 +157,7 @@ constexpr int kPooledMaxBlocks = 2048;  // keeps the select kernel under 64 KiB 
 // cumulative softmax mass tau_p (sum Z in ascending block order, running sum
 // of p = e/Z in sorted order, both sequential).
 __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double param,
+                                     double tau1, double tau2, int32_t n_levels,
                                      const double* __restrict__ S, uint8_t* __restrict__ mask) {
   extern __shared__ double smd[];
   double* s = smd;                 // [nK] scores, block order
@@ -194,6 +195,28 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
   int32_t keep;
   if (mode == 0) {
     keep = (int32_t)min((double)nK, param);
+  } else if (mode == 4) {
+    // pyramid levels ([PSA]: a resolution level per block pair by importance
+    // thresholds): walk the order accumulating the row softmax mass; a block
+    // joins the current level, and the level advances past every threshold
+    // the running sum (including that block) has reached.
+    const double smax = s[idx[0]];
+    for (int c = threadIdx.x; c < nK; c += blockDim.x) e[c] = exp(s[c] - smax);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const double taus[3] = {param, tau1, tau2};
+      double Z = 0.0;
+      for (int64_t c = 0; c < nK; ++c) Z = Z + e[c];
+      double run = 0.0;
+      int lvl = 0;
+      for (int32_t t = 0; t < nK && lvl < n_levels; ++t) {
+        flag[idx[t]] = (uint8_t)(1 + lvl);
+        run = run + e[idx[t]] / Z;
+        while (lvl < n_levels && run >= taus[lvl]) ++lvl;
+      }
+    }
+    __syncthreads();
+    keep = 0;
   } else {
     const double smax = s[idx[0]];
     for (int c = threadIdx.x; c < nK; c += blockDim.x) e[c] = exp(s[c] - smax);
@@ -439,6 +462,77 @@ __global__ void gsel_mark_kernel(int64_t BH, int64_t nQ, int64_t nK, int32_t mod
   }
 }
 
+// ------------------------------------------------------- pyramid lists
+// Quarter mask (16-row quarters of a 64-row augmented block) that row r
+// selects in augmented block ab ([PSA]: logical block size decoupled from the
+// hardware tile): ab in level region l covers logical blocks
+// c = (ab - rb_l) * 2^l + i, i < 2^l, each owning 4 / 2^l quarters; block c
+// contributes its quarters when its mask value is 1 + l.
+struct PyrRegions {
+  int64_t rb[4];  // first augmented block of levels 0..2, then the end
+  int32_t n_levels;
+};
+
+__device__ inline uint32_t pyr_quarters(const uint8_t* mrow, int64_t nK, const PyrRegions& R,
+                                        int64_t ab) {
+  int l = 0;
+  while (l + 1 < R.n_levels && ab >= R.rb[l + 1]) ++l;
+  const int per = 1 << l;            // logical blocks per augmented block
+  const int qpb = 4 >> l;            // quarters per logical block
+  uint32_t q = 0;
+  for (int i = 0; i < per; ++i) {
+    const int64_t c = (ab - R.rb[l]) * per + i;
+    if (c < nK && mrow[c] == 1 + l) q |= ((1u << qpb) - 1) << (i * qpb);
+  }
+  return q;
+}
+
+// One wave per list row: row_ptr[r + 1] = augmented blocks with a quarter.
+__global__ void pyr_count_kernel(int64_t R, int64_t nQ, int64_t nK, PyrRegions reg,
+                                 const uint8_t* __restrict__ mask, int64_t mhs,
+                                 int32_t* __restrict__ row_ptr) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t r = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (blockIdx.x == 0 && threadIdx.x == 0) row_ptr[0] = 0;
+  if (r >= R) return;
+  const int64_t bh = r / nQ, a = r - bh * nQ;
+  const uint8_t* mrow = mask + bh * mhs + a * nK;
+  const int64_t nA = reg.rb[reg.n_levels];
+  int32_t cnt = 0;
+  for (int64_t a0 = 0; a0 < nA; a0 += kWave) {
+    const int64_t ab = a0 + lane;
+    const bool on = ab < nA && pyr_quarters(mrow, nK, reg, ab) != 0;
+    cnt += __popcll(__ballot(on));
+  }
+  if (lane == 0) row_ptr[r + 1] = cnt;
+}
+
+__global__ void pyr_scatter_kernel(int64_t R, int64_t nQ, int64_t nK, PyrRegions reg,
+                                   const uint8_t* __restrict__ mask, int64_t mhs,
+                                   const int32_t* __restrict__ row_ptr,
+                                   int32_t* __restrict__ kv_idx,
+                                   int32_t* __restrict__ kv_quarters) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t r = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (r >= R) return;
+  const int64_t bh = r / nQ, a = r - bh * nQ;
+  const uint8_t* mrow = mask + bh * mhs + a * nK;
+  const int64_t nA = reg.rb[reg.n_levels];
+  int64_t out = row_ptr[r];
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int64_t a0 = 0; a0 < nA; a0 += kWave) {
+    const int64_t ab = a0 + lane;
+    const uint32_t q = ab < nA ? pyr_quarters(mrow, nK, reg, ab) : 0u;
+    const uint64_t bal = __ballot(q != 0);
+    if (q) {
+      const int64_t o = out + __popcll(bal & below);
+      kv_idx[o] = (int32_t)ab;
+      kv_quarters[o] = (int32_t)q;
+    }
+    out += __popcll(bal);
+  }
+}
+
 // -------------------------------------------------------------- compaction
 __device__ inline bool tile_listed(const uint8_t* mask, int64_t mhs, const uint8_t* skip,
                                    int64_t r, int64_t nQ, int64_t nK, int64_t c) {
@@ -627,7 +721,7 @@ int pooled_max_blocks() { return kPooledMaxBlocks; }
 
 hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k, double scale,
                               int32_t mode, double param, uint8_t* mask, void* ws,
-                              hipStream_t st) {
+                              hipStream_t st, const double* levels, int32_t n_levels) {
   const int64_t BH = (int64_t)g.B * g.H;
   if (BH == 0 || g.N == 0) return hipSuccess;
   double* qbar = (double*)ws;
@@ -645,12 +739,13 @@ hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k
                      g.nQ, g.nK, scale, qbar, kbar, S);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (mode >= 2) return launch_pooled_global(g, mode, param, mask, ws, st);
+  if (mode == 2 || mode == 3) return launch_pooled_global(g, mode, param, mask, ws, st);
   int32_t P = 1;
   while (P < g.nK) P <<= 1;
   const size_t sh2 = sizeof(double) * 2 * g.nK + sizeof(int32_t) * P + g.nK + 16;
   hipLaunchKernelGGL(pooled_select_kernel, dim3((unsigned)(BH * g.nQ)), dim3(kSelectThreads),
-                     sh2, st, g.nK, P, mode, param, S, mask);
+                     sh2, st, g.nK, P, mode, param, levels ? levels[1] : 0.0,
+                     levels ? levels[2] : 0.0, n_levels, S, mask);
   return hipGetLastError();
 }
 
@@ -701,6 +796,28 @@ hipError_t launch_compact_scatter(const Geom& g, int64_t R, const uint8_t* mask,
   hipLaunchKernelGGL(compact_scatter_kernel, dim3(grid_for(R, waves, INT32_MAX)),
                      dim3(waves * kWave), 0, st, R, g.nQ, g.nK, mask, mhs, skip, row_ptr,
                      kv_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_pyramid_lists(const Geom& g, int32_t n_levels, const int64_t* rb,
+                                const uint8_t* mask, int64_t mhs, int32_t* row_ptr,
+                                int32_t* kv_idx, int32_t* kv_quarters, bool count_only,
+                                hipStream_t st) {
+  const int64_t R = (int64_t)g.B * g.H * g.nQ;
+  PyrRegions reg;
+  for (int i = 0; i < 4; ++i) reg.rb[i] = i <= n_levels ? rb[i] : rb[n_levels];
+  reg.n_levels = n_levels;
+  const int waves = 4;
+  if (count_only) {
+    hipLaunchKernelGGL(pyr_count_kernel, dim3(grid_for(R, waves, INT32_MAX)), dim3(waves * kWave),
+                       0, st, R, g.nQ, g.nK, reg, mask, mhs, row_ptr);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, R, row_ptr);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(pyr_scatter_kernel, dim3(grid_for(R, waves, INT32_MAX)), dim3(waves * kWave),
+                     0, st, R, g.nQ, g.nK, reg, mask, mhs, row_ptr, kv_idx, kv_quarters);
   return hipGetLastError();
 }
 

@@ -283,6 +283,83 @@ BSA_API bsa_status bsa_update_skip_mask(const bsa_shape* s, const int32_t* row_p
                                 const int32_t* kv_idx, const float* tile_gap, float tau,
                                 uint8_t* skip, void* stream);
 
+/*
+ * Pyramid attention ([PSA]: key/value blocks kept at several resolutions,
+ * each level the average pooling of the finer one; each (query block, key
+ * block) pair attends at the level its importance earns, set by thresholds;
+ * the probabilities stay consistent across levels; the logical block size is
+ * decoupled from the hardware tile).
+ * Levels l = 0 .. n_levels-1 (n_levels in 1..3; N must be a multiple of
+ * 2^(n_levels-1), else BSA_ERR_UNSUPPORTED): level l of key block c holds
+ * block_k / 2^l pooled keys, each the mean of 2^l consecutive tokens of K and
+ * of V; a pooled key stands for its 2^l tokens, so its score gets + l ln 2.
+ * Level masks are uint8: 0 = dropped, 1 + l = level l.
+ * Augmented key blocks: level l occupies blocks [rb_l, rb_{l+1}) with
+ * rb_0 = 0 and rb_{l+1} = rb_l + ceil((N >> l) / block_k); blocks below rb_1
+ * are the original K / V, the others rows of k_pyr / v_pyr (level 1 first).
+ */
+
+/* Rows of k_pyr / v_pyr for n_levels (0 for one level); -1 if invalid. */
+BSA_API int64_t bsa_pyramid_rows(const bsa_shape* s, int32_t n_levels);
+
+/*
+ * Pooled levels 1 .. n_levels-1 of K and V: row (rb_l - rb_1)*block_k + g of
+ * k_pyr is the mean of K rows [g*2^l, (g+1)*2^l), summed in fp32 in ascending
+ * order, divided by 2^l and rounded to dt (nearest even); likewise v_pyr from
+ * V. k_pyr, v_pyr: [B][bsa_pyramid_rows][H][d] by strides; padding rows at
+ * the end of each level are left unwritten.
+ */
+BSA_API bsa_status bsa_build_kv_pyramid(const bsa_shape* s, bsa_dtype dt, int32_t n_levels,
+                                bsa_tensor k, bsa_tensor v, bsa_tensor k_pyr,
+                                bsa_tensor v_pyr, void* stream);
+
+/*
+ * Level mask from the pooled block scores of bsa_build_mask_pooled (same
+ * workspace): row a walks its key blocks in (S desc, c asc) order summing the
+ * row softmax mass p_c of mode 1; a block joins the current level, then the
+ * level advances past every threshold the running sum (including that block)
+ * has reached; blocks after the last level are dropped. levels_tau (host,
+ * [n_levels]) non-decreasing in (0, 1]. The row's best block is at level 0.
+ *   mask  out, [B][H][nQ][nK], values 0 .. n_levels
+ */
+BSA_API bsa_status bsa_build_mask_pyramid(const bsa_shape* s, bsa_dtype dt, bsa_tensor q,
+                                  bsa_tensor k, double scale, int32_t n_levels,
+                                  const double* levels_tau, uint8_t* mask, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
+ * Lists of augmented tiles for a level mask: per row r = (b*H + h)*nQ + a (one
+ * list per (b, h) always), the augmented blocks holding at least one
+ * selected 16-row quarter, ascending, and kv_quarters[e] = bit mask of the
+ * selected quarters (bit i = rows [16i, 16i+16) of the tile). Key block c at
+ * level l covers pooled rows [c*block_k/2^l, (c+1)*block_k/2^l) of level l,
+ * i.e. 4/2^l quarters of augmented block rb_l + c/2^l.
+ *   mask_head_stride  0 (one mask for all heads) or >= nQ*nK
+ *   kv_capacity, nnz_host  as in bsa_compact_block_lists (worst case
+ *                  B*H*nQ*rb_{n_levels})
+ */
+BSA_API bsa_status bsa_compact_pyramid_lists(const bsa_shape* s, int32_t n_levels,
+                                     const uint8_t* mask, int64_t mask_head_stride,
+                                     int32_t* row_ptr, int32_t* kv_idx, int32_t* kv_quarters,
+                                     int64_t kv_capacity, int64_t* nnz_host, void* stream);
+
+/*
+ * Pyramid attention forward (bf16 inputs; fp32 accumulation and softmax, O
+ * rounded to bf16). For query i of row block a, the keys are the rows of the
+ * selected quarters of the row's augmented tiles (padding rows past a level's
+ * N >> l never count); a key of level l scores scale * q_i . k + l ln 2; o_i
+ * is the softmax-weighted mean of the matching value rows, lse_i the natural
+ * log of the weight sum (-inf and o_i = 0 for an empty list).
+ *   k_pyr, v_pyr  as written by bsa_build_kv_pyramid, with the row stride
+ *                 (stride_n) of k and v; ignored for one level
+ *   row_ptr, kv_idx, kv_quarters  as written by bsa_compact_pyramid_lists
+ */
+BSA_API bsa_status bsa_pyramid_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q,
+                                bsa_tensor k, bsa_tensor v, bsa_tensor k_pyr,
+                                bsa_tensor v_pyr, int32_t n_levels, bsa_tensor o, float* lse,
+                                const int32_t* row_ptr, const int32_t* kv_idx,
+                                const int32_t* kv_quarters, float scale, void* stream);
+
 /* Static text for a status code. */
 BSA_API const char* bsa_status_string(bsa_status st);
 
