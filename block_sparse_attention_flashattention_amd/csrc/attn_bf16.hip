@@ -118,6 +118,23 @@ __device__ inline int32_t load_uniform(const int32_t* base, int64_t i) {
   return ((const __attribute__((address_space(4))) int32_t*)base)[i];
 }
 
+// Maximum over lanes 0..31 (every lane receives it): DPP within each 16-lane
+// row (swap neighbours, swap pairs, mirror 8, mirror 16), then the two rows
+// through scalar registers. No LDS traffic, unlike a bpermute shuffle.
+template <int CTRL>
+__device__ inline float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float max_lanes32(float v) {
+  v = fmaxf(v, dpp_move<0xB1>(v));   // quad_perm(1, 0, 3, 2)
+  v = fmaxf(v, dpp_move<0x4E>(v));   // quad_perm(2, 3, 0, 1)
+  v = fmaxf(v, dpp_move<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_move<0x140>(v));  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  return fmaxf(r0, r1);
+}
+
 // Value of lane 0 (an SGPR) for quantities that are uniform across the wave.
 __device__ inline int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -468,9 +485,8 @@ void attn_bf16_kernel(const Bf16Params p) {
     if (GAP) {
       m_blk = part == 0 ? m_loc2 : fmaxf(m_blk, m_loc2);
       if (part == NSUB - 1) {
-        float g = qvalid ? m_blk - m_true : -INFINITY;
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) g = fmaxf(g, __shfl_xor(g, off, 32));
+        // lanes n and n + 32 hold the same row, so lanes 0..31 cover the wave
+        const float g = max_lanes32(qvalid ? m_blk - m_true : -INFINITY);
         if (lane == 0) atomic_max_float(p.tile_gap + gbase + e0 + u / NSUB, g);
         m_true = fmaxf(m_true, m_blk);
       }
