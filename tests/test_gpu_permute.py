@@ -118,3 +118,19 @@ def test_permuted_pooled_path_wan13b_480p_sampled():
                                            w.pooled_param)
     note(f"480p pooled at tau_p {w.pooled_param:.4f}: {100 * dense:.1f}% sparse over per-head "
          f"orders vs {100 * (1 - plain.mean()):.1f}% in (t, y, x) order")
+
+
+def test_permute_tokens_head_dim_64_and_strided_views():
+    """d = 64 rows (8 chunks of 16 bytes) and a non-contiguous head slice."""
+    w = synth.Workload("perm_d64", 1, 4, 64, 3, 5, 7, 64, 64, "bf16", "pooled", 631, True)
+    x = synth.make_qkv(w)
+    P = oracle.make_permutation(w.T, w.Hs, w.Ws, 0, (1, 2, 0))
+    pd = dev(P.astype(np.int32))
+    a = dev(x["k"])
+    sub = a[:, :, 1:3]                       # heads 1..2 of 4: strides of the full tensor
+    s = bsa.shape(w.B, 2, w.d, w.T, w.Hs, w.Ws, w.Bq, w.Bk)
+    out = torch.empty(sub.shape, dtype=a.dtype, device=DEV)
+    bsa.bsa_permute_tokens(s, pd, 0, 0, sub, out)
+    torch.cuda.synchronize()
+    want = oracle.permute_tokens(np.ascontiguousarray(x["k"][:, :, 1:3]), P)
+    np.testing.assert_array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), want)

@@ -128,3 +128,18 @@ def test_pyramid_wan13b_480p_sampled():
                                               w.nQ * w.nK, rows=rows)
     og, lg = gather_rows(host(out["o"]), host(out["lse"]), rows, w.B, w.H, w.N, w.Bq)
     compare(og, lg, o_ref, lse_ref, "480p pyramid")
+
+
+def test_pyramid_head_dim_64_against_oracle():
+    w = synth.Workload("pyr_d64", 1, 2, 64, 4, 9, 16, 64, 64, "bf16", "pooled", 643, True)
+    x = synth.make_qkv(w)
+    taus = [0.3, 0.6, 0.9]
+    out = run_pyramid(w, x, taus)
+    mref, _, _ = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, 4, 0,
+                                          levels_tau=taus)
+    np.testing.assert_array_equal(out["mask"], mref)
+    o_ref, lse_ref = oracle.pyramid_attention(x["q"], x["k"], x["v"], w.Bq, w.Bk, w.scale, mref,
+                                              w.nQ * w.nK)
+    rows = np.arange(w.B * w.H * w.nQ)
+    og, lg = gather_rows(host(out["o"]), host(out["lse"]), rows, w.B, w.H, w.N, w.Bq)
+    compare(og, lg, o_ref, lse_ref, "pyramid d=64")
