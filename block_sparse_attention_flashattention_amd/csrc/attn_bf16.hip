@@ -118,6 +118,12 @@ __device__ inline int32_t load_uniform(const int32_t* base, int64_t i) {
   return ((const __attribute__((address_space(4))) int32_t*)base)[i];
 }
 
+// Maximum that propagates NaN (IEEE maximum, v_maximum3_f32 when chained),
+// for row maxima of scores. fmaxf must first quiet every input not known to
+// be canonical, which for matrix-core results costs one more instruction per
+// score; scores are finite or -inf, where the two agree.
+__device__ inline float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Maximum over lanes 0..31 (every lane receives it): DPP within each 16-lane
 // row (swap neighbours, swap pairs, mirror 8, mirror 16), then the two rows
 // through scalar registers. No LDS traffic, unlike a bpermute shuffle.
@@ -474,8 +480,8 @@ void attn_bf16_kernel(const Bf16Params p) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mloc = fmaxf(mloc, sacc[kb][j]);
-    mloc = fmaxf(mloc, other_half(mloc));
+      for (int j = 0; j < 16; j += 2) mloc = vmax(vmax(mloc, sacc[kb][j]), sacc[kb][j + 1]);
+    mloc = vmax(mloc, other_half(mloc));
     return mloc * p.sl2;
   };
   // Tile gap (once the key block's last step is in) and exponent-base update
@@ -644,11 +650,11 @@ void attn_bf16_kernel(const Bf16Params p) {
 #pragma unroll
         for (int e2 = 0; e2 < C::MPS; e2 += 2) {
           const int e = i * C::MPS + e2, kb2 = e / 16, j = e % 16;
-          mloc = fmaxf(mloc, fmaxf(nxt[kb2][j], nxt[kb2][j + 1]));
+          mloc = vmax(vmax(mloc, nxt[kb2][j]), nxt[kb2][j + 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      mloc = fmaxf(mloc, other_half(mloc));
+      mloc = vmax(mloc, other_half(mloc));
       apply_max(mloc * p.sl2 + (float)level_of(c1), it + 1, part1);
     } else {
       probs(cur, pb, (float)level_of(c0));
