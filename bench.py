@@ -31,6 +31,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse_attn_fwd ms/call + computed-tile TFLOPS as % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+MI355X_SIMDS = 1024         # 256 compute units x 4 SIMDs
+MI355X_XCDS = 8
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_flashattention_amd", "csrc",
@@ -74,15 +76,17 @@ def source_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_for(workload: str):
+def counters_for(workload: str) -> dict:
+    """The counter record of profiles/traffic.json when it was taken on this kernel source and
+    workload, else {}."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     if t.get("source_sha256") != source_sha() or t.get("workload") != workload:
-        return None
-    return t.get("traffic_bytes_per_launch")
+        return {}
+    return t
 
 
 def _counter_mean(folder: str, kernel_substr: str, counter: str) -> tuple[float, int]:
@@ -101,9 +105,13 @@ def _counter_mean(folder: str, kernel_substr: str, counter: str) -> tuple[float,
     return float(np.mean(list(vals.values()))), len(vals)
 
 
-def ingest_counters(workload: str, fetch_dir: str, write_dir: str, copy_f: str, copy_w: str):
+def ingest_counters(workload: str, fetch_dir: str, write_dir: str, copy_f: str, copy_w: str,
+                    sq_dir: str = None, grbm_dir: str = None):
     """HBM bytes per forward launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
-    scaled by what the same counter reads for a device copy of 1 GiB each way."""
+    scaled by what the same counter reads for a device copy of 1 GiB each way. With the
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE folders it also records the fraction of
+    elapsed cycles in which the matrix cores are busy: busy cycles summed over the 1,024
+    SIMDs over (1,024 x elapsed cycles per XCD, GRBM_GUI_ACTIVE summed over the 8 XCDs / 8)."""
     fetch, nf = _counter_mean(fetch_dir, "attn_bf16_kernel", "FETCH_SIZE")
     write, nw = _counter_mean(write_dir, "attn_bf16_kernel", "WRITE_SIZE")
     cf, _ = _counter_mean(copy_f, "copyBuffer", "FETCH_SIZE")
@@ -117,6 +125,12 @@ def ingest_counters(workload: str, fetch_dir: str, write_dir: str, copy_f: str, 
            "copy_fetch_kib_per_gib": cf, "copy_write_kib_per_gib": cw,
            "fetch_scale": f_fetch, "write_scale": f_write,
            "traffic_bytes_per_launch": traffic}
+    if sq_dir and grbm_dir:
+        busy, _ = _counter_mean(sq_dir, "attn_bf16_kernel", "SQ_VALU_MFMA_BUSY_CYCLES")
+        gui, _ = _counter_mean(grbm_dir, "attn_bf16_kernel", "GRBM_GUI_ACTIVE")
+        out["mfma_busy_cycles"] = busy
+        out["grbm_gui_active"] = gui
+        out["mfma_busy_frac"] = busy / (MI355X_SIMDS * gui / MI355X_XCDS)
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
@@ -161,13 +175,15 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the all-tiles timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
-    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
-                                                          "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                    help="turn four rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE "
-                         "of this workload's bench run and of --calibrate-copy-mib 1024) into "
-                         "profiles/traffic.json; no GPU work")
+    ap.add_argument("--ingest-counters", nargs="+", metavar="DIR",
+                    help="turn rocprofv3 --pmc output folders into profiles/traffic.json, no GPU "
+                         "work: FETCH_SIZE and WRITE_SIZE of this workload's bench run, the same "
+                         "two of --calibrate-copy-mib 1024, and optionally a run with "
+                         "SQ_VALU_MFMA_BUSY_CYCLES and one with GRBM_GUI_ACTIVE (4 or 6 folders)")
     args = ap.parse_args()
     if args.ingest_counters:
+        if len(args.ingest_counters) not in (4, 6):
+            raise SystemExit("--ingest-counters takes 4 or 6 folders")
         ingest_counters(args.workload, *args.ingest_counters)
         return
 
@@ -408,6 +424,25 @@ def main():
         dense_speedup = dense_ms / fwd_ms
         log(f"all tiles: {dense_ms:.3f} ms/call, dense-equivalent speedup {dense_speedup:.2f}x")
 
+    # Forward after evicting the caches: write a 1 GiB buffer (beyond the 256 MB Infinity
+    # Cache and the L2s), then time one call; the lists and inputs stay as in the last step.
+    cold_ms = None
+    if w.mask != "skip" and taus_pyr is None and perm is None:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(3):
+            scratch.fill_(1)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            bsa.bsa_sparse_attn_fwd(s, q, k, v, o, lse, row_ptr, kv_idx, shared, w.scale)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del scratch
+        cold_ms = float(np.median(cold))
+        log(f"after a 1 GiB cache flush: {cold_ms:.3f} ms/call (median of 3)")
+
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the same rows
     cpu = None
     if args.cpu_rows > 0:
@@ -448,7 +483,8 @@ def main():
                          f"(first step's mask), {sample_flops / 1e9:.1f} GFLOP fp64 in {cpu_s:.1f} s"}
         log(f"CPU oracle: {cpu['value'] * 1e3:.3f} GFLOP/s")
 
-    traffic = traffic_for(w.name)
+    ctr = counters_for(w.name)
+    traffic = ctr.get("traffic_bytes_per_launch")
     out = {
         "metric": METRIC,
         "value": step_tflops,
@@ -458,6 +494,10 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms_step,
         "ms_per_call": fwd_ms,
+        "ms_per_call_stats": {"median": float(np.median(fwd_ms_each)),
+                              "min": float(np.min(fwd_ms_each)),
+                              "max": float(np.max(fwd_ms_each)),
+                              "after_cache_flush": cold_ms},
         "pct_of_bf16_peak": 100.0 * fwd_tflops / PEAK_BF16_TFLOPS,
         "dense_equiv_speedup": dense_speedup,
         "higher_is_better": True,
@@ -487,6 +527,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": fwd_tflops / PEAK_BF16_TFLOPS,
             "traffic": traffic,
+            "hbm_gbs": traffic / (fwd_ms * 1e-3) / 1e9 if traffic else None,
+            "mfma_busy_frac": ctr.get("mfma_busy_frac"),
         },
         "cpu_baseline": cpu,
     }
