@@ -119,26 +119,29 @@ __device__ inline int32_t load_uniform(const int32_t* base, int64_t i) {
 }
 
 // Maximum that propagates NaN (IEEE maximum, v_maximum3_f32 when chained),
-// for row maxima of scores. fmaxf must first quiet every input not known to
-// be canonical, which for matrix-core results costs one more instruction per
-// score; scores are finite or -inf, where the two agree.
+// for row maxima of scores and for tile gaps. fmaxf must first quiet every
+// input not known to be canonical (matrix-core results, DPP moves), which
+// costs one more instruction per input; the values here are finite or
+// +-inf, where the two agree.
 __device__ inline float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // Maximum over lanes 0..31 (every lane receives it): DPP within each 16-lane
 // row (swap neighbours, swap pairs, mirror 8, mirror 16), then the two rows
-// through scalar registers. No LDS traffic, unlike a bpermute shuffle.
+// through scalar registers. No LDS traffic, unlike a bpermute shuffle. A
+// NaN input (impossible for valid rows) would propagate, and a NaN gap never
+// marks a tile.
 template <int CTRL>
 __device__ inline float dpp_move(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 __device__ inline float max_lanes32(float v) {
-  v = fmaxf(v, dpp_move<0xB1>(v));   // quad_perm(1, 0, 3, 2)
-  v = fmaxf(v, dpp_move<0x4E>(v));   // quad_perm(2, 3, 0, 1)
-  v = fmaxf(v, dpp_move<0x141>(v));  // row_half_mirror
-  v = fmaxf(v, dpp_move<0x140>(v));  // row_mirror
+  v = vmax(v, dpp_move<0xB1>(v));   // quad_perm(1, 0, 3, 2)
+  v = vmax(v, dpp_move<0x4E>(v));   // quad_perm(2, 3, 0, 1)
+  v = vmax(v, dpp_move<0x141>(v));  // row_half_mirror
+  v = vmax(v, dpp_move<0x140>(v));  // row_mirror
   const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
   const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  return fmaxf(r0, r1);
+  return vmax(r0, r1);
 }
 
 // Value of lane 0 (an SGPR) for quantities that are uniform across the wave.
@@ -444,6 +447,14 @@ void attn_bf16_kernel(const Bf16Params p) {
   float m_use = -INFINITY;   // exponent base of p and l (log2 units)
   float m_true = -INFINITY;  // running row max (log2 units), for the tile gaps
   float m_blk = -INFINITY;   // row max of the current key block's steps so far
+  // Gaps of up to 64 consecutive list entries, lane j holding entry gbatch + j,
+  // folded into tile_gap with one 64-lane atomic per batch.
+  float gbuf = -INFINITY;
+  int gbatch = 0;
+  auto flush_gaps = [&](int count) {
+    if (lane < count) atomic_max_float(p.tile_gap + gbase + e0 + gbatch + lane, gbuf);
+    gbuf = -INFINITY;
+  };
   float l_lane = 0.f;        // this lane half's share of the row sum
 
   // ---- pipeline pieces
@@ -493,7 +504,12 @@ void attn_bf16_kernel(const Bf16Params p) {
       if (part == NSUB - 1) {
         // lanes n and n + 32 hold the same row, so lanes 0..31 cover the wave
         const float g = max_lanes32(qvalid ? m_blk - m_true : -INFINITY);
-        if (lane == 0) atomic_max_float(p.tile_gap + gbase + e0 + u / NSUB, g);
+        const int ie = u / NSUB;
+        if (lane == (ie & 63)) gbuf = g;
+        if ((ie & 63) == 63) {
+          flush_gaps(64);
+          gbatch += 64;
+        }
         m_true = fmaxf(m_true, m_blk);
       }
     }
@@ -681,6 +697,7 @@ void attn_bf16_kernel(const Bf16Params p) {
     step(it, sA, sB, false, P0{});
   }
 
+  if (GAP && L > gbatch) flush_gaps(L - gbatch);
   // ---- epilogue: O = O^T / l through LDS for coalesced 16-byte stores.
   const float l_tot = l_lane + other_half(l_lane);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
