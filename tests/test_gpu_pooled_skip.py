@@ -255,6 +255,17 @@ def test_skip_carry_small_bq128_ragged():
     _skip_carry(w, w.steps, w.tau)
 
 
+@pytest.mark.parametrize("Bq", [64, 128])
+def test_skip_carry_gap_batches_with_remainder(Bq):
+    """Lists of 71 entries (a ragged 20-key last block): the kernel folds the
+    gaps of 64 consecutive entries per atomic, so every row has one full batch
+    and a 7-entry remainder; all rows are checked."""
+    w = synth.Workload("skip_batches", 1, 1, 64, 5, 30, 30, Bq, 64, "bf16", "skip", 623, True,
+                       tau=1.0, steps=2)
+    assert w.nK == 71 and w.N % 64 == 20
+    _skip_carry(w, w.steps, w.tau)
+
+
 def test_skip_carry_480p_sampled():
     w = synth.workload("skip_carry_480p")
     rows = sample_rows(w.B, w.H, w.nQ, 2, 23, heads=[0, w.H - 1])
