@@ -71,174 +71,299 @@ __global__ void radial_mask_kernel(int64_t N, int64_t F, int32_t Bq, int32_t Bk,
 }
 
 // ------------------------------------------------------------------ pooled
-// Input element widened to fp64 (exact).
-__device__ inline double widen(const void* p, int dtype, int64_t off) {
+// Four consecutive input elements (channels x .. x+3, 16-byte aligned rows)
+// widened to fp64 (exact), from one 8- or 16-byte load.
+__device__ inline void widen4(const void* p, int dtype, int64_t off, double (&v)[4]) {
   if (dtype == 0) {
-    const uint32_t u = (uint32_t)((const uint16_t*)p)[off] << 16;
-    return (double)__uint_as_float(u);
+    const uint2 u = *(const uint2*)((const uint16_t*)p + off);
+    v[0] = (double)__uint_as_float(u.x << 16);
+    v[1] = (double)__uint_as_float(u.x & 0xffff0000u);
+    v[2] = (double)__uint_as_float(u.y << 16);
+    v[3] = (double)__uint_as_float(u.y & 0xffff0000u);
+  } else {
+    const float4 f = *(const float4*)((const float*)p + off);
+    v[0] = (double)f.x;
+    v[1] = (double)f.y;
+    v[2] = (double)f.z;
+    v[3] = (double)f.w;
   }
-  return (double)((const float*)p)[off];
 }
 
 // Block means of Q (row blocks) and K (column blocks): one thread per
-// (b*H + h, block, channel); tokens summed in ascending order, one division.
+// (b*H + h, block, four channels); each channel's tokens summed in ascending
+// order, one division. Four tokens' loads are in flight at a time.
 __global__ void pool_mean_kernel(int64_t N, int32_t H, int32_t D, int32_t Bq, int32_t Bk,
                                  int64_t nQ, int64_t nK, int64_t BH, int dtype, TensorArg q,
                                  TensorArg k, double* __restrict__ qbar,
                                  double* __restrict__ kbar) {
-  const int64_t per = (nQ + nK) * D;
+  const int32_t D4 = D / 4;
+  const int64_t per = (nQ + nK) * D4;
   const int64_t total = BH * per;
   for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
        t += (int64_t)gridDim.x * blockDim.x) {
     const int64_t bh = t / per;
     const int64_t rem = t - bh * per;
-    const int64_t blk = rem / D;
-    const int32_t x = (int32_t)(rem - blk * D);
+    const int64_t blk = rem / D4;
+    const int32_t x = 4 * (int32_t)(rem - blk * D4);
     const int64_t b = bh / H, h = bh - b * H;
     const bool isq = blk < nQ;
     const int64_t bi = isq ? blk : blk - nQ;
     const int32_t bs = isq ? Bq : Bk;
     const TensorArg& in = isq ? q : k;
     const int64_t i0 = bi * bs, i1 = min(N, i0 + bs);
-    double acc = 0.0;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
     const int64_t base = b * in.sb + h * in.sh + x;
-    for (int64_t i = i0; i < i1; ++i) acc = acc + widen(in.ptr, dtype, base + i * in.sn);
-    const double m = acc / (double)(i1 - i0);
-    if (isq)
-      qbar[(bh * nQ + bi) * D + x] = m;
-    else
-      kbar[(bh * nK + bi) * D + x] = m;
+    int64_t i = i0;
+    for (; i + 4 <= i1; i += 4) {
+      double v[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) widen4(in.ptr, dtype, base + (i + u) * in.sn, v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = acc[c] + v[u][c];
+    }
+    for (; i < i1; ++i) {
+      double v[4];
+      widen4(in.ptr, dtype, base + i * in.sn, v);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = acc[c] + v[c];
+    }
+    const double n = (double)(i1 - i0);
+    double* out = isq ? qbar + (bh * nQ + bi) * D : kbar + (bh * nK + bi) * D;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) out[x + c] = acc[c] / n;
   }
 }
 
 // Pooled scores S[bh][a][c] = scale * (sum over x ascending of qbar*kbar),
-// every product and sum rounded on its own (no fused multiply-add).
-constexpr int kScoreTile = 16;
-__global__ void pooled_scores_kernel(int32_t D, int64_t nQ, int64_t nK, double scale,
-                                     const double* __restrict__ qbar,
-                                     const double* __restrict__ kbar, double* __restrict__ S) {
+// every product and sum rounded on its own (no fused multiply-add). A 16 x 16
+// workgroup computes a 64 x 64 tile, 4 x 4 outputs per thread (rows ty + 16i,
+// columns tx + 16j), with the channels staged through LDS 16 at a time; every
+// output keeps its own sum in ascending channel order. Four outputs per
+// operand read keep LDS bandwidth off the critical path.
+constexpr int kScoreThreads = 16;                    // per side of the workgroup
+constexpr int kScoreSpan = 4;                        // outputs per thread per side
+constexpr int kScoreTile = kScoreThreads * kScoreSpan;  // outputs per tile side
+constexpr int kScoreX = 16;                          // channels per LDS stage
+__global__ __launch_bounds__(kScoreThreads * kScoreThreads) void pooled_scores_kernel(
+    int32_t D, int64_t nQ, int64_t nK, double scale, const double* __restrict__ qbar,
+    const double* __restrict__ kbar, double* __restrict__ S) {
 #pragma clang fp contract(off)
-  extern __shared__ double sm[];
-  const int ld = D + 1;
-  double* qs = sm;
-  double* ks = sm + kScoreTile * ld;
+  __shared__ double qs[kScoreTile][kScoreX + 1];
+  __shared__ double ks[kScoreTile][kScoreX + 1];
   const int64_t bh = blockIdx.z;
   const int64_t a0 = (int64_t)blockIdx.y * kScoreTile, c0 = (int64_t)blockIdx.x * kScoreTile;
-  const int tid = threadIdx.y * kScoreTile + threadIdx.x;
-  for (int e = tid; e < kScoreTile * D; e += kScoreTile * kScoreTile) {
-    const int r = e / D, x = e - r * D;
-    qs[r * ld + x] = (a0 + r < nQ) ? qbar[(bh * nQ + a0 + r) * D + x] : 0.0;
-    ks[r * ld + x] = (c0 + r < nK) ? kbar[(bh * nK + c0 + r) * D + x] : 0.0;
-  }
-  __syncthreads();
-  const int64_t a = a0 + threadIdx.y, c = c0 + threadIdx.x;
-  if (a < nQ && c < nK) {
-    double acc = 0.0;
-    for (int x = 0; x < D; ++x) {
-      const double pr = __dmul_rn(qs[threadIdx.y * ld + x], ks[threadIdx.x * ld + x]);
-      acc = __dadd_rn(acc, pr);
+  const int tx = threadIdx.x, ty = threadIdx.y, tid = ty * kScoreThreads + tx;
+  double acc[kScoreSpan][kScoreSpan];
+#pragma unroll
+  for (int i = 0; i < kScoreSpan; ++i)
+#pragma unroll
+    for (int j = 0; j < kScoreSpan; ++j) acc[i][j] = 0.0;
+  for (int x0 = 0; x0 < D; x0 += kScoreX) {
+    for (int e = tid; e < kScoreTile * kScoreX; e += kScoreThreads * kScoreThreads) {
+      const int r = e / kScoreX, xx = e - r * kScoreX, x = x0 + xx;
+      qs[r][xx] = (a0 + r < nQ && x < D) ? qbar[(bh * nQ + a0 + r) * D + x] : 0.0;
+      ks[r][xx] = (c0 + r < nK && x < D) ? kbar[(bh * nK + c0 + r) * D + x] : 0.0;
     }
-    S[(bh * nQ + a) * nK + c] = __dmul_rn(scale, acc);
+    __syncthreads();
+    const int xn = min(kScoreX, D - x0);
+    for (int xx = 0; xx < xn; ++xx) {
+      double qv[kScoreSpan], kv[kScoreSpan];
+#pragma unroll
+      for (int i = 0; i < kScoreSpan; ++i) qv[i] = qs[ty + kScoreThreads * i][xx];
+#pragma unroll
+      for (int j = 0; j < kScoreSpan; ++j) kv[j] = ks[tx + kScoreThreads * j][xx];
+#pragma unroll
+      for (int i = 0; i < kScoreSpan; ++i)
+#pragma unroll
+        for (int j = 0; j < kScoreSpan; ++j)
+          acc[i][j] = __dadd_rn(acc[i][j], __dmul_rn(qv[i], kv[j]));
+    }
+    __syncthreads();
   }
+#pragma unroll
+  for (int i = 0; i < kScoreSpan; ++i)
+#pragma unroll
+    for (int j = 0; j < kScoreSpan; ++j) {
+      const int64_t a = a0 + ty + kScoreThreads * i, c = c0 + tx + kScoreThreads * j;
+      if (a < nQ && c < nK) S[(bh * nQ + a) * nK + c] = __dmul_rn(scale, acc[i][j]);
+    }
 }
 
-// Order a before b: higher score first, lower block index on ties.
-__device__ inline bool ranks_before(const double* s, int a, int b) {
-  if (b < 0) return a >= 0;
-  if (a < 0) return false;
-  return s[a] > s[b] || (s[a] == s[b] && a < b);
+// acc + a[0] + a[1] + ... + a[n-1], added one at a time in that order (the
+// rounding of a loop on one thread). Every lane of the calling wave reads the
+// same LDS words (a broadcast), 16 ahead of the additions that use them.
+__device__ inline double ordered_sum(const double* a, int64_t n, double acc) {
+  int64_t c = 0;
+  for (; c + 16 <= n; c += 16) {
+    double v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = a[c + u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc = acc + v[u];
+  }
+  for (; c < n; ++c) acc = acc + a[c];
+  return acc;
+}
+
+// A score and its block index; index -1 pads the sort to a power of two.
+struct SortKey {
+  double s;
+  int32_t i;
+  int32_t pad;
+};
+
+// Order a before b: higher score first, lower block index on ties, padding last.
+__device__ inline bool key_before(const SortKey& a, const SortKey& b) {
+  if (b.i < 0) return a.i >= 0;
+  if (a.i < 0) return false;
+  return a.s > b.s || (a.s == b.s && a.i < b.i);
 }
 
 constexpr int kSelectThreads = 256;
 constexpr int kPooledMaxBlocks = 2048;  // keeps the select kernel under 64 KiB of LDS
 
-// One workgroup per (b, h, a): bitonic sort of the row's block indices by
-// (score desc, index asc), then top-k or the shortest prefix reaching the
-// cumulative softmax mass tau_p (sum Z in ascending block order, running sum
-// of p = e/Z in sorted order, both sequential).
+// Bitonic sort of kv[0 .. P) by key_before, P a power of two. The used waves
+// each own a contiguous segment of P / nwu keys; a stage whose pairs stay in
+// the segment runs without a workgroup barrier (a wave's LDS accesses are
+// ordered), only the stages with partner distance >= P / nwu synchronise the
+// workgroup.
+__device__ inline void sort_keys(SortKey* kv, int P) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int pairs = P / 2;
+  const int nwu = min(nw, max(1, pairs / 64));  // waves with pairs to order
+  const int pw = pairs / nwu;                    // pairs per used wave
+  const int seg = P / nwu;                       // keys per used wave
+  for (int kk = 2; kk <= P; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      const bool cross = j >= seg;
+      if (cross) __syncthreads();
+      if (w < nwu) {
+        const int lj = __builtin_ctz(j);
+        for (int p = w * pw + lane; p < (w + 1) * pw; p += 64) {
+          const int i = ((p >> lj) << (lj + 1)) | (p & (j - 1));
+          const int l = i | j;
+          const SortKey x = kv[i], y = kv[l];
+          const bool up = (i & kk) == 0;
+          if (up ? key_before(y, x) : key_before(x, y)) {
+            kv[i] = y;
+            kv[l] = x;
+          }
+        }
+      }
+      if (cross)
+        __syncthreads();
+      else
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    }
+  }
+  __syncthreads();
+}
+
+// One workgroup per (b, h, a): sort of the row's blocks by (score desc, index
+// asc), then top-k, the shortest prefix reaching the cumulative softmax mass
+// tau_p, or the pyramid levels. Z = sum of exp(S - max) in ascending block
+// order and the running sum of p = e / Z in sorted order are sequential, as
+// one thread would add them (the first wave reads 64 terms per LDS access);
+// the quotients are formed in parallel beforehand.
 __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double param,
                                      double tau1, double tau2, int32_t n_levels,
                                      const double* __restrict__ S, uint8_t* __restrict__ mask) {
   extern __shared__ double smd[];
-  double* s = smd;                 // [nK] scores, block order
-  double* e = smd + nK;            // [nK] exp(S - max), block order
-  int32_t* idx = (int32_t*)(smd + 2 * nK);  // [P]
-  uint8_t* flag = (uint8_t*)(idx + P);      // [nK]
+  double* s = smd;                                         // [nK] scores, block order
+  SortKey* kv = (SortKey*)(smd + ((nK + 1) & ~(int64_t)1));  // [P], 16-byte aligned
+  uint8_t* flag = (uint8_t*)(kv + P);                      // [nK]
   __shared__ int32_t keep_sh;
+  __shared__ double z_sh;
   const int64_t row = blockIdx.x;
   const double* srow = S + row * nK;
   for (int c = threadIdx.x; c < P; c += blockDim.x) {
+    SortKey e{0.0, -1, 0};
     if (c < nK) {
-      s[c] = srow[c];
+      const double v = srow[c];
+      s[c] = v;
       flag[c] = 0;
+      e.s = v;
+      e.i = c;
     }
-    idx[c] = c < nK ? c : -1;
+    kv[c] = e;
   }
   __syncthreads();
-  for (int kk = 2; kk <= P; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < P; i += blockDim.x) {
-        const int l = i ^ j;
-        if (l > i) {
-          const int x = idx[i], y = idx[l];
-          const bool up = (i & kk) == 0;
-          const bool swap = up ? ranks_before(s, y, x) : ranks_before(s, x, y);
-          if (swap) {
-            idx[i] = y;
-            idx[l] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
+  sort_keys(kv, P);
+  const double smax = kv[0].s;
   int32_t keep;
   if (mode == 0) {
     keep = (int32_t)min((double)nK, param);
-  } else if (mode == 4) {
-    // pyramid levels ([PSA]: a resolution level per block pair by importance
-    // thresholds): walk the order accumulating the row softmax mass; a block
-    // joins the current level, and the level advances past every threshold
-    // the running sum (including that block) has reached.
-    const double smax = s[idx[0]];
-    for (int c = threadIdx.x; c < nK; c += blockDim.x) e[c] = exp(s[c] - smax);
+  } else {
+    // e = exp(S - max) in block order, over the scores
+    for (int c = threadIdx.x; c < nK; c += blockDim.x) s[c] = exp(s[c] - smax);
     __syncthreads();
-    if (threadIdx.x == 0) {
-      const double taus[3] = {param, tau1, tau2};
-      double Z = 0.0;
-      for (int64_t c = 0; c < nK; ++c) Z = Z + e[c];
-      double run = 0.0;
-      int lvl = 0;
-      for (int32_t t = 0; t < nK && lvl < n_levels; ++t) {
-        flag[idx[t]] = (uint8_t)(1 + lvl);
-        run = run + e[idx[t]] / Z;
-        while (lvl < n_levels && run >= taus[lvl]) ++lvl;
-      }
+    if (threadIdx.x < 64) {
+      const double Z = ordered_sum(s, nK, 0.0);
+      if (threadIdx.x == 0) z_sh = Z;
     }
+    __syncthreads();
+    const double Z = z_sh;
+    // p_t = e[idx_t] / Z in sorted order, each quotient on its own; the
+    // sorted scores are not needed any more
+    for (int t = threadIdx.x; t < nK; t += blockDim.x) kv[t].s = s[kv[t].i] / Z;
     __syncthreads();
     keep = 0;
-  } else {
-    const double smax = s[idx[0]];
-    for (int c = threadIdx.x; c < nK; c += blockDim.x) e[c] = exp(s[c] - smax);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      double Z = 0.0;
-      for (int64_t c = 0; c < nK; ++c) Z = Z + e[c];
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
       double run = 0.0;
-      int32_t kp = (int32_t)nK;
-      for (int32_t t = 0; t < nK; ++t) {
-        run = run + e[idx[t]] / Z;
-        if (run >= param) {
-          kp = t + 1;
-          break;
+      if (mode == 4) {
+        // pyramid levels ([PSA]: a resolution level per block pair by
+        // importance thresholds): walk the order accumulating the row
+        // softmax mass; a block joins the current level, and the level
+        // advances past every threshold the running sum (including that
+        // block) has reached.
+        auto tau_at = [&](int l) { return l == 0 ? param : (l == 1 ? tau1 : tau2); };
+        int lvl = 0;
+        for (int64_t c0 = 0; c0 < nK && lvl < n_levels; c0 += 16) {
+          const int m = (int)min((int64_t)16, nK - c0);
+          double v[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) v[u] = kv[c0 + min(u, m - 1)].s;  // u >= m unused
+          int my_lvl = -1;  // lane u < 16 records the level of entry c0 + u
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            if (u < m && lvl < n_levels) {
+              if (lane == u) my_lvl = lvl;
+              run = run + v[u];
+              while (lvl < n_levels && run >= tau_at(lvl)) ++lvl;
+            }
+          }
+          if (my_lvl >= 0) flag[kv[c0 + lane].i] = (uint8_t)(1 + my_lvl);
         }
+      } else {
+        int32_t kp = (int32_t)nK;
+        bool done = false;
+        for (int64_t c0 = 0; c0 < nK && !done; c0 += 16) {
+          const int m = (int)min((int64_t)16, nK - c0);
+          double v[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) v[u] = kv[c0 + min(u, m - 1)].s;  // u >= m unused
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            if (!done && u < m) {
+              run = run + v[u];
+              if (run >= param) {
+                kp = (int32_t)(c0 + u + 1);
+                done = true;
+              }
+            }
+          }
+        }
+        if (lane == 0) keep_sh = kp;
       }
-      keep_sh = kp;
     }
     __syncthreads();
-    keep = keep_sh;
+    if (mode != 4) keep = keep_sh;
   }
-  for (int t = threadIdx.x; t < keep; t += blockDim.x) flag[idx[t]] = 1;
+  for (int t = threadIdx.x; t < keep; t += blockDim.x) flag[kv[t].i] = 1;
   __syncthreads();
   uint8_t* mrow = mask + row * nK;
   for (int c = threadIdx.x; c < nK; c += blockDim.x) mrow[c] = flag[c];
@@ -727,22 +852,21 @@ hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k
   double* qbar = (double*)ws;
   double* kbar = qbar + BH * g.nQ * g.D;
   double* S = kbar + BH * g.nK * g.D;
-  const int64_t work = BH * (g.nQ + g.nK) * g.D;
+  const int64_t work = BH * (g.nQ + g.nK) * (g.D / 4);
   hipLaunchKernelGGL(pool_mean_kernel, dim3(grid_for(work, 256)), dim3(256), 0, st, g.N, g.H,
                      g.D, g.Bq, g.Bk, g.nQ, g.nK, BH, dtype, q, k, qbar, kbar);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   dim3 grid((unsigned)((g.nK + kScoreTile - 1) / kScoreTile),
             (unsigned)((g.nQ + kScoreTile - 1) / kScoreTile), (unsigned)BH);
-  const size_t sh = sizeof(double) * 2 * kScoreTile * (g.D + 1);
-  hipLaunchKernelGGL(pooled_scores_kernel, grid, dim3(kScoreTile, kScoreTile), sh, st, g.D,
-                     g.nQ, g.nK, scale, qbar, kbar, S);
+  hipLaunchKernelGGL(pooled_scores_kernel, grid, dim3(kScoreThreads, kScoreThreads), 0, st,
+                     g.D, g.nQ, g.nK, scale, qbar, kbar, S);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mode == 2 || mode == 3) return launch_pooled_global(g, mode, param, mask, ws, st);
   int32_t P = 1;
   while (P < g.nK) P <<= 1;
-  const size_t sh2 = sizeof(double) * 2 * g.nK + sizeof(int32_t) * P + g.nK + 16;
+  const size_t sh2 = sizeof(double) * ((g.nK + 1) & ~(int64_t)1) + sizeof(SortKey) * P + g.nK;
   hipLaunchKernelGGL(pooled_select_kernel, dim3((unsigned)(BH * g.nQ)), dim3(kSelectThreads),
                      sh2, st, g.nK, P, mode, param, levels ? levels[1] : 0.0,
                      levels ? levels[2] : 0.0, n_levels, S, mask);
