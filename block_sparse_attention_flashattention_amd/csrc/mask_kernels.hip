@@ -207,29 +207,25 @@ __device__ inline double ordered_sum(const double* a, int64_t n, double acc) {
   return acc;
 }
 
-// A score and its block index; index -1 pads the sort to a power of two.
-struct SortKey {
-  double s;
-  int32_t i;
-  int32_t pad;
-};
-
-// Order a before b: higher score first, lower block index on ties, padding last.
-__device__ inline bool key_before(const SortKey& a, const SortKey& b) {
-  if (b.i < 0) return a.i >= 0;
-  if (a.i < 0) return false;
-  return a.s > b.s || (a.s == b.s && a.i < b.i);
+// Order (sa, ia) before (sb, ib): higher score first, lower block index on
+// ties; index -1 pads the sort to a power of two and goes last.
+__device__ inline bool key_before(double sa, int ia, double sb, int ib) {
+  if (ib < 0) return ia >= 0;
+  if (ia < 0) return false;
+  return sa > sb || (sa == sb && ia < ib);
 }
 
 constexpr int kSelectThreads = 256;
 constexpr int kPooledMaxBlocks = 2048;  // keeps the select kernel under 64 KiB of LDS
 
-// Bitonic sort of kv[0 .. P) by key_before, P a power of two. The used waves
+// Bitonic sort of the keys (ks[t], ki[t]), t < P, by key_before, P a power
+// of two; scores and indices in separate arrays (12 bytes of LDS traffic per
+// key access instead of a padded 16-byte record). The used waves
 // each own a contiguous segment of P / nwu keys; a stage whose pairs stay in
 // the segment runs without a workgroup barrier (a wave's LDS accesses are
 // ordered), only the stages with partner distance >= P / nwu synchronise the
 // workgroup.
-__device__ inline void sort_keys(SortKey* kv, int P) {
+__device__ inline void sort_keys(double* ks, int32_t* ki, int P) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
   const int pairs = P / 2;
@@ -245,11 +241,14 @@ __device__ inline void sort_keys(SortKey* kv, int P) {
         for (int p = w * pw + lane; p < (w + 1) * pw; p += 64) {
           const int i = ((p >> lj) << (lj + 1)) | (p & (j - 1));
           const int l = i | j;
-          const SortKey x = kv[i], y = kv[l];
+          const double xs = ks[i], ys = ks[l];
+          const int xi = ki[i], yi = ki[l];
           const bool up = (i & kk) == 0;
-          if (up ? key_before(y, x) : key_before(x, y)) {
-            kv[i] = y;
-            kv[l] = x;
+          if (up ? key_before(ys, yi, xs, xi) : key_before(xs, xi, ys, yi)) {
+            ks[i] = ys;
+            ki[i] = yi;
+            ks[l] = xs;
+            ki[l] = xi;
           }
         }
       }
@@ -272,27 +271,27 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
                                      double tau1, double tau2, int32_t n_levels,
                                      const double* __restrict__ S, uint8_t* __restrict__ mask) {
   extern __shared__ double smd[];
-  double* s = smd;                                         // [nK] scores, block order
-  SortKey* kv = (SortKey*)(smd + ((nK + 1) & ~(int64_t)1));  // [P], 16-byte aligned
-  uint8_t* flag = (uint8_t*)(kv + P);                      // [nK]
+  double* s = smd;                    // [nK] scores, block order
+  double* ks = smd + nK;              // [P] sort keys: scores, then p in sorted order
+  int32_t* ki = (int32_t*)(ks + P);   // [P] their block indices (-1: padding)
+  uint8_t* flag = (uint8_t*)(ki + P);  // [nK]
   __shared__ int32_t keep_sh;
   __shared__ double z_sh;
   const int64_t row = blockIdx.x;
   const double* srow = S + row * nK;
   for (int c = threadIdx.x; c < P; c += blockDim.x) {
-    SortKey e{0.0, -1, 0};
+    double v = 0.0;
     if (c < nK) {
-      const double v = srow[c];
+      v = srow[c];
       s[c] = v;
       flag[c] = 0;
-      e.s = v;
-      e.i = c;
     }
-    kv[c] = e;
+    ks[c] = v;
+    ki[c] = c < nK ? c : -1;
   }
   __syncthreads();
-  sort_keys(kv, P);
-  const double smax = kv[0].s;
+  sort_keys(ks, ki, P);
+  const double smax = ks[0];
   int32_t keep;
   if (mode == 0) {
     keep = (int32_t)min((double)nK, param);
@@ -308,7 +307,7 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
     const double Z = z_sh;
     // p_t = e[idx_t] / Z in sorted order, each quotient on its own; the
     // sorted scores are not needed any more
-    for (int t = threadIdx.x; t < nK; t += blockDim.x) kv[t].s = s[kv[t].i] / Z;
+    for (int t = threadIdx.x; t < nK; t += blockDim.x) ks[t] = s[ki[t]] / Z;
     __syncthreads();
     keep = 0;
     if (threadIdx.x < 64) {
@@ -326,7 +325,7 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
           const int m = (int)min((int64_t)16, nK - c0);
           double v[16];
 #pragma unroll
-          for (int u = 0; u < 16; ++u) v[u] = kv[c0 + min(u, m - 1)].s;  // u >= m unused
+          for (int u = 0; u < 16; ++u) v[u] = ks[c0 + min(u, m - 1)];  // u >= m unused
           int my_lvl = -1;  // lane u < 16 records the level of entry c0 + u
 #pragma unroll
           for (int u = 0; u < 16; ++u) {
@@ -336,7 +335,7 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
               while (lvl < n_levels && run >= tau_at(lvl)) ++lvl;
             }
           }
-          if (my_lvl >= 0) flag[kv[c0 + lane].i] = (uint8_t)(1 + my_lvl);
+          if (my_lvl >= 0) flag[ki[c0 + lane]] = (uint8_t)(1 + my_lvl);
         }
       } else {
         int32_t kp = (int32_t)nK;
@@ -345,7 +344,7 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
           const int m = (int)min((int64_t)16, nK - c0);
           double v[16];
 #pragma unroll
-          for (int u = 0; u < 16; ++u) v[u] = kv[c0 + min(u, m - 1)].s;  // u >= m unused
+          for (int u = 0; u < 16; ++u) v[u] = ks[c0 + min(u, m - 1)];  // u >= m unused
 #pragma unroll
           for (int u = 0; u < 16; ++u) {
             if (!done && u < m) {
@@ -363,7 +362,7 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
     __syncthreads();
     if (mode != 4) keep = keep_sh;
   }
-  for (int t = threadIdx.x; t < keep; t += blockDim.x) flag[kv[t].i] = 1;
+  for (int t = threadIdx.x; t < keep; t += blockDim.x) flag[ki[t]] = 1;
   __syncthreads();
   uint8_t* mrow = mask + row * nK;
   for (int c = threadIdx.x; c < nK; c += blockDim.x) mrow[c] = flag[c];
@@ -866,7 +865,7 @@ hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k
   if (mode == 2 || mode == 3) return launch_pooled_global(g, mode, param, mask, ws, st);
   int32_t P = 1;
   while (P < g.nK) P <<= 1;
-  const size_t sh2 = sizeof(double) * ((g.nK + 1) & ~(int64_t)1) + sizeof(SortKey) * P + g.nK;
+  const size_t sh2 = sizeof(double) * (g.nK + P) + sizeof(int32_t) * P + g.nK;
   hipLaunchKernelGGL(pooled_select_kernel, dim3((unsigned)(BH * g.nQ)), dim3(kSelectThreads),
                      sh2, st, g.nK, P, mode, param, levels ? levels[1] : 0.0,
                      levels ? levels[2] : 0.0, n_levels, S, mask);
