@@ -440,7 +440,7 @@ struct HeadCut {
   int64_t ties;     // pairs whose key equals the final prefix
   int64_t last;     // tied pairs with index <= last are kept
   int32_t all;      // every pair is kept
-  int32_t pad;
+  int32_t done;     // groups of the current histogram pass that have finished
 };
 
 constexpr int kGselThreads = 256;
@@ -458,18 +458,22 @@ __global__ void gsel_init_kernel(int64_t BH, int64_t nQ, int64_t nK, int32_t mod
   c.ties = 0;
   c.last = n;
   c.all = (mode == 2 ? param >= (double)n : param >= 1.0) ? 1 : 0;
-  c.pad = 0;
+  c.done = 0;
   cut[bh] = c;
 }
 
 // One histogram pass: per (head, group of pairs) the count and mass of the
 // pairs matching the prefix, by the 4-bit digit at `shift`. Each thread
 // walks its pairs in a fixed order into its own LDS slots; slots are then
-// summed in a fixed tree, so the masses are deterministic.
+// summed in a fixed tree, so the masses are deterministic. The last group of
+// a head to finish then adds the groups' histograms in group order and fixes
+// the next digit: the highest bucket in which the remaining count (mode 2)
+// or mass (mode 3) is reached. When the mass is never reached the walk ends
+// in the lowest bucket with the rest counted above it, which keeps every
+// pair.
 __global__ __launch_bounds__(kGselThreads) void gsel_hist_kernel(
     int64_t nQ, int64_t nK, int32_t mode, int32_t shift, const double* __restrict__ S,
-    const double* __restrict__ P, const HeadCut* __restrict__ cut, int64_t* __restrict__ pc,
-    double* __restrict__ pm) {
+    const double* __restrict__ P, HeadCut* cut, int64_t* pc, double* pm) {
   __shared__ double hm[16][kGselThreads];
   __shared__ int32_t hc[16][kGselThreads];
   const int tid = threadIdx.x;
@@ -501,42 +505,48 @@ __global__ __launch_bounds__(kGselThreads) void gsel_hist_kernel(
       }
     __syncthreads();
   }
-  if (tid < 16) {
-    pc[(bh * kGselGroups + g) * 16 + tid] = hc[tid][0];
-    pm[(bh * kGselGroups + g) * 16 + tid] = hm[tid][0];
+  __shared__ int is_last;
+  if (tid < 64) {  // the first wave publishes this group's histogram, then counts it in
+    if (tid < 16) {
+      pc[(bh * kGselGroups + g) * 16 + tid] = hc[tid][0];
+      pm[(bh * kGselGroups + g) * 16 + tid] = hm[tid][0];
+    }
+    __threadfence();
+    if (tid == 0) is_last = atomicAdd(&cut[bh].done, 1) == kGselGroups - 1;
   }
-}
-
-// One thread per head: add the groups' histograms in group order and fix the
-// next digit: the highest bucket in which the remaining count (mode 2) or
-// mass (mode 3) is reached. When the mass is never reached the walk ends in
-// the lowest bucket with the rest counted above it, which keeps every pair.
-__global__ void gsel_choose_kernel(int64_t BH, int32_t mode, int32_t shift,
-                                   const int64_t* __restrict__ pc, const double* __restrict__ pm,
-                                   HeadCut* __restrict__ cut) {
-  const int64_t bh = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (bh >= BH) return;
-  HeadCut c = cut[bh];
-  if (c.all) return;
-  int chosen = 0;
-  for (int b = 15; b >= 0; --b) {
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();  // the other groups' histograms are visible from here
+  __shared__ int64_t bc[16];
+  __shared__ double bm[16];
+  if (tid < 16) {
     int64_t cb = 0;
     double mb = 0.0;
-    for (int g = 0; g < kGselGroups; ++g) {
-      cb += pc[(bh * kGselGroups + g) * 16 + b];
-      mb = mb + pm[(bh * kGselGroups + g) * 16 + b];
+    for (int gg = 0; gg < kGselGroups; ++gg) {
+      cb += pc[(bh * kGselGroups + gg) * 16 + tid];
+      mb = mb + pm[(bh * kGselGroups + gg) * 16 + tid];
     }
-    const bool here = mode == 2 ? cb >= c.need_c : (cb > 0 && mb >= c.need_m);
-    if (here || b == 0) {
-      chosen = b;
-      c.ties = cb;
-      break;
-    }
-    c.need_c -= cb;
-    c.need_m = c.need_m - mb;
+    bc[tid] = cb;
+    bm[tid] = mb;
   }
-  c.prefix |= (uint64_t)chosen << shift;
-  cut[bh] = c;
+  __syncthreads();
+  if (tid == 0) {
+    HeadCut h = c;
+    int chosen = 0;
+    for (int b = 15; b >= 0; --b) {
+      const bool here = mode == 2 ? bc[b] >= h.need_c : (bc[b] > 0 && bm[b] >= h.need_m);
+      if (here || b == 0) {
+        chosen = b;
+        h.ties = bc[b];
+        break;
+      }
+      h.need_c -= bc[b];
+      h.need_m = h.need_m - bm[b];
+    }
+    h.prefix |= (uint64_t)chosen << shift;
+    h.done = 0;  // the next pass counts its groups again
+    cut[bh] = h;
+  }
 }
 
 // One thread per head: among several pairs with the cut key, the ones taken
@@ -890,8 +900,6 @@ hipError_t launch_pooled_global(const Geom& g, int32_t mode, double param, uint8
   for (int shift = 60; shift >= 0; shift -= 4) {
     hipLaunchKernelGGL(gsel_hist_kernel, dim3(kGselGroups, (unsigned)BH), dim3(kGselThreads), 0,
                        st, g.nQ, g.nK, mode, shift, S, P, cut, pc, pm);
-    hipLaunchKernelGGL(gsel_choose_kernel, dim3(grid_for(BH, 64)), dim3(64), 0, st, BH, mode,
-                       shift, pc, pm, cut);
   }
   hipLaunchKernelGGL(gsel_ties_kernel, dim3(grid_for(BH, 64)), dim3(64), 0, st, BH, n, mode, S, P,
                      cut);
