@@ -75,6 +75,9 @@ constexpr int kVStages = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
+// Pyramid lists at half-block steps: capacity of the per-workgroup list of
+// non-empty steps (with its count it keeps four 40 KiB workgroups per CU).
+constexpr int kStepCap = 2046;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
 constexpr int kPfK = 3;  // K fragment reads issued ahead of their score MFMA (slots)
 constexpr int kPfV = 3;  // V fragment reads issued ahead of their P V MFMA (slots)
@@ -276,7 +279,12 @@ void attn_bf16_kernel(const Bf16Params p) {
   using C = Cfg<D, BQ, SUB>;
   using T = typename C::T;
   constexpr int KB = C::KB, NSUB = C::NSUB;
+  // pyramid lists stepped in half blocks: steps whose two quarters are both
+  // unselected are left out (they would only compute masked keys)
+  constexpr bool SL = PYR && NSUB == 2;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+  __shared__ int32_t steplist[SL ? kStepCap : 1];  // (list entry << 1) | half
+  __shared__ int32_t steps_sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -323,17 +331,43 @@ void attn_bf16_kernel(const Bf16Params p) {
     if (GAP && p.lists_shared) gbase = bh * (int64_t)load_uniform(p.row_ptr, p.nQ);
   }
   const int L = e1 - e0;      // listed key blocks
-  const int LS = L * NSUB;    // pipeline steps (SUB keys each)
+  int LS = L * NSUB;          // pipeline steps (SUB keys each)
+  bool use_sl = false;
+  if constexpr (SL) {
+    if (2 * L <= kStepCap) {  // else every half is stepped through
+      use_sl = true;
+      if (w == 0) {
+        int base = 0;
+        for (int j0 = 0; j0 < L; j0 += 64) {
+          const int j = j0 + lane;
+          const int q = j < L ? p.kv_quarters[e0 + j] : 0;
+          const uint64_t m0 = __builtin_amdgcn_ballot_w64((q & 3) != 0);
+          const uint64_t m1 = __builtin_amdgcn_ballot_w64((q & 12) != 0);
+          const uint64_t below = (1ull << lane) - 1;
+          const int pos = base + __popcll(m0 & below) + __popcll(m1 & below);
+          if (q & 3) steplist[pos] = 2 * j;
+          if (q & 12) steplist[pos + ((q & 3) ? 1 : 0)] = 2 * j + 1;
+          base += __popcll(m0) + __popcll(m1);
+        }
+        if (lane == 0) steps_sh = base;
+      }
+      __syncthreads();
+      LS = steps_sh;
+    }
+  }
   const int N32 = (int)p.N;
   const uint16_t* kbase = p.k + b * p.ksb + h * p.ksh;
   const uint16_t* vbase = p.v + b * p.vsb + h * p.vsh;
   const uint16_t* kpbase = PYR ? p.kp + b * p.kpsb + h * p.kpsh : nullptr;
   const uint16_t* vpbase = PYR ? p.vp + b * p.vpsb + h * p.vpsh : nullptr;
   // Step u covers keys [j0, j0 + SUB) with j0 = 64 * (key block of list
-  // entry u / NSUB) + SUB * (u % NSUB); part = u % NSUB is static in the
-  // unrolled loop below.
+  // entry i) + SUB * part: i = u / NSUB and part = u % NSUB (static in the
+  // unrolled loop below), or both from the step list.
+  auto step_code = [&](int u) -> int { return wave_uniform(steplist[u]); };
+  auto entry_of = [&](int u) -> int { return SL && use_sl ? step_code(u) >> 1 : u / NSUB; };
+  auto part_of = [&](int u) -> int { return SL && use_sl ? step_code(u) & 1 : u % NSUB; };
   auto block_of = [&](int u) -> int {
-    const int i = u / NSUB;
+    const int i = entry_of(u);
     return p.row_ptr ? load_uniform(p.kv_idx, e0 + i) : e0 + i;
   };
   // Pyramid level of a key block (0 outside pyramid lists), the first row of
@@ -361,8 +395,8 @@ void attn_bf16_kernel(const Bf16Params p) {
   // (up to) four 16-key quarters (all set outside pyramid lists).
   auto quarters_of = [&](int u) -> int {
     if constexpr (!PYR) return 0xF;
-    const int q = load_uniform(p.kv_quarters, e0 + u / NSUB);
-    return NSUB == 2 ? ((q >> (2 * (u % NSUB))) & 3) | 0xC : q;
+    const int q = load_uniform(p.kv_quarters, e0 + entry_of(u));
+    return NSUB == 2 ? ((q >> (2 * part_of(u))) & 3) | 0xC : q;
   };
 
   LoadPlan<C::LPW> lp;
@@ -390,23 +424,28 @@ void attn_bf16_kernel(const Bf16Params p) {
   using V1 = std::integral_constant<uint32_t, vso[1]>;
   constexpr int PART1 = NSUB == 2 ? 1 : 0;  // part of step 1 (and of every odd step)
 
-  // Key blocks of steps it, it+1, it+2 (rolling).
+  // Key blocks of steps it, it+1, it+2 (rolling), their quarter masks and,
+  // for step lists, their parts.
   int c0 = 0, c1 = 0, c2 = 0;
-  int q0 = 0xF, q1 = 0xF, q2 = 0xF;  // quarter masks of those steps
+  int q0 = 0xF, q1 = 0xF, q2 = 0xF;
+  int r0 = 0, r1 = PART1, r2 = 0;
   if (LS > 0) {
     c0 = block_of(0);
     q0 = quarters_of(0);
-    issue_k(K0{}, c0, 0);
-    issue_v(V0{}, c0, 0);
+    if constexpr (SL) r0 = part_of(0);
+    issue_k(K0{}, c0, r0);
+    issue_v(V0{}, c0, r0);
   }
   if (LS > 1) {
     c1 = block_of(1);
     q1 = quarters_of(1);
-    issue_k(K1{}, c1, PART1);
+    if constexpr (SL) r1 = part_of(1);
+    issue_k(K1{}, c1, r1);
   }
   if (LS > 2) {
     c2 = block_of(2);
     q2 = quarters_of(2);
+    if constexpr (SL) r2 = part_of(2);
   }
 
   // Q rows of this wave as MFMA B operands (k-slice hh*8..+7 of each 16-step).
@@ -576,7 +615,7 @@ void attn_bf16_kernel(const Bf16Params p) {
     else wait_vmcnt<C::LPW>();
     barrier();
     scores(smem + kso[0], sA);
-    const int jv = valid_keys(c0, 0);
+    const int jv = valid_keys(c0, r0);
     apply_max(tile_max(sA, jv < SUB || q0 != 0xF, jv, q0) + (float)level_of(c0), 0, 0);
   }
   // One pipeline step: step `it` has scores in `cur`; when `has_next`, the
@@ -586,15 +625,17 @@ void attn_bf16_kernel(const Bf16Params p) {
   auto step = [&](int it, f32x16(&cur)[KB], f32x16(&nxt)[KB], bool has_next, auto par_c) {
     constexpr int par = decltype(par_c)::value;
     constexpr int part0 = NSUB == 2 ? par : 0, part1 = NSUB == 2 ? 1 - par : 0;
+    const int pk = SL ? r2 : part0, pv = SL ? r1 : part1;  // parts of steps it+2, it+1
     using KS_ = std::integral_constant<uint32_t, kso[par]>;
     using VS_ = std::integral_constant<uint32_t, vso[1 - par]>;
     wait_vmcnt<0>();  // V(it) and K(it+1) done
     wait_lds();
     barrier();
-    if (it + 1 < LS) issue_v(VS_{}, c1, part1);
-    if (it + 2 < LS) issue_k(KS_{}, c2, part0);
+    if (it + 1 < LS) issue_v(VS_{}, c1, pv);
+    if (it + 2 < LS) issue_k(KS_{}, c2, pk);
     const int c3 = it + 3 < LS ? block_of(it + 3) : 0;
     const int q3 = (PYR && it + 3 < LS) ? quarters_of(it + 3) : 0xF;
+    const int r3 = (SL && it + 3 < LS) ? part_of(it + 3) : 0;
     bf16x8 pb[KB][2];
     if (has_next) {
       const char* kt = smem + kso[1 - par];
@@ -652,7 +693,7 @@ void attn_bf16_kernel(const Bf16Params p) {
           asm volatile("" ::"v"(pb[kb][half]));
         }
       asm volatile("" ::"v"(l_lane));
-      const int jv = valid_keys(c1, part1);
+      const int jv = valid_keys(c1, pv);
       if (jv < SUB || q1 != 0xF) mask_keys(nxt, jv, q1);
       // Phase B: slot i issues P V MFMA i of step it and folds MPS scores of
       // step it+1 into the row max.
@@ -682,6 +723,9 @@ void attn_bf16_kernel(const Bf16Params p) {
     q0 = q1;
     q1 = q2;
     q2 = q3;
+    r0 = r1;
+    r1 = r2;
+    r2 = r3;
   };
   int it = 0;
   using P0 = std::integral_constant<int, 0>;

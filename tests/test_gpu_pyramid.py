@@ -143,3 +143,26 @@ def test_pyramid_head_dim_64_against_oracle():
     rows = np.arange(w.B * w.H * w.nQ)
     og, lg = gather_rows(host(out["o"]), host(out["lse"]), rows, w.B, w.H, w.N, w.Bq)
     compare(og, lg, o_ref, lse_ref, "pyramid d=64")
+
+
+@pytest.mark.parametrize("taus", [(1.0,), (0.3, 0.6, 0.9)])
+def test_pyramid_long_rows_sampled(taus):
+    """720p grid, one head at d = 64, row blocks of 64: with tau = 1 every row
+    lists all 1,182 key blocks, more than the forward's list of non-empty half
+    steps holds, so it steps through every half; with three levels the rows
+    are shorter and the empty halves are left out. Sampled rows."""
+    w = synth.Workload("pyr_long", 1, 1, 64, 21, 45, 80, 64, 64, "bf16", "pooled", 644, True)
+    x = synth.make_qkv(w)
+    out = run_pyramid(w, x, list(taus))
+    mref, _, _ = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, 4, 0,
+                                          levels_tau=list(taus))
+    np.testing.assert_array_equal(out["mask"], mref)
+    lens = np.diff(out["rp"])
+    note(f"pyramid long rows {taus}: entries per row {lens.min()}..{lens.max()}")
+    if taus == (1.0,):
+        assert lens.min() > 1023
+    rows = sample_rows(w.B, w.H, w.nQ, 6, 45)
+    o_ref, lse_ref = oracle.pyramid_attention(x["q"], x["k"], x["v"], w.Bq, w.Bk, w.scale, mref,
+                                              w.nQ * w.nK, rows=rows)
+    og, lg = gather_rows(host(out["o"]), host(out["lse"]), rows, w.B, w.H, w.N, w.Bq)
+    compare(og, lg, o_ref, lse_ref, f"pyramid long rows {taus}")
