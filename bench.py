@@ -305,6 +305,7 @@ def main():
         kv_q = torch.empty(cap_p, dtype=torch.int32, device=dev)
 
     fwd_events = []
+    aux_events = []  # skip carry: (kind, start, end, step) of compaction and update
     state = {"i": 0, "capture": None}
 
     def step(record: bool):
@@ -332,12 +333,19 @@ def main():
                 skip.zero_()
             qq, kk_ = step_inputs[si]
             frozen = args.share_after is not None and si >= args.share_after
+            if record:
+                c0 = torch.cuda.Event(enable_timing=True)
+                c1 = torch.cuda.Event(enable_timing=True)
+                c0.record(stream)
             if not frozen or si == args.share_after:
                 if kv_asc is None:
                     bsa.bsa_compact_block_lists(s, ones, 0, skip, row_ptr, kv_idx)
                 else:
                     bsa.bsa_compact_block_lists(s, ones, 0, skip, row_ptr, kv_asc)
                     bsa.bsa_order_block_lists(s, order, row_ptr, 0, kv_asc, kv_idx)
+            if record:
+                c1.record(stream)
+                aux_events.append(("compact", c0, c1, si))
         if state["capture"] is not None:
             torch.cuda.synchronize()
             rp_c = row_ptr.cpu().numpy().astype(np.int64)
@@ -361,7 +369,14 @@ def main():
         if perm is not None:
             bsa.bsa_permute_tokens(s, perm, w.N, 1, op, o)
         if use_gap:
+            if record:
+                u0 = torch.cuda.Event(enable_timing=True)
+                u1 = torch.cuda.Event(enable_timing=True)
+                u0.record(stream)
             bsa.bsa_update_skip_mask(s, row_ptr, kv_idx, gap, taus[si], skip)
+            if record:
+                u1.record(stream)
+                aux_events.append(("update", u0, u1, si))
         state["i"] += 1
 
     # lists of every distinct step, for the FLOP count (outside the timed region)
@@ -388,6 +403,7 @@ def main():
         step(False)
     torch.cuda.synchronize()
     fwd_events.clear()
+    aux_events.clear()
     state["i"] = 0
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -536,13 +552,23 @@ def main():
         by = {}
         for (e0, e1, si), ms in zip(fwd_events, fwd_ms_each):
             by.setdefault(si, []).append(ms)
+        aux = {}
+        for kind, e0, e1, si in aux_events:
+            aux.setdefault((kind, si), []).append(e0.elapsed_time(e1))
+        def aux_ms(kind, si):
+            v = aux.get((kind, si))
+            return float(np.mean(v)) if v else None
         out["per_step"] = [{"step": si, "fwd_ms": float(np.mean(by[si])) if si in by else None,
+                            "compact_ms": aux_ms("compact", si),
+                            "update_ms": aux_ms("update", si),
                             "computed_tflop": per_step_flops[si] / 1e12,
                             "listed_tiles": per_step_tiles[si],
                             "tile_sparsity": 1.0 - per_step_tiles[si] / (R * nK)}
                            for si in range(nsteps_distinct)]
         log("per step (sparsity, fwd ms): " + ", ".join(
             f"{p['tile_sparsity']:.3f}/{p['fwd_ms']:.2f}" for p in out["per_step"]))
+        log("per step (compact + order ms, update ms): " + ", ".join(
+            f"{p['compact_ms'] or 0:.3f}/{p['update_ms'] or 0:.3f}" for p in out["per_step"]))
     print(json.dumps(out))
 
 
