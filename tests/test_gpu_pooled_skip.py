@@ -56,6 +56,18 @@ def test_pooled_mask_d64_bit_exact():
     np.testing.assert_array_equal(got, ref)
 
 
+@pytest.mark.parametrize("mode,param", [(0, 300.0), (1, 0.5), (1, 0.95)])
+def test_pooled_mask_long_rows_bit_exact(mode, param):
+    """720p grid, one head at d = 64: rows of 1,182 key blocks, so the row
+    sort runs 2,048 keys over four waves, several pairs per lane."""
+    w = synth.Workload("pooled_long", 1, 1, 64, 21, 45, 80, 128, 64, "bf16", "pooled", 612, True)
+    x = synth.make_qkv(w)
+    got = _pooled_gpu(w, x, mode, param)
+    ref, _, _ = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, mode, param)
+    note(f"pooled long rows mode={mode} param={param}: {int(ref.sum())} kept of {ref.size}")
+    np.testing.assert_array_equal(got, ref)
+
+
 def test_pooled_mask_wan13b_480p_full():
     w = synth.workload("wan13b_480p")
     note(f"{w.name}: generating inputs")
