@@ -445,6 +445,14 @@ struct HeadCut {
 
 constexpr int kGselThreads = 256;
 constexpr int kGselGroups = 32;  // workgroups per head in a histogram pass
+constexpr int kGselFullPasses = 4;  // passes over every pair; the fifth keeps the candidates
+
+// Per-thread capacity of the candidate store: thread t of a group visits at
+// most ceil(per / kGselThreads) pairs.
+__host__ __device__ inline int64_t gsel_cand_cap(int64_t n) {
+  const int64_t per = (n + kGselGroups - 1) / kGselGroups;
+  return (per + kGselThreads - 1) / kGselThreads;
+}
 
 __global__ void gsel_init_kernel(int64_t BH, int64_t nQ, int64_t nK, int32_t mode, double param,
                                  HeadCut* __restrict__ cut) {
@@ -471,9 +479,15 @@ __global__ void gsel_init_kernel(int64_t BH, int64_t nQ, int64_t nK, int32_t mod
 // or mass (mode 3) is reached. When the mass is never reached the walk ends
 // in the lowest bucket with the rest counted above it, which keeps every
 // pair.
+// After the first passes few pairs still match the prefix: the pass with
+// phase 1 also stores each thread's matching keys (and masses) in its own
+// slice of the candidate store, in its visiting order, and the passes with
+// phase 2 walk only those, keeping the ones that still match. A thread thus
+// adds the same values in the same order as a pass over every pair would.
 __global__ __launch_bounds__(kGselThreads) void gsel_hist_kernel(
     int64_t nQ, int64_t nK, int32_t mode, int32_t shift, const double* __restrict__ S,
-    const double* __restrict__ P, HeadCut* cut, int64_t* pc, double* pm) {
+    const double* __restrict__ P, HeadCut* cut, int64_t* pc, double* pm, int32_t phase,
+    uint64_t* ck, double* cm, int32_t* ccnt) {
   __shared__ double hm[16][kGselThreads];
   __shared__ int32_t hc[16][kGselThreads];
   const int tid = threadIdx.x;
@@ -489,12 +503,45 @@ __global__ __launch_bounds__(kGselThreads) void gsel_hist_kernel(
   const int64_t e0 = g * per, e1 = min(n, e0 + per);
   const double* keys = (mode == 2 ? S : P) + bh * n;
   const double* mass = P + bh * n;
-  for (int64_t e = e0 + tid; e < e1; e += kGselThreads) {
-    const uint64_t u = order_key(keys[e]);
-    if ((u & pmask) != c.prefix) continue;
-    const int b = (int)((u >> shift) & 15);
-    hc[b][tid] += 1;
-    if (mode == 3) hm[b][tid] = hm[b][tid] + mass[e];
+  // candidate slice of this thread: entries cbase + j * kGselThreads
+  const int64_t cbase = (bh * kGselGroups + g) * gsel_cand_cap(n) * kGselThreads + tid;
+  int32_t* my_cnt = ccnt + (bh * kGselGroups + g) * kGselThreads + tid;
+  if (phase < 2) {
+    int32_t j = 0;
+    for (int64_t e = e0 + tid; e < e1; e += kGselThreads) {
+      const uint64_t u = order_key(keys[e]);
+      if ((u & pmask) != c.prefix) continue;
+      const int b = (int)((u >> shift) & 15);
+      hc[b][tid] += 1;
+      if (mode == 3) hm[b][tid] = hm[b][tid] + mass[e];
+      if (phase == 1) {
+        ck[cbase + (int64_t)j * kGselThreads] = u;
+        if (mode == 3) cm[cbase + (int64_t)j * kGselThreads] = mass[e];
+        ++j;
+      }
+    }
+    if (phase == 1) *my_cnt = j;
+  } else {
+    // the candidates still matching move down in place (slot jn <= j)
+    const int32_t m = *my_cnt;
+    int32_t jn = 0;
+    for (int32_t j = 0; j < m; ++j) {
+      const uint64_t u = ck[cbase + (int64_t)j * kGselThreads];
+      if ((u & pmask) != c.prefix) continue;
+      const int b = (int)((u >> shift) & 15);
+      hc[b][tid] += 1;
+      double ms = 0.0;
+      if (mode == 3) {
+        ms = cm[cbase + (int64_t)j * kGselThreads];
+        hm[b][tid] = hm[b][tid] + ms;
+      }
+      if (jn != j) {
+        ck[cbase + (int64_t)jn * kGselThreads] = u;
+        if (mode == 3) cm[cbase + (int64_t)jn * kGselThreads] = ms;
+      }
+      ++jn;
+    }
+    *my_cnt = jn;
   }
   __syncthreads();
   for (int off = kGselThreads / 2; off >= 1; off >>= 1) {
@@ -841,13 +888,19 @@ hipError_t launch_radial_mask(const Geom& g, int32_t h0, int32_t beta, uint8_t* 
 
 size_t pooled_workspace_bytes(const Geom& g) {
   // qbar, kbar, scores; then for the head-wide modes: probabilities, per-group
-  // histogram partials (counts and masses), one cut per head, best blocks
+  // histogram partials (counts and masses), one cut per head, best blocks,
+  // and (from a 256-byte boundary) the candidate store: keys, masses and
+  // per-thread counts
   const int64_t BH = (int64_t)g.B * g.H;
   const int64_t n = BH * (g.nQ + g.nK) * g.D + 2 * BH * g.nQ * g.nK;
   size_t bytes = (size_t)n * sizeof(double);
   bytes += (size_t)BH * kGselGroups * 16 * (sizeof(int64_t) + sizeof(double));
   bytes += (size_t)BH * sizeof(HeadCut);
   bytes += (size_t)BH * g.nQ * sizeof(int32_t);
+  bytes = (bytes + 255) / 256 * 256;
+  const int64_t cand = BH * kGselGroups * gsel_cand_cap(g.nQ * g.nK) * kGselThreads;
+  bytes += (size_t)cand * (sizeof(uint64_t) + sizeof(double));
+  bytes += (size_t)BH * kGselGroups * kGselThreads * sizeof(int32_t);
   return (bytes + 255) / 256 * 256;
 }
 
@@ -893,13 +946,19 @@ hipError_t launch_pooled_global(const Geom& g, int32_t mode, double param, uint8
   double* pm = (double*)(pc + BH * kGselGroups * 16);
   HeadCut* cut = (HeadCut*)(pm + BH * kGselGroups * 16);
   int32_t* best = (int32_t*)(cut + BH);
+  const int64_t cand = BH * kGselGroups * gsel_cand_cap(n) * kGselThreads;
+  const size_t head = ((size_t)((char*)(best + BH * g.nQ) - (char*)ws) + 255) / 256 * 256;
+  uint64_t* ck = (uint64_t*)((char*)ws + head);  // same offset as pooled_workspace_bytes
+  double* cm = (double*)(ck + cand);
+  int32_t* ccnt = (int32_t*)(cm + cand);
   hipLaunchKernelGGL(pooled_rowstats_kernel, dim3((unsigned)(BH * g.nQ)), dim3(kWave), 0, st,
                      g.nK, mode, S, P, best);
   hipLaunchKernelGGL(gsel_init_kernel, dim3(grid_for(BH, 64)), dim3(64), 0, st, BH, g.nQ, g.nK,
                      mode, param, cut);
-  for (int shift = 60; shift >= 0; shift -= 4) {
+  for (int pass = 0, shift = 60; shift >= 0; ++pass, shift -= 4) {
+    const int32_t phase = pass < kGselFullPasses ? 0 : (pass == kGselFullPasses ? 1 : 2);
     hipLaunchKernelGGL(gsel_hist_kernel, dim3(kGselGroups, (unsigned)BH), dim3(kGselThreads), 0,
-                       st, g.nQ, g.nK, mode, shift, S, P, cut, pc, pm);
+                       st, g.nQ, g.nK, mode, shift, S, P, cut, pc, pm, phase, ck, cm, ccnt);
   }
   hipLaunchKernelGGL(gsel_ties_kernel, dim3(grid_for(BH, 64)), dim3(64), 0, st, BH, n, mode, S, P,
                      cut);
