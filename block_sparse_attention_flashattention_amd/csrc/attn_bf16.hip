@@ -294,11 +294,12 @@ void attn_bf16_kernel(const Bf16Params p) {
   // Workgroup -> (head, row block). Hardware dispatch sends workgroup x to
   // XCD x % 8; each XCD gets a contiguous range of the order below, so the
   // row blocks it runs together share their K/V tiles in its L2. Within a
-  // head the order is position-major: bands of kBand row-block slots per
-  // frame, all frames of a band before the next band. Row blocks at the same
-  // in-frame position in different frames visit the same key frames in the
-  // same ascending order, so concurrently running ones reuse each other's
-  // tiles while they are still cached.
+  // head the order is position-major when U > 0 (shared lists): bands of
+  // kBand row-block slots per frame, all frames of a band before the next
+  // band. Row blocks at the same in-frame position in different frames visit
+  // the same key frames in the same ascending order, so concurrently running
+  // ones reuse each other's tiles while they are still cached. With U = 0
+  // (per-head lists, tiny frames) row blocks run in plain order.
   const int64_t G = gridDim.x, wg = blockIdx.x;
   const int64_t xcd = wg % kXcds, kk = wg / kXcds, q8 = G / kXcds, r8 = G % kXcds;
   const int64_t lid = xcd * q8 + min(xcd, r8) + kk;
@@ -842,6 +843,12 @@ hipError_t launch_attn_bf16(const Geom& g, const AttnArgs& a, hipStream_t st) {
   p.N = g.N; p.nQ = g.nQ; p.nK = g.nK; p.H = g.H;
   p.T = g.T; p.F = g.F; p.U = (int32_t)((g.F + g.Bq - 1) / g.Bq);
   if ((int64_t)g.T * p.U > g.nQ + g.nQ / 4) p.U = 0;  // tiny frames: plain row order
+  // Per-head lists come from content-based masks (pooled, pyramid, skip
+  // carry), where neighbouring row blocks of a head pick similar key blocks:
+  // plain row order shares their tiles in L2. Shared lists (the radial mask)
+  // band by frame distance, so row blocks at the same in-frame position of
+  // different frames are the ones that visit the same key frames.
+  if (a.row_ptr && !a.lists_shared) p.U = 0;
   if (g.D == 64) return g.Bq == 64 ? launch<64, 64>(g, p, st) : launch<64, 128>(g, p, st);
   return g.Bq == 64 ? launch<128, 64>(g, p, st) : launch<128, 128>(g, p, st);
 }
