@@ -207,6 +207,14 @@ __device__ inline double ordered_sum(const double* a, int64_t n, double acc) {
   return acc;
 }
 
+// Order-preserving map of a double to 64 bits (larger value -> larger key;
+// -0 and +0 map alike).
+__device__ inline uint64_t order_key(double v) {
+  if (v == 0.0) v = 0.0;
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  return (b >> 63) ? ~b : (b | (1ull << 63));
+}
+
 // Order (sa, ia) before (sb, ib): higher score first, lower block index on
 // ties; index -1 pads the sort to a power of two and goes last.
 __device__ inline bool key_before(double sa, int ia, double sb, int ib) {
@@ -261,6 +269,56 @@ __device__ inline void sort_keys(double* ks, int32_t* ki, int P) {
   __syncthreads();
 }
 
+constexpr int kTopM = 128;  // cumulative mass: pairs sorted before a full sort is needed
+
+// Key of the T-th pair of the row in (score desc, index asc) order, fixed 4
+// bits at a time from the top (radix select over order_key of the scores),
+// and how many pairs with exactly that key are among the first T (taken in
+// ascending block index) and exist in all. Called by the whole workgroup.
+struct RowCut {
+  uint64_t key;
+  int32_t take_eq;
+  int32_t n_eq;
+};
+__device__ inline RowCut select_kth(const double* s, int64_t nK, int T) {
+  __shared__ int32_t hist[16];
+  __shared__ uint64_t rs_prefix;
+  __shared__ int32_t rs_want, rs_eq;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid == 0) {
+    rs_prefix = 0;
+    rs_want = T;
+  }
+  for (int shift = 60; shift >= 0; shift -= 4) {
+    if (tid < 16) hist[tid] = 0;
+    __syncthreads();
+    const uint64_t prefix = rs_prefix;
+    const uint64_t pmask = shift >= 60 ? 0 : (~0ull << (shift + 4));
+    for (int64_t c = tid; c < nK; c += blockDim.x) {
+      const uint64_t u = order_key(s[c]);
+      if ((u & pmask) == prefix) atomicAdd(&hist[(int)((u >> shift) & 15)], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // the highest bucket b whose count from the top (buckets b .. 15)
+      // reaches the pairs still wanted
+      const int want = rs_want;
+      int sfx = 0;
+      if (lane < 16)
+        for (int j = lane; j < 16; ++j) sfx += hist[j];
+      const uint64_t m = __builtin_amdgcn_ballot_w64(lane < 16 && sfx >= want);
+      const int b = m ? 63 - __builtin_clzll(m) : 0;
+      if (lane == b) {
+        rs_prefix = prefix | ((uint64_t)b << shift);
+        rs_want = want - (sfx - hist[b]);
+        rs_eq = hist[b];
+      }
+    }
+    __syncthreads();
+  }
+  return RowCut{rs_prefix, rs_want, rs_eq};
+}
+
 // One workgroup per (b, h, a): sort of the row's blocks by (score desc, index
 // asc), then top-k, the shortest prefix reaching the cumulative softmax mass
 // tau_p, or the pyramid levels. Z = sum of exp(S - max) in ascending block
@@ -279,14 +337,78 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
   __shared__ double z_sh;
   const int64_t row = blockIdx.x;
   const double* srow = S + row * nK;
-  for (int c = threadIdx.x; c < P; c += blockDim.x) {
-    double v = 0.0;
-    if (c < nK) {
-      v = srow[c];
-      s[c] = v;
-      flag[c] = 0;
+  for (int c = threadIdx.x; c < nK; c += blockDim.x) {
+    s[c] = srow[c];
+    flag[c] = 0;
+  }
+  __syncthreads();
+  uint8_t* mrow = mask + row * nK;
+  // Fast paths for long rows, no full sort: top-k marks the pairs before the
+  // k-th key; cumulative mass sorts only the first kTopM pairs (the head of
+  // the full order) and stops there if the mass is reached. A cut inside a
+  // run of equal keys, or mass not reached, takes the full sort below.
+  if ((mode == 0 || mode == 1) && nK > kTopM && !(mode == 0 && param >= (double)nK)) {
+    const int T = mode == 0 ? (int)max(1.0, param) : kTopM;
+    const RowCut cut = select_kth(s, nK, T);
+    if (cut.take_eq == cut.n_eq) {  // every pair with the cut key is taken
+      if (mode == 0) {
+        for (int c = threadIdx.x; c < nK; c += blockDim.x)
+          mrow[c] = order_key(s[c]) >= cut.key ? 1 : 0;
+        return;
+      }
+      __shared__ double cs[kTopM];
+      __shared__ int32_t ci[kTopM];
+      __shared__ int32_t ncand;
+      if (threadIdx.x == 0) ncand = 0;
+      __syncthreads();
+      for (int c = threadIdx.x; c < nK; c += blockDim.x)
+        if (order_key(s[c]) >= cut.key) {
+          const int pos = atomicAdd(&ncand, 1);
+          cs[pos] = s[c];
+          ci[pos] = c;
+        }
+      __syncthreads();
+      sort_keys(cs, ci, kTopM);
+      const double smax0 = cs[0];
+      for (int c = threadIdx.x; c < nK; c += blockDim.x) ks[c] = exp(s[c] - smax0);
+      __syncthreads();
+      if (threadIdx.x < 64) {
+        const double Z = ordered_sum(ks, nK, 0.0);
+        if (threadIdx.x == 0) z_sh = Z;
+      }
+      __syncthreads();
+      const double Z0 = z_sh;
+      for (int t = threadIdx.x; t < kTopM; t += blockDim.x) cs[t] = ks[ci[t]] / Z0;
+      __syncthreads();
+      if (threadIdx.x < 64) {
+        int32_t kp = -1;  // not reached within the first kTopM pairs
+        double run = 0.0;
+        for (int t0 = 0; t0 < kTopM && kp < 0; t0 += 16) {
+          double v[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) v[u] = cs[t0 + u];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            if (kp < 0) {
+              run = run + v[u];
+              if (run >= param) kp = t0 + u + 1;
+            }
+          }
+        }
+        if (threadIdx.x == 0) keep_sh = kp;
+      }
+      __syncthreads();
+      const int32_t kp = keep_sh;
+      if (kp > 0) {
+        for (int t = threadIdx.x; t < kp; t += blockDim.x) flag[ci[t]] = 1;
+        __syncthreads();
+        for (int c = threadIdx.x; c < nK; c += blockDim.x) mrow[c] = flag[c];
+        return;
+      }
     }
-    ks[c] = v;
+  }
+  for (int c = threadIdx.x; c < P; c += blockDim.x) {
+    ks[c] = c < nK ? s[c] : 0.0;
     ki[c] = c < nK ? c : -1;
   }
   __syncthreads();
@@ -364,7 +486,6 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
   }
   for (int t = threadIdx.x; t < keep; t += blockDim.x) flag[ki[t]] = 1;
   __syncthreads();
-  uint8_t* mrow = mask + row * nK;
   for (int c = threadIdx.x; c < nK; c += blockDim.x) mrow[c] = flag[c];
 }
 
@@ -422,13 +543,6 @@ __global__ __launch_bounds__(kWave) void pooled_rowstats_kernel(int64_t nK, int3
   for (int64_t c = lane; c < nK; c += kWave) pr[c] = ex[c] / Z;
 }
 
-// Order-preserving map of a double to 64 bits (larger value -> larger key;
-// -0 and +0 map alike).
-__device__ inline uint64_t order_key(double v) {
-  if (v == 0.0) v = 0.0;
-  const uint64_t b = (uint64_t)__double_as_longlong(v);
-  return (b >> 63) ? ~b : (b | (1ull << 63));
-}
 
 // The cut of one head, found 4 bits at a time from the top (radix select in
 // (key desc, index asc) order). `need_c` / `need_m` are the pairs / mass
