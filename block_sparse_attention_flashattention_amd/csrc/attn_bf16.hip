@@ -283,7 +283,8 @@ void attn_bf16_kernel(const Bf16Params p) {
   // unselected are left out (they would only compute masked keys)
   constexpr bool SL = PYR && NSUB == 2;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
-  __shared__ int32_t steplist[SL ? kStepCap : 1];  // (list entry << 1) | half
+  // step descriptors: (augmented block << 5) | (half << 4) | quarter bits
+  __shared__ int32_t steplist[SL ? kStepCap : 1];
   __shared__ int32_t steps_sh;
 
   const int tid = threadIdx.x;
@@ -342,12 +343,15 @@ void attn_bf16_kernel(const Bf16Params p) {
         for (int j0 = 0; j0 < L; j0 += 64) {
           const int j = j0 + lane;
           const int q = j < L ? p.kv_quarters[e0 + j] : 0;
+          const int c = j < L ? p.kv_idx[e0 + j] : 0;
           const uint64_t m0 = __builtin_amdgcn_ballot_w64((q & 3) != 0);
           const uint64_t m1 = __builtin_amdgcn_ballot_w64((q & 12) != 0);
           const uint64_t below = (1ull << lane) - 1;
           const int pos = base + __popcll(m0 & below) + __popcll(m1 & below);
-          if (q & 3) steplist[pos] = 2 * j;
-          if (q & 12) steplist[pos + ((q & 3) ? 1 : 0)] = 2 * j + 1;
+          // a half step's two quarters in bits 0-1; bits 2-3 set (it has no
+          // third or fourth quarter)
+          if (q & 3) steplist[pos] = (c << 5) | (q & 3) | 0xC;
+          if (q & 12) steplist[pos + ((q & 3) ? 1 : 0)] = (c << 5) | 16 | ((q >> 2) & 3) | 0xC;
           base += __popcll(m0) + __popcll(m1);
         }
         if (lane == 0) steps_sh = base;
@@ -365,9 +369,10 @@ void attn_bf16_kernel(const Bf16Params p) {
   // entry i) + SUB * part: i = u / NSUB and part = u % NSUB (static in the
   // unrolled loop below), or both from the step list.
   auto step_code = [&](int u) -> int { return wave_uniform(steplist[u]); };
-  auto entry_of = [&](int u) -> int { return SL && use_sl ? step_code(u) >> 1 : u / NSUB; };
-  auto part_of = [&](int u) -> int { return SL && use_sl ? step_code(u) & 1 : u % NSUB; };
+  auto entry_of = [&](int u) -> int { return u / NSUB; };
+  auto part_of = [&](int u) -> int { return SL && use_sl ? (step_code(u) >> 4) & 1 : u % NSUB; };
   auto block_of = [&](int u) -> int {
+    if (SL && use_sl) return step_code(u) >> 5;
     const int i = entry_of(u);
     return p.row_ptr ? load_uniform(p.kv_idx, e0 + i) : e0 + i;
   };
@@ -396,6 +401,7 @@ void attn_bf16_kernel(const Bf16Params p) {
   // (up to) four 16-key quarters (all set outside pyramid lists).
   auto quarters_of = [&](int u) -> int {
     if constexpr (!PYR) return 0xF;
+    if (SL && use_sl) return step_code(u) & 15;
     const int q = load_uniform(p.kv_quarters, e0 + entry_of(u));
     return NSUB == 2 ? ((q >> (2 * part_of(u))) & 3) | 0xC : q;
   };
@@ -623,8 +629,15 @@ void attn_bf16_kernel(const Bf16Params p) {
   // scores of step it+1 are computed into `nxt` meanwhile. Every LDS read of
   // the previous step has completed before the barrier (lgkmcnt(0)), so the
   // stages it read may be refilled right after it. `par` = it % 2.
-  auto step = [&](int it, f32x16(&cur)[KB], f32x16(&nxt)[KB], bool has_next, auto par_c) {
+  // With LSL (pyramid step list in use) the descriptor of step it+3 is read
+  // from LDS at the top of step it, at a clamped index so that the read is
+  // unconditional, and decoded at the end of the step, when the step's own
+  // LDS waits have covered it. The list path instead reads list entries with
+  // scalar loads, which lgkmcnt counts together with LDS reads.
+  auto step = [&](int it, f32x16(&cur)[KB], f32x16(&nxt)[KB], bool has_next, auto par_c,
+                  auto lsl_c) __attribute__((always_inline)) {
     constexpr int par = decltype(par_c)::value;
+    constexpr bool LSL = decltype(lsl_c)::value;
     constexpr int part0 = NSUB == 2 ? par : 0, part1 = NSUB == 2 ? 1 - par : 0;
     const int pk = SL ? r2 : part0, pv = SL ? r1 : part1;  // parts of steps it+2, it+1
     using KS_ = std::integral_constant<uint32_t, kso[par]>;
@@ -634,9 +647,10 @@ void attn_bf16_kernel(const Bf16Params p) {
     barrier();
     if (it + 1 < LS) issue_v(VS_{}, c1, pv);
     if (it + 2 < LS) issue_k(KS_{}, c2, pk);
-    const int c3 = it + 3 < LS ? block_of(it + 3) : 0;
-    const int q3 = (PYR && it + 3 < LS) ? quarters_of(it + 3) : 0xF;
-    const int r3 = (SL && it + 3 < LS) ? part_of(it + 3) : 0;
+    const int code3 = LSL ? steplist[min(it + 3, kStepCap - 1)] : 0;
+    int c3 = LSL ? 0 : (it + 3 < LS ? block_of(it + 3) : 0);
+    int q3 = (PYR && !LSL && it + 3 < LS) ? quarters_of(it + 3) : 0xF;
+    int r3 = (SL && !LSL && it + 3 < LS) ? part_of(it + 3) : 0;
     bf16x8 pb[KB][2];
     if (has_next) {
       const char* kt = smem + kso[1 - par];
@@ -718,6 +732,14 @@ void attn_bf16_kernel(const Bf16Params p) {
       probs(cur, pb, (float)level_of(c0));
       accumulate(smem + vso[par], pb);
     }
+    if constexpr (LSL) {
+      const int code = wave_uniform(code3);
+      if (it + 3 < LS) {
+        c3 = code >> 5;
+        q3 = code & 15;
+        r3 = (code >> 4) & 1;
+      }
+    }
     c0 = c1;
     c1 = c2;
     c2 = c3;
@@ -728,18 +750,40 @@ void attn_bf16_kernel(const Bf16Params p) {
     r1 = r2;
     r2 = r3;
   };
-  int it = 0;
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  for (; it + 2 < LS; it += 2) {
-    step(it, sA, sB, true, P0{});
-    step(it + 1, sB, sA, true, P1{});
-  }
-  if (it + 1 < LS) {
-    step(it, sA, sB, true, P0{});
-    step(it + 1, sB, sA, false, P1{});
-  } else if (it < LS) {
-    step(it, sA, sB, false, P0{});
+  // the whole pipeline, as its own loop for each way of reading the list
+  auto run = [&](auto lsl_c) __attribute__((always_inline)) {
+    int it = 0;
+    for (; it + 2 < LS; it += 2) {
+      step(it, sA, sB, true, P0{}, lsl_c);
+      step(it + 1, sB, sA, true, P1{}, lsl_c);
+    }
+    if (it + 1 < LS) {
+      step(it, sA, sB, true, P0{}, lsl_c);
+      step(it + 1, sB, sA, false, P1{}, lsl_c);
+    } else if (it < LS) {
+      step(it, sA, sB, false, P0{}, lsl_c);
+    }
+  };
+  if constexpr (SL) {
+    if (use_sl)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
+  } else {
+    using F = std::false_type;
+    int it = 0;
+    for (; it + 2 < LS; it += 2) {
+      step(it, sA, sB, true, P0{}, F{});
+      step(it + 1, sB, sA, true, P1{}, F{});
+    }
+    if (it + 1 < LS) {
+      step(it, sA, sB, true, P0{}, F{});
+      step(it + 1, sB, sA, false, P1{}, F{});
+    } else if (it < LS) {
+      step(it, sA, sB, false, P0{}, F{});
+    }
   }
 
   if (GAP && L > gbatch) flush_gaps(L - gbatch);
