@@ -334,32 +334,6 @@ void attn_bf16_kernel(const Bf16Params p) {
   }
   const int L = e1 - e0;      // listed key blocks
   int LS = L * NSUB;          // pipeline steps (SUB keys each)
-  bool use_sl = false;
-  if constexpr (SL) {
-    if (2 * L <= kStepCap) {  // else every half is stepped through
-      use_sl = true;
-      if (w == 0) {
-        int base = 0;
-        for (int j0 = 0; j0 < L; j0 += 64) {
-          const int j = j0 + lane;
-          const int q = j < L ? p.kv_quarters[e0 + j] : 0;
-          const int c = j < L ? p.kv_idx[e0 + j] : 0;
-          const uint64_t m0 = __builtin_amdgcn_ballot_w64((q & 3) != 0);
-          const uint64_t m1 = __builtin_amdgcn_ballot_w64((q & 12) != 0);
-          const uint64_t below = (1ull << lane) - 1;
-          const int pos = base + __popcll(m0 & below) + __popcll(m1 & below);
-          // a half step's two quarters in bits 0-1; bits 2-3 set (it has no
-          // third or fourth quarter)
-          if (q & 3) steplist[pos] = (c << 5) | (q & 3) | 0xC;
-          if (q & 12) steplist[pos + ((q & 3) ? 1 : 0)] = (c << 5) | 16 | ((q >> 2) & 3) | 0xC;
-          base += __popcll(m0) + __popcll(m1);
-        }
-        if (lane == 0) steps_sh = base;
-      }
-      __syncthreads();
-      LS = steps_sh;
-    }
-  }
   const int N32 = (int)p.N;
   const uint16_t* kbase = p.k + b * p.ksb + h * p.ksh;
   const uint16_t* vbase = p.v + b * p.vsb + h * p.vsh;
@@ -368,11 +342,9 @@ void attn_bf16_kernel(const Bf16Params p) {
   // Step u covers keys [j0, j0 + SUB) with j0 = 64 * (key block of list
   // entry i) + SUB * part: i = u / NSUB and part = u % NSUB (static in the
   // unrolled loop below), or both from the step list.
-  auto step_code = [&](int u) -> int { return wave_uniform(steplist[u]); };
   auto entry_of = [&](int u) -> int { return u / NSUB; };
-  auto part_of = [&](int u) -> int { return SL && use_sl ? (step_code(u) >> 4) & 1 : u % NSUB; };
+  auto part_of = [&](int u) -> int { return u % NSUB; };
   auto block_of = [&](int u) -> int {
-    if (SL && use_sl) return step_code(u) >> 5;
     const int i = entry_of(u);
     return p.row_ptr ? load_uniform(p.kv_idx, e0 + i) : e0 + i;
   };
@@ -401,10 +373,48 @@ void attn_bf16_kernel(const Bf16Params p) {
   // (up to) four 16-key quarters (all set outside pyramid lists).
   auto quarters_of = [&](int u) -> int {
     if constexpr (!PYR) return 0xF;
-    if (SL && use_sl) return step_code(u) & 15;
     const int q = load_uniform(p.kv_quarters, e0 + entry_of(u));
     return NSUB == 2 ? ((q >> (2 * part_of(u))) & 3) | 0xC : q;
   };
+
+  // Pyramid step list: wave 0 lists the half steps with a selected quarter
+  // as descriptors (first key row in k or kp / 32 << 10 | valid rows << 4 |
+  // level << 2 | the half's two quarter bits), so that a step needs one LDS
+  // word and no address arithmetic on its level.
+  bool use_sl = false;
+  auto d_row0 = [](int d) -> int { return (d >> 10) << 5; };
+  auto d_valid = [](int d) -> int { return (d >> 4) & 63; };
+  auto d_level = [](int d) -> int { return (d >> 2) & 3; };
+  auto d_quarters = [](int d) -> int { return (d & 3) | 0xC; };
+  if constexpr (SL) {
+    // else every half is stepped through (row offsets fit 22 bits below 2^27)
+    if (2 * L <= kStepCap && N32 < (1 << 27)) {
+      use_sl = true;
+      if (w == 0) {
+        int base = 0;
+        for (int j0 = 0; j0 < L; j0 += 64) {
+          const int j = j0 + lane;
+          const int q = j < L ? p.kv_quarters[e0 + j] : 0;
+          const int c = j < L ? p.kv_idx[e0 + j] : 0;
+          const uint64_t m0 = __builtin_amdgcn_ballot_w64((q & 3) != 0);
+          const uint64_t m1 = __builtin_amdgcn_ballot_w64((q & 12) != 0);
+          const uint64_t below = (1ull << lane) - 1;
+          const int pos = base + __popcll(m0 & below) + __popcll(m1 & below);
+          auto desc = [&](int part) {
+            return ((first_key(c, part) >> 5) << 10) | (valid_keys(c, part) << 4) |
+                   (level_of(c) << 2) | ((q >> (2 * part)) & 3);
+          };
+          if (q & 3) steplist[pos] = desc(0);
+          if (q & 12) steplist[pos + ((q & 3) ? 1 : 0)] = desc(1);
+          base += __popcll(m0) + __popcll(m1);
+        }
+        if (lane == 0) steps_sh = base;
+      }
+      __syncthreads();
+      LS = steps_sh;
+    }
+  }
+  auto step_code = [&](int u) -> int { return wave_uniform(steplist[u]); };
 
   LoadPlan<C::LPW> lp;
   make_plan<D, C::NW, C::LPW>(lp, w, lane, p.ksn, p.vsn);
@@ -425,6 +435,14 @@ void attn_bf16_kernel(const Bf16Params p) {
     issue_rows<C::NW, C::LPW, decltype(so_c)::value>(
         lp.v, rows_rsrc(base, p.vsn, j0, valid_keys(c, part)), wave_lds);
   };
+  auto issue_kd = [&](auto so_c, int d) {
+    issue_rows<C::NW, C::LPW, decltype(so_c)::value>(
+        lp.k, rows_rsrc(d_level(d) ? kpbase : kbase, p.ksn, d_row0(d), d_valid(d)), wave_lds);
+  };
+  auto issue_vd = [&](auto so_c, int d) {
+    issue_rows<C::NW, C::LPW, decltype(so_c)::value>(
+        lp.v, rows_rsrc(d_level(d) ? vpbase : vbase, p.vsn, d_row0(d), d_valid(d)), wave_lds);
+  };
   using K0 = std::integral_constant<uint32_t, kso[0]>;
   using K1 = std::integral_constant<uint32_t, kso[1]>;
   using V0 = std::integral_constant<uint32_t, vso[0]>;
@@ -432,27 +450,38 @@ void attn_bf16_kernel(const Bf16Params p) {
   constexpr int PART1 = NSUB == 2 ? 1 : 0;  // part of step 1 (and of every odd step)
 
   // Key blocks of steps it, it+1, it+2 (rolling), their quarter masks and,
-  // for step lists, their parts.
+  // for step lists, their parts; with the pyramid step list in use, c0..c2
+  // hold the steps' descriptors instead.
   int c0 = 0, c1 = 0, c2 = 0;
   int q0 = 0xF, q1 = 0xF, q2 = 0xF;
   int r0 = 0, r1 = PART1, r2 = 0;
-  if (LS > 0) {
-    c0 = block_of(0);
-    q0 = quarters_of(0);
-    if constexpr (SL) r0 = part_of(0);
-    issue_k(K0{}, c0, r0);
-    issue_v(V0{}, c0, r0);
-  }
-  if (LS > 1) {
-    c1 = block_of(1);
-    q1 = quarters_of(1);
-    if constexpr (SL) r1 = part_of(1);
-    issue_k(K1{}, c1, r1);
-  }
-  if (LS > 2) {
-    c2 = block_of(2);
-    q2 = quarters_of(2);
-    if constexpr (SL) r2 = part_of(2);
+  if (SL && use_sl) {
+    if (LS > 0) {
+      c0 = step_code(0);
+      issue_kd(K0{}, c0);
+      issue_vd(V0{}, c0);
+    }
+    if (LS > 1) {
+      c1 = step_code(1);
+      issue_kd(K1{}, c1);
+    }
+    if (LS > 2) c2 = step_code(2);
+  } else {
+    if (LS > 0) {
+      c0 = block_of(0);
+      q0 = quarters_of(0);
+      issue_k(K0{}, c0, r0);
+      issue_v(V0{}, c0, r0);
+    }
+    if (LS > 1) {
+      c1 = block_of(1);
+      q1 = quarters_of(1);
+      issue_k(K1{}, c1, r1);
+    }
+    if (LS > 2) {
+      c2 = block_of(2);
+      q2 = quarters_of(2);
+    }
   }
 
   // Q rows of this wave as MFMA B operands (k-slice hh*8..+7 of each 16-step).
@@ -616,15 +645,31 @@ void attn_bf16_kernel(const Bf16Params p) {
   // stages last read before that barrier, and waited for at the start of
   // step j+1.
   f32x16 sA[KB], sB[KB];
-  if (LS > 0) {
-    // prologue: scores and max of step 0
-    if (LS > 1) wait_vmcnt<2 * C::LPW>();  // K0 done; V0, K1 may fly
-    else wait_vmcnt<C::LPW>();
-    barrier();
-    scores(smem + kso[0], sA);
-    const int jv = valid_keys(c0, r0);
-    apply_max(tile_max(sA, jv < SUB || q0 != 0xF, jv, q0) + (float)level_of(c0), 0, 0);
-  }
+  // per-step quantities from a block (and part) or, with LSL, a descriptor
+  auto lev = [&](auto lsl_c, int c) -> int {
+    if constexpr (decltype(lsl_c)::value) return d_level(c);
+    else return level_of(c);
+  };
+  auto vkeys = [&](auto lsl_c, int c, int part) -> int {
+    if constexpr (decltype(lsl_c)::value) return d_valid(c);
+    else return valid_keys(c, part);
+  };
+  auto qmask = [&](auto lsl_c, int c, int q) -> int {
+    if constexpr (decltype(lsl_c)::value) return d_quarters(c);
+    else return q;
+  };
+  auto first_scores = [&](auto lsl_c) __attribute__((always_inline)) {
+    if (LS > 0) {
+      // prologue: scores and max of step 0
+      if (LS > 1) wait_vmcnt<2 * C::LPW>();  // K0 done; V0, K1 may fly
+      else wait_vmcnt<C::LPW>();
+      barrier();
+      scores(smem + kso[0], sA);
+      const int jv = vkeys(lsl_c, c0, r0), qm0 = qmask(lsl_c, c0, q0);
+      apply_max(tile_max(sA, jv < SUB || qm0 != 0xF, jv, qm0) + (float)lev(lsl_c, c0), 0, 0);
+    }
+  };
+  if constexpr (!SL) first_scores(std::false_type{});
   // One pipeline step: step `it` has scores in `cur`; when `has_next`, the
   // scores of step it+1 are computed into `nxt` meanwhile. Every LDS read of
   // the previous step has completed before the barrier (lgkmcnt(0)), so the
@@ -645,8 +690,13 @@ void attn_bf16_kernel(const Bf16Params p) {
     wait_vmcnt<0>();  // V(it) and K(it+1) done
     wait_lds();
     barrier();
-    if (it + 1 < LS) issue_v(VS_{}, c1, pv);
-    if (it + 2 < LS) issue_k(KS_{}, c2, pk);
+    if constexpr (LSL) {
+      if (it + 1 < LS) issue_vd(VS_{}, c1);
+      if (it + 2 < LS) issue_kd(KS_{}, c2);
+    } else {
+      if (it + 1 < LS) issue_v(VS_{}, c1, pv);
+      if (it + 2 < LS) issue_k(KS_{}, c2, pk);
+    }
     const int code3 = LSL ? steplist[min(it + 3, kStepCap - 1)] : 0;
     int c3 = LSL ? 0 : (it + 3 < LS ? block_of(it + 3) : 0);
     int q3 = (PYR && !LSL && it + 3 < LS) ? quarters_of(it + 3) : 0xF;
@@ -676,7 +726,7 @@ void attn_bf16_kernel(const Bf16Params p) {
       // probabilities of step it (exp2, bf16 pair, row-sum dot).
       // a pooled key stands for 2^level tokens: its weight 2^level p, i.e.
       // + level in the log2 exponent
-      const float neg_m = (float)level_of(c0) - m_use;
+      const float neg_m = (float)lev(lsl_c, c0) - m_use;
 #pragma unroll
       for (int i = 0; i < kPfK; ++i) kbuf[i] = kread(i);
 #pragma unroll
@@ -708,8 +758,8 @@ void attn_bf16_kernel(const Bf16Params p) {
           asm volatile("" ::"v"(pb[kb][half]));
         }
       asm volatile("" ::"v"(l_lane));
-      const int jv = valid_keys(c1, pv);
-      if (jv < SUB || q1 != 0xF) mask_keys(nxt, jv, q1);
+      const int jv = vkeys(lsl_c, c1, pv), qm1 = qmask(lsl_c, c1, q1);
+      if (jv < SUB || qm1 != 0xF) mask_keys(nxt, jv, qm1);
       // Phase B: slot i issues P V MFMA i of step it and folds MPS scores of
       // step it+1 into the row max.
       float mloc = -INFINITY;
@@ -727,18 +777,14 @@ void attn_bf16_kernel(const Bf16Params p) {
         __builtin_amdgcn_sched_barrier(0);
       }
       mloc = vmax(mloc, other_half(mloc));
-      apply_max(mloc * p.sl2 + (float)level_of(c1), it + 1, part1);
+      apply_max(mloc * p.sl2 + (float)lev(lsl_c, c1), it + 1, part1);
     } else {
-      probs(cur, pb, (float)level_of(c0));
+      probs(cur, pb, (float)lev(lsl_c, c0));
       accumulate(smem + vso[par], pb);
     }
     if constexpr (LSL) {
       const int code = wave_uniform(code3);
-      if (it + 3 < LS) {
-        c3 = code >> 5;
-        q3 = code & 15;
-        r3 = (code >> 4) & 1;
-      }
+      if (it + 3 < LS) c3 = code;
     }
     c0 = c1;
     c1 = c2;
@@ -754,6 +800,7 @@ void attn_bf16_kernel(const Bf16Params p) {
   using P1 = std::integral_constant<int, 1>;
   // the whole pipeline, as its own loop for each way of reading the list
   auto run = [&](auto lsl_c) __attribute__((always_inline)) {
+    first_scores(lsl_c);
     int it = 0;
     for (; it + 2 < LS; it += 2) {
       step(it, sA, sB, true, P0{}, lsl_c);
