@@ -72,30 +72,47 @@ __global__ void radial_mask_kernel(int64_t N, int64_t F, int32_t Bq, int32_t Bk,
 
 // ------------------------------------------------------------------ pooled
 // Four consecutive input elements (channels x .. x+3, 16-byte aligned rows)
-// widened to fp64 (exact), from one 8- or 16-byte load.
-__device__ inline void widen4(const void* p, int dtype, int64_t off, double (&v)[4]) {
-  if (dtype == 0) {
-    const uint2 u = *(const uint2*)((const uint16_t*)p + off);
-    v[0] = (double)__uint_as_float(u.x << 16);
-    v[1] = (double)__uint_as_float(u.x & 0xffff0000u);
-    v[2] = (double)__uint_as_float(u.y << 16);
-    v[3] = (double)__uint_as_float(u.y & 0xffff0000u);
+// as loaded: 8 bytes of bf16 (DT 0) or 16 of fp32 (DT 1).
+template <int DT>
+struct Raw4;
+template <>
+struct Raw4<0> {
+  uint2 u;
+};
+template <>
+struct Raw4<1> {
+  float4 f;
+};
+template <int DT>
+__device__ inline Raw4<DT> load4(const void* p, int64_t off) {
+  if constexpr (DT == 0) return {*(const uint2*)((const uint16_t*)p + off)};
+  else return {*(const float4*)((const float*)p + off)};
+}
+// acc[c] += element c, widened to fp64 (exact), one rounded add per channel.
+template <int DT>
+__device__ inline void add4(double (&acc)[4], const Raw4<DT>& r) {
+  if constexpr (DT == 0) {
+    acc[0] = acc[0] + (double)__uint_as_float(r.u.x << 16);
+    acc[1] = acc[1] + (double)__uint_as_float(r.u.x & 0xffff0000u);
+    acc[2] = acc[2] + (double)__uint_as_float(r.u.y << 16);
+    acc[3] = acc[3] + (double)__uint_as_float(r.u.y & 0xffff0000u);
   } else {
-    const float4 f = *(const float4*)((const float*)p + off);
-    v[0] = (double)f.x;
-    v[1] = (double)f.y;
-    v[2] = (double)f.z;
-    v[3] = (double)f.w;
+    acc[0] = acc[0] + (double)r.f.x;
+    acc[1] = acc[1] + (double)r.f.y;
+    acc[2] = acc[2] + (double)r.f.z;
+    acc[3] = acc[3] + (double)r.f.w;
   }
 }
 
 // Block means of Q (row blocks) and K (column blocks): one thread per
 // (b*H + h, block, four channels); each channel's tokens summed in ascending
-// order, one division. Four tokens' loads are in flight at a time.
+// order, one division. The sum is a chain of dependent adds, so the loads of
+// U tokens are issued together, as raw words, before they are added in order:
+// the kernel is bound by memory latency unless many loads are in flight.
+template <int DT, int U>
 __global__ void pool_mean_kernel(int64_t N, int32_t H, int32_t D, int32_t Bq, int32_t Bk,
-                                 int64_t nQ, int64_t nK, int64_t BH, int dtype, TensorArg q,
-                                 TensorArg k, double* __restrict__ qbar,
-                                 double* __restrict__ kbar) {
+                                 int64_t nQ, int64_t nK, int64_t BH, TensorArg q, TensorArg k,
+                                 double* __restrict__ qbar, double* __restrict__ kbar) {
   const int32_t D4 = D / 4;
   const int64_t per = (nQ + nK) * D4;
   const int64_t total = BH * per;
@@ -114,21 +131,14 @@ __global__ void pool_mean_kernel(int64_t N, int32_t H, int32_t D, int32_t Bq, in
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
     const int64_t base = b * in.sb + h * in.sh + x;
     int64_t i = i0;
-    for (; i + 4 <= i1; i += 4) {
-      double v[4][4];
+    for (; i + U <= i1; i += U) {
+      Raw4<DT> r[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) widen4(in.ptr, dtype, base + (i + u) * in.sn, v[u]);
+      for (int u = 0; u < U; ++u) r[u] = load4<DT>(in.ptr, base + (i + u) * in.sn);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = acc[c] + v[u][c];
+      for (int u = 0; u < U; ++u) add4<DT>(acc, r[u]);
     }
-    for (; i < i1; ++i) {
-      double v[4];
-      widen4(in.ptr, dtype, base + i * in.sn, v);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c] = acc[c] + v[c];
-    }
+    for (; i < i1; ++i) add4<DT>(acc, load4<DT>(in.ptr, base + i * in.sn));
     const double n = (double)(i1 - i0);
     double* out = isq ? qbar + (bh * nQ + bi) * D : kbar + (bh * nK + bi) * D;
 #pragma unroll
@@ -141,7 +151,8 @@ __global__ void pool_mean_kernel(int64_t N, int32_t H, int32_t D, int32_t Bq, in
 // workgroup computes a 64 x 64 tile, 4 x 4 outputs per thread (rows ty + 16i,
 // columns tx + 16j), with the channels staged through LDS 16 at a time; every
 // output keeps its own sum in ascending channel order. Four outputs per
-// operand read keep LDS bandwidth off the critical path.
+// operand read keep LDS bandwidth off the critical path. The next stage's
+// operands are loaded into registers while the current one is computed.
 constexpr int kScoreThreads = 16;                    // per side of the workgroup
 constexpr int kScoreSpan = 4;                        // outputs per thread per side
 constexpr int kScoreTile = kScoreThreads * kScoreSpan;  // outputs per tile side
@@ -160,13 +171,27 @@ __global__ __launch_bounds__(kScoreThreads * kScoreThreads) void pooled_scores_k
   for (int i = 0; i < kScoreSpan; ++i)
 #pragma unroll
     for (int j = 0; j < kScoreSpan; ++j) acc[i][j] = 0.0;
+  constexpr int kPer = kScoreTile * kScoreX / (kScoreThreads * kScoreThreads);  // per thread
+  double pq[kPer], pk[kPer];
+  auto fetch = [&](int x0) {
+#pragma unroll
+    for (int s = 0; s < kPer; ++s) {
+      const int e = tid + s * kScoreThreads * kScoreThreads;
+      const int r = e / kScoreX, x = x0 + e % kScoreX;
+      pq[s] = (a0 + r < nQ && x < D) ? qbar[(bh * nQ + a0 + r) * D + x] : 0.0;
+      pk[s] = (c0 + r < nK && x < D) ? kbar[(bh * nK + c0 + r) * D + x] : 0.0;
+    }
+  };
+  fetch(0);
   for (int x0 = 0; x0 < D; x0 += kScoreX) {
-    for (int e = tid; e < kScoreTile * kScoreX; e += kScoreThreads * kScoreThreads) {
-      const int r = e / kScoreX, xx = e - r * kScoreX, x = x0 + xx;
-      qs[r][xx] = (a0 + r < nQ && x < D) ? qbar[(bh * nQ + a0 + r) * D + x] : 0.0;
-      ks[r][xx] = (c0 + r < nK && x < D) ? kbar[(bh * nK + c0 + r) * D + x] : 0.0;
+#pragma unroll
+    for (int s = 0; s < kPer; ++s) {
+      const int e = tid + s * kScoreThreads * kScoreThreads;
+      qs[e / kScoreX][e % kScoreX] = pq[s];
+      ks[e / kScoreX][e % kScoreX] = pk[s];
     }
     __syncthreads();
+    if (x0 + kScoreX < D) fetch(x0 + kScoreX);
     const int xn = min(kScoreX, D - x0);
     for (int xx = 0; xx < xn; ++xx) {
       double qv[kScoreSpan], kv[kScoreSpan];
@@ -1029,8 +1054,12 @@ hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k
   double* kbar = qbar + BH * g.nQ * g.D;
   double* S = kbar + BH * g.nK * g.D;
   const int64_t work = BH * (g.nQ + g.nK) * (g.D / 4);
-  hipLaunchKernelGGL(pool_mean_kernel, dim3(grid_for(work, 256)), dim3(256), 0, st, g.N, g.H,
-                     g.D, g.Bq, g.Bk, g.nQ, g.nK, BH, dtype, q, k, qbar, kbar);
+  if (dtype == 0)
+    hipLaunchKernelGGL((pool_mean_kernel<0, 16>), dim3(grid_for(work, 256)), dim3(256), 0, st,
+                       g.N, g.H, g.D, g.Bq, g.Bk, g.nQ, g.nK, BH, q, k, qbar, kbar);
+  else
+    hipLaunchKernelGGL((pool_mean_kernel<1, 8>), dim3(grid_for(work, 256)), dim3(256), 0, st,
+                       g.N, g.H, g.D, g.Bq, g.Bk, g.nQ, g.nK, BH, q, k, qbar, kbar);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   dim3 grid((unsigned)((g.nK + kScoreTile - 1) / kScoreTile),
