@@ -240,31 +240,29 @@ __device__ inline uint64_t order_key(double v) {
   return (b >> 63) ? ~b : (b | (1ull << 63));
 }
 
-// Order (sa, ia) before (sb, ib): higher score first, lower block index on
-// ties; index -1 pads the sort to a power of two and goes last.
-__device__ inline bool key_before(double sa, int ia, double sb, int ib) {
-  if (ib < 0) return ia >= 0;
-  if (ia < 0) return false;
-  return sa > sb || (sa == sb && ia < ib);
-}
 
 constexpr int kSelectThreads = 256;
 constexpr int kPooledMaxBlocks = 2048;  // keeps the select kernel under 64 KiB of LDS
 
-// Bitonic sort of the keys (ks[t], ki[t]), t < P, by key_before, P a power
-// of two; scores and indices in separate arrays (12 bytes of LDS traffic per
-// key access instead of a padded 16-byte record). The used waves
-// each own a contiguous segment of P / nwu keys; a stage whose pairs stay in
-// the segment runs without a workgroup barrier (a wave's LDS accesses are
-// ordered), only the stages with partner distance >= P / nwu synchronise the
-// workgroup.
-__device__ inline void sort_keys(double* ks, int32_t* ki, int P) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+// Bitonic sort of the pairs (ks[t], ki[t]), t < P, P a power of two, into
+// descending order_key of the score, ascending block index on equal keys
+// (for scores: higher score first, lower block on ties; -0 and +0 alike).
+// Padding to a power of two is key 0 with index -1, below every score's key.
+// Keys and indices in separate arrays (12 bytes of LDS traffic per access
+// instead of a padded 16-byte record); each compare-exchange is branch-free
+// (both elements written back). The used waves each own a contiguous segment
+// of P / nwu keys; a stage whose pairs stay in the segment runs without a
+// workgroup barrier (a wave's LDS accesses are ordered), only the stages with
+// partner distance >= P / nwu synchronise the workgroup.
+__device__ inline void sort_keys(uint64_t* ks, int32_t* ki, int P) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
   const int pairs = P / 2;
-  const int nwu = min(nw, max(1, pairs / 64));  // waves with pairs to order
-  const int pw = pairs / nwu;                    // pairs per used wave
-  const int seg = P / nwu;                       // keys per used wave
+  // waves with pairs to order, pairs per used wave, keys per used wave
+  const int nwu = __builtin_amdgcn_readfirstlane(min(nw, max(1, pairs / 64)));
+  const int pw = __builtin_amdgcn_readfirstlane(pairs / nwu);
+  const int seg = __builtin_amdgcn_readfirstlane(P / nwu);
   for (int kk = 2; kk <= P; kk <<= 1) {
     for (int j = kk >> 1; j > 0; j >>= 1) {
       const bool cross = j >= seg;
@@ -274,15 +272,16 @@ __device__ inline void sort_keys(double* ks, int32_t* ki, int P) {
         for (int p = w * pw + lane; p < (w + 1) * pw; p += 64) {
           const int i = ((p >> lj) << (lj + 1)) | (p & (j - 1));
           const int l = i | j;
-          const double xs = ks[i], ys = ks[l];
+          const uint64_t xs = ks[i], ys = ks[l];
           const int xi = ki[i], yi = ki[l];
           const bool up = (i & kk) == 0;
-          if (up ? key_before(ys, yi, xs, xi) : key_before(xs, xi, ys, yi)) {
-            ks[i] = ys;
-            ki[i] = yi;
-            ks[l] = xs;
-            ki[l] = xi;
-          }
+          // y belongs before x (indices are distinct except among padding)
+          const bool yfirst = ys > xs || (ys == xs && yi < xi);
+          const bool swap = up == yfirst;
+          ks[i] = swap ? ys : xs;
+          ki[i] = swap ? yi : xi;
+          ks[l] = swap ? xs : ys;
+          ki[l] = swap ? xi : yi;
         }
       }
       if (cross)
@@ -296,10 +295,24 @@ __device__ inline void sort_keys(double* ks, int32_t* ki, int P) {
 
 constexpr int kTopM = 128;  // cumulative mass: pairs sorted before a full sort is needed
 
+// Slot for this lane's item among those of the workgroup with `pred` set, in
+// no particular order: one LDS atomic per wave (on *count) instead of one per
+// item. Called by every lane of the wave.
+__device__ inline int wave_append(bool pred, int32_t* count) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t m = __builtin_amdgcn_ballot_w64(pred);
+  int base = 0;
+  if (lane == 0 && m) base = atomicAdd(count, __popcll(m));
+  base = __shfl(base, 0);
+  return base + __popcll(m & ((1ull << lane) - 1));
+}
+
 // Key of the T-th pair of the row in (score desc, index asc) order, fixed 4
 // bits at a time from the top (radix select over order_key of the scores),
 // and how many pairs with exactly that key are among the first T (taken in
-// ascending block index) and exist in all. Called by the whole workgroup.
+// ascending block index) and exist in all. Once at most 64 pairs match the
+// fixed prefix, one wave ranks those pairs' keys directly instead of running
+// the remaining passes. Called by the whole workgroup.
 struct RowCut {
   uint64_t key;
   int32_t take_eq;
@@ -309,20 +322,35 @@ __device__ inline RowCut select_kth(const double* s, int64_t nK, int T) {
   __shared__ int32_t hist[16];
   __shared__ uint64_t rs_prefix;
   __shared__ int32_t rs_want, rs_eq;
+  __shared__ uint64_t cand[64];
+  __shared__ int32_t ncand;
   const int tid = threadIdx.x, lane = tid & 63;
   if (tid == 0) {
     rs_prefix = 0;
     rs_want = T;
+    rs_eq = INT32_MAX;
   }
   for (int shift = 60; shift >= 0; shift -= 4) {
     if (tid < 16) hist[tid] = 0;
     __syncthreads();
     const uint64_t prefix = rs_prefix;
     const uint64_t pmask = shift >= 60 ? 0 : (~0ull << (shift + 4));
-    for (int64_t c = tid; c < nK; c += blockDim.x) {
-      const uint64_t u = order_key(s[c]);
-      if ((u & pmask) == prefix) atomicAdd(&hist[(int)((u >> shift) & 15)], 1);
+    // per-wave digit counts by ballot (lane d counts digit d), one LDS atomic
+    // per wave and digit: the keys crowd into few digits, where one atomic
+    // per key would serialise
+    int mycnt = 0;
+    for (int64_t c0 = 0; c0 < nK; c0 += blockDim.x) {
+      const int64_t c = c0 + tid;
+      const uint64_t u = c < nK ? order_key(s[c]) : 0;
+      const bool match = c < nK && (u & pmask) == prefix;
+      const int dig = (int)((u >> shift) & 15);
+#pragma unroll
+      for (int d = 0; d < 16; ++d) {
+        const int n = __popcll(__builtin_amdgcn_ballot_w64(match && dig == d));
+        mycnt += lane == d ? n : 0;
+      }
     }
+    if (lane < 16 && mycnt) atomicAdd(&hist[lane], mycnt);
     __syncthreads();
     if (tid < 64) {
       // the highest bucket b whose count from the top (buckets b .. 15)
@@ -340,8 +368,87 @@ __device__ inline RowCut select_kth(const double* s, int64_t nK, int T) {
       }
     }
     __syncthreads();
+    if (shift > 0 && rs_eq <= 64) {
+      // the pairs left: key bits above shift equal to the prefix
+      const uint64_t pm = ~0ull << shift, pre = rs_prefix;
+      if (tid == 0) ncand = 0;
+      __syncthreads();
+      for (int64_t c0 = 0; c0 < nK; c0 += blockDim.x) {
+        const int64_t c = c0 + tid;
+        const uint64_t u = c < nK ? order_key(s[c]) : 0;
+        const bool hit = c < nK && (u & pm) == pre;
+        const int pos = wave_append(hit, &ncand);
+        if (hit) cand[pos] = u;
+      }
+      __syncthreads();
+      if (tid < 64) {
+        // the want-th largest key among them, its multiplicity and how many
+        // of its pairs are wanted
+        const int m = ncand, want = rs_want;
+        const uint64_t mine = lane < m ? cand[lane] : 0;
+        int above = 0, same = 0;
+        for (int j = 0; j < m; ++j) {
+          const uint64_t o = cand[j];
+          above += o > mine;
+          same += o == mine;
+        }
+        const bool hit = lane < m && above < want && want <= above + same;
+        const uint64_t hm = __builtin_amdgcn_ballot_w64(hit);
+        if (lane == __builtin_ctzll(hm)) {
+          rs_prefix = mine;
+          rs_want = want - above;
+          rs_eq = same;
+        }
+      }
+      __syncthreads();
+      break;
+    }
   }
   return RowCut{rs_prefix, rs_want, rs_eq};
+}
+
+// Called by the first wave. Walks the probabilities pv[0..n) of a row in
+// sorted order, adding them to a running sum one at a time in that order (the
+// rounding of a loop on one thread); entry t (block idx[t]) gets level
+// #{l < nl : sum before t >= tau_l} (entry 0 level 0) and is flagged 1 +
+// level when that is below nl. The sums form one chain of adds without a
+// branch; lane u keeps the sum before entry c0 + u of each 16-entry chunk, and
+// the levels are set in parallel. Stops after the chunk in which the sum
+// reaches tau_{nl-1} (every later entry is dropped); returns whether it did.
+// The thresholds are non-decreasing; nl is 1..3.
+__device__ inline bool walk_mass(const double* pv, const int32_t* idx, int64_t n, double tau0,
+                                 double tau1, double tau2, int nl, uint8_t* flag) {
+  const int lane = threadIdx.x & 63;
+  const double last = nl == 1 ? tau0 : (nl == 2 ? tau1 : tau2);
+  double run = 0.0;
+  for (int64_t c0 = 0; c0 < n; c0 += 16) {
+    const int m = (int)min((int64_t)16, n - c0);
+    double v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = pv[c0 + min(u, m - 1)];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (u >= m) v[u] = 0.0;  // run + 0 = run: the sum is >= +0
+    // the chain first (each intermediate sum in its own register), the
+    // lane's pick afterwards, so that no select waits inside the chain
+    double pre[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      pre[u] = run;
+      run = run + v[u];
+    }
+    double ex = pre[0];
+#pragma unroll
+    for (int u = 1; u < 16; ++u) ex = lane == u ? pre[u] : ex;
+    if (lane < m) {
+      int lvl = 0;
+      if (c0 + lane > 0)
+        lvl = (ex >= tau0 ? 1 : 0) + (nl > 1 && ex >= tau1 ? 1 : 0) + (nl > 2 && ex >= tau2 ? 1 : 0);
+      if (lvl < nl) flag[idx[c0 + lane]] = (uint8_t)(1 + lvl);
+    }
+    if (run >= last) return true;
+  }
+  return false;
 }
 
 // One workgroup per (b, h, a): sort of the row's blocks by (score desc, index
@@ -381,20 +488,25 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
           mrow[c] = order_key(s[c]) >= cut.key ? 1 : 0;
         return;
       }
-      __shared__ double cs[kTopM];
+      __shared__ uint64_t ck[kTopM];  // sort keys, then the probabilities
       __shared__ int32_t ci[kTopM];
       __shared__ int32_t ncand;
+      double* cs = (double*)ck;
       if (threadIdx.x == 0) ncand = 0;
       __syncthreads();
-      for (int c = threadIdx.x; c < nK; c += blockDim.x)
-        if (order_key(s[c]) >= cut.key) {
-          const int pos = atomicAdd(&ncand, 1);
-          cs[pos] = s[c];
+      for (int64_t c0 = 0; c0 < nK; c0 += blockDim.x) {
+        const int c = (int)(c0 + threadIdx.x);
+        const uint64_t u = c < nK ? order_key(s[c]) : 0;
+        const bool hit = c < nK && u >= cut.key;
+        const int pos = wave_append(hit, &ncand);
+        if (hit) {
+          ck[pos] = u;
           ci[pos] = c;
         }
+      }
       __syncthreads();
-      sort_keys(cs, ci, kTopM);
-      const double smax0 = cs[0];
+      sort_keys(ck, ci, kTopM);
+      const double smax0 = s[ci[0]];
       for (int c = threadIdx.x; c < nK; c += blockDim.x) ks[c] = exp(s[c] - smax0);
       __syncthreads();
       if (threadIdx.x < 64) {
@@ -405,45 +517,34 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
       const double Z0 = z_sh;
       for (int t = threadIdx.x; t < kTopM; t += blockDim.x) cs[t] = ks[ci[t]] / Z0;
       __syncthreads();
+      // flags of the first kTopM pairs; if the mass is not reached there,
+      // they are a subset of what the full sort below keeps
       if (threadIdx.x < 64) {
-        int32_t kp = -1;  // not reached within the first kTopM pairs
-        double run = 0.0;
-        for (int t0 = 0; t0 < kTopM && kp < 0; t0 += 16) {
-          double v[16];
-#pragma unroll
-          for (int u = 0; u < 16; ++u) v[u] = cs[t0 + u];
-#pragma unroll
-          for (int u = 0; u < 16; ++u) {
-            if (kp < 0) {
-              run = run + v[u];
-              if (run >= param) kp = t0 + u + 1;
-            }
-          }
-        }
-        if (threadIdx.x == 0) keep_sh = kp;
+        const bool reached = walk_mass(cs, ci, kTopM, param, param, param, 1, flag);
+        if (threadIdx.x == 0) keep_sh = reached ? 1 : 0;
       }
       __syncthreads();
-      const int32_t kp = keep_sh;
-      if (kp > 0) {
-        for (int t = threadIdx.x; t < kp; t += blockDim.x) flag[ci[t]] = 1;
-        __syncthreads();
+      if (keep_sh) {
         for (int c = threadIdx.x; c < nK; c += blockDim.x) mrow[c] = flag[c];
         return;
       }
     }
   }
+  uint64_t* kk = (uint64_t*)ks;  // sort keys, then the probabilities in ks
   for (int c = threadIdx.x; c < P; c += blockDim.x) {
-    ks[c] = c < nK ? s[c] : 0.0;
+    kk[c] = c < nK ? order_key(s[c]) : 0;
     ki[c] = c < nK ? c : -1;
   }
   __syncthreads();
-  sort_keys(ks, ki, P);
-  const double smax = ks[0];
+  sort_keys(kk, ki, P);
+  const double smax = s[ki[0]];
   int32_t keep;
   if (mode == 0) {
     keep = (int32_t)min((double)nK, param);
   } else {
-    // e = exp(S - max) in block order, over the scores
+    // e = exp(S - max) in block order, over the scores (once every thread
+    // has read the maximum from them)
+    __syncthreads();
     for (int c = threadIdx.x; c < nK; c += blockDim.x) s[c] = exp(s[c] - smax);
     __syncthreads();
     if (threadIdx.x < 64) {
@@ -456,58 +557,14 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
     // sorted scores are not needed any more
     for (int t = threadIdx.x; t < nK; t += blockDim.x) ks[t] = s[ki[t]] / Z;
     __syncthreads();
+    // mode 1: the shortest prefix whose running mass reaches tau_p (entry t
+    // kept while the mass before it is below tau_p); mode 4, pyramid levels
+    // ([PSA]: a resolution level per block pair by importance thresholds):
+    // a block joins the current level, and the level advances past every
+    // threshold that the running mass including that block has reached
     keep = 0;
-    if (threadIdx.x < 64) {
-      const int lane = threadIdx.x;
-      double run = 0.0;
-      if (mode == 4) {
-        // pyramid levels ([PSA]: a resolution level per block pair by
-        // importance thresholds): walk the order accumulating the row
-        // softmax mass; a block joins the current level, and the level
-        // advances past every threshold the running sum (including that
-        // block) has reached.
-        auto tau_at = [&](int l) { return l == 0 ? param : (l == 1 ? tau1 : tau2); };
-        int lvl = 0;
-        for (int64_t c0 = 0; c0 < nK && lvl < n_levels; c0 += 16) {
-          const int m = (int)min((int64_t)16, nK - c0);
-          double v[16];
-#pragma unroll
-          for (int u = 0; u < 16; ++u) v[u] = ks[c0 + min(u, m - 1)];  // u >= m unused
-          int my_lvl = -1;  // lane u < 16 records the level of entry c0 + u
-#pragma unroll
-          for (int u = 0; u < 16; ++u) {
-            if (u < m && lvl < n_levels) {
-              if (lane == u) my_lvl = lvl;
-              run = run + v[u];
-              while (lvl < n_levels && run >= tau_at(lvl)) ++lvl;
-            }
-          }
-          if (my_lvl >= 0) flag[ki[c0 + lane]] = (uint8_t)(1 + my_lvl);
-        }
-      } else {
-        int32_t kp = (int32_t)nK;
-        bool done = false;
-        for (int64_t c0 = 0; c0 < nK && !done; c0 += 16) {
-          const int m = (int)min((int64_t)16, nK - c0);
-          double v[16];
-#pragma unroll
-          for (int u = 0; u < 16; ++u) v[u] = ks[c0 + min(u, m - 1)];  // u >= m unused
-#pragma unroll
-          for (int u = 0; u < 16; ++u) {
-            if (!done && u < m) {
-              run = run + v[u];
-              if (run >= param) {
-                kp = (int32_t)(c0 + u + 1);
-                done = true;
-              }
-            }
-          }
-        }
-        if (lane == 0) keep_sh = kp;
-      }
-    }
+    if (threadIdx.x < 64) walk_mass(ks, ki, nK, param, tau1, tau2, mode == 4 ? n_levels : 1, flag);
     __syncthreads();
-    if (mode != 4) keep = keep_sh;
   }
   for (int t = threadIdx.x; t < keep; t += blockDim.x) flag[ki[t]] = 1;
   __syncthreads();
