@@ -68,6 +68,26 @@ def test_pooled_mask_long_rows_bit_exact(mode, param):
     np.testing.assert_array_equal(got, ref)
 
 
+@pytest.mark.parametrize("mode,param", [(0, 77.0), (0, 300.0), (1, 0.3), (1, 0.95)])
+def test_pooled_mask_long_rows_ties_bit_exact(mode, param):
+    """Rows of 400 key blocks in which the keys repeat every seven blocks, so
+    every score comes in a tie group of 57 or 58 blocks: the k-th or 128th
+    pair of a row falls inside a tie group, the radix select ends with equal
+    keys among its last candidates, and the long-row paths must fall back
+    to the full sort that takes tied blocks in ascending order."""
+    w = synth.Workload("pooled_ties_long", 1, 2, 64, 25, 32, 32, 128, 64, "bf16", "pooled", 614,
+                       True)
+    x = synth.make_qkv(w)
+    k = x["k"].reshape(w.B, w.nK, w.Bk, w.H, w.d)
+    x["k"] = np.ascontiguousarray(k[:, np.arange(w.nK) % 7].reshape(x["k"].shape))
+    got = _pooled_gpu(w, x, mode, param)
+    ref, S, _ = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, mode, param,
+                                         want_scores=True)
+    assert np.all(S[..., 7:] == S[..., :-7])   # scores repeat with the keys
+    note(f"pooled tied long rows mode={mode} param={param}: {int(ref.sum())} kept")
+    np.testing.assert_array_equal(got, ref)
+
+
 def test_pooled_mask_wan13b_480p_full():
     w = synth.workload("wan13b_480p")
     note(f"{w.name}: generating inputs")
