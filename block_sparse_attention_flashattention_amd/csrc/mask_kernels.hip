@@ -421,14 +421,17 @@ __device__ inline bool walk_mass(const double* pv, const int32_t* idx, int64_t n
   const int lane = threadIdx.x & 63;
   const double last = nl == 1 ? tau0 : (nl == 2 ? tau1 : tau2);
   double run = 0.0;
-  for (int64_t c0 = 0; c0 < n; c0 += 16) {
-    const int m = (int)min((int64_t)16, n - c0);
+  for (int c0 = 0; c0 < (int)n; c0 += 16) {
+    const int m = min(16, (int)n - c0);
     double v[16];
+    if (m == 16) {  // a whole chunk: contiguous reads
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = pv[c0 + min(u, m - 1)];
+      for (int u = 0; u < 16; ++u) v[u] = pv[c0 + u];
+    } else {
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (u >= m) v[u] = 0.0;  // run + 0 = run: the sum is >= +0
+      for (int u = 0; u < 16; ++u) v[u] = u < m ? pv[c0 + min(u, m - 1)] : 0.0;
+    }
+    // (entries past n add 0: run + 0 = run, the sum being >= +0)
     // the chain first (each intermediate sum in its own register), the
     // lane's pick afterwards, so that no select waits inside the chain
     double pre[16];
