@@ -645,6 +645,7 @@ struct HeadCut {
 constexpr int kGselThreads = 256;
 constexpr int kGselGroups = 32;  // workgroups per head in a histogram pass
 constexpr int kGselFullPasses = 4;  // passes over every pair; the fifth keeps the candidates
+constexpr int kGselBatch = 8;       // pairs per thread whose loads are issued together
 
 // Per-thread capacity of the candidate store: thread t of a group visits at
 // most ceil(per / kGselThreads) pairs.
@@ -705,18 +706,34 @@ __global__ __launch_bounds__(kGselThreads) void gsel_hist_kernel(
   // candidate slice of this thread: entries cbase + j * kGselThreads
   const int64_t cbase = (bh * kGselGroups + g) * gsel_cand_cap(n) * kGselThreads + tid;
   int32_t* my_cnt = ccnt + (bh * kGselGroups + g) * kGselThreads + tid;
+  // Each thread's pairs are handled in its fixed visiting order; their keys
+  // (and masses) are loaded kGselBatch at a time before they are counted, so
+  // that the loads are in flight together instead of one memory latency per
+  // pair.
   if (phase < 2) {
     int32_t j = 0;
-    for (int64_t e = e0 + tid; e < e1; e += kGselThreads) {
-      const uint64_t u = order_key(keys[e]);
-      if ((u & pmask) != c.prefix) continue;
-      const int b = (int)((u >> shift) & 15);
-      hc[b][tid] += 1;
-      if (mode == 3) hm[b][tid] = hm[b][tid] + mass[e];
-      if (phase == 1) {
-        ck[cbase + (int64_t)j * kGselThreads] = u;
-        if (mode == 3) cm[cbase + (int64_t)j * kGselThreads] = mass[e];
-        ++j;
+    for (int64_t eb = e0 + tid; eb < e1; eb += (int64_t)kGselBatch * kGselThreads) {
+      uint64_t ub[kGselBatch];
+      double mb[kGselBatch];
+#pragma unroll
+      for (int i = 0; i < kGselBatch; ++i) {
+        const int64_t e = eb + (int64_t)i * kGselThreads;
+        ub[i] = e < e1 ? order_key(keys[e]) : 0;
+        mb[i] = (mode == 3 && e < e1) ? mass[e] : 0.0;
+      }
+#pragma unroll
+      for (int i = 0; i < kGselBatch; ++i) {
+        const int64_t e = eb + (int64_t)i * kGselThreads;
+        const uint64_t u = ub[i];
+        if (e >= e1 || (u & pmask) != c.prefix) continue;
+        const int b = (int)((u >> shift) & 15);
+        hc[b][tid] += 1;
+        if (mode == 3) hm[b][tid] = hm[b][tid] + mb[i];
+        if (phase == 1) {
+          ck[cbase + (int64_t)j * kGselThreads] = u;
+          if (mode == 3) cm[cbase + (int64_t)j * kGselThreads] = mb[i];
+          ++j;
+        }
       }
     }
     if (phase == 1) *my_cnt = j;
@@ -724,21 +741,29 @@ __global__ __launch_bounds__(kGselThreads) void gsel_hist_kernel(
     // the candidates still matching move down in place (slot jn <= j)
     const int32_t m = *my_cnt;
     int32_t jn = 0;
-    for (int32_t j = 0; j < m; ++j) {
-      const uint64_t u = ck[cbase + (int64_t)j * kGselThreads];
-      if ((u & pmask) != c.prefix) continue;
-      const int b = (int)((u >> shift) & 15);
-      hc[b][tid] += 1;
-      double ms = 0.0;
-      if (mode == 3) {
-        ms = cm[cbase + (int64_t)j * kGselThreads];
-        hm[b][tid] = hm[b][tid] + ms;
+    for (int32_t jb = 0; jb < m; jb += kGselBatch) {
+      uint64_t ub[kGselBatch];
+      double mb[kGselBatch];
+#pragma unroll
+      for (int i = 0; i < kGselBatch; ++i) {
+        const int64_t slot = cbase + (int64_t)(jb + i) * kGselThreads;
+        ub[i] = jb + i < m ? ck[slot] : 0;
+        mb[i] = (mode == 3 && jb + i < m) ? cm[slot] : 0.0;
       }
-      if (jn != j) {
-        ck[cbase + (int64_t)jn * kGselThreads] = u;
-        if (mode == 3) cm[cbase + (int64_t)jn * kGselThreads] = ms;
+#pragma unroll
+      for (int i = 0; i < kGselBatch; ++i) {
+        const int32_t j = jb + i;
+        const uint64_t u = ub[i];
+        if (j >= m || (u & pmask) != c.prefix) continue;
+        const int b = (int)((u >> shift) & 15);
+        hc[b][tid] += 1;
+        if (mode == 3) hm[b][tid] = hm[b][tid] + mb[i];
+        if (jn != j) {
+          ck[cbase + (int64_t)jn * kGselThreads] = u;
+          if (mode == 3) cm[cbase + (int64_t)jn * kGselThreads] = mb[i];
+        }
+        ++jn;
       }
-      ++jn;
     }
     *my_cnt = jn;
   }
