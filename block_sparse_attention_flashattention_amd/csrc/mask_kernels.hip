@@ -768,12 +768,14 @@ __global__ __launch_bounds__(kGselThreads) void gsel_hist_kernel(
     *my_cnt = jn;
   }
   __syncthreads();
+  // slot i += slot i + off for every bucket, off halving: the fixed tree of
+  // sums, its 16 * off additions of a level spread over all threads
   for (int off = kGselThreads / 2; off >= 1; off >>= 1) {
-    if (tid < off)
-      for (int b = 0; b < 16; ++b) {
-        hc[b][tid] += hc[b][tid + off];
-        hm[b][tid] = hm[b][tid] + hm[b][tid + off];
-      }
+    for (int idx = tid; idx < 16 * off; idx += kGselThreads) {
+      const int b = idx / off, i = idx - b * off;
+      hc[b][i] += hc[b][i + off];
+      hm[b][i] = hm[b][i] + hm[b][i + off];
+    }
     __syncthreads();
   }
   __shared__ int is_last;
