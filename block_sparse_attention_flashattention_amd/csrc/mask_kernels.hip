@@ -295,6 +295,53 @@ __device__ inline void sort_keys(uint64_t* ks, int32_t* ki, int P) {
 
 constexpr int kTopM = 128;  // cumulative mass: pairs sorted before a full sort is needed
 
+// The same bitonic network as sort_keys for kTopM = 128 pairs, run by one
+// wave in registers: element e sits in lane e % 64, register e / 64;
+// partners at distance 64 are the lane's two registers, closer ones come
+// from lane ^ j by a cross-lane shuffle, so no stage waits on LDS. Reads the
+// pairs from (ks, ki) and writes them back sorted; called by the first wave.
+__device__ inline void sort128_wave(uint64_t* ks, int32_t* ki) {
+  const int lane = threadIdx.x & 63;
+  uint64_t k[2] = {ks[lane], ks[lane + 64]};
+  int32_t x[2] = {ki[lane], ki[lane + 64]};
+  for (int kk = 2; kk <= 128; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      if (j == 64) {
+        // elements lane (lower) and lane + 64 of this lane; kk = 128, so the
+        // lower position takes the element that comes first
+        const bool first0 = k[0] > k[1] || (k[0] == k[1] && x[0] < x[1]);
+        if (!first0) {
+          const uint64_t kt = k[0];
+          const int32_t xt = x[0];
+          k[0] = k[1];
+          x[0] = x[1];
+          k[1] = kt;
+          x[1] = xt;
+        }
+        continue;
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int e = r * 64 + lane;
+        const uint32_t lo = __shfl_xor((uint32_t)k[r], j);
+        const uint32_t hi = __shfl_xor((uint32_t)(k[r] >> 32), j);
+        const uint64_t ko = ((uint64_t)hi << 32) | lo;
+        const int32_t xo = __shfl_xor(x[r], j);
+        const bool lower = (e & j) == 0, up = (e & kk) == 0;
+        const bool mine_first = k[r] > ko || (k[r] == ko && x[r] < xo);
+        // the lower position of an ascending pair holds the first element
+        const bool keep = (lower == up) == mine_first;
+        k[r] = keep ? k[r] : ko;
+        x[r] = keep ? x[r] : xo;
+      }
+    }
+  }
+  ks[lane] = k[0];
+  ki[lane] = x[0];
+  ks[lane + 64] = k[1];
+  ki[lane + 64] = x[1];
+}
+
 // Slot for this lane's item among those of the workgroup with `pred` set, in
 // no particular order: one LDS atomic per wave (on *count) instead of one per
 // item. Called by every lane of the wave.
@@ -508,7 +555,8 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
         }
       }
       __syncthreads();
-      sort_keys(ck, ci, kTopM);
+      if (threadIdx.x < 64) sort128_wave(ck, ci);
+      __syncthreads();
       const double smax0 = s[ci[0]];
       for (int c = threadIdx.x; c < nK; c += blockDim.x) ks[c] = exp(s[c] - smax0);
       __syncthreads();
