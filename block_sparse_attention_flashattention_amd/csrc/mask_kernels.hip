@@ -377,9 +377,9 @@ __device__ inline RowCut select_kth(const double* s, int64_t nK, int T) {
     rs_want = T;
     rs_eq = INT32_MAX;
   }
+  if (tid < 16) hist[tid] = 0;
+  __syncthreads();
   for (int shift = 60; shift >= 0; shift -= 4) {
-    if (tid < 16) hist[tid] = 0;
-    __syncthreads();
     const uint64_t prefix = rs_prefix;
     const uint64_t pmask = shift >= 60 ? 0 : (~0ull << (shift + 4));
     // per-wave digit counts by ballot (lane d counts digit d), one LDS atomic
@@ -413,6 +413,9 @@ __device__ inline RowCut select_kth(const double* s, int64_t nK, int T) {
         rs_want = want - (sfx - hist[b]);
         rs_eq = hist[b];
       }
+      // cleared for the next pass once this wave has read it (a wave's LDS
+      // accesses are ordered); the barrier below publishes it
+      if (lane < 16) hist[lane] = 0;
     }
     __syncthreads();
     if (shift > 0 && rs_eq <= 64) {
