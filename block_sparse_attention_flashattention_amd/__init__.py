@@ -20,7 +20,7 @@ __all__ = [
     "bsa_update_skip_mask", "ORDER_ASCENDING", "ORDER_RADIAL",
     "bsa_make_token_permutation", "bsa_permute_tokens", "PERM_AXES", "PERM_BOXES",
     "bsa_pyramid_rows", "bsa_build_kv_pyramid", "bsa_build_mask_pyramid",
-    "bsa_compact_pyramid_lists", "bsa_pyramid_attn_fwd",
+    "bsa_compact_pyramid_lists", "bsa_pyramid_attn_fwd", "bsa_check_block_lists",
     "bsa_status_string", "bsa_last_error",
 ]
 
@@ -99,6 +99,7 @@ def lib() -> C.CDLL:
             "bsa_sparse_attn_fwd": (i32, [SP, i32, Tensor, Tensor, Tensor, Tensor, p, p, p, i32,
                                           f32, p, p]),
             "bsa_update_skip_mask": (i32, [SP, p, p, p, f32, p, p]),
+            "bsa_check_block_lists": (i32, [SP, i32, p, p, i64, i64, i32, i32, p]),
             "bsa_status_string": (C.c_char_p, [i32]),
             "bsa_last_error": (C.c_char_p, []),
         }
@@ -267,3 +268,24 @@ def bsa_update_skip_mask(s: Shape, row_ptr, kv_idx, tile_gap, tau: float, skip, 
     _check("bsa_update_skip_mask",
            lib().bsa_update_skip_mask(C.byref(s), _ptr(row_ptr), _ptr(kv_idx), _ptr(tile_gap),
                                       tau, _ptr(skip), _stream(stream)))
+
+
+def bsa_check_block_lists(s: Shape, lists_shared: int, row_ptr, kv_idx, n_blocks: int = 0,
+                          ascending: bool = False, kv_len: int | None = None, stream=None):
+    """Debug check of block lists. numpy int32 arrays are checked on the host,
+    torch tensors on the device they live on (the call then synchronises)."""
+    import numpy as np
+    on_device = not isinstance(row_ptr, np.ndarray)
+    if on_device:
+        rp, kv = _ptr(row_ptr), _ptr(kv_idx)
+        n = kv_idx.numel() if kv_idx is not None else 0
+        st = _stream(stream)
+    else:
+        row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+        kv_idx = np.ascontiguousarray(kv_idx if kv_idx is not None else [], dtype=np.int32)
+        rp, kv = row_ptr.ctypes.data, kv_idx.ctypes.data
+        n, st = kv_idx.size, None
+    _check("bsa_check_block_lists",
+           lib().bsa_check_block_lists(C.byref(s), lists_shared, rp, kv,
+                                       n if kv_len is None else kv_len, n_blocks,
+                                       1 if ascending else 0, 1 if on_device else 0, st))

@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libbsa.so")
 
 ARCH = "gfx950"
 SOURCES = ["api.cpp", "mask_kernels.hip", "attn_bf16.hip", "attn_f32.hip", "permute_kernels.hip",
-           "pyramid_kernels.hip"]
+           "pyramid_kernels.hip", "list_check.hip"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-fvisibility=hidden",
           # packed fp32 VALU forms are kept out of every kernel

@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "bsa.h"
@@ -82,6 +83,40 @@ bsa_status check_tensor(const char* name, const bsa_tensor& t, int elem_bytes) {
 bsa::TensorArg arg(const bsa_tensor& t) { return {t.ptr, t.stride_b, t.stride_n, t.stride_h}; }
 
 int elem_bytes(bsa_dtype dt) { return dt == BSA_BF16 ? 2 : 4; }
+
+const char* rule_text(int rule) {
+  switch (rule) {
+    case 1: return "row_ptr[0] is not 0";
+    case 2: return "row_ptr decreases";
+    case 3: return "row_ptr beyond kv_len";
+    case 4: return "entry outside the key blocks";
+    case 5: return "entry repeated in the row";
+    case 6: return "row not in ascending order";
+  }
+  return "?";
+}
+
+bsa_status list_result(int64_t row, int rule) {
+  if (rule == 0) return ok();
+  return fail(BSA_ERR_INVALID, "block lists, row %lld: rule %d (%s)", (long long)row, rule,
+              rule_text(rule));
+}
+
+// Lists of a consuming call, checked on the device when BSA_CHECK=1.
+bsa_status debug_check(const bsa::Geom& g, bool shared, const int32_t* row_ptr,
+                       const int32_t* kv_idx, int64_t n_blocks, bool ascending,
+                       hipStream_t st) {
+  const char* env = getenv("BSA_CHECK");
+  if (!env || strcmp(env, "1") != 0 || !row_ptr) return BSA_OK;
+  const int64_t R = shared ? g.nQ : (int64_t)g.B * g.H * g.nQ;
+  if (R == 0) return BSA_OK;
+  int rule = 0;
+  int64_t row = -1;
+  hipError_t e = bsa::check_lists_device(row_ptr, kv_idx, R, -1, n_blocks, ascending, &rule, &row,
+                                         st);
+  if (e != hipSuccess) return device(e, "block list check");
+  return list_result(row, rule);
+}
 
 }  // namespace
 
@@ -214,6 +249,9 @@ bsa_status bsa_order_block_lists(const bsa_shape* s, int32_t order, const int32_
   if (!row_ptr || !kv_in || !kv_out)
     return fail(BSA_ERR_INVALID, "row_ptr, kv_in and kv_out are required");
   if (kv_in == kv_out) return fail(BSA_ERR_INVALID, "kv_out must not alias kv_in");
+  if ((st = debug_check(g, lists_shared, row_ptr, kv_in, g.nK, true, (hipStream_t)stream)) !=
+      BSA_OK)
+    return st;
   return device(bsa::launch_order_lists(g, R, order, row_ptr, kv_in, kv_out, (hipStream_t)stream),
                 "list order launch");
 }
@@ -434,6 +472,9 @@ bsa_status bsa_pyramid_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, 
   a.vp = n_levels > 1 ? arg(v_pyr) : arg(v);
   a.kv_quarters = kv_quarters;
   pyramid_regions(g, n_levels, a.pyr_rb);
+  if ((st = debug_check(g, false, row_ptr, kv_idx, a.pyr_rb[n_levels], false,
+                        (hipStream_t)stream)) != BSA_OK)
+    return st;
   return device(bsa::launch_attn_bf16(g, a, (hipStream_t)stream), "pyramid attention launch");
 }
 
@@ -452,6 +493,9 @@ bsa_status bsa_sparse_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, b
   if ((row_ptr == nullptr) != (kv_idx == nullptr))
     return fail(BSA_ERR_INVALID, "row_ptr and kv_idx must both be set or both be NULL");
   if (tile_gap && !row_ptr) return fail(BSA_ERR_INVALID, "tile_gap needs block lists");
+  // Gaps feed bsa_update_skip_mask, which reads per-head lists only.
+  if (tile_gap && lists_shared)
+    return fail(BSA_ERR_UNSUPPORTED, "tile_gap needs per-head lists (lists_shared = 0)");
   if (empty(g)) return ok();
   const int eb = elem_bytes(dt);
   if ((st = check_tensor("q", q, eb)) != BSA_OK) return st;
@@ -477,6 +521,7 @@ bsa_status bsa_sparse_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, b
   a.scale = scale;
   a.tile_gap = tile_gap;
   hipStream_t str = (hipStream_t)stream;
+  if ((st = debug_check(g, lists_shared, row_ptr, kv_idx, g.nK, false, str)) != BSA_OK) return st;
   return device(dt == BSA_BF16 ? bsa::launch_attn_bf16(g, a, str) : bsa::launch_attn_f32(g, a, str),
                 "attention launch");
 }
@@ -494,9 +539,38 @@ bsa_status bsa_update_skip_mask(const bsa_shape* s, const int32_t* row_ptr,
   if (!row_ptr || !kv_idx || !tile_gap || !skip)
     return fail(BSA_ERR_INVALID, "row_ptr, kv_idx, tile_gap and skip are required");
   const float tau2 = (float)((double)tau * 1.4426950408889634);
+  if ((st = debug_check(g, false, row_ptr, kv_idx, g.nK, false, (hipStream_t)stream)) != BSA_OK)
+    return st;
   return device(bsa::launch_skip_update(g, row_ptr, kv_idx, tile_gap, tau2, skip,
                                         (hipStream_t)stream),
                 "skip update launch");
+}
+
+bsa_status bsa_check_block_lists(const bsa_shape* s, int32_t lists_shared,
+                                 const int32_t* row_ptr, const int32_t* kv_idx, int64_t kv_len,
+                                 int64_t n_blocks, int32_t ascending, int32_t on_device,
+                                 void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  if (lists_shared != 0 && lists_shared != 1)
+    return fail(BSA_ERR_INVALID, "lists_shared must be 0 or 1");
+  if (on_device != 0 && on_device != 1) return fail(BSA_ERR_INVALID, "on_device must be 0 or 1");
+  if (kv_len < 0 || n_blocks < 0) return fail(BSA_ERR_INVALID, "kv_len and n_blocks must be >= 0");
+  if (!row_ptr) return fail(BSA_ERR_INVALID, "row_ptr is NULL");
+  if (!kv_idx && kv_len > 0) return fail(BSA_ERR_INVALID, "kv_idx is NULL");
+  const int64_t R = lists_shared ? g.nQ : (int64_t)g.B * g.H * g.nQ;
+  const int64_t nb = n_blocks ? n_blocks : g.nK;
+  int rule = 0;
+  int64_t row = -1;
+  if (!on_device) {
+    row = bsa::check_lists_host(row_ptr, kv_idx, R, kv_len, nb, ascending != 0, &rule);
+    return list_result(row, rule);
+  }
+  hipError_t e = bsa::check_lists_device(row_ptr, kv_idx, R, kv_len, nb, ascending != 0, &rule,
+                                         &row, (hipStream_t)stream);
+  if (e != hipSuccess) return device(e, "block list check");
+  return list_result(row, rule);
 }
 
 }  // extern "C"

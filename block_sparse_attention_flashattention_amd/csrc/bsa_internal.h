@@ -56,6 +56,15 @@ hipError_t launch_skip_update(const Geom& g, const int32_t* row_ptr, const int32
                               const float* tile_gap, float tau2, uint8_t* skip,
                               hipStream_t st);
 
+// ---- debug checks of block lists (list_check.hip). Both return the first
+// failing row (or -1) and its rule in *rule (0 = none). kv_len < 0 on the
+// device takes row_ptr[R] as the length of kv.
+int64_t check_lists_host(const int32_t* row_ptr, const int32_t* kv, int64_t R, int64_t kv_len,
+                         int64_t n_blocks, bool ascending, int* rule);
+hipError_t check_lists_device(const int32_t* row_ptr, const int32_t* kv, int64_t R,
+                              int64_t kv_len, int64_t n_blocks, bool ascending, int* rule,
+                              int64_t* row, hipStream_t st);
+
 // ---- token orders (permute_kernels.hip)
 hipError_t launch_make_permutation(const Geom& g, int32_t kind, const int32_t* axes,
                                    int32_t* perm, hipStream_t st);

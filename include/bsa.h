@@ -253,8 +253,9 @@ BSA_API bsa_status bsa_permute_tokens(const bsa_shape* s, bsa_dtype dt, const in
  *               means every tile (dense attention)
  *   lists_shared 1: one list row per a for every (b, h) (row_ptr [nQ+1]);
  *               0: row_ptr [B*H*nQ+1]
- *   tile_gap    nullable, out fp32, one value per list entry (per (b, h) and
- *               list entry when lists_shared: index (b*H + h)*nnz + e):
+ *   tile_gap    nullable, out fp32, one value per list entry; needs
+ *               per-head lists (lists_shared = 0, else BSA_ERR_UNSUPPORTED),
+ *               the lists bsa_update_skip_mask reads:
  *               with the listed tiles of a row visited in list order and
  *               m_run(r) the running maximum of row r's scaled scores over
  *               the tiles visited before, the maximum over valid rows r of
@@ -359,6 +360,34 @@ BSA_API bsa_status bsa_pyramid_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_te
                                 bsa_tensor v_pyr, int32_t n_levels, bsa_tensor o, float* lse,
                                 const int32_t* row_ptr, const int32_t* kv_idx,
                                 const int32_t* kv_quarters, float scale, void* stream);
+
+/*
+ * Debug check of block lists ([Lite] sections 三 and 六: the forward walks only
+ * the listed tiles, so a row must name each of its kept key blocks once, and
+ * only blocks that exist). Rules, reported for the first failing row r
+ * (lowest r, then lowest rule):
+ *   1 row_ptr[0] != 0;  2 row_ptr[r+1] < row_ptr[r];  3 row_ptr[r+1] > kv_len;
+ *   4 an entry outside [0, n_blocks);  5 an entry twice in one row;
+ *   6 (ascending = 1 only) a row not in strictly ascending order.
+ *   lists_shared  1: R = nQ list rows; 0: R = B*H*nQ
+ *   n_blocks      key blocks an entry may name (0 = nK; for pyramid lists
+ *                 the number of augmented blocks)
+ *   kv_len        entries of kv_idx that may be read (>= 0)
+ *   on_device     0: row_ptr and kv_idx are HOST pointers, checked on the
+ *                 calling thread (stream unused); 1: DEVICE pointers, checked
+ *                 by kernels on `stream`; the call then synchronises stream
+ * Reads only row_ptr[0..R] and kv_idx[0..kv_len). Returns BSA_OK, or
+ * BSA_ERR_INVALID with "row r: rule k ..." in bsa_last_error().
+ * With the environment variable BSA_CHECK=1, bsa_sparse_attn_fwd,
+ * bsa_update_skip_mask, bsa_order_block_lists and bsa_pyramid_attn_fwd run
+ * this check on their device lists first (kv_len = row_ptr[R]; ascending
+ * order required for the input of bsa_order_block_lists), synchronising the
+ * stream, and return BSA_ERR_INVALID without launching anything when it fails.
+ */
+BSA_API bsa_status bsa_check_block_lists(const bsa_shape* s, int32_t lists_shared,
+                                         const int32_t* row_ptr, const int32_t* kv_idx,
+                                         int64_t kv_len, int64_t n_blocks, int32_t ascending,
+                                         int32_t on_device, void* stream);
 
 /* Static text for a status code. */
 BSA_API const char* bsa_status_string(bsa_status st);

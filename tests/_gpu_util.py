@@ -51,8 +51,9 @@ def radial_lists(s, h0, beta=2):
 
 
 def run_fwd(s, q, k, v, row_ptr=None, kv_idx=None, shared=0, scale=None, gap_len=0):
-    o = torch.empty_like(q)
-    lse = torch.empty(s.batch * s.heads * s.N, dtype=torch.float32, device=DEV)
+    # NaN-filled outputs: a row block the kernel never writes stays NaN
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((s.batch * s.heads * s.N,), float("nan"), dtype=torch.float32, device=DEV)
     gap = torch.full((gap_len,), float("nan"), dtype=torch.float32, device=DEV) if gap_len else None
     bsa.bsa_sparse_attn_fwd(s, q, k, v, o, lse, row_ptr, kv_idx, shared, scale, gap)
     torch.cuda.synchronize()
@@ -104,3 +105,23 @@ def sample_rows(B, H, nQ, per_head, seed, heads=None, extra=()):
             pick |= set(r.choice(nQ, size=min(nQ, per_head), replace=False).tolist())
             rows += [base + a for a in sorted(pick) if 0 <= a < nQ]
     return np.array(rows, dtype=np.int64)
+
+
+def assert_all_written(s, o, lse, row_ptr=None, shared=0, label=""):
+    """Every element of O is written (no NaN left from the fill) and every
+    query of a row block with a non-empty list has a finite LSE; rows with an
+    empty list have LSE = -inf. Checked on the device over the whole tensors."""
+    assert not bool(torch.isnan(o).any()), f"{label}: O has unwritten (NaN) elements"
+    B, H, N, bq = s.batch, s.heads, s.N, s.block_q
+    nQ = -(-N // bq)
+    if row_ptr is None:
+        nonempty = torch.ones(B * H * nQ, dtype=torch.bool, device=DEV)
+    else:
+        rp = row_ptr[: (nQ if shared else B * H * nQ) + 1].long()
+        nonempty = (rp[1:] > rp[:-1])
+        if shared:
+            nonempty = nonempty.repeat(B * H)
+    tok = nonempty.view(B * H, nQ).repeat_interleave(bq, dim=1)[:, :N].reshape(-1)
+    lse_ok = torch.where(tok, torch.isfinite(lse), torch.isneginf(lse))
+    assert bool(lse_ok.all()), f"{label}: {int((~lse_ok).sum())} LSE values wrong or unwritten"
+    note(f"{label}: all {o.numel()} O values and {lse.numel()} LSE values written")

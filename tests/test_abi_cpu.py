@@ -6,6 +6,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import block_sparse_attention_flashattention_amd as bsa
@@ -33,7 +34,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     out = subprocess.run(["nm", "-D", "--defined-only", bsa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (bsa_\w+)", out))
@@ -91,6 +92,9 @@ def test_fwd_argument_validation(L):
     assert fwd(L, s, row_ptr=P) == INVALID                      # lists half given
     assert fwd(L, s, shared=2, row_ptr=P, kv_idx=P) == INVALID
     assert fwd(L, s, gap=P) == INVALID                          # gaps need lists
+    # gaps feed the skip update, which reads per-head lists only
+    assert fwd(L, s, shared=1, row_ptr=P, kv_idx=P, gap=P) == UNSUPPORTED
+    assert "per-head" in bsa.bsa_last_error()
     # fp32: strides must be multiples of 4 elements
     assert fwd(L, s, dt=1, q=T(sn=130)) == INVALID
 
@@ -225,3 +229,88 @@ def test_pyramid_validation(L):
     assert fwd(dt=1) == UNSUPPORTED                  # bf16 only
     assert fwd(qm=None) == INVALID
     assert fwd(kp=T(P + 768, sn=64)) == INVALID      # k_pyr row stride differs from k
+
+
+# ------------------------------------------------ debug check of block lists
+def lists_of(rows):
+    rp = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    kv = np.array([c for r in rows for c in r], dtype=np.int32)
+    return rp, kv
+
+
+def check(s, rp, kv, shared=1, n_blocks=0, ascending=False, kv_len=None):
+    try:
+        bsa.bsa_check_block_lists(s, shared, rp, kv, n_blocks, ascending, kv_len)
+        return 0, ""
+    except bsa.BsaError as e:
+        return e.status, e.detail
+
+
+# S(): N = 105 tokens, Bq = 128 -> nQ = 1, nK = 2; per-head lists: B*H*nQ = 2 rows
+@pytest.mark.parametrize("rows,shared,asc,expect", [
+    ([[0, 1]], 1, True, (0, None, None)),
+    ([[1, 0]], 1, False, (0, None, None)),             # any order when ascending is not asked
+    ([[1, 0]], 1, True, (INVALID, 0, 6)),
+    ([[0, 0]], 1, False, (INVALID, 0, 5)),
+    ([[0, 0]], 1, True, (INVALID, 0, 5)),
+    ([[0, 2]], 1, False, (INVALID, 0, 4)),              # key block 2 does not exist
+    ([[-1]], 1, False, (INVALID, 0, 4)),
+    ([[], [1]], 0, True, (0, None, None)),              # empty rows are fine
+    ([[1], [1, 5, 1]], 0, False, (INVALID, 1, 4)),      # rule 4 before rule 5 in one row
+])
+def test_list_check_rules_on_host(L, rows, shared, asc, expect):
+    s = S()
+    rp, kv = lists_of(rows)
+    status, detail = check(s, rp, kv, shared=shared, ascending=asc)
+    assert status == expect[0]
+    if status:
+        assert f"row {expect[1]}: rule {expect[2]}" in detail
+
+
+def test_list_check_row_pointer_rules_on_host(L):
+    s = S()
+    kv = np.array([0, 1, 0], np.int32)
+    assert check(s, np.array([1, 2, 3], np.int32), kv, shared=0)[1].startswith(
+        "block lists, row 0: rule 1")
+    assert "row 1: rule 2" in check(s, np.array([0, 2, 1], np.int32), kv, shared=0)[1]
+    assert "row 1: rule 3" in check(s, np.array([0, 1, 3], np.int32), kv, shared=0, kv_len=2)[1]
+    # a pointer past kv_len is reported at its row; nothing past kv_len is read
+    assert "row 0: rule 3" in check(s, np.array([0, 9, 3], np.int32), kv, shared=0)[1]
+    # pyramid-style lists name augmented blocks: n_blocks widens the range
+    assert check(s, np.array([0, 1], np.int32), np.array([3], np.int32), n_blocks=4)[0] == 0
+    assert check(s, np.array([0, 1], np.int32), np.array([3], np.int32))[0] == INVALID
+
+
+def test_list_check_matches_brute_force_on_random_lists(L):
+    """The host check against a direct restatement of the list contract on
+    random, partly corrupted lists: valid iff every row holds distinct blocks
+    in range (and ascending when asked)."""
+    r = np.random.default_rng(5)
+    s = S(batch=2, heads=3, frames=4, height=8, width=8, block_q=64)   # nQ = nK = 4
+    R, nK = 2 * 3 * 4, 4
+    for trial in range(300):
+        rows = [sorted(r.choice(nK, size=r.integers(0, nK + 1), replace=False).tolist())
+                for _ in range(R)]
+        if trial % 3 == 1:
+            rows[r.integers(R)] = r.integers(-1, nK + 1, size=r.integers(1, 5)).tolist()
+        elif trial % 3 == 2:
+            rr = rows[r.integers(R)]
+            r.shuffle(rr)
+        rp, kv = lists_of(rows)
+        for asc in (False, True):
+            ok = all(len(set(x)) == len(x) and all(0 <= c < nK for c in x)
+                     and (not asc or x == sorted(x)) for x in rows)
+            assert (check(s, rp, kv, shared=0, ascending=asc)[0] == 0) == ok, (rows, asc)
+
+
+def test_list_check_argument_validation(L):
+    s = S()
+    call = lambda **kw: L.bsa_check_block_lists(
+        C.byref(s), kw.get("shared", 1), kw.get("rp", P), kw.get("kv", P), kw.get("n", 4),
+        kw.get("nb", 0), 0, kw.get("dev", 0), None)
+    assert call(shared=2) == INVALID
+    assert call(dev=2) == INVALID
+    assert call(n=-1) == INVALID
+    assert call(nb=-1) == INVALID
+    assert call(rp=None) == INVALID
+    assert call(kv=None) == INVALID

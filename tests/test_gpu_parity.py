@@ -13,8 +13,8 @@ import torch
 import block_sparse_attention_flashattention_amd as bsa
 import oracle
 import synth
-from _gpu_util import (DEV, GAP_ABS, compare, dev, gather_rows, host, note, radial_lists,
-                       run_fwd, sample_rows, shape_of)
+from _gpu_util import (DEV, GAP_ABS, assert_all_written, compare, dev, gather_rows, host, note,
+                       radial_lists, run_fwd, sample_rows, shape_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -100,6 +100,7 @@ def test_fwd_bf16_small_full_compare(d, Bq, mode):
         kv = torch.empty(R * w.nK, dtype=torch.int32, device=DEV)
         bsa.bsa_compact_block_lists(s, dev(mask_np), mhs, None, rp, kv)
     o, lse, _ = run_fwd(s, q, k, v, rp, kv, shared, w.scale)
+    assert_all_written(s, o, lse, rp, shared, f"d={d} Bq={Bq} {mode}")
     o_ref, lse_ref, _ = oracle.attention(x["q"], x["k"], x["v"], w.Bq, w.Bk, w.scale, mask_np, mhs)
     rows = np.arange(w.B * w.H * w.nQ)
     og, lg = gather_rows(host(o), host(lse), rows, w.B, w.H, w.N, w.Bq)
@@ -167,6 +168,8 @@ def _full_radial(name, per_head, seed):
     np.testing.assert_array_equal(host(kv)[:kv_ref.size], kv_ref)
     note(f"{name}: masks and lists bit-exact ({kv_ref.size} tiles per head)")
     o, lse, _ = run_fwd(s, q, k, v, rp, kv, 1, w.scale)
+    # the position-major workgroup order covers every row block of every head
+    assert_all_written(s, o, lse, rp, 1, name)
     heads = sorted({0, w.H - 1, w.H // 2})
     F_blocks = [a for a in range(1, w.nQ) if (a * w.Bq) // w.F != ((a + 1) * w.Bq - 1) // w.F]
     rows = sample_rows(w.B, w.H, w.nQ, per_head, seed, heads=heads, extra=F_blocks[:2])

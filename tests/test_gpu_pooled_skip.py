@@ -17,8 +17,8 @@ import torch
 import block_sparse_attention_flashattention_amd as bsa
 import oracle
 import synth
-from _gpu_util import (DEV, GAP_ABS, compare, dev, gather_rows, host, note, radial_lists,
-                       run_fwd, sample_rows, shape_of)
+from _gpu_util import (DEV, GAP_ABS, assert_all_written, compare, dev, gather_rows, host, note,
+                       radial_lists, run_fwd, sample_rows, shape_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -116,6 +116,7 @@ def test_pooled_then_forward_wan13b_480p_sampled():
     kv = torch.empty(R * w.nK, dtype=torch.int32, device=DEV)
     bsa.bsa_compact_block_lists(s, mask, w.nQ * w.nK, None, rp, kv)
     o, lse, _ = run_fwd(s, q, k, v, rp, kv, 0, w.scale)
+    assert_all_written(s, o, lse, rp, 0, "480p pooled")
     mask_h = host(mask).reshape(w.B, w.H, w.nQ, w.nK)
     rows = sample_rows(w.B, w.H, w.nQ, 3, 21, heads=[0, 5, w.H - 1])
     o_ref, lse_ref, _ = oracle.attention(x["q"], x["k"], x["v"], w.Bq, w.Bk, w.scale, mask_h,
@@ -219,12 +220,13 @@ def _skip_carry(w, steps, tau, rows=None, order=bsa.ORDER_ASCENDING, freeze_afte
         skip_prev = host(skip).reshape(R, nK).copy()
         nnz = bsa.bsa_compact_block_lists(s, ones, 0, skip, rp, kv_asc, want_nnz=True)
         bsa.bsa_order_block_lists(s, order, rp, 0, kv_asc, kv)
-        o = torch.empty_like(q)
-        lse = torch.empty(w.B * w.H * w.N, dtype=torch.float32, device=DEV)
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full((w.B * w.H * w.N,), float("nan"), dtype=torch.float32, device=DEV)
         bsa.bsa_sparse_attn_fwd(s, q, k, v, o, lse, rp, kv, 0, w.scale, None if frozen else gap)
         if not frozen:
             bsa.bsa_update_skip_mask(s, rp, kv, gap, tau_s, skip)
         torch.cuda.synchronize()
+        assert_all_written(s, o, lse, rp, 0, f"{w.name} step {st}")
         rp_h, kv_h = host(rp).astype(np.int64), host(kv)[:nnz]
         skip_new = host(skip).reshape(R, nK)
         # lists are the complement of the carried set, in the requested order
@@ -299,9 +301,11 @@ def test_skip_carry_gap_batches_with_remainder(Bq):
 
 
 def test_skip_carry_480p_sampled():
+    """All ten denoising steps of the 480p carry (sigma 0.5 -> 0.05), each
+    checked against the oracle from the GPU's previous skip set."""
     w = synth.workload("skip_carry_480p")
     rows = sample_rows(w.B, w.H, w.nQ, 2, 23, heads=[0, w.H - 1])
-    _skip_carry(w, 4, 2.0, rows=rows)
+    _skip_carry(w, w.steps, 2.0, rows=rows)
 
 
 def test_skip_carry_480p_workload_tau_marks_nothing():
@@ -327,7 +331,56 @@ def test_skip_carry_small_bq128_ragged_radial_order():
 def test_skip_carry_480p_sampled_radial_order():
     w = synth.workload("skip_carry_480p")
     rows = sample_rows(w.B, w.H, w.nQ, 2, 25, heads=[0, w.H - 1])
-    _skip_carry(w, 3, 2.0, rows=rows, order=bsa.ORDER_RADIAL)
+    _skip_carry(w, w.steps, 2.0, rows=rows, order=bsa.ORDER_RADIAL)
+
+
+def _gpu_steps(w, s, v, skip, steps, order, tau):
+    """Carry on the GPU over the given steps (no oracle); returns each step's
+    O and LSE and leaves the carried set in `skip`."""
+    R, nK = w.B * w.H * w.nQ, w.nK
+    ones = torch.ones(w.nQ * nK, dtype=torch.uint8, device=DEV)
+    rp = torch.empty(R + 1, dtype=torch.int32, device=DEV)
+    kv_asc = torch.empty(R * nK, dtype=torch.int32, device=DEV)
+    kv = torch.empty(R * nK, dtype=torch.int32, device=DEV)
+    gap = torch.empty(R * nK, dtype=torch.float32, device=DEV)
+    outs = []
+    for st in steps:
+        x = synth.make_step_qk(w, st)
+        q, k = dev(x["q"]), dev(x["k"])
+        bsa.bsa_compact_block_lists(s, ones, 0, skip, rp, kv_asc)
+        bsa.bsa_order_block_lists(s, order, rp, 0, kv_asc, kv)
+        o = torch.empty_like(q)
+        lse = torch.empty(w.B * w.H * w.N, dtype=torch.float32, device=DEV)
+        bsa.bsa_sparse_attn_fwd(s, q, k, v, o, lse, rp, kv, 0, w.scale, gap)
+        bsa.bsa_update_skip_mask(s, rp, kv, gap, tau, skip)
+        torch.cuda.synchronize()
+        outs.append((o.view(torch.int16).cpu().numpy(), lse.cpu().numpy()))
+    return outs
+
+
+def test_skip_carry_save_and_restore_resumes_bit_exactly(tmp_path):
+    """LiteAttention summary page, section 六: the skip mask persists across
+    steps. Ten steps in one run equal five steps, the carried set saved to a
+    file and loaded into a fresh buffer, then the other five: same skip sets,
+    same O and LSE bit for bit (the kernels are deterministic)."""
+    w = synth.Workload("skip_resume", 1, 3, 128, 6, 10, 14, 64, 64, "bf16", "skip", 624, True,
+                       tau=1.0, steps=10)
+    s = shape_of(w)
+    v = dev(synth.make_qkv(w, step=0, want=("v",))["v"])
+    R = w.B * w.H * w.nQ * w.nK
+    full = torch.zeros(R, dtype=torch.uint8, device=DEV)
+    outs_full = _gpu_steps(w, s, v, full, range(10), bsa.ORDER_RADIAL, w.tau)
+    half = torch.zeros(R, dtype=torch.uint8, device=DEV)
+    outs_a = _gpu_steps(w, s, v, half, range(5), bsa.ORDER_RADIAL, w.tau)
+    np.save(tmp_path / "skip.npy", half.cpu().numpy())
+    resumed = dev(np.load(tmp_path / "skip.npy"))
+    del half
+    outs_b = _gpu_steps(w, s, v, resumed, range(5, 10), bsa.ORDER_RADIAL, w.tau)
+    assert torch.equal(resumed, full)
+    for i, ((o1, l1), (o2, l2)) in enumerate(zip(outs_full, outs_a + outs_b)):
+        np.testing.assert_array_equal(o1, o2, err_msg=f"step {i}")
+        np.testing.assert_array_equal(l1, l2, err_msg=f"step {i}")
+    note(f"resumed carry: {int(full.sum())} tiles skipped after 10 steps, identical")
 
 
 def test_skip_carry_tau_schedule_then_shared_mask():
@@ -401,6 +454,7 @@ def test_fwd_hunyuan_4x_radial_sampled():
     kv = torch.empty(s.nQ * s.nK, dtype=torch.int32, device=DEV)
     bsa.bsa_compact_block_lists(s, mask, 0, None, rp, kv)
     o, lse, _ = run_fwd(s, q, k, v, rp, kv, 1, w.scale)
+    assert_all_written(s, o, lse, rp, 1, w.name)
     ref_mask = oracle.build_mask_radial(w.T, w.Hs, w.Ws, w.Bq, w.Bk, w.h0, w.beta)
     np.testing.assert_array_equal(host(mask).reshape(w.nQ, w.nK), ref_mask)
     heads = [0, w.H - 1]

@@ -15,7 +15,8 @@ import torch
 import block_sparse_attention_flashattention_amd as bsa
 import oracle
 import synth
-from _gpu_util import DEV, compare, dev, gather_rows, host, note, sample_rows, shape_of
+from _gpu_util import (DEV, assert_all_written, compare, dev, gather_rows, host, note,
+                       sample_rows, shape_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,10 +47,11 @@ def run_pyramid(w, x, taus, rows=None):
     kv = torch.empty(cap, dtype=torch.int32, device=DEV)
     qm = torch.empty(cap, dtype=torch.int32, device=DEV)
     nnz = bsa.bsa_compact_pyramid_lists(s, L, mask, w.nQ * w.nK, rp, kv, qm, want_nnz=True)
-    o = torch.empty_like(q)
-    lse = torch.empty(R * w.Bq, dtype=torch.float32, device=DEV)[: w.B * w.H * w.N]
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((R * w.Bq,), float("nan"), dtype=torch.float32, device=DEV)[: w.B * w.H * w.N]
     bsa.bsa_pyramid_attn_fwd(s, q, k, v, kp, vp, L, o, lse, rp, kv, qm, w.scale)
     torch.cuda.synchronize()
+    assert_all_written(s, o, lse, rp, 0, f"pyramid {w.name} {L} levels")
     return dict(kp=kp, vp=vp, mask=host(mask).reshape(w.B, w.H, w.nQ, w.nK), rp=host(rp),
                 kv=host(kv)[:nnz], qm=host(qm)[:nnz], o=o, lse=lse, nnz=nnz, prow=prow)
 

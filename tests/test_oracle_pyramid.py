@@ -7,9 +7,13 @@ consistent across levels. Pinned by: level 0 everywhere equals binary block
 attention; keys and values that are constant inside every group of tokens
 give the same output at any mix of levels (this fixes the +level*ln 2 weight
 of a pooled key); constant V is reproduced; the level mask relates exactly
-to the per-row cumulative-mass mask at each threshold; the tile lists are
-checked by decoding them back into (level, block) pairs.
+to the per-row cumulative-mass mask at each threshold; the tile lists match
+a layout worked out by hand (tests/golden/pyramid_lists_296.txt), and,
+decoded into pooled key rows with numpy alone, give the attention the oracle
+computes from the level mask.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -97,28 +101,99 @@ def test_regions_by_hand(oracle_lib):
     assert rb.tolist() == [0, 5, 8, 10] and rr.tolist() == [296, 148, 74]
 
 
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pyramid_lists_296.txt")
+
+
+def golden_rows():
+    rows = []
+    with open(GOLDEN) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            m, want = line.split("|")
+            pairs = [tuple(int(x) for x in t.split(":")) for t in want.split()]
+            rows.append(([int(x) for x in m.split()], pairs))
+    return rows
+
+
+def test_pyramid_lists_golden_by_hand(oracle_lib):
+    """N = 296, three levels, ragged last block: lists worked out by hand from
+    the level layout (tests/golden/pyramid_lists_296.txt)."""
+    rows = golden_rows()
+    N, bk, L = 296, 64, 3
+    nQ, nK = len(rows), 5
+    m = np.array([r[0] for r in rows], np.uint8).reshape(1, 1, nQ, nK)
+    rp, kv, qm = oracle.compact_pyramid(m, 1, 1, nQ, nK, N, bk, L, nQ * nK)
+    want_rp = np.cumsum([0] + [len(r[1]) for r in rows])
+    np.testing.assert_array_equal(rp, want_rp)
+    for a, (_, pairs) in enumerate(rows):
+        got = list(zip(kv[rp[a]:rp[a + 1]].tolist(), qm[rp[a]:rp[a + 1]].tolist()))
+        assert got == pairs, (a, got, pairs)
+
+
+def decode_and_attend(q, k, v, bq, bk, scale, n_levels, rp, kv, qm, rows):
+    """Attention of the given list rows evaluated from the lists alone: each
+    entry (augmented block, quarter bits) names pooled key rows of one level
+    (level l region = augmented blocks [rb_l, rb_l+1), N >> l valid rows);
+    pooled row g of level l is the mean of tokens g*2^l .. g*2^l + 2^l - 1 of
+    K and of V, and its score carries + l ln 2 (it stands for 2^l tokens)."""
+    B, N, H, D = q.shape
+    nQ = -(-N // bq)
+    starts, valid = [0], []
+    for l in range(n_levels):
+        valid.append(N >> l)
+        starts.append(starts[-1] + -(-(N >> l) // bk))
+    outs = []
+    for row in rows:
+        bh, a = divmod(int(row), nQ)
+        b, h = divmod(bh, H)
+        keys, vals, bias = [], [], []
+        for ab, bits in zip(kv[rp[row]:rp[row + 1]], qm[rp[row]:rp[row + 1]]):
+            l = max(i for i in range(n_levels) if starts[i] <= ab)
+            g = 1 << l
+            for quarter in range(4):
+                if not (bits >> quarter) & 1:
+                    continue
+                for pr in range((ab - starts[l]) * bk + quarter * (bk // 4),
+                                (ab - starts[l]) * bk + (quarter + 1) * (bk // 4)):
+                    if pr >= valid[l]:
+                        continue
+                    keys.append(k[b, pr * g:(pr + 1) * g, h].mean(axis=0))
+                    vals.append(v[b, pr * g:(pr + 1) * g, h].mean(axis=0))
+                    bias.append(l * np.log(2.0))
+        qi = q[b, a * bq:min(N, (a + 1) * bq), h]
+        if not keys:
+            outs.append((np.zeros_like(qi), np.full(len(qi), -np.inf)))
+            continue
+        s = scale * qi @ np.array(keys).T + np.array(bias)[None, :]
+        mx = s.max(axis=1, keepdims=True)
+        p = np.exp(s - mx)
+        outs.append((p @ np.array(vals) / p.sum(axis=1, keepdims=True),
+                     mx[:, 0] + np.log(p.sum(axis=1))))
+    return outs
+
+
 @pytest.mark.parametrize("N", [256, 296, 1000])
 def test_pyramid_lists_decode_to_the_mask(oracle_lib, N):
-    B, H, bq, bk, L = 2, 2, 64, 64, 3
+    """The lists, decoded into pooled key rows with no help from the oracle,
+    give the attention the oracle computes from the level mask itself."""
+    B, H, D, bq, bk, L = 1, 2, 8, 64, 64, 3
     nQ, nK = -(-N // bq), -(-N // bk)
     r = np.random.default_rng(N)
+    q, k, v = (r.standard_normal((B, N, H, D)) for _ in range(3))
     m = r.integers(0, 4, size=(B, H, nQ, nK)).astype(np.uint8)
+    m[..., 0, :] = 0                                 # one empty row per head
     rp, kv, qm = oracle.compact_pyramid(m, B, H, nQ, nK, N, bk, L, nQ * nK)
-    rb, _ = oracle.pyramid_regions(N, bk, L)
     assert rp[-1] == kv.size == qm.size
     for row in range(B * H * nQ):
         e0, e1 = rp[row], rp[row + 1]
         assert np.all(np.diff(kv[e0:e1]) > 0) and np.all(qm[e0:e1] > 0)
-        got = {(int(a), q_) for a, qq in zip(kv[e0:e1], qm[e0:e1]) for q_ in range(4)
-               if qq >> q_ & 1}
-        want = set()
-        mrow = m.reshape(-1, nK)[row]
-        for c in np.nonzero(mrow)[0]:
-            l = int(mrow[c]) - 1
-            per = bk >> l                                # pooled rows of a block
-            for row0 in range(c * per, (c + 1) * per, bk // 4):
-                want.add((int(rb[l] + row0 // bk), (row0 % bk) // (bk // 4)))
-        assert got == want
+    o_ref, l_ref = oracle.pyramid_attention(q, k, v, bq, bk, 0.5, m, nQ * nK)
+    rows = np.arange(B * H * nQ)
+    for row, (o, lse) in zip(rows, decode_and_attend(q, k, v, bq, bk, 0.5, L, rp, kv, qm, rows)):
+        n = len(o)
+        np.testing.assert_allclose(o, o_ref[row, :n], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, l_ref[row, :n], rtol=0, atol=1e-12)
     # all level 0: the plain ascending lists with whole tiles
     ones = (m > 0).astype(np.uint8)
     rp1, kv1, qm1 = oracle.compact_pyramid(ones, B, H, nQ, nK, N, bk, L, nQ * nK)
@@ -126,3 +201,20 @@ def test_pyramid_lists_decode_to_the_mask(oracle_lib, N):
     np.testing.assert_array_equal(rp1, rp0)
     np.testing.assert_array_equal(kv1, kv0)
     assert np.all(qm1 == 15)
+
+
+def test_decode_catches_a_shifted_quarter(oracle_lib):
+    """The decode check is sharp: moving one selected quarter of one entry to
+    its neighbour changes the decoded attention."""
+    N, B, H, D, bq, bk, L = 296, 1, 1, 8, 64, 64, 3
+    rows = golden_rows()
+    nQ, nK = len(rows), 5
+    m = np.array([r[0] for r in rows], np.uint8).reshape(1, 1, nQ, nK)
+    rp, kv, qm = oracle.compact_pyramid(m, B, H, nQ, nK, N, bk, L, nQ * nK)
+    r = np.random.default_rng(11)
+    q, k, v = (r.standard_normal((B, N, H, D)) for _ in range(3))
+    o_ref, _ = oracle.pyramid_attention(q, k, v, bq, bk, 0.5, m, nQ * nK)
+    bad = qm.copy()
+    bad[1] = 6                                       # row 0, block 5: quarters 1,2 not 2,3
+    (o_bad, _), = decode_and_attend(q, k, v, bq, bk, 0.5, L, rp, kv, bad, [0])
+    assert np.abs(o_bad - o_ref[0, :len(o_bad)]).max() > 1e-3

@@ -45,3 +45,38 @@ def test_skip_set_grows_monotonically_and_rows_never_empty(oracle_lib, order):
         skip = new
         total.append(int(skip.sum()))
     assert total[-1] > 0
+
+
+def _run_steps(w, v, skip, steps, order):
+    """Advance the carried skip set over the given denoising steps; returns the
+    final set and each step's (o, lse) as computed."""
+    outs = []
+    for s in steps:
+        qk = synth.make_step_qk(w, s)
+        o, lse, _, skip = oracle.skip_step(qk["q"], qk["k"], v, w.Bq, w.Bk, w.scale, skip, w.tau,
+                                           order=order)
+        outs.append((o, lse))
+    return skip, outs
+
+
+@pytest.mark.parametrize("order", [oracle.ORDER_ASCENDING, oracle.ORDER_RADIAL])
+def test_skip_set_save_and_restore_resumes_exactly(oracle_lib, tmp_path, order):
+    """LiteAttention summary page, section 六: the skip mask persists across
+    denoising steps. The carried set is the whole state of the carry, so ten
+    steps in one run equal five steps, the set written to disk and read back,
+    then the other five: same sets, same outputs, bit for bit."""
+    w = small_workload().with_(steps=10, tau=1.0)
+    v = synth.make_qkv(w, step=0, want=("v",))["v"]
+    zero = np.zeros((w.B, w.H, w.nQ, w.nK), np.uint8)
+    full, outs_full = _run_steps(w, v, zero, range(10), order)
+    half, outs_a = _run_steps(w, v, zero, range(5), order)
+    path = tmp_path / "skip.npy"
+    np.save(path, half)
+    restored = np.load(path)                     # allow_pickle defaults to False
+    assert restored.dtype == np.uint8 and np.array_equal(restored, half)
+    resumed, outs_b = _run_steps(w, v, restored, range(5, 10), order)
+    np.testing.assert_array_equal(resumed, full)
+    for (o1, l1), (o2, l2) in zip(outs_full, outs_a + outs_b):
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(l1, l2)
+    assert full.sum() > half.sum() > 0          # the set grew in both halves
