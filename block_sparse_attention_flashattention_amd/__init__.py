@@ -16,6 +16,7 @@ import os
 __all__ = [
     "BsaError", "Shape", "shape", "lib", "BSA_BF16", "BSA_F32",
     "bsa_build_mask_radial", "bsa_pooled_workspace_bytes", "bsa_build_mask_pooled",
+    "bsa_build_mask_pooled_noalloc",
     "bsa_compact_block_lists", "bsa_order_block_lists", "bsa_sparse_attn_fwd",
     "bsa_update_skip_mask", "ORDER_ASCENDING", "ORDER_RADIAL",
     "bsa_make_token_permutation", "bsa_permute_tokens", "PERM_AXES", "PERM_BOXES",
@@ -84,6 +85,7 @@ def lib() -> C.CDLL:
             "bsa_build_mask_radial": (i32, [SP, i32, i32, p, p]),
             "bsa_pooled_workspace_bytes": (sz, [SP]),
             "bsa_build_mask_pooled": (i32, [SP, i32, Tensor, Tensor, f64, i32, f64, p, p, sz, p]),
+            "bsa_build_mask_pooled_noalloc": (i32, [SP, i32, Tensor, Tensor, f64, i32, f64, p, p]),
             "bsa_compact_block_lists": (i32, [SP, p, i64, p, p, p, i64, C.POINTER(i64), p]),
             "bsa_order_block_lists": (i32, [SP, i32, p, i32, p, p, p]),
             "bsa_make_token_permutation": (i32, [SP, i32, C.POINTER(i32), p, p]),
@@ -172,6 +174,13 @@ def bsa_build_mask_pooled(s: Shape, q, k, scale: float, mode: int, param: float,
            lib().bsa_build_mask_pooled(C.byref(s), _dtype(q), _tensor(q), _tensor(k), scale,
                                        mode, param, _ptr(mask), _ptr(workspace), nbytes,
                                        _stream(stream)))
+
+
+def bsa_build_mask_pooled_noalloc(s: Shape, q, k, scale: float, mode: int, param: float, mask,
+                                  stream=None):
+    _check("bsa_build_mask_pooled_noalloc",
+           lib().bsa_build_mask_pooled_noalloc(C.byref(s), _dtype(q), _tensor(q), _tensor(k),
+                                               scale, mode, param, _ptr(mask), _stream(stream)))
 
 
 def bsa_compact_block_lists(s: Shape, mask, mask_head_stride: int, skip, row_ptr, kv_idx,

@@ -155,13 +155,15 @@ size_t bsa_pooled_workspace_bytes(const bsa_shape* s) {
   return bsa::pooled_workspace_bytes(g);
 }
 
-bsa_status bsa_build_mask_pooled(const bsa_shape* s, bsa_dtype dt, bsa_tensor q,
-                                 bsa_tensor k, double scale, int32_t mode, double param,
-                                 uint8_t* mask, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
-  bsa::Geom g;
-  bsa_status st = make_geom(s, &g);
-  if (st != BSA_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the pooled builders: everything but the scratch.
+bsa_status check_pooled(const bsa::Geom& g, bsa_dtype dt, const bsa_tensor& q,
+                        const bsa_tensor& k, double scale, int32_t mode, double param,
+                        const uint8_t* mask) {
+  bsa_status st;
   if (dt != BSA_BF16 && dt != BSA_F32) return fail(BSA_ERR_UNSUPPORTED, "dtype %d", (int)dt);
   if (!isfinite(scale)) return fail(BSA_ERR_INVALID, "scale is not finite");
   if (mode == 0 || mode == 2) {
@@ -176,10 +178,48 @@ bsa_status bsa_build_mask_pooled(const bsa_shape* s, bsa_dtype dt, bsa_tensor q,
   if (g.nK > bsa::pooled_max_blocks())
     return fail(BSA_ERR_UNSUPPORTED, "pooled selection supports at most %d key blocks",
                 bsa::pooled_max_blocks());
-  if (empty(g)) return ok();
+  if (empty(g)) return BSA_OK;
   if ((st = check_tensor("q", q, elem_bytes(dt))) != BSA_OK) return st;
   if ((st = check_tensor("k", k, elem_bytes(dt))) != BSA_OK) return st;
   if (!mask) return fail(BSA_ERR_INVALID, "mask is NULL");
+  return BSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bsa_status bsa_build_mask_pooled_noalloc(const bsa_shape* s, bsa_dtype dt, bsa_tensor q,
+                                         bsa_tensor k, double scale, int32_t mode, double param,
+                                         uint8_t* mask, void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  if ((st = check_pooled(g, dt, q, k, scale, mode, param, mask)) != BSA_OK) return st;
+  if (empty(g)) return ok();
+  const size_t need = bsa::pooled_scratch_need(g, mode);
+  if (need > bsa::kStaticScratchBytes)
+    return fail(BSA_ERR_CAPACITY,
+                "mode %d at this shape needs %zu bytes of scratch; the library's static scratch "
+                "holds %zu (use bsa_build_mask_pooled with a workspace)",
+                mode, need, bsa::kStaticScratchBytes);
+  void* ws = nullptr;
+  hipError_t e = bsa::static_scratch(&ws);
+  if (e != hipSuccess) return device(e, "static scratch lookup");
+  return device(bsa::launch_pooled_mask(g, dt == BSA_BF16 ? 0 : 1, arg(q), arg(k), scale, mode,
+                                        param, mask, ws, (hipStream_t)stream),
+                "pooled mask launch");
+}
+
+bsa_status bsa_build_mask_pooled(const bsa_shape* s, bsa_dtype dt, bsa_tensor q,
+                                 bsa_tensor k, double scale, int32_t mode, double param,
+                                 uint8_t* mask, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  if ((st = check_pooled(g, dt, q, k, scale, mode, param, mask)) != BSA_OK) return st;
+  if (empty(g)) return ok();
   const size_t need = bsa::pooled_workspace_bytes(g);
   if (!workspace || workspace_bytes < need)
     return fail(BSA_ERR_INVALID, "workspace needs %zu bytes", need);

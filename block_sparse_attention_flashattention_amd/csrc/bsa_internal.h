@@ -23,6 +23,12 @@ hipError_t launch_radial_mask(const Geom& g, int32_t h0, int32_t beta, uint8_t* 
                               hipStream_t st);
 
 size_t pooled_workspace_bytes(const Geom& g);
+// Scratch bytes the pooled builder uses in `mode` (at most the workspace size),
+// and the device address of the library's static scratch on the current
+// device (kStaticScratchBytes; shared by every call on that device).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+size_t pooled_scratch_need(const Geom& g, int32_t mode);
+hipError_t static_scratch(void** ptr);
 hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k, double scale,
                               int32_t mode, double param, uint8_t* mask, void* ws,
                               hipStream_t st, const double* levels = nullptr,

@@ -10,6 +10,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -1182,6 +1184,40 @@ size_t pooled_workspace_bytes(const Geom& g) {
 }
 
 int pooled_max_blocks() { return kPooledMaxBlocks; }
+
+size_t pooled_scratch_need(const Geom& g, int32_t mode) {
+  if (mode == 2 || mode == 3) return pooled_workspace_bytes(g);
+  // per-row modes: pooled means of Q and K and the score matrix only
+  const int64_t BH = (int64_t)g.B * g.H;
+  const size_t n = (size_t)(BH * (g.nQ + g.nK) * g.D + BH * g.nQ * g.nK);
+  return (n * sizeof(double) + 255) / 256 * 256;
+}
+
+// Scratch of the pooled builder for callers that cannot allocate: one
+// file-scope device array, held by every GPU the library runs on until the
+// process ends. In host code the array's name is only a host-side stand-in;
+// its device address comes from hipGetSymbolAddress, looked up once per
+// device (with that device current) and kept.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k, double scale,
                               int32_t mode, double param, uint8_t* mask, void* ws,

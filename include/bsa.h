@@ -151,6 +151,24 @@ BSA_API bsa_status bsa_build_mask_pooled(const bsa_shape* s, bsa_dtype dt, bsa_t
                                  void* stream);
 
 /*
+ * bsa_build_mask_pooled without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same modes, parameters, result and
+ * errors as bsa_build_mask_pooled; the scratch it needs comes from a static
+ * device array inside the library of 64 MiB (64 << 20 bytes) per GPU, held
+ * from library load until the process ends. Modes 0 and 1 need
+ * 8*(B*H*(nQ + nK)*d + B*H*nQ*nK) bytes rounded up to 256 (the 480p layer
+ * with 12 heads: 37.7 MB), modes 2 and 3 bsa_pooled_workspace_bytes(s);
+ * a shape and mode that need more return BSA_ERR_CAPACITY before anything is
+ * enqueued. The call allocates nothing. Every call on one GPU shares that
+ * GPU's scratch: calls that overlap in time on the same GPU (other streams,
+ * other host threads) race and must be serialised by the caller.
+ */
+BSA_API bsa_status bsa_build_mask_pooled_noalloc(const bsa_shape* s, bsa_dtype dt, bsa_tensor q,
+                                                 bsa_tensor k, double scale, int32_t mode,
+                                                 double param, uint8_t* mask, void* stream);
+
+/*
  * Per-row lists of kept key blocks ([Lite] sections 三 and 六: a skipped tile
  * must cost no softmax and no memory transfer, so the loader walks only the
  * listed tiles).

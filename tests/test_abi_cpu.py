@@ -34,7 +34,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     out = subprocess.run(["nm", "-D", "--defined-only", bsa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (bsa_\w+)", out))
@@ -314,3 +314,24 @@ def test_list_check_argument_validation(L):
     assert call(nb=-1) == INVALID
     assert call(rp=None) == INVALID
     assert call(kv=None) == INVALID
+
+
+def test_pooled_noalloc_validation(L):
+    """Same argument checks as the workspace form; shapes whose scratch would
+    exceed the static 64 MiB are refused before anything is enqueued."""
+    def call(shape=S(), mode=1, param=0.5, mask=P, dt=0):
+        return L.bsa_build_mask_pooled_noalloc(C.byref(shape), dt, T(), T(P + 256), 0.1, mode,
+                                               param, mask, None)
+    assert call(mode=5) == INVALID
+    assert call(param=0.0) == INVALID
+    assert call(mask=None) == INVALID
+    assert call(dt=3) == UNSUPPORTED
+    assert call(shape=S(frames=33, height=100, width=100)) == UNSUPPORTED   # > 2048 key blocks
+    # 480p layer, 12 heads: per-row modes fit (37.7 MB) -- not launched here;
+    # head-wide modes need 108 MiB and are refused with CAPACITY
+    big = S(heads=12, frames=21, height=30, width=52, block_q=64)
+    assert call(shape=big, mode=3, param=0.5) == CAPACITY
+    assert call(shape=big, mode=2, param=4) == CAPACITY
+    assert "static scratch" in bsa.bsa_last_error()
+    # 720p shape at 40 heads: even the per-row modes exceed it
+    assert call(shape=S(heads=40, frames=21, height=45, width=80)) == CAPACITY
