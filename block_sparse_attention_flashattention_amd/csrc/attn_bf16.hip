@@ -157,7 +157,11 @@ __device__ inline void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
 }
 __device__ inline void barrier() { asm volatile("s_barrier" ::: "memory"); }
-__device__ inline void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Wait for every LDS and scalar-memory access of this wave. Issued through
+// the builtin (not inline assembly) so that the compiler's own wait-count
+// pass sees it and knows that no scalar load is outstanding afterwards.
+// Encoding: vmcnt 63 (bits 3:0 and 15:14), expcnt 7 (bits 6:4), lgkmcnt 0.
+__device__ inline void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Float max into global memory, independent of arrival order: non-negative
 // values order like signed ints, negative ones inversely like unsigned ints.
@@ -260,8 +264,10 @@ __device__ inline void issue_rows(const uint32_t* off, const i32x4& rs, uint32_t
 __device__ inline i32x4 rows_rsrc(const uint16_t* base, int64_t sn, int j0, int rows) {
   const uint64_t a = (uint64_t)(base + (int64_t)j0 * sn);
   // wave-uniform by construction; readfirstlane keeps the descriptor in SGPRs
+  // (the row count first, so that its product is a scalar multiply)
+  const int32_t r = wave_uniform(rows);
   return i32x4{wave_uniform((int32_t)(uint32_t)a), wave_uniform((int32_t)((a >> 32) & 0xffff)),
-               wave_uniform(rows * (int32_t)sn * 2), kRsrcWord3};
+               r * (int32_t)sn * 2, kRsrcWord3};
 }
 
 __device__ inline bf16x8 join(i16x4 lo, i16x4 hi) {
@@ -698,9 +704,6 @@ void attn_bf16_kernel(const Bf16Params p) {
       if (it + 2 < LS) issue_k(KS_{}, c2, pk);
     }
     const int code3 = LSL ? steplist[min(it + 3, kStepCap - 1)] : 0;
-    int c3 = LSL ? 0 : (it + 3 < LS ? block_of(it + 3) : 0);
-    int q3 = (PYR && !LSL && it + 3 < LS) ? quarters_of(it + 3) : 0xF;
-    int r3 = (SL && !LSL && it + 3 < LS) ? part_of(it + 3) : 0;
     bf16x8 pb[KB][2];
     if (has_next) {
       const char* kt = smem + kso[1 - par];
@@ -729,6 +732,8 @@ void attn_bf16_kernel(const Bf16Params p) {
       const float neg_m = (float)lev(lsl_c, c0) - m_use;
 #pragma unroll
       for (int i = 0; i < kPfK; ++i) kbuf[i] = kread(i);
+      // the first fragment reads go out together, ahead of the first MFMA
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < C::NA; ++i) {
         if (i + kPfK < C::NA) kbuf[(i + kPfK) % (kPfK + 1)] = kread(i + kPfK);
@@ -782,9 +787,18 @@ void attn_bf16_kernel(const Bf16Params p) {
       probs(cur, pb, (float)lev(lsl_c, c0));
       accumulate(smem + vso[par], pb);
     }
+    // The list entries of step it+3 are read here, after the last LDS wait
+    // of the step: scalar loads count in lgkmcnt and may complete out of
+    // order, so one in flight would turn every LDS wait above into a wait for
+    // everything.
+    int c3 = 0, q3 = 0xF, r3 = 0;
     if constexpr (LSL) {
       const int code = wave_uniform(code3);
       if (it + 3 < LS) c3 = code;
+    } else {
+      c3 = it + 3 < LS ? block_of(it + 3) : 0;
+      q3 = (PYR && it + 3 < LS) ? quarters_of(it + 3) : 0xF;
+      r3 = (SL && it + 3 < LS) ? part_of(it + 3) : 0;
     }
     c0 = c1;
     c1 = c2;
