@@ -76,21 +76,47 @@ def source_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def counters_for(workload: str) -> dict:
-    """The counter record of profiles/traffic.json when it was taken on this kernel source and
-    workload, else {}."""
+def variant_key(args, w) -> str:
+    """Name of a measured configuration: the workload plus every option that
+    changes what the forward kernel runs on (a counter record is kept per
+    key)."""
+    parts = [w.name]
+    if w.mask == "skip":
+        parts.append(f"tau={args.tau_schedule or w.tau}")
+        parts.append(f"order={args.order}")
+        if args.share_after is not None:
+            parts.append(f"share={args.share_after}")
+    if args.pooled_mode is not None:
+        parts.append(f"mode={args.pooled_mode}:param={args.pooled_param}")
+    if args.token_order:
+        parts.append(f"order={args.token_order}")
+    if args.pyramid:
+        parts.append(f"pyramid={args.pyramid}")
+    return ":".join(parts)
+
+
+def _load_records() -> dict:
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return {}
-    if t.get("source_sha256") != source_sha() or t.get("workload") != workload:
+    return t.get("records", {}) if isinstance(t, dict) else {}
+
+
+def counters_for(key: str) -> dict:
+    """The counter record of profiles/traffic.json for this configuration when it was taken on
+    this kernel source, else {}."""
+    t = _load_records().get(key, {})
+    if t.get("source_sha256") != source_sha():
         return {}
     return t
 
 
-def _counter_mean(folder: str, kernel_substr: str, counter: str) -> tuple[float, int]:
-    """Mean per-dispatch value of a rocprofv3 counter over the dispatches of a kernel."""
+def _counter_mean(folder: str, kernel_substr: str, counter: str,
+                  window: tuple = (0, None)) -> tuple[float, int]:
+    """Mean per-dispatch value of a rocprofv3 counter over the dispatches of a kernel, taking
+    only the dispatches window[0]:window[1] of that kernel in dispatch order."""
     import csv
     import glob
     vals = {}
@@ -98,43 +124,151 @@ def _counter_mean(folder: str, kernel_substr: str, counter: str) -> tuple[float,
         with open(f) as fh:
             for r in csv.DictReader(fh):
                 if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
-                    vals[(f, r["Dispatch_Id"])] = vals.get((f, r["Dispatch_Id"]), 0.0) + \
-                        float(r["Counter_Value"])
-    if not vals:
-        raise SystemExit(f"no {counter} rows for kernels matching {kernel_substr!r} in {folder}")
-    return float(np.mean(list(vals.values()))), len(vals)
+                    key = (f, int(r["Dispatch_Id"]))
+                    vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    sel = [vals[k] for k in sorted(vals)][window[0]:window[1]]
+    if not sel:
+        raise SystemExit(f"no {counter} rows for kernels matching {kernel_substr!r} in {folder} "
+                         f"(window {window})")
+    return float(np.mean(sel)), len(sel)
 
 
-def ingest_counters(workload: str, fetch_dir: str, write_dir: str, copy_f: str, copy_w: str,
-                    sq_dir: str = None, grbm_dir: str = None):
+def ingest_counters(key: str, window: tuple, fetch_dir: str, write_dir: str, copy_f: str,
+                    copy_w: str, sq_dir: str = None):
     """HBM bytes per forward launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
     scaled by what the same counter reads for a device copy of 1 GiB each way. With the
-    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE folders it also records the fraction of
-    elapsed cycles in which the matrix cores are busy: busy cycles summed over the 1,024
-    SIMDs over (1,024 x elapsed cycles per XCD, GRBM_GUI_ACTIVE summed over the 8 XCDs / 8)."""
-    fetch, nf = _counter_mean(fetch_dir, "attn_bf16_kernel", "FETCH_SIZE")
-    write, nw = _counter_mean(write_dir, "attn_bf16_kernel", "WRITE_SIZE")
+    folder of a run that took SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and TA_BUSY_avr it
+    also records the fraction of elapsed cycles in which the matrix cores are busy (busy
+    cycles summed over the 1,024 SIMDs over 1,024 x elapsed cycles per XCD, GRBM_GUI_ACTIVE
+    being summed over the 8 XCDs), the texture-address busy fraction and the L2 hit rate. Stored under the
+    configuration's key in profiles/traffic.json. Only the forward dispatches of the timed
+    steps count (window: their range in the run's dispatch order)."""
+    fetch, nf = _counter_mean(fetch_dir, "attn_bf16_kernel", "FETCH_SIZE", window)
+    write, nw = _counter_mean(write_dir, "attn_bf16_kernel", "WRITE_SIZE", window)
     cf, _ = _counter_mean(copy_f, "copyBuffer", "FETCH_SIZE")
     cw, _ = _counter_mean(copy_w, "copyBuffer", "WRITE_SIZE")
     kib = float(1 << 20)  # 1 GiB in KiB, each way
     f_fetch, f_write = kib / cf, kib / cw
     traffic = (fetch * f_fetch + write * f_write) * 1024.0
-    out = {"workload": workload, "source_sha256": source_sha(),
+    out = {"source_sha256": source_sha(),
            "kernel": "attn_bf16_kernel", "dispatches": [nf, nw],
            "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
            "copy_fetch_kib_per_gib": cf, "copy_write_kib_per_gib": cw,
            "fetch_scale": f_fetch, "write_scale": f_write,
            "traffic_bytes_per_launch": traffic}
-    if sq_dir and grbm_dir:
-        busy, _ = _counter_mean(sq_dir, "attn_bf16_kernel", "SQ_VALU_MFMA_BUSY_CYCLES")
-        gui, _ = _counter_mean(grbm_dir, "attn_bf16_kernel", "GRBM_GUI_ACTIVE")
+    if sq_dir:
+        busy, _ = _counter_mean(sq_dir, "attn_bf16_kernel", "SQ_VALU_MFMA_BUSY_CYCLES", window)
+        gui, _ = _counter_mean(sq_dir, "attn_bf16_kernel", "GRBM_GUI_ACTIVE", window)
         out["mfma_busy_cycles"] = busy
         out["grbm_gui_active"] = gui
         out["mfma_busy_frac"] = busy / (MI355X_SIMDS * gui / MI355X_XCDS)
+        try:
+            ta, _ = _counter_mean(sq_dir, "attn_bf16_kernel", "TA_BUSY_avr", window)
+            out["ta_busy_frac"] = ta / (gui / MI355X_XCDS)
+        except SystemExit:
+            pass
+        try:
+            hit, _ = _counter_mean(sq_dir, "attn_bf16_kernel", "TCC_HIT_sum", window)
+            miss, _ = _counter_mean(sq_dir, "attn_bf16_kernel", "TCC_MISS_sum", window)
+            out["l2_hit_frac"] = hit / max(1.0, hit + miss)
+        except SystemExit:
+            pass
+    recs = _load_records()
+    recs[key] = out
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
-        json.dump(out, f, indent=1)
-    print(json.dumps(out))
+        json.dump({"records": recs}, f, indent=1, sort_keys=True)
+    print(json.dumps({key: out}))
+
+
+def _trace_durations(folder: str, kernel_substr: str) -> list:
+    """Durations (ms) of the dispatches of a kernel, in dispatch order, from a rocprofv3
+    --kernel-trace csv folder."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if kernel_substr in r["Kernel_Name"]:
+                    rows.append((int(r["Dispatch_Id"]),
+                                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6))
+    if not rows:
+        raise SystemExit(f"no {kernel_substr!r} dispatches in {folder}")
+    return [d for _, d in sorted(rows)]
+
+
+def summarize(args, key: str, w, trace_dir: str, bench_log: str):
+    """Markdown summary of a profiled bench run: the forward's dispatches split by their role
+    in the run (list capture, warm-up, timed, all-tiles, after a cache flush; the order
+    bench.py issues them in), the timed calls' mean against the bench line's own HIP-event
+    time, and the counter record of this configuration."""
+    durs = _trace_durations(trace_dir, "attn_bf16_kernel")
+    with open(bench_log) as fh:
+        line = [l for l in fh if l.startswith("{") and '"metric"' in l][-1]
+    b = json.loads(line)
+    n_cap = w.steps if w.mask == "skip" else 1
+    roles = ["list capture"] * n_cap + ["warm-up"] * b["warmup"] + ["timed"] * b["steps"]
+    if b["config"].get("dense_ms_per_call") is not None:
+        roles += ["all tiles"] * 3
+    if b["ms_per_call_stats"].get("after_cache_flush") is not None:
+        roles += ["after cache flush"] * 3
+    if w.mask == "pooled" and b.get("cpu_baseline") is not None:
+        roles += ["mask for the CPU sample"]
+    if len(roles) != len(durs):
+        raise SystemExit(f"{len(durs)} forward dispatches in the trace, {len(roles)} expected")
+    timed = [d for r, d in zip(roles, durs) if r == "timed"]
+    if w.mask == "skip":
+        per = [p["computed_tflop"] * 1e12 for p in b["per_step"]]
+        flops = [per[i % len(per)] for i in range(len(timed))]
+    else:
+        flops = [b["config"]["computed_tflop_per_call"] * 1e12] * len(timed)
+    flop = float(np.mean(flops))
+    t_mean = float(np.mean(timed))
+    frac_trace = float(np.sum(flops)) / (np.sum(timed) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+    out = [f"Configuration `{key}`, kernel source sha256 `{source_sha()}`.", "",
+           "| dispatches | count | mean ms |", "|---|---|---|"]
+    for role in dict.fromkeys(roles):
+        ds = [d for r, d in zip(roles, durs) if r == role]
+        out.append(f"| {role} | {len(ds)} | {np.mean(ds):.3f} |")
+    out += ["", "| quantity | value |", "|---|---|",
+            f"| computed-tile TFLOP per call | {flop / 1e12:.4f} |",
+            f"| timed calls, trace mean | {t_mean:.3f} ms |",
+            f"| timed calls, bench HIP events | {b['ms_per_call']:.3f} ms |",
+            f"| fraction of 2,500 TFLOP/s, from the trace | {frac_trace:.4f} |",
+            f"| fraction of 2,500 TFLOP/s, bench line | {b['roofline']['frac']:.4f} |",
+            f"| trace / bench | {frac_trace / b['roofline']['frac']:.4f} |"]
+    if w.mask == "skip":
+        out += ["", "| step | listed tiles | sparsity | TFLOP | trace mean ms | % of peak |",
+                "|---|---|---|---|---|---|"]
+        for p in b["per_step"]:
+            ds = [d for i, d in enumerate(timed) if i % len(b["per_step"]) == p["step"]]
+            if ds:
+                m = float(np.mean(ds))
+                out.append(f"| {p['step']} | {p['listed_tiles']} | {p['tile_sparsity']:.3f} | "
+                           f"{p['computed_tflop']:.4f} | {m:.3f} | "
+                           f"{100 * p['computed_tflop'] / (m * 1e-3) / PEAK_BF16_TFLOPS:.1f} |")
+        out.append("")
+    c = counters_for(key)
+    if c:
+        tr = c["traffic_bytes_per_launch"]
+        out += [f"| HBM traffic per launch (FETCH_SIZE x {c['fetch_scale']:.5f} + WRITE_SIZE x "
+                f"{c['write_scale']:.5f}) | {tr / 1e9:.3f} GB |",
+                f"| HBM bandwidth at the trace mean | {tr / (t_mean * 1e-3) / 1e9:.0f} GB/s "
+                f"({100 * tr / (t_mean * 1e-3) / 1e9 / PEAK_HBM_GBS:.1f}% of 8 TB/s) |"]
+        if "mfma_busy_frac" in c:
+            out.append(f"| matrix cores busy (SQ_VALU_MFMA_BUSY_CYCLES / (1,024 x "
+                       f"GRBM_GUI_ACTIVE / 8)) | {100 * c['mfma_busy_frac']:.1f}% |")
+            out.append(f"| engine clock under the counter run (GRBM_GUI_ACTIVE / 8 per "
+                       f"trace-mean call) | {c['grbm_gui_active'] / 8 / (t_mean * 1e-3) / 1e9:.2f} "
+                       f"GHz |")
+        if "ta_busy_frac" in c:
+            out.append(f"| texture address unit busy (TA_BUSY_avr) | "
+                       f"{100 * c['ta_busy_frac']:.1f}% |")
+        if "l2_hit_frac" in c:
+            out.append(f"| L2 hit rate (TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)) | "
+                       f"{100 * c['l2_hit_frac']:.1f}% |")
+    print("\n".join(out))
 
 
 def main():
@@ -176,15 +310,29 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-counters", nargs="+", metavar="DIR",
-                    help="turn rocprofv3 --pmc output folders into profiles/traffic.json, no GPU "
-                         "work: FETCH_SIZE and WRITE_SIZE of this workload's bench run, the same "
-                         "two of --calibrate-copy-mib 1024, and optionally a run with "
-                         "SQ_VALU_MFMA_BUSY_CYCLES and one with GRBM_GUI_ACTIVE (4 or 6 folders)")
+                    help="turn rocprofv3 --pmc output folders into this configuration's record "
+                         "in profiles/traffic.json, no GPU work: FETCH_SIZE and WRITE_SIZE of "
+                         "the configuration's bench run, the same two of --calibrate-copy-mib "
+                         "1024, and optionally a run with SQ_VALU_MFMA_BUSY_CYCLES, "
+                         "GRBM_GUI_ACTIVE and TA_BUSY_avr (4 or 5 folders)")
+    ap.add_argument("--summarize", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"),
+                    help="print a markdown summary of a rocprofv3 --kernel-trace run of this "
+                         "configuration's bench (its folder and the bench's stdout), no GPU work")
     args = ap.parse_args()
-    if args.ingest_counters:
-        if len(args.ingest_counters) not in (4, 6):
-            raise SystemExit("--ingest-counters takes 4 or 6 folders")
-        ingest_counters(args.workload, *args.ingest_counters)
+    if args.ingest_counters or args.summarize:
+        import synth
+        w0 = synth.workload(args.workload)
+        if args.tau is not None:
+            import dataclasses
+            w0 = dataclasses.replace(w0, tau=args.tau)
+        key = variant_key(args, w0)
+        if args.ingest_counters:
+            if len(args.ingest_counters) not in (4, 5):
+                raise SystemExit("--ingest-counters takes 4 or 5 folders")
+            lo = (w0.steps if w0.mask == "skip" else 1) + args.warmup
+            ingest_counters(key, (lo, lo + args.steps), *args.ingest_counters)
+        else:
+            summarize(args, key, w0, *args.summarize)
         return
 
     if args.gpus != 1:
@@ -499,7 +647,7 @@ def main():
                          f"(first step's mask), {sample_flops / 1e9:.1f} GFLOP fp64 in {cpu_s:.1f} s"}
         log(f"CPU oracle: {cpu['value'] * 1e3:.3f} GFLOP/s")
 
-    ctr = counters_for(w.name)
+    ctr = counters_for(variant_key(args, w))
     traffic = ctr.get("traffic_bytes_per_launch")
     out = {
         "metric": METRIC,
@@ -545,6 +693,7 @@ def main():
             "traffic": traffic,
             "hbm_gbs": traffic / (fwd_ms * 1e-3) / 1e9 if traffic else None,
             "mfma_busy_frac": ctr.get("mfma_busy_frac"),
+            "counters": variant_key(args, w) if ctr else None,
         },
         "cpu_baseline": cpu,
     }
