@@ -10,6 +10,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "bsa_internal.h"
@@ -234,6 +235,41 @@ __device__ inline double ordered_sum(const double* a, int64_t n, double acc) {
   return acc;
 }
 
+// The same sum as ordered_sum (acc + a[0] + ... + a[n-1] in that order), with
+// the LDS reads two values at a time and one 16-value chunk ahead of the
+// additions, so the chain of adds does not wait for the reads. `a` is
+// 16-byte aligned.
+__device__ inline double ordered_sum_ahead(const double* a, int64_t n, double acc) {
+  typedef double d2 __attribute__((ext_vector_type(2)));
+  const d2* a2 = (const d2*)a;
+  int64_t c = 0;
+  if (n >= 16) {
+    d2 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = a2[u];
+    for (; c + 32 <= n; c += 16) {
+      d2 y[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) y[u] = a2[(c + 16) / 2 + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc = acc + x[u].x;
+        acc = acc + x[u].y;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = y[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc = acc + x[u].x;
+      acc = acc + x[u].y;
+    }
+    c += 16;
+  }
+  for (; c < n; ++c) acc = acc + a[c];
+  return acc;
+}
+
 // Order-preserving map of a double to 64 bits (larger value -> larger key;
 // -0 and +0 map alike).
 __device__ inline uint64_t order_key(double v) {
@@ -245,6 +281,11 @@ __device__ inline uint64_t order_key(double v) {
 
 constexpr int kSelectThreads = 256;
 constexpr int kPooledMaxBlocks = 2048;  // keeps the select kernel under 64 KiB of LDS
+// First mask byte of a row left to the full sort (mask values are 0..3).
+constexpr uint8_t kSelectMarker = 0xFF;
+// Rows per workgroup of the one-wave-per-row select (at most; fewer when their
+// LDS would pass 64 KiB) and of the pass that finishes the rows it marked.
+constexpr int kSelectRowsPerGroup = 4;
 
 // Bitonic sort of the pairs (ks[t], ki[t]), t < P, P a power of two, into
 // descending order_key of the score, ascending block index on equal keys
@@ -468,37 +509,41 @@ __device__ inline RowCut select_kth(const double* s, int64_t nK, int T) {
 // the levels are set in parallel. Stops after the chunk in which the sum
 // reaches tau_{nl-1} (every later entry is dropped); returns whether it did.
 // The thresholds are non-decreasing; nl is 1..3.
+// CH entries per chunk (16, or 8 where registers are scarce; the sums are
+// the same either way).
+template <int CH = 16>
 __device__ inline bool walk_mass(const double* pv, const int32_t* idx, int64_t n, double tau0,
                                  double tau1, double tau2, int nl, uint8_t* flag) {
   const int lane = threadIdx.x & 63;
   const double last = nl == 1 ? tau0 : (nl == 2 ? tau1 : tau2);
   double run = 0.0;
-  for (int c0 = 0; c0 < (int)n; c0 += 16) {
-    const int m = min(16, (int)n - c0);
-    double v[16];
-    if (m == 16) {  // a whole chunk: contiguous reads
+  for (int c0 = 0; c0 < (int)n; c0 += CH) {
+    const int m = min(CH, (int)n - c0);
+    double v[CH];
+    if (m == CH) {  // a whole chunk: contiguous reads
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = pv[c0 + u];
+      for (int u = 0; u < CH; ++u) v[u] = pv[c0 + u];
     } else {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = u < m ? pv[c0 + min(u, m - 1)] : 0.0;
+      for (int u = 0; u < CH; ++u) v[u] = u < m ? pv[c0 + min(u, m - 1)] : 0.0;
     }
     // (entries past n add 0: run + 0 = run, the sum being >= +0)
     // the chain first (each intermediate sum in its own register), the
     // lane's pick afterwards, so that no select waits inside the chain
-    double pre[16];
+    double pre[CH];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < CH; ++u) {
       pre[u] = run;
       run = run + v[u];
     }
     double ex = pre[0];
 #pragma unroll
-    for (int u = 1; u < 16; ++u) ex = lane == u ? pre[u] : ex;
+    for (int u = 1; u < CH; ++u) ex = lane == u ? pre[u] : ex;
     if (lane < m) {
       int lvl = 0;
       if (c0 + lane > 0)
-        lvl = (ex >= tau0 ? 1 : 0) + (nl > 1 && ex >= tau1 ? 1 : 0) + (nl > 2 && ex >= tau2 ? 1 : 0);
+        lvl = (ex >= tau0 ? 1 : 0) + (nl > 1 && ex >= tau1 ? 1 : 0) +
+              (nl > 2 && ex >= tau2 ? 1 : 0);
       if (lvl < nl) flag[idx[c0 + lane]] = (uint8_t)(1 + lvl);
     }
     if (run >= last) return true;
@@ -514,7 +559,8 @@ __device__ inline bool walk_mass(const double* pv, const int32_t* idx, int64_t n
 // the quotients are formed in parallel beforehand.
 __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double param,
                                      double tau1, double tau2, int32_t n_levels,
-                                     const double* __restrict__ S, uint8_t* __restrict__ mask) {
+                                     const double* __restrict__ S, uint8_t* __restrict__ mask,
+                                     int32_t only_marked, int64_t R) {
   extern __shared__ double smd[];
   double* s = smd;                    // [nK] scores, block order
   double* ks = smd + nK;              // [P] sort keys: scores, then p in sorted order
@@ -522,109 +568,357 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
   uint8_t* flag = (uint8_t*)(ki + P);  // [nK]
   __shared__ int32_t keep_sh;
   __shared__ double z_sh;
-  const int64_t row = blockIdx.x;
-  const double* srow = S + row * nK;
-  for (int c = threadIdx.x; c < nK; c += blockDim.x) {
-    s[c] = srow[c];
-    flag[c] = 0;
-  }
-  __syncthreads();
-  uint8_t* mrow = mask + row * nK;
-  // Fast paths for long rows, no full sort: top-k marks the pairs before the
-  // k-th key; cumulative mass sorts only the first kTopM pairs (the head of
-  // the full order) and stops there if the mass is reached. A cut inside a
-  // run of equal keys, or mass not reached, takes the full sort below.
-  if ((mode == 0 || mode == 1) && nK > kTopM && !(mode == 0 && param >= (double)nK)) {
-    const int T = mode == 0 ? (int)max(1.0, param) : kTopM;
-    const RowCut cut = select_kth(s, nK, T);
-    if (cut.take_eq == cut.n_eq) {  // every pair with the cut key is taken
-      if (mode == 0) {
-        for (int c = threadIdx.x; c < nK; c += blockDim.x)
-          mrow[c] = order_key(s[c]) >= cut.key ? 1 : 0;
-        return;
-      }
-      __shared__ uint64_t ck[kTopM];  // sort keys, then the probabilities
-      __shared__ int32_t ci[kTopM];
-      __shared__ int32_t ncand;
-      double* cs = (double*)ck;
-      if (threadIdx.x == 0) ncand = 0;
-      __syncthreads();
-      for (int64_t c0 = 0; c0 < nK; c0 += blockDim.x) {
-        const int c = (int)(c0 + threadIdx.x);
-        const uint64_t u = c < nK ? order_key(s[c]) : 0;
-        const bool hit = c < nK && u >= cut.key;
-        const int pos = wave_append(hit, &ncand);
-        if (hit) {
-          ck[pos] = u;
-          ci[pos] = c;
+  // after pooled_select_wave_kernel: only the rows it left marked, a few
+  // rows per workgroup; else one row
+  const int64_t rows_per = only_marked ? kSelectRowsPerGroup : 1;
+  const int64_t row_end = min(R, ((int64_t)blockIdx.x + 1) * rows_per);
+  for (int64_t row = (int64_t)blockIdx.x * rows_per; row < row_end; ++row) {
+    uint8_t* mrow = mask + row * nK;
+    if (only_marked && mrow[0] != kSelectMarker) continue;  // uniform: one byte for all
+    const double* srow = S + row * nK;
+    for (int c = threadIdx.x; c < nK; c += blockDim.x) {
+      s[c] = srow[c];
+      flag[c] = 0;
+    }
+    __syncthreads();
+    // Fast paths for long rows, no full sort: top-k marks the pairs before the
+    // k-th key; cumulative mass sorts only the first kTopM pairs (the head of
+    // the full order) and stops there if the mass is reached. A cut inside a
+    // run of equal keys, or mass not reached, takes the full sort below.
+    if (!only_marked && (mode == 0 || mode == 1) && nK > kTopM &&
+        !(mode == 0 && param >= (double)nK)) {
+      const int T = mode == 0 ? (int)max(1.0, param) : kTopM;
+      const RowCut cut = select_kth(s, nK, T);
+      if (cut.take_eq == cut.n_eq) {  // every pair with the cut key is taken
+        if (mode == 0) {
+          for (int c = threadIdx.x; c < nK; c += blockDim.x)
+            mrow[c] = order_key(s[c]) >= cut.key ? 1 : 0;
+          return;
+        }
+        __shared__ uint64_t ck[kTopM];  // sort keys, then the probabilities
+        __shared__ int32_t ci[kTopM];
+        __shared__ int32_t ncand;
+        double* cs = (double*)ck;
+        if (threadIdx.x == 0) ncand = 0;
+        __syncthreads();
+        for (int64_t c0 = 0; c0 < nK; c0 += blockDim.x) {
+          const int c = (int)(c0 + threadIdx.x);
+          const uint64_t u = c < nK ? order_key(s[c]) : 0;
+          const bool hit = c < nK && u >= cut.key;
+          const int pos = wave_append(hit, &ncand);
+          if (hit) {
+            ck[pos] = u;
+            ci[pos] = c;
+          }
+        }
+        __syncthreads();
+        if (threadIdx.x < 64) sort128_wave(ck, ci);
+        __syncthreads();
+        const double smax0 = s[ci[0]];
+        for (int c = threadIdx.x; c < nK; c += blockDim.x) ks[c] = exp(s[c] - smax0);
+        __syncthreads();
+        if (threadIdx.x < 64) {
+          const double Z = ordered_sum(ks, nK, 0.0);
+          if (threadIdx.x == 0) z_sh = Z;
+        }
+        __syncthreads();
+        const double Z0 = z_sh;
+        for (int t = threadIdx.x; t < kTopM; t += blockDim.x) cs[t] = ks[ci[t]] / Z0;
+        __syncthreads();
+        // flags of the first kTopM pairs; if the mass is not reached there,
+        // they are a subset of what the full sort below keeps
+        if (threadIdx.x < 64) {
+          const bool reached = walk_mass(cs, ci, kTopM, param, param, param, 1, flag);
+          if (threadIdx.x == 0) keep_sh = reached ? 1 : 0;
+        }
+        __syncthreads();
+        if (keep_sh) {
+          for (int c = threadIdx.x; c < nK; c += blockDim.x) mrow[c] = flag[c];
+          return;
         }
       }
+    }
+    uint64_t* kk = (uint64_t*)ks;  // sort keys, then the probabilities in ks
+    for (int c = threadIdx.x; c < P; c += blockDim.x) {
+      kk[c] = c < nK ? order_key(s[c]) : 0;
+      ki[c] = c < nK ? c : -1;
+    }
+    __syncthreads();
+    sort_keys(kk, ki, P);
+    const double smax = s[ki[0]];
+    int32_t keep;
+    if (mode == 0) {
+      keep = (int32_t)min((double)nK, param);
+    } else {
+      // e = exp(S - max) in block order, over the scores (once every thread
+      // has read the maximum from them)
       __syncthreads();
-      if (threadIdx.x < 64) sort128_wave(ck, ci);
-      __syncthreads();
-      const double smax0 = s[ci[0]];
-      for (int c = threadIdx.x; c < nK; c += blockDim.x) ks[c] = exp(s[c] - smax0);
+      for (int c = threadIdx.x; c < nK; c += blockDim.x) s[c] = exp(s[c] - smax);
       __syncthreads();
       if (threadIdx.x < 64) {
-        const double Z = ordered_sum(ks, nK, 0.0);
+        const double Z = ordered_sum(s, nK, 0.0);
         if (threadIdx.x == 0) z_sh = Z;
       }
       __syncthreads();
-      const double Z0 = z_sh;
-      for (int t = threadIdx.x; t < kTopM; t += blockDim.x) cs[t] = ks[ci[t]] / Z0;
+      const double Z = z_sh;
+      // p_t = e[idx_t] / Z in sorted order, each quotient on its own; the
+      // sorted scores are not needed any more
+      for (int t = threadIdx.x; t < nK; t += blockDim.x) ks[t] = s[ki[t]] / Z;
       __syncthreads();
-      // flags of the first kTopM pairs; if the mass is not reached there,
-      // they are a subset of what the full sort below keeps
-      if (threadIdx.x < 64) {
-        const bool reached = walk_mass(cs, ci, kTopM, param, param, param, 1, flag);
-        if (threadIdx.x == 0) keep_sh = reached ? 1 : 0;
-      }
+      // mode 1: the shortest prefix whose running mass reaches tau_p (entry t
+      // kept while the mass before it is below tau_p); mode 4, pyramid levels
+      // ([PSA]: a resolution level per block pair by importance thresholds):
+      // a block joins the current level, and the level advances past every
+      // threshold that the running mass including that block has reached
+      keep = 0;
+      if (threadIdx.x < 64)
+        walk_mass(ks, ki, nK, param, tau1, tau2, mode == 4 ? n_levels : 1, flag);
       __syncthreads();
-      if (keep_sh) {
-        for (int c = threadIdx.x; c < nK; c += blockDim.x) mrow[c] = flag[c];
-        return;
-      }
+    }
+    for (int t = threadIdx.x; t < keep; t += blockDim.x) flag[ki[t]] = 1;
+    __syncthreads();
+    for (int c = threadIdx.x; c < nK; c += blockDim.x) mrow[c] = flag[c];
+    __syncthreads();  // the next row refills the shared arrays
+  }
+}
+
+// The common per-row case (top-k, and cumulative mass whose prefix lies in
+// the first kTopM pairs) with one wave per row and four rows per workgroup:
+// the work of a row is mostly sequential (the ordered sums), so a row holds
+// one wave instead of a workgroup, no step waits on a workgroup barrier, and
+// four times as many rows run at once. Same arithmetic as the fast path of
+// pooled_select_kernel: the cut key by a radix select (one bit per pass, the
+// last few candidates ranked directly), the first kTopM pairs sorted, Z in
+// ascending block order, the running mass in sorted order. A row whose cut
+// falls inside a run of equal keys (cumulative mass), or whose mass is not
+// reached within kTopM pairs, gets kSelectMarker in its first mask byte and
+// is finished by pooled_select_kernel (only_marked).
+
+__host__ __device__ inline size_t select_wave_lds(int64_t nK) {
+  // scores, then exponentials, then flags [nK] doubles; candidate keys /
+  // probabilities [kTopM] and their indices [kTopM]
+  return (sizeof(double) * (size_t)nK + 12 * kTopM + 15) / 16 * 16;  // 16-byte aligned slices
+}
+
+template <int NC>  // 64-key chunks per row held in registers (nK <= 64 * NC)
+__global__ __launch_bounds__(kWave * kSelectRowsPerGroup) void pooled_select_wave_kernel(
+    int64_t R, int64_t nK, int32_t mode, double param, const double* __restrict__ S,
+    uint8_t* __restrict__ mask) {
+  extern __shared__ double smw[];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + w;
+  if (row >= R) return;  // the whole wave (no workgroup barrier below)
+  char* base = (char*)smw + (size_t)w * select_wave_lds(nK);
+  double* s = (double*)base;
+  uint64_t* ck = (uint64_t*)(s + nK);
+  int32_t* ci = (int32_t*)(ck + kTopM);
+  const double* srow = S + row * nK;
+  uint8_t* mrow = mask + row * nK;
+  // the row's scores (all loads in flight together) into LDS, and their
+  // sort keys into registers: key[i] is block 64 i + lane (0 past the row,
+  // below every score's key, and never counted)
+  uint64_t key[NC];
+  {
+    double v[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int64_t c = i * kWave + lane;
+      v[i] = c < nK ? srow[c] : 0.0;
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int64_t c = i * kWave + lane;
+      key[i] = c < nK ? order_key(v[i]) : 0;
+      if (c < nK) s[c] = v[i];
     }
   }
-  uint64_t* kk = (uint64_t*)ks;  // sort keys, then the probabilities in ks
-  for (int c = threadIdx.x; c < P; c += blockDim.x) {
-    kk[c] = c < nK ? order_key(s[c]) : 0;
-    ki[c] = c < nK ? c : -1;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  // ---- key of the T-th pair in (score desc, index asc) order, one bit per
+  // pass from the highest bit in which the row's keys differ; `want` counts
+  // the pairs still wanted among those matching the bits fixed so far. The
+  // passes over the upper half of the key compare 32-bit words only.
+  const int T = mode == 0 ? (int)max(1.0, param) : kTopM;
+  uint64_t kmax = 0, kmin = ~0ull;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    if (i * kWave + lane < nK) {
+      kmax = key[i] > kmax ? key[i] : kmax;
+      kmin = key[i] < kmin ? key[i] : kmin;
+    }
   }
-  __syncthreads();
-  sort_keys(kk, ki, P);
-  const double smax = s[ki[0]];
-  int32_t keep;
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t xa = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(kmax >> 32), off) << 32) |
+                        (uint32_t)__shfl_xor((int)(uint32_t)kmax, off);
+    const uint64_t xi = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(kmin >> 32), off) << 32) |
+                        (uint32_t)__shfl_xor((int)(uint32_t)kmin, off);
+    kmax = xa > kmax ? xa : kmax;
+    kmin = xi < kmin ? xi : kmin;
+  }
+  const int top = kmax == kmin ? -1 : 63 - __builtin_clzll(kmax ^ kmin);
+  // bits above `top` are common to every key of the row
+  uint64_t prefix = top >= 63 ? 0 : kmax & (~0ull << (top + 1));
+  int want = T;
+  uint64_t cut = kmax;
+  int take_eq = want, n_eq = (int)nK;  // every key equal (top < 0)
+  for (int bit = top; bit >= 0; --bit) {
+    int ones = 0, match = 0;
+    if (bit >= 32) {
+      const int b32 = bit - 32;
+      const uint32_t hi = b32 == 31 ? 0u : (~0u << (b32 + 1));
+      const uint32_t ph = (uint32_t)(prefix >> 32);
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const uint32_t kh = (uint32_t)(key[i] >> 32);
+        const bool m = i * kWave + lane < nK && (kh & hi) == ph;
+        ones += __popcll(__builtin_amdgcn_ballot_w64(m && ((kh >> b32) & 1u)));
+        match += __popcll(__builtin_amdgcn_ballot_w64(m));
+      }
+    } else {
+      const uint32_t lo = bit == 31 ? 0u : (~0u << (bit + 1));
+      const uint32_t ph = (uint32_t)(prefix >> 32), pl = (uint32_t)prefix;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const uint32_t kh = (uint32_t)(key[i] >> 32), kl = (uint32_t)key[i];
+        const bool m = i * kWave + lane < nK && kh == ph && (kl & lo) == pl;
+        ones += __popcll(__builtin_amdgcn_ballot_w64(m && ((kl >> bit) & 1u)));
+        match += __popcll(__builtin_amdgcn_ballot_w64(m));
+      }
+    }
+    int left;
+    if (ones >= want) {
+      prefix |= 1ull << bit;
+      left = ones;
+    } else {
+      want -= ones;
+      left = match - ones;
+    }
+    if (left == match && left > kWave && bit > 0) {
+      // no pair dropped out: skip the bits below in which the pairs left all
+      // agree (their largest and smallest key share them)
+      const uint64_t pm = ~0ull << bit;
+      uint64_t gmax = 0, gmin = ~0ull;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        if (i * kWave + lane < nK && (key[i] & pm) == prefix) {
+          gmax = key[i] > gmax ? key[i] : gmax;
+          gmin = key[i] < gmin ? key[i] : gmin;
+        }
+      }
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint64_t xa =
+            ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(gmax >> 32), off) << 32) |
+            (uint32_t)__shfl_xor((int)(uint32_t)gmax, off);
+        const uint64_t xi =
+            ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(gmin >> 32), off) << 32) |
+            (uint32_t)__shfl_xor((int)(uint32_t)gmin, off);
+        gmax = xa > gmax ? xa : gmax;
+        gmin = xi < gmin ? xi : gmin;
+      }
+      if (gmax == gmin) {  // every pair left has the same key
+        cut = gmax;
+        take_eq = want;
+        n_eq = left;
+        break;
+      }
+      const int nb = 63 - __builtin_clzll(gmax ^ gmin);  // below `bit`
+      prefix = gmax & (~0ull << (nb + 1));
+      bit = nb + 1;  // the next pass decides bit nb
+      continue;
+    }
+    if (left <= kWave) {
+      // the pairs left (bits from `bit` up equal the prefix), one per lane;
+      // the want-th largest key among them and its multiplicity
+      const uint64_t pm = ~0ull << bit;
+      int got = 0;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const bool hit = i * kWave + lane < nK && (key[i] & pm) == prefix;
+        const uint64_t hm = __builtin_amdgcn_ballot_w64(hit);
+        if (hit) ck[got + __popcll(hm & ((1ull << lane) - 1))] = key[i];
+        got += __popcll(hm);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      const uint64_t mine = lane < got ? ck[lane] : 0;
+      int above = 0, same = 0;
+      for (int j = 0; j < got; ++j) {
+        const uint64_t o = ck[j];
+        above += o > mine;
+        same += o == mine;
+      }
+      const bool pick = lane < got && above < want && want <= above + same;
+      const int src = __builtin_ctzll(__builtin_amdgcn_ballot_w64(pick));
+      cut = ((uint64_t)(uint32_t)__shfl((int)(uint32_t)(mine >> 32), src) << 32) |
+            (uint32_t)__shfl((int)(uint32_t)mine, src);
+      take_eq = __shfl(want - above, src);
+      n_eq = __shfl(same, src);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      break;
+    }
+    if (bit == 0) {  // more than a wave of pairs share the cut key
+      cut = prefix;
+      take_eq = want;
+      n_eq = left;
+    }
+  }
   if (mode == 0) {
-    keep = (int32_t)min((double)nK, param);
-  } else {
-    // e = exp(S - max) in block order, over the scores (once every thread
-    // has read the maximum from them)
-    __syncthreads();
-    for (int c = threadIdx.x; c < nK; c += blockDim.x) s[c] = exp(s[c] - smax);
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      const double Z = ordered_sum(s, nK, 0.0);
-      if (threadIdx.x == 0) z_sh = Z;
+    // keys above the cut, and of those equal to it the first take_eq in
+    // ascending block order
+    int seen = 0;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int64_t c = i * kWave + lane;
+      const bool eq = c < nK && key[i] == cut;
+      const uint64_t em = __builtin_amdgcn_ballot_w64(eq);
+      const int rank = seen + __popcll(em & ((1ull << lane) - 1));
+      if (c < nK) mrow[c] = (key[i] > cut || (eq && rank < take_eq)) ? 1 : 0;
+      seen += __popcll(em);
     }
-    __syncthreads();
-    const double Z = z_sh;
-    // p_t = e[idx_t] / Z in sorted order, each quotient on its own; the
-    // sorted scores are not needed any more
-    for (int t = threadIdx.x; t < nK; t += blockDim.x) ks[t] = s[ki[t]] / Z;
-    __syncthreads();
-    // mode 1: the shortest prefix whose running mass reaches tau_p (entry t
-    // kept while the mass before it is below tau_p); mode 4, pyramid levels
-    // ([PSA]: a resolution level per block pair by importance thresholds):
-    // a block joins the current level, and the level advances past every
-    // threshold that the running mass including that block has reached
-    keep = 0;
-    if (threadIdx.x < 64) walk_mass(ks, ki, nK, param, tau1, tau2, mode == 4 ? n_levels : 1, flag);
-    __syncthreads();
+    return;
   }
-  for (int t = threadIdx.x; t < keep; t += blockDim.x) flag[ki[t]] = 1;
-  __syncthreads();
-  for (int c = threadIdx.x; c < nK; c += blockDim.x) mrow[c] = flag[c];
+  if (take_eq != n_eq) {  // cut inside a run of equal keys: the full sort decides
+    if (lane == 0) mrow[0] = kSelectMarker;
+    return;
+  }
+  // ---- the kTopM pairs at or above the cut, sorted
+  {
+    int got = 0;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int64_t c = i * kWave + lane;
+      const bool hit = c < nK && key[i] >= cut;
+      const uint64_t hm = __builtin_amdgcn_ballot_w64(hit);
+      const int pos = got + __popcll(hm & ((1ull << lane) - 1));
+      if (hit) {
+        ck[pos] = key[i];
+        ci[pos] = (int32_t)c;
+      }
+      got += __popcll(hm);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  sort128_wave(ck, ci);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  // ---- e = exp(S - max) in place, Z in ascending block order, p of the
+  // sorted pairs, running mass
+  const double smax0 = s[ci[0]];
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  for (int64_t c = lane; c < nK; c += kWave) s[c] = exp(s[c] - smax0);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const double Z = ordered_sum_ahead(s, nK, 0.0);
+  double* cs = (double*)ck;
+  for (int t = lane; t < kTopM; t += kWave) cs[t] = s[ci[t]] / Z;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  uint8_t* flag = (uint8_t*)s;  // the exponentials are used up
+  for (int64_t c = lane; c < nK; c += kWave) flag[c] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const bool reached = walk_mass<8>(cs, ci, kTopM, param, param, param, 1, flag);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (!reached) {
+    if (lane == 0) mrow[0] = kSelectMarker;
+    return;
+  }
+  for (int64_t c = lane; c < nK; c += kWave) mrow[c] = flag[c];
 }
 
 // ------------------------------------------------------- global selection
@@ -1245,10 +1539,31 @@ hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k
   if (mode == 2 || mode == 3) return launch_pooled_global(g, mode, param, mask, ws, st);
   int32_t P = 1;
   while (P < g.nK) P <<= 1;
+  const int64_t R = BH * g.nQ;
+  int32_t only_marked = 0;
+  if ((mode == 0 || mode == 1) && g.nK > kTopM && !(mode == 0 && param >= (double)g.nK)) {
+    const size_t per = select_wave_lds(g.nK);
+    const int64_t rpg = std::min<int64_t>(kSelectRowsPerGroup, (int64_t)(65536 / per));
+    const dim3 grid((unsigned)((R + rpg - 1) / rpg)), block((unsigned)(kWave * rpg));
+    if (g.nK <= 8 * kWave)
+      hipLaunchKernelGGL(pooled_select_wave_kernel<8>, grid, block, per * rpg, st, R, g.nK, mode,
+                         param, S, mask);
+    else if (g.nK <= 16 * kWave)
+      hipLaunchKernelGGL(pooled_select_wave_kernel<16>, grid, block, per * rpg, st, R, g.nK, mode,
+                         param, S, mask);
+    else
+      hipLaunchKernelGGL(pooled_select_wave_kernel<32>, grid, block, per * rpg, st, R, g.nK, mode,
+                         param, S, mask);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (mode == 0) return hipSuccess;  // top-k never needs the full sort
+    only_marked = 1;
+  }
   const size_t sh2 = sizeof(double) * (g.nK + P) + sizeof(int32_t) * P + g.nK;
-  hipLaunchKernelGGL(pooled_select_kernel, dim3((unsigned)(BH * g.nQ)), dim3(kSelectThreads),
-                     sh2, st, g.nK, P, mode, param, levels ? levels[1] : 0.0,
-                     levels ? levels[2] : 0.0, n_levels, S, mask);
+  const int64_t groups = only_marked ? (R + kSelectRowsPerGroup - 1) / kSelectRowsPerGroup : R;
+  hipLaunchKernelGGL(pooled_select_kernel, dim3((unsigned)groups), dim3(kSelectThreads), sh2, st,
+                     g.nK, P, mode, param, levels ? levels[1] : 0.0, levels ? levels[2] : 0.0,
+                     n_levels, S, mask, only_marked, R);
   return hipGetLastError();
 }
 

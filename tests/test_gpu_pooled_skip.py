@@ -68,23 +68,27 @@ def test_pooled_mask_long_rows_bit_exact(mode, param):
     np.testing.assert_array_equal(got, ref)
 
 
-@pytest.mark.parametrize("mode,param", [(0, 77.0), (0, 300.0), (1, 0.3), (1, 0.95)])
-def test_pooled_mask_long_rows_ties_bit_exact(mode, param):
-    """Rows of 400 key blocks in which the keys repeat every seven blocks, so
-    every score comes in a tie group of 57 or 58 blocks: the k-th or 128th
-    pair of a row falls inside a tie group, the radix select ends with equal
-    keys among its last candidates, and the long-row paths must fall back
-    to the full sort that takes tied blocks in ascending order."""
+@pytest.mark.parametrize("period,mode,param", [(7, 0, 77.0), (7, 0, 300.0), (7, 1, 0.3),
+                                               (7, 1, 0.95), (3, 0, 77.0), (3, 1, 0.3)])
+def test_pooled_mask_long_rows_ties_bit_exact(period, mode, param):
+    """Rows of 400 key blocks in which the keys repeat every `period` blocks,
+    so every score comes in a tie group of 57 or 58 blocks (period 7) or of
+    133 or 134 (period 3, more than one wave of candidates with the cut key):
+    the k-th or 128th pair of a row falls inside a tie group, the radix
+    select ends with equal keys among its last candidates, and the long-row
+    paths must take tied blocks in ascending order (top-k directly,
+    cumulative mass through the full sort)."""
     w = synth.Workload("pooled_ties_long", 1, 2, 64, 25, 32, 32, 128, 64, "bf16", "pooled", 614,
                        True)
     x = synth.make_qkv(w)
     k = x["k"].reshape(w.B, w.nK, w.Bk, w.H, w.d)
-    x["k"] = np.ascontiguousarray(k[:, np.arange(w.nK) % 7].reshape(x["k"].shape))
+    x["k"] = np.ascontiguousarray(k[:, np.arange(w.nK) % period].reshape(x["k"].shape))
     got = _pooled_gpu(w, x, mode, param)
     ref, S, _ = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, mode, param,
                                          want_scores=True)
-    assert np.all(S[..., 7:] == S[..., :-7])   # scores repeat with the keys
-    note(f"pooled tied long rows mode={mode} param={param}: {int(ref.sum())} kept")
+    assert np.all(S[..., period:] == S[..., :-period])   # scores repeat with the keys
+    note(f"pooled tied long rows period={period} mode={mode} param={param}: "
+         f"{int(ref.sum())} kept")
     np.testing.assert_array_equal(got, ref)
 
 
