@@ -1028,9 +1028,8 @@ __global__ void gsel_init_kernel(int64_t BH, int64_t nQ, int64_t nK, int32_t mod
 // pair.
 // After the first passes few pairs still match the prefix: the pass with
 // phase 1 also stores each thread's matching keys (and masses) in its own
-// slice of the candidate store, in its visiting order, and the passes with
-// phase 2 walk only those, keeping the ones that still match. A thread thus
-// adds the same values in the same order as a pass over every pair would.
+// slice of the candidate store, in its visiting order, and gsel_finish_kernel
+// runs the remaining passes over those alone.
 __global__ __launch_bounds__(kGselThreads) void gsel_hist_kernel(
     int64_t nQ, int64_t nK, int32_t mode, int32_t shift, const double* __restrict__ S,
     const double* __restrict__ P, HeadCut* cut, int64_t* pc, double* pm, int32_t phase,
@@ -1057,7 +1056,7 @@ __global__ __launch_bounds__(kGselThreads) void gsel_hist_kernel(
   // (and masses) are loaded kGselBatch at a time before they are counted, so
   // that the loads are in flight together instead of one memory latency per
   // pair.
-  if (phase < 2) {
+  {
     int32_t j = 0;
     for (int64_t eb = e0 + tid; eb < e1; eb += (int64_t)kGselBatch * kGselThreads) {
       uint64_t ub[kGselBatch];
@@ -1084,35 +1083,6 @@ __global__ __launch_bounds__(kGselThreads) void gsel_hist_kernel(
       }
     }
     if (phase == 1) *my_cnt = j;
-  } else {
-    // the candidates still matching move down in place (slot jn <= j)
-    const int32_t m = *my_cnt;
-    int32_t jn = 0;
-    for (int32_t jb = 0; jb < m; jb += kGselBatch) {
-      uint64_t ub[kGselBatch];
-      double mb[kGselBatch];
-#pragma unroll
-      for (int i = 0; i < kGselBatch; ++i) {
-        const int64_t slot = cbase + (int64_t)(jb + i) * kGselThreads;
-        ub[i] = jb + i < m ? ck[slot] : 0;
-        mb[i] = (mode == 3 && jb + i < m) ? cm[slot] : 0.0;
-      }
-#pragma unroll
-      for (int i = 0; i < kGselBatch; ++i) {
-        const int32_t j = jb + i;
-        const uint64_t u = ub[i];
-        if (j >= m || (u & pmask) != c.prefix) continue;
-        const int b = (int)((u >> shift) & 15);
-        hc[b][tid] += 1;
-        if (mode == 3) hm[b][tid] = hm[b][tid] + mb[i];
-        if (jn != j) {
-          ck[cbase + (int64_t)jn * kGselThreads] = u;
-          if (mode == 3) cm[cbase + (int64_t)jn * kGselThreads] = mb[i];
-        }
-        ++jn;
-      }
-    }
-    *my_cnt = jn;
   }
   __syncthreads();
   // slot i += slot i + off for every bucket, off halving: the fixed tree of
@@ -1166,6 +1136,239 @@ __global__ __launch_bounds__(kGselThreads) void gsel_hist_kernel(
     h.prefix |= (uint64_t)chosen << shift;
     h.done = 0;  // the next pass counts its groups again
     cut[bh] = h;
+  }
+}
+
+// The digits after the candidate store is filled, in one workgroup per head.
+// While more candidates match the prefix than fit in LDS, a pass fixes the
+// next 4-bit digit as gsel_hist_kernel does (thread t walks its slices (g, t)
+// in a fixed order; its per-bucket counts and masses are summed in the same
+// fixed tree). Then the matching candidates are compacted into LDS in that
+// same visiting order (a
+// count pass, an exclusive scan over the threads, a write pass), sorted by
+// key (descending, then by position) and walked run by run of equal keys: a
+// run whose count (mode 2) or mass (mode 3, its masses added in sorted order)
+// reaches what is still needed holds the cut; otherwise its pairs are taken
+// and the walk goes on, ending in the last run when nothing reaches.
+// Deterministic.
+constexpr int kFinishCap = 2048;  // candidates sorted in LDS
+
+__global__ __launch_bounds__(kGselThreads) void gsel_finish_kernel(
+    int64_t nQ, int64_t nK, int32_t mode, int32_t first_shift, HeadCut* cut,
+    const uint64_t* __restrict__ ck, const double* __restrict__ cm,
+    const int32_t* __restrict__ ccnt) {
+  // sort arrays (40 KiB) or digit slots (48 KiB), one at a time
+  __shared__ __attribute__((aligned(16))) char pool[16 * kGselThreads * 12];
+  uint64_t* lk = (uint64_t*)pool;                                // [kFinishCap] keys, 0 = pad
+  int32_t* li = (int32_t*)(pool + 8 * kFinishCap);               // positions in lm, -1 = pad
+  double* lm = (double*)(pool + 12 * kFinishCap);                // masses, compacted order
+  double(*hm)[kGselThreads] = (double(*)[kGselThreads])pool;     // [16][threads]
+  int32_t(*hc)[kGselThreads] = (int32_t(*)[kGselThreads])(pool + 8 * 16 * kGselThreads);
+  __shared__ int32_t toff[kGselThreads + 1];
+  __shared__ HeadCut hs;
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x, n = nQ * nK;
+  if (tid == 0) hs = cut[bh];
+  __syncthreads();
+  if (hs.all) return;
+  const int64_t cap = gsel_cand_cap(n);
+  // this thread's candidates matching (pm, pre), in a fixed order: groups in
+  // chunks of kVisit, and within a chunk entry j of every group before entry
+  // j + 1, so that a chunk's loads (keys, and masses when asked) are in
+  // flight together (a slice holds about one candidate per group)
+  constexpr int kVisit = 16;
+  int32_t mg[kGselGroups];
+#pragma unroll
+  for (int g = 0; g < kGselGroups; ++g) mg[g] = ccnt[(bh * kGselGroups + g) * kGselThreads + tid];
+  auto visit = [&](uint64_t pm, uint64_t pre, bool with_mass, auto&& fn) {
+#pragma unroll
+    for (int g0 = 0; g0 < kGselGroups; g0 += kVisit) {
+      int32_t jmax = 0;
+#pragma unroll
+      for (int i = 0; i < kVisit; ++i) jmax = max(jmax, mg[g0 + i]);
+      for (int32_t j = 0; j < jmax; ++j) {
+        uint64_t ub[kVisit];
+        double mb[kVisit];
+#pragma unroll
+        for (int i = 0; i < kVisit; ++i) {
+          const int64_t slot = ((bh * kGselGroups + g0 + i) * cap + j) * kGselThreads + tid;
+          const bool in = j < mg[g0 + i];
+          ub[i] = in ? ck[slot] : 0;
+          mb[i] = in && with_mass ? cm[slot] : 0.0;
+        }
+#pragma unroll
+        for (int i = 0; i < kVisit; ++i)
+          if (j < mg[g0 + i] && (ub[i] & pm) == pre) fn(ub[i], mb[i]);
+      }
+    }
+  };
+  // exclusive prefix over the threads of per-thread counts (toff[t] is
+  // thread t's offset, toff[kGselThreads] the total): within each wave by
+  // shuffles, then across the four waves
+  __shared__ int32_t wsum[kGselThreads / 64];
+  auto scan_counts = [&](int32_t mine) {
+    const int lane = tid & 63, wv = tid >> 6;
+    int32_t x = mine;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    int32_t base = 0;
+    for (int v = 0; v < wv; ++v) base += wsum[v];
+    toff[tid] = base + x - mine;
+    if (tid == kGselThreads - 1) toff[kGselThreads] = base + x;
+    __syncthreads();
+  };
+  const bool m3 = mode == 3;
+  int shift = first_shift;  // bits above shift + 3 are fixed
+  int32_t total = 0;
+  for (;;) {
+    const uint64_t pm = shift >= 0 ? ~0ull << (shift + 4) : ~0ull, pre = hs.prefix;
+    int32_t mine = 0;
+    visit(pm, pre, false, [&](uint64_t, double) { ++mine; });
+    scan_counts(mine);
+    total = toff[kGselThreads];
+    if (total <= kFinishCap) break;
+    if (shift < 0) {  // every key bit fixed: one run of equal keys holds the cut
+      if (tid == 0) {
+        HeadCut h = hs;
+        h.ties = total;
+        h.done = 0;
+        cut[bh] = h;
+      }
+      return;
+    }
+    // one more digit over the candidates
+    int32_t cnt[16];
+    double mas[16];
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      cnt[d] = 0;
+      mas[d] = 0.0;
+    }
+    visit(pm, pre, m3, [&](uint64_t u, double mv) {
+      const int b = (int)((u >> shift) & 15);
+#pragma unroll
+      for (int d = 0; d < 16; ++d) {  // registers indexed by constants only
+        cnt[d] += d == b ? 1 : 0;
+        if (m3 && d == b) mas[d] = mas[d] + mv;
+      }
+    });
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      hc[d][tid] = cnt[d];
+      hm[d][tid] = mas[d];
+    }
+    __syncthreads();
+    for (int off = kGselThreads / 2; off >= 1; off >>= 1) {
+      for (int idx = tid; idx < 16 * off; idx += kGselThreads) {
+        const int d = idx / off, i = idx - d * off;
+        hc[d][i] += hc[d][i + off];
+        hm[d][i] = hm[d][i] + hm[d][i + off];
+      }
+      __syncthreads();
+    }
+    if (tid == 0) {
+      HeadCut h = hs;
+      int chosen = 0;
+      for (int d = 15; d >= 0; --d) {
+        const bool here =
+            mode == 2 ? hc[d][0] >= h.need_c : (hc[d][0] > 0 && hm[d][0] >= h.need_m);
+        if (here || d == 0) {
+          chosen = d;
+          h.ties = hc[d][0];
+          break;
+        }
+        h.need_c -= hc[d][0];
+        h.need_m = h.need_m - hm[d][0];
+      }
+      h.prefix |= (uint64_t)chosen << shift;
+      hs = h;
+    }
+    __syncthreads();
+    shift -= 4;
+  }
+  // compact, sort
+  const uint64_t pm = shift >= 0 ? ~0ull << (shift + 4) : ~0ull, pre = hs.prefix;
+  int32_t pos = toff[tid];
+  visit(pm, pre, m3, [&](uint64_t u, double mv) {
+    lk[pos] = u;
+    li[pos] = pos;
+    lm[pos] = mv;
+    ++pos;
+  });
+  int P = 2;
+  while (P < total) P <<= 1;
+  for (int i = total + tid; i < P; i += kGselThreads) {
+    lk[i] = 0;
+    li[i] = -1;
+  }
+  __syncthreads();
+  sort_keys(lk, li, P);
+  // Walk, by the first wave, 64 sorted entries at a time: the running count
+  // and mass (mass added by a fixed shuffle tree within each chunk, chunks in
+  // order). The cut run is the first run of equal keys whose end reaches what
+  // is needed (count: need_c, mass: need_m), else the last run; what the ties
+  // kernel still needs is need less all runs before the cut run.
+  if (tid < 64) {
+    const int lane = tid;
+    HeadCut h = hs;
+    uint64_t key = pre;  // no candidate left: the prefix stands
+    int64_t ties = 0, start_c = 0;
+    double start_m = 0.0;
+    int64_t last_end = 0;      // entries before the current run
+    double last_end_m = 0.0;   // their mass
+    double carry = 0.0;        // mass of the chunks before this one
+    for (int t0 = 0; t0 < total; t0 += 64) {
+      const int t = t0 + lane;
+      const bool in = t < total;
+      const uint64_t kt = in ? lk[t] : 0;
+      double cum = in && m3 ? lm[li[t]] : 0.0;
+      for (int d = 1; d < 64; d <<= 1) {
+        const double y = __shfl_up(cum, d);
+        if (lane >= d) cum = cum + y;
+      }
+      cum = carry + cum;
+      const bool run_end = in && (t == total - 1 || lk[t + 1] != kt);
+      const bool reach =
+          run_end && (mode == 2 ? (int64_t)(t + 1) >= h.need_c : cum >= h.need_m);
+      const uint64_t ends = __builtin_amdgcn_ballot_w64(run_end);
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(reach);
+      const uint64_t last = __builtin_amdgcn_ballot_w64(in && t == total - 1);
+      if (hit || last) {  // the cut run ends at entry t0 + src
+        const int src = __builtin_ctzll(hit ? hit : last);
+        const uint64_t below = ends & ((1ull << src) - 1);
+        if (below) {
+          const int e = 63 - __builtin_clzll(below);
+          start_c = t0 + e + 1;
+          start_m = __shfl(cum, e);
+        } else {
+          start_c = last_end;
+          start_m = last_end_m;
+        }
+        const uint32_t khi = (uint32_t)__shfl((int)(uint32_t)(kt >> 32), src);
+        const uint32_t klo = (uint32_t)__shfl((int)(uint32_t)kt, src);
+        key = ((uint64_t)khi << 32) | klo;
+        ties = t0 + src + 1 - start_c;
+        break;
+      }
+      if (ends) {
+        const int e = 63 - __builtin_clzll(ends);
+        last_end = t0 + e + 1;
+        last_end_m = __shfl(cum, e);
+      }
+      carry = __shfl(cum, 63);
+    }
+    if (lane == 0) {
+      h.need_c -= start_c;
+      h.need_m = h.need_m - start_m;
+      h.prefix = key;
+      h.ties = ties;
+      h.done = 0;
+      cut[bh] = h;
+    }
   }
 }
 
@@ -1587,11 +1790,16 @@ hipError_t launch_pooled_global(const Geom& g, int32_t mode, double param, uint8
                      g.nK, mode, S, P, best);
   hipLaunchKernelGGL(gsel_init_kernel, dim3(grid_for(BH, 64)), dim3(64), 0, st, BH, g.nQ, g.nK,
                      mode, param, cut);
-  for (int pass = 0, shift = 60; shift >= 0; ++pass, shift -= 4) {
-    const int32_t phase = pass < kGselFullPasses ? 0 : (pass == kGselFullPasses ? 1 : 2);
+  // passes over every pair, the last of them filling the candidate store;
+  // then the remaining digits over the candidates in one launch
+  int shift = 60;
+  for (int pass = 0; pass <= kGselFullPasses; ++pass, shift -= 4) {
+    const int32_t phase = pass < kGselFullPasses ? 0 : 1;
     hipLaunchKernelGGL(gsel_hist_kernel, dim3(kGselGroups, (unsigned)BH), dim3(kGselThreads), 0,
                        st, g.nQ, g.nK, mode, shift, S, P, cut, pc, pm, phase, ck, cm, ccnt);
   }
+  hipLaunchKernelGGL(gsel_finish_kernel, dim3((unsigned)BH), dim3(kGselThreads), 0, st, g.nQ,
+                     g.nK, mode, shift, cut, ck, cm, ccnt);
   hipLaunchKernelGGL(gsel_ties_kernel, dim3(grid_for(BH, 64)), dim3(64), 0, st, BH, n, mode, S, P,
                      cut);
   hipLaunchKernelGGL(gsel_mark_kernel, dim3(grid_for(BH * n, 256)), dim3(256), 0, st, BH, g.nQ,
