@@ -280,7 +280,15 @@ __device__ inline uint64_t order_key(double v) {
 
 
 constexpr int kSelectThreads = 256;
-constexpr int kPooledMaxBlocks = 2048;  // keeps the select kernel under 64 KiB of LDS
+constexpr int kPooledMaxBlocks = 2048;  // rows held in LDS by the select kernels
+// Longer rows (up to kLongMaxBlocks key blocks) take the long-row kernels:
+// one lane per row for the row statistics, one workgroup per row, keys in
+// registers, for the selection.
+constexpr int kLongMaxBlocks = 8192;
+constexpr int kLongThreads = 512;
+constexpr int kLongKeys = kLongMaxBlocks / kLongThreads;  // keys per thread
+constexpr int kLongBatch = 512;   // pairs sorted per step of the cumulative walk
+constexpr int kLongCap = 1024;    // LDS entries of a step
 // First mask byte of a row left to the full sort (mask values are 0..3).
 constexpr uint8_t kSelectMarker = 0xFF;
 // Rows per workgroup of the one-wave-per-row select (at most; fewer when their
@@ -511,12 +519,15 @@ __device__ inline RowCut select_kth(const double* s, int64_t nK, int T) {
 // The thresholds are non-decreasing; nl is 1..3.
 // CH entries per chunk (16, or 8 where registers are scarce; the sums are
 // the same either way).
+// With run_io the walk continues a row's earlier walk: the sum starts from
+// *run_io and is left there, and the entries are the row's pos0, pos0 + 1, ...
 template <int CH = 16>
 __device__ inline bool walk_mass(const double* pv, const int32_t* idx, int64_t n, double tau0,
-                                 double tau1, double tau2, int nl, uint8_t* flag) {
+                                 double tau1, double tau2, int nl, uint8_t* flag,
+                                 double* run_io = nullptr, int64_t pos0 = 0) {
   const int lane = threadIdx.x & 63;
   const double last = nl == 1 ? tau0 : (nl == 2 ? tau1 : tau2);
-  double run = 0.0;
+  double run = run_io ? *run_io : 0.0;
   for (int c0 = 0; c0 < (int)n; c0 += CH) {
     const int m = min(CH, (int)n - c0);
     double v[CH];
@@ -541,13 +552,17 @@ __device__ inline bool walk_mass(const double* pv, const int32_t* idx, int64_t n
     for (int u = 1; u < CH; ++u) ex = lane == u ? pre[u] : ex;
     if (lane < m) {
       int lvl = 0;
-      if (c0 + lane > 0)
+      if (pos0 + c0 + lane > 0)
         lvl = (ex >= tau0 ? 1 : 0) + (nl > 1 && ex >= tau1 ? 1 : 0) +
               (nl > 2 && ex >= tau2 ? 1 : 0);
       if (lvl < nl) flag[idx[c0 + lane]] = (uint8_t)(1 + lvl);
     }
-    if (run >= last) return true;
+    if (run >= last) {
+      if (run_io) *run_io = run;
+      return true;
+    }
   }
+  if (run_io) *run_io = run;
   return false;
 }
 
@@ -1419,6 +1434,352 @@ __global__ void gsel_mark_kernel(int64_t BH, int64_t nQ, int64_t nK, int32_t mod
   }
 }
 
+// ------------------------------------------------------- long rows
+// Row statistics with one lane per row (64 rows per workgroup): the row's
+// maximum score and its first block (S desc, c asc), then Z = sum of
+// exp(S - max) in ascending block order, one add at a time as in the short
+// kernels. Scores pass through LDS in 64 x 64 tiles, read row segment by
+// row segment (coalesced) and walked by the lane of their row.
+__global__ __launch_bounds__(kWave) void pooled_rowz_kernel(int64_t R, int64_t nK,
+                                                           const double* __restrict__ S,
+                                                           double* __restrict__ zrow,
+                                                           double* __restrict__ mrow,
+                                                           int32_t* __restrict__ best) {
+  __shared__ double tile[kWave][kWave + 1];
+  const int lane = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * kWave, r = r0 + lane;
+  auto load_tile = [&](int64_t c0) {
+#pragma unroll 16
+    for (int i = 0; i < kWave; ++i) {
+      const int64_t rr = r0 + i, cc = c0 + lane;
+      tile[i][lane] = (rr < R && cc < nK) ? S[rr * nK + cc] : 0.0;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  };
+  double m = -INFINITY;
+  int32_t arg = INT32_MAX;
+  for (int64_t c0 = 0; c0 < nK; c0 += kWave) {
+    load_tile(c0);
+    const int w = (int)min((int64_t)kWave, nK - c0);
+    for (int j = 0; j < w; ++j) {
+      const double v = tile[lane][j];
+      if (v > m || (v == m && c0 + j < arg)) {
+        m = v;
+        arg = (int32_t)(c0 + j);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+  double Z = 0.0;
+  for (int64_t c0 = 0; c0 < nK; c0 += kWave) {
+    load_tile(c0);
+    const int w = (int)min((int64_t)kWave, nK - c0);
+    for (int j = 0; j < w; ++j) Z = Z + exp(tile[lane][j] - m);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+  if (r < R) {
+    zrow[r] = Z;
+    mrow[r] = m;
+    if (best) best[r] = arg;
+  }
+}
+
+// Head-wide mass for long rows: p = exp(S - max) / Z of the row, elementwise.
+__global__ void pooled_prob_kernel(int64_t total, int64_t nK, const double* __restrict__ S,
+                                   const double* __restrict__ zrow,
+                                   const double* __restrict__ mrow, double* __restrict__ P) {
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = t / nK;
+    P[t] = exp(S[t] - mrow[r]) / zrow[r];
+  }
+}
+
+// Inverse of order_key (the score of a key; -0 comes back as +0).
+__device__ inline double key_score(uint64_t u) {
+  const uint64_t b = (u >> 63) ? (u & ~(1ull << 63)) : ~u;
+  return __longlong_as_double((long long)b);
+}
+
+// Per-row selection for long rows, one workgroup per row; block c is key
+// kk of thread c % 256 with kk = c / 256 (coalesced loads; ascending block
+// order is (kk, thread)). Sums over the workgroup go through per-wave ballots
+// and a small LDS array. Top-k: the key of the k-th pair by a radix select
+// (one bit per pass, from the highest bit in which the keys in play differ,
+// skipping bits they all share), then the pairs above it and the first of
+// those equal to it in block order. Cumulative mass and pyramid levels: the
+// pairs in (score desc, block asc) order in steps: the pairs above the
+// kLongBatch-th largest key still in play, sorted in LDS, then the run of
+// pairs equal to that key in block order, each walked with the running mass
+// of walk_mass (p = exp(S - max) / Z with the row's max and Z from
+// pooled_rowz_kernel), until the last threshold is reached or every pair has
+// been walked. The same arithmetic as the short kernels and the oracle.
+struct LongCut {
+  uint64_t key;
+  int32_t take_eq;  // pairs equal to key among the T wanted
+  int32_t n_eq;     // pairs equal to key in play
+};
+
+__global__ __launch_bounds__(kLongThreads) void pooled_select_long_kernel(
+    int64_t nK, int32_t mode, double param, double tau1, double tau2, int32_t n_levels,
+    const double* __restrict__ S, const double* __restrict__ zrow,
+    const double* __restrict__ mrow, uint8_t* __restrict__ mask) {
+  __shared__ uint64_t ck[kLongCap];  // step keys, then their probabilities
+  __shared__ int32_t ci[kLongCap];   // their blocks
+  __shared__ uint8_t flag[kLongMaxBlocks];
+  __shared__ int64_t red_i[kLongThreads / 64][2];
+  __shared__ uint64_t red_u[kLongThreads / 64][2];
+  __shared__ double run_sh;
+  __shared__ int32_t done_sh;
+  __shared__ int32_t na_sh;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  constexpr int NW = kLongThreads / 64;
+  const int64_t row = blockIdx.x;
+  const double* srow = S + row * nK;
+  uint8_t* out = mask + row * nK;
+  uint64_t key[kLongKeys];
+  {
+    double v[kLongKeys];
+#pragma unroll
+    for (int kk = 0; kk < kLongKeys; ++kk) {
+      const int64_t c = (int64_t)kk * kLongThreads + tid;
+      v[kk] = c < nK ? srow[c] : 0.0;
+    }
+#pragma unroll
+    for (int kk = 0; kk < kLongKeys; ++kk) {
+      const int64_t c = (int64_t)kk * kLongThreads + tid;
+      key[kk] = c < nK ? order_key(v[kk]) : 0;
+      if (c < nK) flag[c] = 0;
+    }
+  }
+  // workgroup sums of two per-thread counts / min-max of keys
+  auto sum2 = [&](int64_t a, int64_t b, int64_t& sa, int64_t& sb) {
+    for (int off = 32; off >= 1; off >>= 1) {
+      a += __shfl_xor(a, off);
+      b += __shfl_xor(b, off);
+    }
+    if (lane == 0) {
+      red_i[wv][0] = a;
+      red_i[wv][1] = b;
+    }
+    __syncthreads();
+    sa = sb = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      sa += red_i[v][0];
+      sb += red_i[v][1];
+    }
+    __syncthreads();
+  };
+  auto minmax = [&](uint64_t mx, uint64_t mn, uint64_t& gmx, uint64_t& gmn) {
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint64_t xa =
+          ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(mx >> 32), off) << 32) |
+          (uint32_t)__shfl_xor((int)(uint32_t)mx, off);
+      const uint64_t xi =
+          ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(mn >> 32), off) << 32) |
+          (uint32_t)__shfl_xor((int)(uint32_t)mn, off);
+      mx = xa > mx ? xa : mx;
+      mn = xi < mn ? xi : mn;
+    }
+    if (lane == 0) {
+      red_u[wv][0] = mx;
+      red_u[wv][1] = mn;
+    }
+    __syncthreads();
+    gmx = 0;
+    gmn = ~0ull;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      gmx = red_u[v][0] > gmx ? red_u[v][0] : gmx;
+      gmn = red_u[v][1] < gmn ? red_u[v][1] : gmn;
+    }
+    __syncthreads();
+  };
+  // the T-th largest key among those below `hi` (every key when !bounded);
+  // bits from `from` down are undecided, the ones above equal `prefix` for
+  // every key in play
+  auto select = [&](int64_t T, bool bounded, uint64_t hi, int64_t n_play) -> LongCut {
+    auto in_play = [&](int kk) {
+      return (int64_t)kk * kLongThreads + tid < nK && (!bounded || key[kk] < hi);
+    };
+    uint64_t mx = 0, mn = ~0ull;
+#pragma unroll
+    for (int kk = 0; kk < kLongKeys; ++kk)
+      if (in_play(kk)) {
+        mx = key[kk] > mx ? key[kk] : mx;
+        mn = key[kk] < mn ? key[kk] : mn;
+      }
+    uint64_t gmx, gmn;
+    minmax(mx, mn, gmx, gmn);
+    int64_t want = T;
+    if (gmx == gmn) return LongCut{gmx, (int32_t)want, (int32_t)n_play};  // one key in play
+    int bit = 63 - __builtin_clzll(gmx ^ gmn);
+    uint64_t prefix = bit >= 63 ? 0 : gmx & (~0ull << (bit + 1));
+    for (;;) {
+      const uint64_t hm = bit >= 63 ? 0 : ~0ull << (bit + 1);
+      int64_t ones = 0, match = 0;
+#pragma unroll
+      for (int kk = 0; kk < kLongKeys; ++kk) {
+        const bool m = in_play(kk) && (key[kk] & hm) == prefix;
+        ones += m && ((key[kk] >> bit) & 1);
+        match += m;
+      }
+      int64_t so, sm;
+      sum2(ones, match, so, sm);
+      int64_t left;
+      if (so >= want) {
+        prefix |= 1ull << bit;
+        left = so;
+      } else {
+        want -= so;
+        left = sm - so;
+      }
+      if (bit == 0) return LongCut{prefix, (int32_t)want, (int32_t)left};
+      // the bits below on which the keys left all agree
+      const uint64_t pm = ~0ull << bit;
+      mx = 0;
+      mn = ~0ull;
+#pragma unroll
+      for (int kk = 0; kk < kLongKeys; ++kk)
+        if (in_play(kk) && (key[kk] & pm) == prefix) {
+          mx = key[kk] > mx ? key[kk] : mx;
+          mn = key[kk] < mn ? key[kk] : mn;
+        }
+      minmax(mx, mn, gmx, gmn);
+      if (gmx == gmn) return LongCut{gmx, (int32_t)want, (int32_t)left};
+      bit = 63 - __builtin_clzll(gmx ^ gmn);
+      prefix = gmx & (~0ull << (bit + 1));
+    }
+  };
+  // rank of this thread's key kk among those with eq set, in block order:
+  // calls fn(kk, rank) for each; returns the number of them
+  auto in_block_order = [&](auto&& pred, auto&& fn) -> int64_t {
+    int64_t seen = 0;
+#pragma unroll
+    for (int kk = 0; kk < kLongKeys; ++kk) {  // unrolled: keys stay in registers
+      if ((int64_t)kk * kLongThreads < nK) {  // uniform
+        const bool e = (int64_t)kk * kLongThreads + tid < nK && pred(kk);
+        const uint64_t bm = __builtin_amdgcn_ballot_w64(e);
+        if (lane == 0) red_i[wv][0] = __popcll(bm);
+        __syncthreads();
+        int64_t base = seen;
+        for (int v = 0; v < wv; ++v) base += red_i[v][0];
+        for (int v = 0; v < NW; ++v) seen += red_i[v][0];
+        __syncthreads();
+        if (e) fn(kk, base + __popcll(bm & ((1ull << lane) - 1)));
+      }
+    }
+    return seen;
+  };
+  const double smax = mrow[row], Z = zrow[row];
+  if (mode == 0) {
+    const int64_t T = (int64_t)min((double)nK, param);
+    const LongCut cut = select(T, false, 0, nK);
+#pragma unroll
+    for (int kk = 0; kk < kLongKeys; ++kk) {
+      const int64_t c = (int64_t)kk * kLongThreads + tid;
+      if (c < nK && key[kk] > cut.key) flag[c] = 1;
+    }
+    in_block_order([&](int kk) { return key[kk] == cut.key; },
+                   [&](int kk, int64_t rank) {
+                     if (rank < cut.take_eq) flag[(int64_t)kk * kLongThreads + tid] = 1;
+                   });
+  } else {
+    const int nl = mode == 4 ? n_levels : 1;
+    if (tid == 0) {
+      run_sh = 0.0;
+      done_sh = 0;
+    }
+    __syncthreads();
+    int64_t walked = 0;
+    bool bounded = false;
+    uint64_t hi = 0;
+    for (;;) {
+      int64_t cnt = 0, dummy = 0;
+#pragma unroll
+      for (int kk = 0; kk < kLongKeys; ++kk)
+        cnt += (int64_t)kk * kLongThreads + tid < nK && (!bounded || key[kk] < hi);
+      int64_t left;
+      sum2(cnt, dummy, left, dummy);
+      if (left == 0) break;
+      const LongCut cut = select(min(left, (int64_t)kLongBatch), bounded, hi, left);
+      // the pairs above the cut key still in play, sorted
+      if (tid == 0) na_sh = 0;
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < kLongKeys; ++kk) {
+        const int64_t c = (int64_t)kk * kLongThreads + tid;
+        const bool a = c < nK && key[kk] > cut.key && (!bounded || key[kk] < hi);
+        const int pos = wave_append(a, &na_sh);
+        if (a) {
+          ck[pos] = key[kk];
+          ci[pos] = (int32_t)c;
+        }
+      }
+      __syncthreads();
+      const int na = na_sh;
+      __syncthreads();
+      if (na > 0) {
+        int P = 2;
+        while (P < na) P <<= 1;
+        for (int i = na + tid; i < P; i += kLongThreads) {
+          ck[i] = 0;
+          ci[i] = -1;
+        }
+        __syncthreads();
+        sort_keys(ck, ci, P);
+        double* cs = (double*)ck;
+        for (int t = tid; t < na; t += kLongThreads) cs[t] = exp(key_score(ck[t]) - smax) / Z;
+        __syncthreads();
+        if (tid < 64) {
+          double run = run_sh;
+          const bool reached = walk_mass<8>(cs, ci, na, param, tau1, tau2, nl, flag, &run,
+                                            walked);
+          if (lane == 0) {
+            run_sh = run;
+            done_sh = reached;
+          }
+        }
+        __syncthreads();
+        walked += na;
+        if (done_sh) break;
+      }
+      // the run of pairs equal to the cut key, in block order, kLongCap at a time
+      const double pe = exp(key_score(cut.key) - smax) / Z;
+      for (int64_t r0 = 0;; r0 += kLongCap) {
+        const int64_t got = in_block_order(
+            [&](int kk) { return key[kk] == cut.key; },
+            [&](int kk, int64_t rank) {
+              if (rank >= r0 && rank < r0 + kLongCap) {
+                ci[rank - r0] = (int32_t)((int64_t)kk * kLongThreads + tid);
+                ((double*)ck)[rank - r0] = pe;
+              }
+            });
+        const int64_t m = min((int64_t)kLongCap, got - r0);
+        __syncthreads();
+        if (m > 0 && tid < 64) {
+          double run = run_sh;
+          const bool reached = walk_mass<8>((const double*)ck, ci, m, param, tau1, tau2, nl,
+                                            flag, &run, walked);
+          if (lane == 0) {
+            run_sh = run;
+            done_sh = reached;
+          }
+        }
+        __syncthreads();
+        walked += max((int64_t)0, m);
+        if (done_sh || r0 + kLongCap >= got) break;
+      }
+      if (done_sh) break;
+      bounded = true;
+      hi = cut.key;
+    }
+  }
+  __syncthreads();
+  for (int64_t c = tid; c < nK; c += kLongThreads) out[c] = flag[c];
+}
+
 // ------------------------------------------------------- pyramid lists
 // Quarter mask (16-row quarters of a 64-row augmented block) that row r
 // selects in augmented block ab ([PSA]: logical block size decoupled from the
@@ -1680,13 +2041,15 @@ size_t pooled_workspace_bytes(const Geom& g) {
   return (bytes + 255) / 256 * 256;
 }
 
-int pooled_max_blocks() { return kPooledMaxBlocks; }
+int pooled_max_blocks() { return kLongMaxBlocks; }
 
 size_t pooled_scratch_need(const Geom& g, int32_t mode) {
   if (mode == 2 || mode == 3) return pooled_workspace_bytes(g);
-  // per-row modes: pooled means of Q and K and the score matrix only
+  // per-row modes: pooled means of Q and K and the score matrix only (and,
+  // for long rows, each row's maximum and Z)
   const int64_t BH = (int64_t)g.B * g.H;
-  const size_t n = (size_t)(BH * (g.nQ + g.nK) * g.D + BH * g.nQ * g.nK);
+  size_t n = (size_t)(BH * (g.nQ + g.nK) * g.D + BH * g.nQ * g.nK);
+  if (g.nK > kPooledMaxBlocks) n += (size_t)(2 * BH * g.nQ);
   return (n * sizeof(double) + 255) / 256 * 256;
 }
 
@@ -1740,9 +2103,20 @@ hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mode == 2 || mode == 3) return launch_pooled_global(g, mode, param, mask, ws, st);
+  const int64_t R = BH * g.nQ;
+  if (g.nK > kPooledMaxBlocks) {
+    // long rows: row maxima and Z after the scores, then one workgroup per row
+    double* zrow = S + R * g.nK;
+    double* mrow = zrow + R;
+    hipLaunchKernelGGL(pooled_rowz_kernel, dim3((unsigned)((R + kWave - 1) / kWave)),
+                       dim3(kWave), 0, st, R, g.nK, S, zrow, mrow, (int32_t*)nullptr);
+    hipLaunchKernelGGL(pooled_select_long_kernel, dim3((unsigned)R), dim3(kLongThreads), 0, st,
+                       g.nK, mode, param, levels ? levels[1] : 0.0, levels ? levels[2] : 0.0,
+                       n_levels, S, zrow, mrow, mask);
+    return hipGetLastError();
+  }
   int32_t P = 1;
   while (P < g.nK) P <<= 1;
-  const int64_t R = BH * g.nQ;
   int32_t only_marked = 0;
   if ((mode == 0 || mode == 1) && g.nK > kTopM && !(mode == 0 && param >= (double)g.nK)) {
     const size_t per = select_wave_lds(g.nK);
@@ -1786,8 +2160,20 @@ hipError_t launch_pooled_global(const Geom& g, int32_t mode, double param, uint8
   uint64_t* ck = (uint64_t*)((char*)ws + head);  // same offset as pooled_workspace_bytes
   double* cm = (double*)(ck + cand);
   int32_t* ccnt = (int32_t*)(cm + cand);
-  hipLaunchKernelGGL(pooled_rowstats_kernel, dim3((unsigned)(BH * g.nQ)), dim3(kWave), 0, st,
-                     g.nK, mode, S, P, best);
+  if (g.nK > kPooledMaxBlocks) {
+    // long rows: maxima, Z and best blocks one lane per row (kept in the
+    // candidate store until the probabilities are formed), then p elementwise
+    double* zrow = (double*)ck;
+    double* mrow = zrow + BH * g.nQ;
+    hipLaunchKernelGGL(pooled_rowz_kernel, dim3((unsigned)((BH * g.nQ + kWave - 1) / kWave)),
+                       dim3(kWave), 0, st, BH * g.nQ, g.nK, S, zrow, mrow, best);
+    if (mode == 3)
+      hipLaunchKernelGGL(pooled_prob_kernel, dim3(grid_for(BH * n, 256)), dim3(256), 0, st,
+                         BH * n, g.nK, S, zrow, mrow, P);
+  } else {
+    hipLaunchKernelGGL(pooled_rowstats_kernel, dim3((unsigned)(BH * g.nQ)), dim3(kWave), 0, st,
+                       g.nK, mode, S, P, best);
+  }
   hipLaunchKernelGGL(gsel_init_kernel, dim3(grid_for(BH, 64)), dim3(64), 0, st, BH, g.nQ, g.nK,
                      mode, param, cut);
   // passes over every pair, the last of them filling the candidate store;

@@ -143,7 +143,9 @@ BSA_API size_t bsa_pooled_workspace_bytes(const bsa_shape* s);
  *   mask        out, [B][H][nQ][nK]
  *   workspace   device buffer of at least bsa_pooled_workspace_bytes(s)
  *               bytes, 256-byte aligned; contents on return are unspecified.
- * Supports nK <= 2048 key blocks (BSA_ERR_UNSUPPORTED beyond).
+ * Supports nK <= 8192 key blocks (BSA_ERR_UNSUPPORTED beyond); rows of more
+ * than 2048 blocks (the 4x-length video grid has 7,425) take a path with one
+ * workgroup per row and the same results.
  */
 BSA_API bsa_status bsa_build_mask_pooled(const bsa_shape* s, bsa_dtype dt, bsa_tensor q,
                                  bsa_tensor k, double scale, int32_t mode, double param,
@@ -158,7 +160,8 @@ BSA_API bsa_status bsa_build_mask_pooled(const bsa_shape* s, bsa_dtype dt, bsa_t
  * device array inside the library of 64 MiB (64 << 20 bytes) per GPU, held
  * from library load until the process ends. Modes 0 and 1 need
  * 8*(B*H*(nQ + nK)*d + B*H*nQ*nK) bytes rounded up to 256 (the 480p layer
- * with 12 heads: 37.7 MB), modes 2 and 3 bsa_pooled_workspace_bytes(s);
+ * with 12 heads: 37.7 MB; 16*B*H*nQ bytes more when nK > 2048), modes 2
+ * and 3 bsa_pooled_workspace_bytes(s);
  * a shape and mode that need more return BSA_ERR_CAPACITY before anything is
  * enqueued. The call allocates nothing. Every call on one GPU shares that
  * GPU's scratch: calls that overlap in time on the same GPU (other streams,
@@ -339,6 +342,7 @@ BSA_API bsa_status bsa_build_kv_pyramid(const bsa_shape* s, bsa_dtype dt, int32_
  * level advances past every threshold the running sum (including that block)
  * has reached; blocks after the last level are dropped. levels_tau (host,
  * [n_levels]) non-decreasing in (0, 1]. The row's best block is at level 0.
+ * Same key-block limit as bsa_build_mask_pooled (nK <= 8192).
  *   mask  out, [B][H][nQ][nK], values 0 .. n_levels
  */
 BSA_API bsa_status bsa_build_mask_pyramid(const bsa_shape* s, bsa_dtype dt, bsa_tensor q,

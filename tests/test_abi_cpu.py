@@ -138,7 +138,10 @@ def test_pooled_validation(L):
     assert call(mask=None) == INVALID
     assert call(scale=float("inf")) == INVALID
     assert call(dt=3) == UNSUPPORTED
-    big = S(frames=33, height=100, width=100)   # 330,000 tokens -> 5,157 key blocks
+    long_rows = S(frames=33, height=100, width=100)   # 330,000 tokens -> 5,157 key blocks
+    assert call(shape=long_rows) == INVALID              # supported; the workspace is short
+    assert "workspace" in bsa.bsa_last_error()
+    big = S(frames=60, height=100, width=100)   # 600,000 tokens -> 9,375 key blocks
     assert call(shape=big) == UNSUPPORTED
 
 
@@ -326,7 +329,7 @@ def test_pooled_noalloc_validation(L):
     assert call(param=0.0) == INVALID
     assert call(mask=None) == INVALID
     assert call(dt=3) == UNSUPPORTED
-    assert call(shape=S(frames=33, height=100, width=100)) == UNSUPPORTED   # > 2048 key blocks
+    assert call(shape=S(frames=60, height=100, width=100)) == UNSUPPORTED   # > 8192 key blocks
     # 480p layer, 12 heads: per-row modes fit (37.7 MB) -- not launched here;
     # head-wide modes need 108 MiB and are refused with CAPACITY
     big = S(heads=12, frames=21, height=30, width=52, block_q=64)

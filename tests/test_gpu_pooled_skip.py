@@ -92,6 +92,56 @@ def test_pooled_mask_long_rows_ties_bit_exact(period, mode, param):
     np.testing.assert_array_equal(got, ref)
 
 
+# Rows longer than the in-LDS select holds (nK > 2048) take one workgroup
+# per row: N = 163,840 tokens, 1,280 row blocks of 2,560 key blocks.
+def _very_long():
+    return synth.Workload("pooled_very_long", 1, 1, 64, 40, 32, 128, 128, 64, "bf16", "pooled",
+                          615, True)
+
+
+@pytest.mark.parametrize("mode,param", [(0, 300.0), (0, 2000.0), (1, 0.3), (1, 0.95), (1, 1.0)])
+def test_pooled_mask_rows_over_2048_blocks_bit_exact(mode, param):
+    """Top-k and cumulative mass over rows of 2,560 key blocks; the mass walk
+    takes the sorted pairs in steps of 512 (tau 0.95 and 1.0 need several)."""
+    w = _very_long()
+    assert w.nK > 2048
+    x = synth.make_qkv(w)
+    got = _pooled_gpu(w, x, mode, param)
+    ref, _, _ = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, mode, param)
+    note(f"pooled rows of {w.nK} blocks mode={mode} param={param}: {int(ref.sum())} kept")
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("period,mode,param", [(2, 0, 77.0), (2, 1, 0.3), (3, 1, 0.6)])
+def test_pooled_mask_rows_over_2048_blocks_ties_bit_exact(period, mode, param):
+    """Rows of 2,560 key blocks whose keys repeat every 2 or 3 blocks: tie
+    groups of 1,280 or 853-854 blocks, longer than one LDS step of the walk
+    for period 2, taken in ascending block order."""
+    w = _very_long()
+    x = synth.make_qkv(w)
+    k = x["k"].reshape(w.B, w.nK, w.Bk, w.H, w.d)
+    x["k"] = np.ascontiguousarray(k[:, np.arange(w.nK) % period].reshape(x["k"].shape))
+    got = _pooled_gpu(w, x, mode, param)
+    ref, S, _ = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, mode, param,
+                                         want_scores=True)
+    assert np.all(S[..., period:] == S[..., :-period])
+    note(f"pooled tied rows of {w.nK} blocks period={period} mode={mode}: {int(ref.sum())} kept")
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("mode,param", [(2, 40000.0), (3, 0.3)])
+def test_pooled_global_rows_over_2048_blocks(mode, param):
+    """Head-wide selection over rows of 2,560 key blocks (row statistics one
+    lane per row, probabilities elementwise)."""
+    w = _very_long()
+    x = synth.make_qkv(w)
+    got = _pooled_gpu(w, x, mode, param)
+    ref, _, margin = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, mode, param)
+    note(f"head-wide rows of {w.nK} blocks mode={mode}: {int(ref.sum())} kept, "
+         f"{int(np.sum(got != ref))} differ, head margin {margin[:, :, 0].min():.3e}")
+    _check_global(got, ref, margin, mode, "rows over 2048 blocks")
+
+
 def test_pooled_mask_wan13b_480p_full():
     w = synth.workload("wan13b_480p")
     note(f"{w.name}: generating inputs")

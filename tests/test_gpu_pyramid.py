@@ -168,3 +168,24 @@ def test_pyramid_long_rows_sampled(taus):
                                               w.nQ * w.nK, rows=rows)
     og, lg = gather_rows(host(out["o"]), host(out["lse"]), rows, w.B, w.H, w.N, w.Bq)
     compare(og, lg, o_ref, lse_ref, f"pyramid long rows {taus}")
+
+
+@pytest.mark.parametrize("taus", [(1.0,), (0.3, 0.6, 0.9)])
+def test_pyramid_mask_rows_over_2048_blocks(taus):
+    """Level masks over rows of 2,560 key blocks (one workgroup per row, the
+    sorted walk in steps of 512), bit-exact against the oracle."""
+    w = synth.Workload("pyr_very_long", 1, 1, 64, 40, 32, 128, 128, 64, "bf16", "pooled", 645,
+                       True)
+    assert w.nK > 2048
+    x = synth.make_qkv(w)
+    s = shape_of(w)
+    ws = torch.empty(bsa.bsa_pooled_workspace_bytes(s), dtype=torch.uint8, device=DEV)
+    mask = torch.empty(w.B * w.H * w.nQ * w.nK, dtype=torch.uint8, device=DEV)
+    bsa.bsa_build_mask_pyramid(s, dev(x["q"]), dev(x["k"]), w.scale, list(taus), mask, ws)
+    torch.cuda.synchronize()
+    got = host(mask).reshape(w.B, w.H, w.nQ, w.nK)
+    mref, _, _ = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, 4, 0,
+                                          levels_tau=list(taus))
+    note(f"pyramid level mask rows of {w.nK} blocks {taus}: "
+         f"{[int((mref == l).sum()) for l in range(len(taus) + 1)]} per level")
+    np.testing.assert_array_equal(got, mref)
