@@ -298,8 +298,9 @@ def main():
     ap.add_argument("--token-order", default=None, metavar="SPEC",
                     help="pooled workloads: gather Q/K/V into a token order before blocking "
                          "and scatter O back, inside the step: axes:A,B,C (slowest..fastest, "
-                         "0 frame 1 row 2 column), boxes:T,H,W (box extent), or paro (head h "
-                         "takes axis order h mod 6)")
+                         "0 frame 1 row 2 column), boxes:T,H,W (box extent), paro (head h "
+                         "takes axis order h mod 6), or choose (each head the axis order whose "
+                         "pooled mask keeps the fewest tiles, chosen once before timing)")
     ap.add_argument("--pyramid", default=None, metavar="T0[,T1[,T2]]",
                     help="pooled workloads: pyramid attention with these level thresholds "
                          "(cumulative mass; level l pools 2^l tokens); the step builds the "
@@ -424,9 +425,27 @@ def main():
         orders = list(itertools.permutations(range(3)))
         perm = torch.empty(w.H * w.N, dtype=torch.int32, device=dev)   # one order per head
         spec = args.token_order
+        chosen = None
+        if spec == "choose":
+            # per-head order chosen once, before timing, by the kept-tile count of the pooled
+            # selection under each of the six axis orders
+            dtc = bsa.BSA_BF16 if q.dtype == torch.bfloat16 else bsa.BSA_F32
+            wso = torch.empty(bsa.bsa_token_orders_workspace_bytes(s, dtc), dtype=torch.uint8,
+                              device=dev)
+            och = torch.empty(w.H, dtype=torch.int32, device=dev)
+            cnt = torch.empty((w.H, 6), dtype=torch.int64, device=dev)
+            bsa.bsa_choose_token_orders(s, q, k, w.scale, w.pooled_mode, w.pooled_param, och,
+                                        cnt, wso)
+            torch.cuda.synchronize()
+            chosen = och.cpu().tolist()
+            log(f"chosen orders per head {chosen}; kept tiles identity "
+                f"{cnt[:, 0].sum().item()}, chosen {cnt[torch.arange(w.H), och.long()].sum().item()}")
+            del wso
         for h in range(w.H):
             sl = perm[h * w.N:(h + 1) * w.N]
-            if spec == "paro":
+            if spec == "choose":
+                bsa.bsa_make_token_permutation(s, bsa.PERM_AXES, bsa.AXIS_ORDERS[chosen[h]], sl)
+            elif spec == "paro":
                 bsa.bsa_make_token_permutation(s, bsa.PERM_AXES, orders[h % 6], sl)
             else:
                 kind, vals = spec.split(":")

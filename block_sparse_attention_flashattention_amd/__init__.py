@@ -20,6 +20,7 @@ __all__ = [
     "bsa_compact_block_lists", "bsa_order_block_lists", "bsa_sparse_attn_fwd",
     "bsa_update_skip_mask", "ORDER_ASCENDING", "ORDER_RADIAL",
     "bsa_make_token_permutation", "bsa_permute_tokens", "PERM_AXES", "PERM_BOXES",
+    "bsa_token_orders_workspace_bytes", "bsa_choose_token_orders", "AXIS_ORDERS",
     "bsa_pyramid_rows", "bsa_build_kv_pyramid", "bsa_build_mask_pyramid",
     "bsa_compact_pyramid_lists", "bsa_pyramid_attn_fwd", "bsa_check_block_lists",
     "bsa_status_string", "bsa_last_error",
@@ -90,6 +91,9 @@ def lib() -> C.CDLL:
             "bsa_order_block_lists": (i32, [SP, i32, p, i32, p, p, p]),
             "bsa_make_token_permutation": (i32, [SP, i32, C.POINTER(i32), p, p]),
             "bsa_permute_tokens": (i32, [SP, i32, p, i64, i32, Tensor, Tensor, p]),
+            "bsa_token_orders_workspace_bytes": (sz, [SP, i32]),
+            "bsa_choose_token_orders": (i32, [SP, i32, Tensor, Tensor, f64, i32, f64, p, p, p, sz,
+                                              p]),
             "bsa_pyramid_rows": (i64, [SP, i32]),
             "bsa_build_kv_pyramid": (i32, [SP, i32, i32, Tensor, Tensor, Tensor, Tensor, p]),
             "bsa_build_mask_pyramid": (i32, [SP, i32, Tensor, Tensor, f64, i32,
@@ -208,6 +212,23 @@ def bsa_make_token_permutation(s: Shape, kind: int, axes, perm, stream=None):
     ax = (C.c_int32 * 3)(*[int(a) for a in axes])
     _check("bsa_make_token_permutation",
            lib().bsa_make_token_permutation(C.byref(s), kind, ax, _ptr(perm), _stream(stream)))
+
+
+# the six axis orders in the numbering of bsa_choose_token_orders
+AXIS_ORDERS = ((0, 1, 2), (0, 2, 1), (1, 0, 2), (1, 2, 0), (2, 0, 1), (2, 1, 0))
+
+
+def bsa_token_orders_workspace_bytes(s: Shape, dtype_code: int) -> int:
+    return int(lib().bsa_token_orders_workspace_bytes(C.byref(s), dtype_code))
+
+
+def bsa_choose_token_orders(s: Shape, q, k, scale: float, mode: int, param: float, order_out,
+                            counts_out, workspace, stream=None):
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("bsa_choose_token_orders",
+           lib().bsa_choose_token_orders(C.byref(s), _dtype(q), _tensor(q), _tensor(k), scale,
+                                         mode, param, _ptr(order_out), _ptr(counts_out),
+                                         _ptr(workspace), nbytes, _stream(stream)))
 
 
 def bsa_permute_tokens(s: Shape, perm, perm_head_stride: int, scatter: int, x, out,

@@ -341,6 +341,75 @@ bsa_status bsa_permute_tokens(const bsa_shape* s, bsa_dtype dt, const int32_t* p
                 "permute launch");
 }
 
+// Workspace of bsa_choose_token_orders, each part from a 256-byte boundary:
+// the order's permutation, Q and K gathered into it (contiguous [B][N][H][d]),
+// the pooled mask, the per-head counts and the pooled builder's scratch.
+struct OrderWs {
+  size_t perm, qp, kp, mask, counts, pooled, total;
+};
+static OrderWs order_ws_layout(const bsa::Geom& g, int eb) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  OrderWs w;
+  const size_t tok = (size_t)g.B * g.N * g.H * g.D * eb;
+  w.perm = 0;
+  w.qp = w.perm + up((size_t)g.N * sizeof(int32_t));
+  w.kp = w.qp + up(tok);
+  w.mask = w.kp + up(tok);
+  w.counts = w.mask + up((size_t)g.B * g.H * g.nQ * g.nK);
+  w.pooled = w.counts + up((size_t)g.H * 6 * sizeof(unsigned long long));
+  w.total = w.pooled + up(bsa::pooled_scratch_need(g, 1));
+  return w;
+}
+
+size_t bsa_token_orders_workspace_bytes(const bsa_shape* s, bsa_dtype dt) {
+  bsa::Geom g;
+  if (make_geom(s, &g) != BSA_OK || (dt != BSA_BF16 && dt != BSA_F32)) return 0;
+  return order_ws_layout(g, elem_bytes(dt)).total;
+}
+
+bsa_status bsa_choose_token_orders(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, bsa_tensor k,
+                                   double scale, int32_t mode, double param, int32_t* order_out,
+                                   uint64_t* counts_out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  bsa::Geom g;
+  bsa_status st = make_geom(s, &g);
+  if (st != BSA_OK) return st;
+  if (mode != 0 && mode != 1)
+    return fail(BSA_ERR_INVALID, "order choice scores per-row selection (mode 0 or 1), got %d",
+                mode);
+  if (!order_out && !empty(g)) return fail(BSA_ERR_INVALID, "order_out is NULL");
+  if ((st = check_pooled(g, dt, q, k, scale, mode, param, (const uint8_t*)order_out)) != BSA_OK)
+    return st;
+  if (empty(g)) return ok();
+  const int eb = elem_bytes(dt);
+  const OrderWs L = order_ws_layout(g, eb);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(BSA_ERR_INVALID, "workspace needs %zu bytes", L.total);
+  if ((uintptr_t)workspace % 256) return fail(BSA_ERR_INVALID, "workspace not 256-byte aligned");
+  char* base = (char*)workspace;
+  int32_t* perm = (int32_t*)(base + L.perm);
+  uint8_t* mask = (uint8_t*)(base + L.mask);
+  unsigned long long* counts =
+      counts_out ? (unsigned long long*)counts_out : (unsigned long long*)(base + L.counts);
+  const int64_t sn = (int64_t)g.H * g.D, sb = (int64_t)g.N * sn;
+  const bsa::TensorArg qp{base + L.qp, sb, sn, g.D}, kp{base + L.kp, sb, sn, g.D};
+  const hipStream_t hs = (hipStream_t)stream;
+  static const int32_t kAxes[6][3] = {{0, 1, 2}, {0, 2, 1}, {1, 0, 2},
+                                      {1, 2, 0}, {2, 0, 1}, {2, 1, 0}};
+  hipError_t e = bsa::launch_zero_counts(counts, (int64_t)g.H * 6, hs);
+  for (int o = 0; o < 6 && e == hipSuccess; ++o) {
+    e = bsa::launch_make_permutation(g, 0, kAxes[o], perm, hs);
+    if (e == hipSuccess) e = bsa::launch_permute_tokens(g, eb, perm, 0, 0, arg(q), qp, hs);
+    if (e == hipSuccess) e = bsa::launch_permute_tokens(g, eb, perm, 0, 0, arg(k), kp, hs);
+    if (e == hipSuccess)
+      e = bsa::launch_pooled_mask(g, dt == BSA_BF16 ? 0 : 1, qp, kp, scale, mode, param, mask,
+                                  base + L.pooled, hs);
+    if (e == hipSuccess) e = bsa::launch_count_kept(g, o, mask, counts, hs);
+  }
+  if (e == hipSuccess) e = bsa::launch_choose_order(g.H, counts, order_out, hs);
+  return device(e, "token order choice launch");
+}
+
 // Level regions of pyramid lists: rb[l] = first augmented key block of level
 // l (each level's N >> l pooled rows padded to whole 64-row blocks).
 static void pyramid_regions(const bsa::Geom& g, int32_t n_levels, int64_t rb[4]) {

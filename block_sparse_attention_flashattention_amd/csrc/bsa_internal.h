@@ -77,6 +77,11 @@ hipError_t launch_make_permutation(const Geom& g, int32_t kind, const int32_t* a
 hipError_t launch_permute_tokens(const Geom& g, int elem_bytes, const int32_t* perm,
                                  int64_t perm_head_stride, int32_t scatter, TensorArg in,
                                  TensorArg out, hipStream_t st);
+hipError_t launch_zero_counts(unsigned long long* counts, int64_t n, hipStream_t st);
+hipError_t launch_count_kept(const Geom& g, int32_t order, const uint8_t* mask,
+                             unsigned long long* counts, hipStream_t st);
+hipError_t launch_choose_order(int32_t H, const unsigned long long* counts, int32_t* order_out,
+                               hipStream_t st);
 
 // ---- attention forward
 struct AttnArgs {

@@ -9,7 +9,9 @@
 // made of temporal chunks, spatial patches or spatio-temporal cubes.
 //
 // Both kernels are pure data movement (integer index math; bytes copied as
-// they are), bound by HBM bandwidth.
+// they are), bound by HBM bandwidth. The per-head choice among the six axis
+// orders counts the tiles a pooled mask keeps under each order (exact
+// integer sums; the orchestration is in api.cpp).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -73,6 +75,52 @@ __global__ void permute_rows_kernel(int64_t B, int64_t N, int64_t H, int64_t cpr
   }
 }
 
+// counts[i] = 0 for i < n (a kernel rather than a memset, so that the call
+// can sit in a captured graph).
+__global__ void zero_counts_kernel(unsigned long long* counts, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    counts[i] = 0;
+}
+
+// Kept tiles of each (b, h) mask slice of `per` bytes, added to
+// counts[h * kOrders + order]: 16 mask bytes per thread and step, a wave
+// reduction, one 64-bit atomic per wave (integer sums: any order gives the
+// same total). grid.y = B * H.
+constexpr int kOrders = 6;
+__global__ void count_kept_kernel(int64_t per, int32_t H, int32_t order,
+                                  const uint8_t* __restrict__ mask,
+                                  unsigned long long* __restrict__ counts) {
+  const int64_t bh = blockIdx.y;
+  const uint8_t* m = mask + bh * per;
+  unsigned long long n = 0;
+  for (int64_t i = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) * 16; i < per;
+       i += (int64_t)gridDim.x * blockDim.x * 16) {
+    if (i + 16 <= per && ((uintptr_t)(m + i) & 15) == 0) {
+      const u32x4 v = *(const u32x4*)(m + i);
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) n += ((v[w] >> (8 * b)) & 0xff) != 0;
+    } else {
+      for (int64_t j = i; j < per && j < i + 16; ++j) n += m[j] != 0;
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) n += __shfl_xor(n, off);
+  if ((threadIdx.x & 63) == 0 && n) atomicAdd(&counts[(bh % H) * kOrders + order], n);
+}
+
+// Per head: the order with the fewest kept tiles, ties to the lower index.
+__global__ void choose_order_kernel(int32_t H, const unsigned long long* __restrict__ counts,
+                                    int32_t* __restrict__ order_out) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  int best = 0;
+  for (int o = 1; o < kOrders; ++o)
+    if (counts[h * kOrders + o] < counts[h * kOrders + best]) best = o;
+  order_out[h] = best;
+}
+
 inline unsigned grid_for(int64_t work, int threads, int64_t cap = 1 << 20) {
   int64_t g = (work + threads - 1) / threads;
   if (g < 1) g = 1;
@@ -101,6 +149,30 @@ hipError_t launch_permute_tokens(const Geom& g, int elem_bytes, const int32_t* p
                      (int64_t)g.B, g.N, (int64_t)g.H, cpr, perm, perm_head_stride, scatter,
                      (const char*)in.ptr, in.sb * eb, in.sn * eb, in.sh * eb, (char*)out.ptr,
                      out.sb * eb, out.sn * eb, out.sh * eb);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_counts(unsigned long long* counts, int64_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_counts_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, counts, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_count_kept(const Geom& g, int32_t order, const uint8_t* mask,
+                             unsigned long long* counts, hipStream_t st) {
+  const int64_t per = g.nQ * g.nK, BH = (int64_t)g.B * g.H;
+  if (per == 0 || BH == 0) return hipSuccess;
+  const unsigned gx = grid_for((per + 16 * 256 - 1) / (16 * 256), 1, 1024);
+  hipLaunchKernelGGL(count_kept_kernel, dim3(gx, (unsigned)BH), dim3(256), 0, st, per, g.H,
+                     order, mask, counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_choose_order(int32_t H, const unsigned long long* counts, int32_t* order_out,
+                               hipStream_t st) {
+  if (H == 0) return hipSuccess;
+  hipLaunchKernelGGL(choose_order_kernel, dim3((H + 63) / 64), dim3(64), 0, st, H, counts,
+                     order_out);
   return hipGetLastError();
 }
 

@@ -243,6 +243,33 @@ BSA_API bsa_status bsa_make_token_permutation(const bsa_shape* s, int32_t kind,
                                       void* stream);
 
 /*
+ * Per-head choice of the token order ([PARO] section 二: each head takes the
+ * one of the six frame/row/column axis orders under which its attention is
+ * most sparsity-friendly; the quantization side of that choice is not built).
+ * Reading taken: order o (the axis orders of bsa_make_token_permutation kind
+ * 0 in lexicographic order: 0 = (0,1,2) the identity, 1 = (0,2,1),
+ * 2 = (1,0,2), 3 = (1,2,0), 4 = (2,0,1), 5 = (2,1,0)) scores, for head h, the
+ * number of tiles that bsa_build_mask_pooled (mode 0 or 1 with param) keeps
+ * for that head, summed over the batch, when Q and K are gathered into order
+ * o; the head takes the order with the fewest, ties to the lower index.
+ * Exact integer counts over bit-exact masks.
+ *   order_out   out, int32 [H] (device): the chosen order per head
+ *   counts_out  out, uint64 [H][6] (device) kept tiles per head and order,
+ *               or NULL
+ *   workspace   device buffer of at least bsa_token_orders_workspace_bytes
+ *               (s, dt) bytes, 256-byte aligned (Q and K in one order, one
+ *               pooled mask and the pooled builder's scratch)
+ * Same limits and errors as bsa_build_mask_pooled; modes other than 0 and 1
+ * return BSA_ERR_INVALID.
+ */
+BSA_API size_t bsa_token_orders_workspace_bytes(const bsa_shape* s, bsa_dtype dt);
+BSA_API bsa_status bsa_choose_token_orders(const bsa_shape* s, bsa_dtype dt, bsa_tensor q,
+                                           bsa_tensor k, double scale, int32_t mode,
+                                           double param, int32_t* order_out,
+                                           uint64_t* counts_out, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
+/*
  * Moves the tokens of a [B][N][H][d] tensor into or out of a token order
  * (pure data movement; bytes are copied as they are):
  *   scatter 0 (gather):  out[b][i'][h] = in[b][perm_h[i']][h]

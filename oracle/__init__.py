@@ -67,6 +67,9 @@ def lib():
         L.oracle_pyramid_regions.restype = None
         L.oracle_compact_pyramid.argtypes = [i64] * 7 + [p, i64, p, p, p]
         L.oracle_compact_pyramid.restype = i64
+        L.oracle_choose_token_orders.argtypes = ([i64] * 8 + [C.c_int, p, p, d, C.c_int, d, p,
+                                                                p])
+        L.oracle_choose_token_orders.restype = C.c_int
         _lib = L
     return _lib
 
@@ -201,6 +204,25 @@ def make_permutation(T: int, Hs: int, Ws: int, kind: int, axes) -> np.ndarray:
     perm = np.empty(T * Hs * Ws, dtype=np.int32)
     lib().oracle_make_permutation(T, Hs, Ws, int(kind), _ptr(ax), _ptr(perm))
     return perm
+
+
+def choose_token_orders(q: np.ndarray, k: np.ndarray, T: int, Hs: int, Ws: int, bq: int,
+                        bk: int, scale: float, mode: int, param: float):
+    """Per-head token order ([PARO] section 二, reading in bsa_oracle.c):
+    (order per head [H], kept tiles per head and order [H][6]). q, k are
+    [B][N][H][d] bf16 bits (uint16) or float32."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    B, N, H, D = q.shape
+    assert N == T * Hs * Ws and k.shape == q.shape and k.dtype == q.dtype
+    orders = np.empty(H, dtype=np.int32)
+    counts = np.empty((H, 6), dtype=np.int64)
+    rc = lib().oracle_choose_token_orders(B, H, T, Hs, Ws, D, bq, bk, _dtype_code(q), _ptr(q),
+                                          _ptr(k), float(scale), int(mode), float(param),
+                                          _ptr(orders), _ptr(counts))
+    if rc != 0:
+        raise ValueError("oracle_choose_token_orders: bad arguments")
+    return orders, counts
 
 
 def permute_tokens(x: np.ndarray, perm: np.ndarray, scatter: bool = False) -> np.ndarray:

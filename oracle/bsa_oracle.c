@@ -452,6 +452,68 @@ void oracle_make_permutation(int64_t T, int64_t Hs, int64_t Ws, int kind,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Per-head order choice ([PARO] section 二: a head takes, among the six    */
+/* axis orders, the one under which its attention is most sparsity-        */
+/* friendly; the pages give no formula, and the quantization side of the   */
+/* choice is out of scope here). Reading: order o (axis orders in           */
+/* lexicographic order, 0 = (0,1,2) ... 5 = (2,1,0)) scores, for head h,    */
+/* the number of tiles oracle_build_mask_pooled (mode 0 or 1, param) keeps  */
+/* for that head over the batch once Q and K are gathered into order o;     */
+/* the head takes the fewest, ties to the lower order. q, k contiguous      */
+/* [B][N][H][D] of dtype (0 bf16 bits, 1 float). counts_out [H][6].         */
+/* Returns 0, or -1 on a bad argument or allocation failure.               */
+/* ------------------------------------------------------------------------ */
+int oracle_choose_token_orders(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws,
+                               int64_t D, int64_t bq, int64_t bk, int dtype, const void* q,
+                               const void* k, double scale, int mode, double param,
+                               int32_t* order_out, int64_t* counts_out) {
+  static const int64_t axes[6][3] = {{0, 1, 2}, {0, 2, 1}, {1, 0, 2},
+                                     {1, 2, 0}, {2, 0, 1}, {2, 1, 0}};
+  if ((mode != 0 && mode != 1) || (dtype != 0 && dtype != 1)) return -1;
+  const int64_t N = T * Hs * Ws, nQ = (N + bq - 1) / bq, nK = (N + bk - 1) / bk;
+  const size_t esz = dtype == 0 ? 2 : 4, row = (size_t)D * esz;
+  int32_t* perm = malloc(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+  char* qp = malloc((size_t)(B * N * H) * row + 1);
+  char* kp = malloc((size_t)(B * N * H) * row + 1);
+  uint8_t* mask = malloc((size_t)(B * H * nQ * nK) + 1);
+  int bad = !perm || !qp || !kp || !mask;
+  for (int64_t i = 0; i < H * 6; ++i) counts_out[i] = 0;
+  for (int o = 0; o < 6 && !bad; ++o) {
+    oracle_make_permutation(T, Hs, Ws, 0, axes[o], perm);
+    /* gather: new position i' holds original token perm[i'] */
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t i = 0; i < N; ++i)
+        for (int64_t h = 0; h < H; ++h) {
+          const size_t dst = (size_t)((b * N + i) * H + h) * row;
+          const size_t src = (size_t)((b * N + perm[i]) * H + h) * row;
+          memcpy(qp + dst, (const char*)q + src, row);
+          memcpy(kp + dst, (const char*)k + src, row);
+        }
+    if (oracle_build_mask_pooled(B, H, N, D, bq, bk, dtype, qp, N * H * D, H * D, D, kp,
+                                 N * H * D, H * D, D, scale, mode, param, mask, NULL, NULL,
+                                 NULL, 0) != 0) {
+      bad = 1;
+      break;
+    }
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t h = 0; h < H; ++h) {
+        const uint8_t* m = mask + (b * H + h) * nQ * nK;
+        int64_t n = 0;
+        for (int64_t e = 0; e < nQ * nK; ++e) n += m[e] != 0;
+        counts_out[h * 6 + o] += n;
+      }
+  }
+  for (int64_t h = 0; h < H && !bad; ++h) {
+    int best = 0;
+    for (int o = 1; o < 6; ++o)
+      if (counts_out[h * 6 + o] < counts_out[h * 6 + best]) best = o;
+    order_out[h] = best;
+  }
+  free(perm); free(qp); free(kp); free(mask);
+  return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Pyramid attention ([PSA]: key/value blocks kept at several resolutions,  */
 /* each coarser level the average of the finer one; each pair of query and */
 /* key block attends at its assigned level; the probabilities stay          */

@@ -32,6 +32,10 @@ void oracle_order_lists(int64_t N, int64_t bq, int64_t bk, int64_t nQ, int64_t R
                         const int32_t* row_ptr, const int32_t* kv_in, int32_t* kv_out);
 void oracle_make_permutation(int64_t T, int64_t Hs, int64_t Ws, int kind, const int64_t* axes,
                              int32_t* perm);
+int oracle_choose_token_orders(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws,
+                               int64_t D, int64_t bq, int64_t bk, int dtype, const void* q,
+                               const void* k, double scale, int mode, double param,
+                               int32_t* order_out, int64_t* counts_out);
 int oracle_pyramid_attention(int64_t B, int64_t H, int64_t N, int64_t D, int64_t bq, int64_t bk,
                              int dtype, const void* q, int64_t qsb, int64_t qsn, int64_t qsh,
                              const void* k, int64_t ksb, int64_t ksn, int64_t ksh,
@@ -130,6 +134,19 @@ static void run_case(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
                            0.2, pmask, nQ * nK, R, rows, o, lse, gap, order) == 0);
   CHECK(oracle_attention(B, H, N, D, bq, bk, 0, qb, sb, sn, sh, qb, sb, sn, sh, qb, sb, sn, sh,
                          0.2, rmask, 0, R, rows, o, lse, NULL, 0) == 0);
+
+  /* per-head order choice over the six axis orders (both per-row modes) */
+  {
+    int32_t ord[8];
+    int64_t cnt[8 * 6];
+    if (H <= 8) {
+      CHECK(oracle_choose_token_orders(B, H, T, Hs, Ws, D, bq, bk, 1, q, k, 0.3, 1, 0.5, ord,
+                                       cnt) == 0);
+      CHECK(oracle_choose_token_orders(B, H, T, Hs, Ws, D, bq, bk, 0, qb, qb, 0.3, 0, 2.0, ord,
+                                       cnt) == 0);
+      for (int64_t h = 0; h < H; ++h) CHECK(ord[h] >= 0 && ord[h] < 6);
+    }
+  }
 
   /* permutations: all axis orders and a few boxes */
   int32_t* perm = malloc(sizeof(int32_t) * N);

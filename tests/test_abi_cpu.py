@@ -34,7 +34,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     out = subprocess.run(["nm", "-D", "--defined-only", bsa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (bsa_\w+)", out))

@@ -134,3 +134,62 @@ def test_permute_tokens_head_dim_64_and_strided_views():
     torch.cuda.synchronize()
     want = oracle.permute_tokens(np.ascontiguousarray(x["k"][:, :, 1:3]), P)
     np.testing.assert_array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), want)
+
+
+def _choose_gpu(w, x, mode, param):
+    s = shape_of(w)
+    q, k = dev(x["q"]), dev(x["k"])
+    dt = bsa.BSA_BF16 if q.dtype == torch.bfloat16 else bsa.BSA_F32
+    ws = torch.empty(bsa.bsa_token_orders_workspace_bytes(s, dt), dtype=torch.uint8, device=DEV)
+    orders = torch.full((w.H,), -1, dtype=torch.int32, device=DEV)
+    counts = torch.zeros((w.H, 6), dtype=torch.int64, device=DEV)
+    bsa.bsa_choose_token_orders(s, q, k, w.scale, mode, param, orders, counts, ws)
+    torch.cuda.synchronize()
+    return host(orders), host(counts)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode,param", [(0, 5.0), (1, 0.5)])
+def test_choose_token_orders_bit_exact(dtype, mode, param):
+    """Per-head order choice: kept-tile counts of all six orders and the
+    chosen order equal the oracle's (integer sums of bit-exact masks)."""
+    w = synth.Workload("orders_small", 2, 3, 64, 8, 12, 20, 64, 64, dtype, "pooled", 631, True)
+    x = synth.make_qkv(w)
+    got_o, got_c = _choose_gpu(w, x, mode, param)
+    ref_o, ref_c = oracle.choose_token_orders(x["q"], x["k"], w.T, w.Hs, w.Ws, w.Bq, w.Bk,
+                                              w.scale, mode, param)
+    note(f"orders {dtype} mode={mode}: chosen {got_o.tolist()}, counts {got_c.tolist()}")
+    np.testing.assert_array_equal(got_c, ref_c)
+    np.testing.assert_array_equal(got_o, ref_o)
+
+
+def test_choose_token_orders_prefers_frames_fastest():
+    """Tokens keyed by their (row, column) position, the same in every frame:
+    with 64 frames and 64-token blocks the frame-fastest orders put one
+    position in each block, keep one block per row and win (order 3, the
+    lower of the tied pair)."""
+    w = synth.Workload("orders_pos", 1, 2, 64, 64, 4, 8, 64, 64, "f32", "pooled", 632, True)
+    r = np.random.default_rng(8)
+    pos = r.standard_normal((w.Hs, w.Ws, w.H, w.d)) * 3.0
+    xq = np.broadcast_to(pos[None], (w.T, w.Hs, w.Ws, w.H, w.d)).reshape(1, w.N, w.H, w.d)
+    xq = (xq + 0.01 * r.standard_normal(xq.shape)).astype(np.float32)
+    x = {"q": xq, "k": xq.copy()}
+    got_o, got_c = _choose_gpu(w, x, 1, 0.9)
+    ref_o, ref_c = oracle.choose_token_orders(x["q"], x["k"], w.T, w.Hs, w.Ws, w.Bq, w.Bk,
+                                              w.scale, 1, 0.9)
+    np.testing.assert_array_equal(got_c, ref_c)
+    assert np.all(got_o == 3) and np.all(got_c[:, 3] == w.nQ)
+
+
+def test_choose_token_orders_wan13b_480p():
+    """The 480p layer (12 heads): the order each head takes and the kept
+    tiles under every order, against the oracle."""
+    w = synth.workload("wan13b_480p")
+    x = synth.make_qkv(w)
+    got_o, got_c = _choose_gpu(w, x, w.pooled_mode, w.pooled_param)
+    ref_o, ref_c = oracle.choose_token_orders(x["q"], x["k"], w.T, w.Hs, w.Ws, w.Bq, w.Bk,
+                                              w.scale, w.pooled_mode, w.pooled_param)
+    note(f"480p orders chosen {got_o.tolist()}; kept tiles of order 0 "
+         f"{got_c[:, 0].tolist()}, of the chosen {got_c[np.arange(w.H), got_o].tolist()}")
+    np.testing.assert_array_equal(got_c, ref_c)
+    np.testing.assert_array_equal(got_o, ref_o)
