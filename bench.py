@@ -76,6 +76,23 @@ def source_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def stratified_rows(BH: int, nQ: int, per_head: int, N: int, bq: int, F: int, rng) -> np.ndarray:
+    """Row blocks for the CPU baseline, per head: the first, the last (ragged), about a
+    quarter of them straddling a frame boundary (F tokens per frame), the rest uniform."""
+    straddle = [a for a in range(nQ) if (a * bq) // F != (min(N, (a + 1) * bq) - 1) // F]
+    picks = []
+    for bh in range(BH):
+        pick = {0, nQ - 1}
+        if straddle:
+            pick |= set(rng.choice(straddle, size=min(len(straddle), max(1, per_head // 4)),
+                                   replace=False).tolist())
+        free = [a for a in range(nQ) if a not in pick]
+        more = max(0, min(len(free), per_head - len(pick)))
+        pick |= set(rng.choice(free, size=more, replace=False).tolist())
+        picks += [bh * nQ + a for a in sorted(pick)]
+    return np.array(picks, dtype=np.int64)
+
+
 def variant_key(args, w) -> str:
     """Name of a measured configuration: the workload plus every option that
     changes what the forward kernel runs on (a counter record is kept per
@@ -645,7 +662,7 @@ def main():
                 torch.cuda.synchronize()
                 mask_h = mask.cpu().numpy().reshape(BH, nQ, nK)
             mhs = nQ * nK
-        rows = np.sort(rng.choice(BH * nQ, size=min(args.cpu_rows, BH * nQ), replace=False))
+        rows = stratified_rows(BH, nQ, max(4, args.cpu_rows // BH), w.N, w.Bq, w.Hs * w.Ws, rng)
         rr = rows % nQ
         ra = np.minimum(w.N, (rr + 1) * w.Bq) - rr * w.Bq
         per_row_keys = []
@@ -660,10 +677,21 @@ def main():
         t0 = time.time()
         oracle.attention(x["q"], x["k"], x["v"], w.Bq, w.Bk, w.scale, mask_h, mhs, rows=rows)
         cpu_s = time.time() - t0
+        # the same count over every row block (the oracle computes kept tiles at full size)
+        bsz = (np.minimum(w.N, (np.arange(nK) + 1) * w.Bk) - np.arange(nK) * w.Bk).astype(
+            np.float64)
+        rsz = (np.minimum(w.N, (np.arange(nQ) + 1) * w.Bq) - np.arange(nQ) * w.Bq).astype(
+            np.float64)
+        kept = (mask_h != 0).astype(np.float64) @ bsz
+        full_flops = 4.0 * w.d * float(np.sum(kept * rsz)) * (BH if mhs == 0 else 1)
         cpu = {"value": sample_flops / cpu_s / 1e12, "unit": "TFLOP/s",
                "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"{len(rows)} of {BH * nQ} row blocks of {w.name} "
-                         f"(first step's mask), {sample_flops / 1e9:.1f} GFLOP fp64 in {cpu_s:.1f} s"}
+               "sample": f"{len(rows)} of {BH * nQ} row blocks of {w.name} (first step's mask), "
+                         f"stratified per head: first, last (ragged), frame-straddling and "
+                         f"uniform ones; {sample_flops / 1e9:.1f} GFLOP fp64 in {cpu_s:.1f} s",
+               "extrapolated_full_call_s": cpu_s * full_flops / sample_flops,
+               "extrapolation": "sample time scaled by computed-tile flop of the whole call "
+                                "(an extrapolation, not a measurement)"}
         log(f"CPU oracle: {cpu['value'] * 1e3:.3f} GFLOP/s")
 
     ctr = counters_for(variant_key(args, w))
