@@ -140,8 +140,8 @@ def build_mask_pooled(q: np.ndarray, k: np.ndarray, bq: int, bk: int, scale: flo
     scores = np.zeros((B, H, nQ, nK), dtype=np.float64) if want_scores else None
     margin = np.zeros((B, H, nQ), dtype=np.float64)
     lt = np.ascontiguousarray(levels_tau if levels_tau is not None else [], dtype=np.float64)
-    if mode == 4 and not (1 <= lt.size <= 3 and np.all(np.diff(lt) >= 0)):
-        raise ValueError("pyramid levels need 1..3 non-decreasing thresholds")
+    if mode == 4 and not (1 <= lt.size <= 4 and np.all(np.diff(lt) >= 0)):
+        raise ValueError("pyramid levels need 1..4 non-decreasing thresholds")
     rc = lib().oracle_build_mask_pooled(
         B, H, N, D, bq, bk, dt, _ptr(q), *_strides(q), _ptr(k), *_strides(k),
         float(scale), int(mode), float(param), _ptr(mask),
@@ -251,11 +251,14 @@ def pyramid_regions(N: int, bk: int, n_levels: int):
 
 def compact_pyramid(mask: np.ndarray, B: int, H: int, nQ: int, nK: int, N: int, bk: int,
                     n_levels: int, mask_head_stride: int):
-    """Augmented-tile lists of a pyramid mask: (row_ptr, kv_idx, kv_quarters)."""
+    """Augmented-tile lists of a pyramid mask (1 to 4 levels): (row_ptr, kv_idx, kv_eighths),
+    bit i of an entry's eighths = pooled rows i*bk/8 .. (i+1)*bk/8 - 1 of the block."""
     mask = np.ascontiguousarray(mask, dtype=np.uint8)
     L = lib()
     nnz = L.oracle_compact_pyramid(B, H, nQ, nK, N, bk, n_levels, _ptr(mask), mask_head_stride,
                                    None, None, None)
+    if nnz < 0:
+        raise ValueError("compact_pyramid: n_levels outside 1..4 or a mask value above it")
     row_ptr = np.zeros(B * H * nQ + 1, np.int32)
     kv = np.zeros(max(nnz, 1), np.int32)
     qm = np.zeros(max(nnz, 1), np.uint8)

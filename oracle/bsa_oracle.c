@@ -630,19 +630,23 @@ void oracle_pyramid_regions(int64_t N, int64_t bk, int64_t n_levels, int64_t* re
 
 /* Lists of augmented tiles for a pyramid mask ([PSA]: the logical block    */
 /* size is decoupled from the hardware tile). Logical block c at level l    */
-/* covers pooled rows [c*bk/2^l, (c+1)*bk/2^l) of region l, i.e. quarters   */
-/* (bk/4 rows each) of augmented block region_block[l] + c*bk/2^l / bk.     */
-/* Per row: every augmented block with at least one selected quarter, in    */
-/* ascending block order, with the bit mask of its selected quarters.       */
+/* (l = 0..3) covers pooled rows [c*bk/2^l, (c+1)*bk/2^l) of region l,      */
+/* i.e. eighths (bk/8 rows each) of augmented block                         */
+/* region_block[l] + c*bk/2^l / bk. Per row: every augmented block with at  */
+/* least one selected eighth, in ascending block order, with the bit mask   */
+/* of its selected eighths (bit i = rows i*bk/8 .. (i+1)*bk/8 - 1).         */
 int64_t oracle_compact_pyramid(int64_t B, int64_t H, int64_t nQ, int64_t nK, int64_t N,
                                int64_t bk, int64_t n_levels, const uint8_t* mask,
                                int64_t mask_head_stride, int32_t* row_ptr, int32_t* kv_idx,
-                               uint8_t* kv_quarters) {
-  int64_t rb[4], rr[4];
+                               uint8_t* kv_eighths) {
+  int64_t rb[5], rr[5];
+  if (n_levels < 1 || n_levels > 4) return -1;
   oracle_pyramid_regions(N, bk, n_levels, rb, rr);
   int64_t nA = rb[n_levels];
   uint8_t* qm = (uint8_t*)calloc((size_t)(nA > 0 ? nA : 1), 1);
+  if (!qm) return -1;
   int64_t nnz = 0;
+  int bad = 0;
   for (int64_t bh = 0; bh < B * H; ++bh)
     for (int64_t a = 0; a < nQ; ++a) {
       int64_t r = bh * nQ + a;
@@ -651,21 +655,25 @@ int64_t oracle_compact_pyramid(int64_t B, int64_t H, int64_t nQ, int64_t nK, int
       for (int64_t c = 0; c < nK; ++c) {
         int v = mask[bh * mask_head_stride + a * nK + c];
         if (!v) continue;
+        if (v > n_levels) {                          /* not a level of this pyramid */
+          bad = 1;
+          continue;
+        }
         int64_t l = v - 1, per = bk >> l;          /* pooled rows of the block */
         int64_t row0 = c * per;                      /* first pooled row in region */
-        for (int64_t rr0 = row0; rr0 < row0 + per; rr0 += bk / 4)
-          qm[rb[l] + rr0 / bk] |= (uint8_t)(1u << ((rr0 % bk) / (bk / 4)));
+        for (int64_t rr0 = row0; rr0 < row0 + per; rr0 += bk / 8)
+          qm[rb[l] + rr0 / bk] |= (uint8_t)(1u << ((rr0 % bk) / (bk / 8)));
       }
       for (int64_t ab = 0; ab < nA; ++ab)
         if (qm[ab]) {
           if (kv_idx) kv_idx[nnz] = (int32_t)ab;
-          if (kv_quarters) kv_quarters[nnz] = qm[ab];
+          if (kv_eighths) kv_eighths[nnz] = qm[ab];
           ++nnz;
         }
     }
   if (row_ptr) row_ptr[B * H * nQ] = (int32_t)nnz;
   free(qm);
-  return nnz;
+  return bad ? -1 : nnz;
 }
 
 /* ------------------------------------------------------------------------ */

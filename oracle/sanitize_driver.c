@@ -48,7 +48,7 @@ void oracle_pyramid_regions(int64_t N, int64_t bk, int64_t n_levels, int64_t* re
 int64_t oracle_compact_pyramid(int64_t B, int64_t H, int64_t nQ, int64_t nK, int64_t N,
                                int64_t bk, int64_t n_levels, const uint8_t* mask,
                                int64_t mask_head_stride, int32_t* row_ptr, int32_t* kv_idx,
-                               uint8_t* kv_quarters);
+                               uint8_t* kv_eighths);
 int oracle_attention(int64_t B, int64_t H, int64_t N, int64_t D, int64_t bq, int64_t bk,
                      int dtype, const void* q, int64_t qsb, int64_t qsn, int64_t qsh,
                      const void* k, int64_t ksb, int64_t ksn, int64_t ksh, const void* v,
@@ -155,17 +155,19 @@ static void run_case(int64_t B, int64_t H, int64_t T, int64_t Hs, int64_t Ws, in
   const int64_t box[3] = {2, 3, 2};
   oracle_make_permutation(T, Hs, Ws, 1, box, perm);
 
-  /* pyramid: regions, lists and attention on a level mask (N even needed) */
-  if (N % 4 == 0) {
-    int64_t rb[4], rr[4];
-    oracle_pyramid_regions(N, bk, 3, rb, rr);
+  /* pyramid: regions, lists and attention on a level mask, three and four
+     levels (N a multiple of 2^(levels-1)) */
+  for (int64_t L = 3; L <= 4; ++L) {
+    if (N % ((int64_t)1 << (L - 1)) != 0) continue;
+    int64_t rb[5], rr[5];
+    oracle_pyramid_regions(N, bk, L, rb, rr);
     uint8_t* lv = malloc((size_t)(R * nK));
-    for (int64_t i = 0; i < R * nK; ++i) lv[i] = (uint8_t)(uniform() * 4.0);
-    const int64_t nA = rb[3];
+    for (int64_t i = 0; i < R * nK; ++i) lv[i] = (uint8_t)(uniform() * (double)(L + 1));
+    const int64_t nA = rb[L];
     int32_t* prp = malloc(sizeof(int32_t) * (R + 1));
     int32_t* pkv = malloc(sizeof(int32_t) * (R * nA + 1));
     uint8_t* pqm = malloc((size_t)(R * nA + 1));
-    const int64_t pn = oracle_compact_pyramid(B, H, nQ, nK, N, bk, 3, lv, nQ * nK, prp, pkv, pqm);
+    const int64_t pn = oracle_compact_pyramid(B, H, nQ, nK, N, bk, L, lv, nQ * nK, prp, pkv, pqm);
     CHECK(pn == prp[R]);
     CHECK(oracle_pyramid_attention(B, H, N, D, bq, bk, 1, q, sb, sn, sh, k, sb, sn, sh, v, sb,
                                    sn, sh, 0.2, lv, nQ * nK, R, rows, o, lse) == 0);

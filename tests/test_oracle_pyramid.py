@@ -8,9 +8,10 @@ attention; keys and values that are constant inside every group of tokens
 give the same output at any mix of levels (this fixes the +level*ln 2 weight
 of a pooled key); constant V is reproduced; the level mask relates exactly
 to the per-row cumulative-mass mask at each threshold; the tile lists match
-a layout worked out by hand (tests/golden/pyramid_lists_296.txt), and,
-decoded into pooled key rows with numpy alone, give the attention the oracle
-computes from the level mask.
+layouts worked out by hand for three and four levels
+(tests/golden/pyramid_lists_296*.txt), and, decoded into pooled key rows
+with numpy alone, give the attention the oracle computes from the level
+mask.
 """
 import os
 
@@ -41,17 +42,17 @@ def test_level_zero_everywhere_is_block_attention(oracle_lib):
     np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12, equal_nan=True)
 
 
-@pytest.mark.parametrize("levels", [(1, 2), (1, 3), (1, 2, 3)])
+@pytest.mark.parametrize("levels", [(1, 2), (1, 3), (1, 2, 3), (1, 4), (1, 2, 3, 4)])
 def test_group_constant_keys_and_values_give_level_zero_output(oracle_lib, levels):
-    """If every group of 4 consecutive tokens shares one key and one value, a
+    """If every group of 8 consecutive tokens shares one key and one value, a
     pooled key equals each of its tokens, and with weight 2^l it carries the
     same probability mass: any mix of levels gives the level-0 output."""
     B, N, H, D, bq, bk = 1, 256, 2, 8, 32, 64
     r = np.random.default_rng(3)
-    base = r.standard_normal((B, N // 4, H, D, 3))
+    base = r.standard_normal((B, N // 8, H, D, 3))
     q = r.standard_normal((B, N, H, D))
-    k = np.repeat(base[..., 0], 4, axis=1)
-    v = np.repeat(base[..., 1], 4, axis=1)
+    k = np.repeat(base[..., 0], 8, axis=1)
+    v = np.repeat(base[..., 1], 8, axis=1)
     nQ, nK = N // bq, N // bk
     mix = r.choice(np.array(levels, np.uint8), size=(B, H, nQ, nK))
     ones = np.ones_like(mix)
@@ -71,14 +72,15 @@ def test_constant_values_are_reproduced_at_every_level(oracle_lib):
     q, k, _ = rand_qkv(B, N, H, D, 4)
     c = np.random.default_rng(5).standard_normal(D)
     v = np.broadcast_to(c, (B, N, H, D)).copy()
-    m = np.random.default_rng(6).integers(0, 4, size=(B, H, 8, 2)).astype(np.uint8)
+    m = np.random.default_rng(6).integers(0, 5, size=(B, H, 8, 2)).astype(np.uint8)
     m[..., 0] = np.maximum(m[..., 0], 1)     # no empty row
     o, _ = oracle.pyramid_attention(q, k, v, bq, bk, 0.5, m, 16)
     np.testing.assert_allclose(o.reshape(-1, D), np.broadcast_to(c, (o.size // D, D)),
                                rtol=0, atol=1e-12)
 
 
-@pytest.mark.parametrize("taus", [(0.3, 0.6, 0.9), (0.5, 0.5, 0.8), (0.2, 0.95), (0.7,)])
+@pytest.mark.parametrize("taus", [(0.3, 0.6, 0.9), (0.5, 0.5, 0.8), (0.2, 0.95), (0.7,),
+                                  (0.2, 0.4, 0.6, 0.8)])
 def test_level_mask_matches_cumulative_mass_at_each_threshold(oracle_lib, taus):
     r = np.random.default_rng(7)
     base = r.standard_normal((300, 8))
@@ -99,14 +101,18 @@ def test_regions_by_hand(oracle_lib):
     # N = 296: 296, 148, 74 rows -> 5, 3, 2 blocks
     rb, rr = oracle.pyramid_regions(296, 64, 3)
     assert rb.tolist() == [0, 5, 8, 10] and rr.tolist() == [296, 148, 74]
+    # four levels: 296, 148, 74, 37 rows -> 5, 3, 2, 1 blocks
+    rb, rr = oracle.pyramid_regions(296, 64, 4)
+    assert rb.tolist() == [0, 5, 8, 10, 11] and rr.tolist() == [296, 148, 74, 37]
 
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pyramid_lists_296.txt")
+GOLDEN4 = os.path.join(os.path.dirname(__file__), "golden", "pyramid_lists_296_four_levels.txt")
 
 
-def golden_rows():
+def golden_rows(path=GOLDEN):
     rows = []
-    with open(GOLDEN) as f:
+    with open(path) as f:
         for line in f:
             if line.startswith("#") or not line.strip():
                 continue
@@ -116,11 +122,12 @@ def golden_rows():
     return rows
 
 
-def test_pyramid_lists_golden_by_hand(oracle_lib):
-    """N = 296, three levels, ragged last block: lists worked out by hand from
-    the level layout (tests/golden/pyramid_lists_296.txt)."""
-    rows = golden_rows()
-    N, bk, L = 296, 64, 3
+@pytest.mark.parametrize("path,L", [(GOLDEN, 3), (GOLDEN4, 4)])
+def test_pyramid_lists_golden_by_hand(oracle_lib, path, L):
+    """N = 296, three or four levels, ragged last block: lists worked out by
+    hand from the level layout (tests/golden/pyramid_lists_296*.txt)."""
+    rows = golden_rows(path)
+    N, bk = 296, 64
     nQ, nK = len(rows), 5
     m = np.array([r[0] for r in rows], np.uint8).reshape(1, 1, nQ, nK)
     rp, kv, qm = oracle.compact_pyramid(m, 1, 1, nQ, nK, N, bk, L, nQ * nK)
@@ -133,7 +140,7 @@ def test_pyramid_lists_golden_by_hand(oracle_lib):
 
 def decode_and_attend(q, k, v, bq, bk, scale, n_levels, rp, kv, qm, rows):
     """Attention of the given list rows evaluated from the lists alone: each
-    entry (augmented block, quarter bits) names pooled key rows of one level
+    entry (augmented block, eighth bits) names pooled key rows of one level
     (level l region = augmented blocks [rb_l, rb_l+1), N >> l valid rows);
     pooled row g of level l is the mean of tokens g*2^l .. g*2^l + 2^l - 1 of
     K and of V, and its score carries + l ln 2 (it stands for 2^l tokens)."""
@@ -151,11 +158,11 @@ def decode_and_attend(q, k, v, bq, bk, scale, n_levels, rp, kv, qm, rows):
         for ab, bits in zip(kv[rp[row]:rp[row + 1]], qm[rp[row]:rp[row + 1]]):
             l = max(i for i in range(n_levels) if starts[i] <= ab)
             g = 1 << l
-            for quarter in range(4):
-                if not (bits >> quarter) & 1:
+            for eighth in range(8):
+                if not (bits >> eighth) & 1:
                     continue
-                for pr in range((ab - starts[l]) * bk + quarter * (bk // 4),
-                                (ab - starts[l]) * bk + (quarter + 1) * (bk // 4)):
+                for pr in range((ab - starts[l]) * bk + eighth * (bk // 8),
+                                (ab - starts[l]) * bk + (eighth + 1) * (bk // 8)):
                     if pr >= valid[l]:
                         continue
                     keys.append(k[b, pr * g:(pr + 1) * g, h].mean(axis=0))
@@ -173,15 +180,16 @@ def decode_and_attend(q, k, v, bq, bk, scale, n_levels, rp, kv, qm, rows):
     return outs
 
 
+@pytest.mark.parametrize("L", [3, 4])
 @pytest.mark.parametrize("N", [256, 296, 1000])
-def test_pyramid_lists_decode_to_the_mask(oracle_lib, N):
+def test_pyramid_lists_decode_to_the_mask(oracle_lib, N, L):
     """The lists, decoded into pooled key rows with no help from the oracle,
     give the attention the oracle computes from the level mask itself."""
-    B, H, D, bq, bk, L = 1, 2, 8, 64, 64, 3
+    B, H, D, bq, bk = 1, 2, 8, 64, 64
     nQ, nK = -(-N // bq), -(-N // bk)
-    r = np.random.default_rng(N)
+    r = np.random.default_rng(N + L)
     q, k, v = (r.standard_normal((B, N, H, D)) for _ in range(3))
-    m = r.integers(0, 4, size=(B, H, nQ, nK)).astype(np.uint8)
+    m = r.integers(0, L + 1, size=(B, H, nQ, nK)).astype(np.uint8)
     m[..., 0, :] = 0                                 # one empty row per head
     rp, kv, qm = oracle.compact_pyramid(m, B, H, nQ, nK, N, bk, L, nQ * nK)
     assert rp[-1] == kv.size == qm.size
@@ -200,12 +208,12 @@ def test_pyramid_lists_decode_to_the_mask(oracle_lib, N):
     rp0, kv0 = oracle.compact(ones, B, H, nQ, nK, nQ * nK)
     np.testing.assert_array_equal(rp1, rp0)
     np.testing.assert_array_equal(kv1, kv0)
-    assert np.all(qm1 == 15)
+    assert np.all(qm1 == 255)
 
 
-def test_decode_catches_a_shifted_quarter(oracle_lib):
-    """The decode check is sharp: moving one selected quarter of one entry to
-    its neighbour changes the decoded attention."""
+def test_decode_catches_a_shifted_eighth(oracle_lib):
+    """The decode check is sharp: moving the selected eighths of one entry by
+    two eighths changes the decoded attention."""
     N, B, H, D, bq, bk, L = 296, 1, 1, 8, 64, 64, 3
     rows = golden_rows()
     nQ, nK = len(rows), 5
@@ -215,6 +223,12 @@ def test_decode_catches_a_shifted_quarter(oracle_lib):
     q, k, v = (r.standard_normal((B, N, H, D)) for _ in range(3))
     o_ref, _ = oracle.pyramid_attention(q, k, v, bq, bk, 0.5, m, nQ * nK)
     bad = qm.copy()
-    bad[1] = 6                                       # row 0, block 5: quarters 1,2 not 2,3
+    bad[1] = 60                                      # row 0, block 5: eighths 2-5, not 4-7
     (o_bad, _), = decode_and_attend(q, k, v, bq, bk, 0.5, L, rp, kv, bad, [0])
     assert np.abs(o_bad - o_ref[0, :len(o_bad)]).max() > 1e-3
+
+
+def test_compaction_rejects_levels_above_the_pyramid(oracle_lib):
+    m = np.array([[[[1, 4, 0, 0, 0]]]], np.uint8)      # level 3 in a three-level pyramid
+    with pytest.raises(ValueError):
+        oracle.compact_pyramid(m, 1, 1, 1, 5, 296, 64, 3, 5)
