@@ -55,7 +55,7 @@ def tile_flops(row_ptr: np.ndarray, kv_idx: np.ndarray, N: int, Bq: int, Bk: int
 
 
 def pyramid_flops(row_ptr, kv_idx, kv_q, N, Bq, Bk, d, nQ, rb) -> float:
-    """4 d |R_a| (keys of the selected quarters) summed over pyramid tiles; a
+    """4 d |R_a| (keys of the selected eighths) summed over pyramid tiles; a
     level-l tile's keys are pooled rows, N >> l of them in level l."""
     rows = np.repeat(np.arange(len(row_ptr) - 1), np.diff(row_ptr))
     a = rows % nQ
@@ -65,9 +65,9 @@ def pyramid_flops(row_ptr, kv_idx, kv_q, N, Bq, Bk, d, nQ, rb) -> float:
     start = (ab - np.asarray(rb)[lev]) * Bk
     valid = np.clip((N >> lev) - start, 0, Bk)
     keys = np.zeros_like(ab)
-    for qd in range(4):
-        on = (kv_q.astype(np.int64) >> qd) & 1
-        keys += on * np.clip(valid - 16 * qd, 0, 16)
+    for e in range(8):
+        on = (kv_q.astype(np.int64) >> e) & 1
+        keys += on * np.clip(valid - (Bk // 8) * e, 0, Bk // 8)
     return 4.0 * d * float(np.sum(ra * keys))
 
 
@@ -318,7 +318,7 @@ def main():
                          "0 frame 1 row 2 column), boxes:T,H,W (box extent), paro (head h "
                          "takes axis order h mod 6), or choose (each head the axis order whose "
                          "pooled mask keeps the fewest tiles, chosen once before timing)")
-    ap.add_argument("--pyramid", default=None, metavar="T0[,T1[,T2]]",
+    ap.add_argument("--pyramid", default=None, metavar="T0[,T1[,T2[,T3]]]",
                     help="pooled workloads: pyramid attention with these level thresholds "
                          "(cumulative mass; level l pools 2^l tokens); the step builds the "
                          "K/V levels, the level mask and the tile lists, then runs the forward")

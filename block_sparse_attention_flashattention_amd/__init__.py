@@ -259,27 +259,27 @@ def bsa_build_mask_pyramid(s: Shape, q, k, scale: float, levels_tau, mask, works
 
 
 def bsa_compact_pyramid_lists(s: Shape, n_levels: int, mask, mask_head_stride: int, row_ptr,
-                              kv_idx, kv_quarters, kv_capacity: int | None = None,
+                              kv_idx, kv_eighths, kv_capacity: int | None = None,
                               want_nnz: bool = False, stream=None):
     if kv_capacity is None:
         kv_capacity = kv_idx.numel() if kv_idx is not None else 0
     nnz = C.c_int64(-1)
     _check("bsa_compact_pyramid_lists",
            lib().bsa_compact_pyramid_lists(C.byref(s), n_levels, _ptr(mask), mask_head_stride,
-                                           _ptr(row_ptr), _ptr(kv_idx), _ptr(kv_quarters),
+                                           _ptr(row_ptr), _ptr(kv_idx), _ptr(kv_eighths),
                                            kv_capacity, C.byref(nnz) if want_nnz else None,
                                            _stream(stream)))
     return int(nnz.value) if want_nnz else None
 
 
 def bsa_pyramid_attn_fwd(s: Shape, q, k, v, k_pyr, v_pyr, n_levels: int, o, lse, row_ptr,
-                         kv_idx, kv_quarters, scale: float | None = None, stream=None):
+                         kv_idx, kv_eighths, scale: float | None = None, stream=None):
     if scale is None:
         scale = 1.0 / float(s.head_dim) ** 0.5
     _check("bsa_pyramid_attn_fwd",
            lib().bsa_pyramid_attn_fwd(C.byref(s), _dtype(q), _tensor(q), _tensor(k), _tensor(v),
                                       _tensor(k_pyr), _tensor(v_pyr), n_levels, _tensor(o),
-                                      _ptr(lse), _ptr(row_ptr), _ptr(kv_idx), _ptr(kv_quarters),
+                                      _ptr(lse), _ptr(row_ptr), _ptr(kv_idx), _ptr(kv_eighths),
                                       scale, _stream(stream)))
 
 

@@ -412,14 +412,14 @@ bsa_status bsa_choose_token_orders(const bsa_shape* s, bsa_dtype dt, bsa_tensor 
 
 // Level regions of pyramid lists: rb[l] = first augmented key block of level
 // l (each level's N >> l pooled rows padded to whole 64-row blocks).
-static void pyramid_regions(const bsa::Geom& g, int32_t n_levels, int64_t rb[4]) {
+static void pyramid_regions(const bsa::Geom& g, int32_t n_levels, int64_t rb[5]) {
   rb[0] = 0;
-  for (int l = 1; l <= 3; ++l)
+  for (int l = 1; l <= 4; ++l)
     rb[l] = l <= n_levels ? rb[l - 1] + (((g.N >> (l - 1)) + g.Bk - 1) / g.Bk) : rb[l - 1];
 }
 
 static bsa_status check_levels(const bsa::Geom& g, int32_t n_levels) {
-  if (n_levels < 1 || n_levels > 3) return fail(BSA_ERR_INVALID, "n_levels %d not in 1..3", n_levels);
+  if (n_levels < 1 || n_levels > 4) return fail(BSA_ERR_INVALID, "n_levels %d not in 1..4", n_levels);
   if (g.N % (int64_t(1) << (n_levels - 1)))
     return fail(BSA_ERR_UNSUPPORTED, "N = %lld is not a multiple of %d (pooling groups)",
                 (long long)g.N, 1 << (n_levels - 1));
@@ -428,8 +428,8 @@ static bsa_status check_levels(const bsa::Geom& g, int32_t n_levels) {
 
 int64_t bsa_pyramid_rows(const bsa_shape* s, int32_t n_levels) {
   bsa::Geom g;
-  if (make_geom(s, &g) != BSA_OK || n_levels < 1 || n_levels > 3) return -1;
-  int64_t rb[4];
+  if (make_geom(s, &g) != BSA_OK || n_levels < 1 || n_levels > 4) return -1;
+  int64_t rb[5];
   pyramid_regions(g, n_levels, rb);
   return (rb[n_levels] - rb[1 < n_levels ? 1 : n_levels]) * g.Bk;
 }
@@ -447,7 +447,7 @@ bsa_status bsa_build_kv_pyramid(const bsa_shape* s, bsa_dtype dt, int32_t n_leve
   if ((st = check_tensor("v", v, eb)) != BSA_OK) return st;
   if ((st = check_tensor("k_pyr", k_pyr, eb)) != BSA_OK) return st;
   if ((st = check_tensor("v_pyr", v_pyr, eb)) != BSA_OK) return st;
-  int64_t rb[4];
+  int64_t rb[5];
   pyramid_regions(g, n_levels, rb);
   return device(bsa::launch_kv_pyramid(g, eb, n_levels, rb, arg(k), arg(v), arg(k_pyr),
                                        arg(v_pyr), (hipStream_t)stream),
@@ -463,9 +463,9 @@ bsa_status bsa_build_mask_pyramid(const bsa_shape* s, bsa_dtype dt, bsa_tensor q
   if (st != BSA_OK) return st;
   if (dt != BSA_BF16 && dt != BSA_F32) return fail(BSA_ERR_UNSUPPORTED, "dtype %d", (int)dt);
   if (!isfinite(scale)) return fail(BSA_ERR_INVALID, "scale is not finite");
-  if (n_levels < 1 || n_levels > 3) return fail(BSA_ERR_INVALID, "n_levels %d not in 1..3", n_levels);
+  if (n_levels < 1 || n_levels > 4) return fail(BSA_ERR_INVALID, "n_levels %d not in 1..4", n_levels);
   if (!levels_tau) return fail(BSA_ERR_INVALID, "levels_tau is NULL");
-  double taus[3] = {0, 0, 0};
+  double taus[4] = {0, 0, 0, 0};
   for (int l = 0; l < n_levels; ++l) {
     taus[l] = levels_tau[l];
     if (!(taus[l] > 0.0 && taus[l] <= 1.0) || (l > 0 && taus[l] < taus[l - 1]))
@@ -490,17 +490,17 @@ bsa_status bsa_build_mask_pyramid(const bsa_shape* s, bsa_dtype dt, bsa_tensor q
 
 bsa_status bsa_compact_pyramid_lists(const bsa_shape* s, int32_t n_levels, const uint8_t* mask,
                                      int64_t mask_head_stride, int32_t* row_ptr, int32_t* kv_idx,
-                                     int32_t* kv_quarters, int64_t kv_capacity,
+                                     int32_t* kv_eighths, int64_t kv_capacity,
                                      int64_t* nnz_host, void* stream) {
   bsa::Geom g;
   bsa_status st = make_geom(s, &g);
   if (st != BSA_OK) return st;
-  if (n_levels < 1 || n_levels > 3) return fail(BSA_ERR_INVALID, "n_levels %d not in 1..3", n_levels);
+  if (n_levels < 1 || n_levels > 4) return fail(BSA_ERR_INVALID, "n_levels %d not in 1..4", n_levels);
   if (mask_head_stride != 0 && mask_head_stride < g.nQ * g.nK)
     return fail(BSA_ERR_INVALID, "mask_head_stride must be 0 or >= nQ*nK");
   if (kv_capacity < 0) return fail(BSA_ERR_INVALID, "kv_capacity < 0");
   if (!row_ptr) return fail(BSA_ERR_INVALID, "row_ptr is NULL");
-  int64_t rb[4];
+  int64_t rb[5];
   pyramid_regions(g, n_levels, rb);
   const int64_t R = (int64_t)g.B * g.H * g.nQ, nA = rb[n_levels];
   if (R * nA > kI32Max)
@@ -511,8 +511,8 @@ bsa_status bsa_compact_pyramid_lists(const bsa_shape* s, int32_t n_levels, const
     return device(bsa::launch_zero_row_ptr(row_ptr, str), "pyramid lists launch");
   }
   if (!mask) return fail(BSA_ERR_INVALID, "mask is NULL");
-  if ((!kv_idx || !kv_quarters) && kv_capacity > 0)
-    return fail(BSA_ERR_INVALID, "kv_idx and kv_quarters are required");
+  if ((!kv_idx || !kv_eighths) && kv_capacity > 0)
+    return fail(BSA_ERR_INVALID, "kv_idx and kv_eighths are required");
   if (!nnz_host && kv_capacity < R * nA)
     return fail(BSA_ERR_CAPACITY, "without nnz_host, kv_capacity must cover every tile (%lld)",
                 (long long)(R * nA));
@@ -528,11 +528,11 @@ bsa_status bsa_compact_pyramid_lists(const bsa_shape* s, int32_t n_levels, const
     if (nnz > kv_capacity)
       return fail(BSA_ERR_CAPACITY, "%d tiles exceed kv_capacity %lld", nnz,
                   (long long)kv_capacity);
-    if (nnz > 0 && (!kv_idx || !kv_quarters))
-      return fail(BSA_ERR_INVALID, "kv_idx and kv_quarters are required");
+    if (nnz > 0 && (!kv_idx || !kv_eighths))
+      return fail(BSA_ERR_INVALID, "kv_idx and kv_eighths are required");
   }
   return device(bsa::launch_pyramid_lists(g, n_levels, rb, mask, mask_head_stride, row_ptr,
-                                          kv_idx, kv_quarters, false, str),
+                                          kv_idx, kv_eighths, false, str),
                 "pyramid list scatter");
 }
 
@@ -540,7 +540,7 @@ bsa_status bsa_pyramid_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, 
                                 bsa_tensor v, bsa_tensor k_pyr, bsa_tensor v_pyr,
                                 int32_t n_levels, bsa_tensor o, float* lse,
                                 const int32_t* row_ptr, const int32_t* kv_idx,
-                                const int32_t* kv_quarters, float scale, void* stream) {
+                                const int32_t* kv_eighths, float scale, void* stream) {
   bsa::Geom g;
   bsa_status st = make_geom(s, &g);
   if (st != BSA_OK) return st;
@@ -548,8 +548,8 @@ bsa_status bsa_pyramid_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, 
   if ((st = check_levels(g, n_levels)) != BSA_OK) return st;
   if (!isfinite(scale) || scale < 0.f)
     return fail(BSA_ERR_INVALID, "scale must be finite and >= 0");
-  if (!row_ptr || !kv_idx || !kv_quarters)
-    return fail(BSA_ERR_INVALID, "row_ptr, kv_idx and kv_quarters are required");
+  if (!row_ptr || !kv_idx || !kv_eighths)
+    return fail(BSA_ERR_INVALID, "row_ptr, kv_idx and kv_eighths are required");
   if (empty(g)) return ok();
   const int eb = 2;
   if ((st = check_tensor("q", q, eb)) != BSA_OK) return st;
@@ -579,7 +579,7 @@ bsa_status bsa_pyramid_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q, 
   a.tile_gap = nullptr;
   a.kp = n_levels > 1 ? arg(k_pyr) : arg(k);
   a.vp = n_levels > 1 ? arg(v_pyr) : arg(v);
-  a.kv_quarters = kv_quarters;
+  a.kv_eighths = kv_eighths;
   pyramid_regions(g, n_levels, a.pyr_rb);
   if ((st = debug_check(g, false, row_ptr, kv_idx, a.pyr_rb[n_levels], false,
                         (hipStream_t)stream)) != BSA_OK)

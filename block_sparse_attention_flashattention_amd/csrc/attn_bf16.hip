@@ -100,12 +100,12 @@ struct Bf16Params {
   int64_t F;     // tokens per frame
   // pyramid attention: key blocks >= rb1 are pooled levels held in kp / vp
   // (same row strides as k / v); level l region = blocks [rb_l, rb_{l+1}),
-  // N >> l valid rows; kv_quarters = selected 16-row quarters per entry
+  // N >> l valid rows; kv_eighths = selected 8-row eighths per entry
   const uint16_t* kp;
   const uint16_t* vp;
   int64_t kpsb, kpsh, vpsb, vpsh;
-  const int32_t* kv_quarters;
-  int32_t rb1, rb2, rb3;
+  const int32_t* kv_eighths;
+  int32_t rb1, rb2, rb3, rb4;
 };
 
 __device__ inline float other_half(float x) {
@@ -285,11 +285,13 @@ void attn_bf16_kernel(const Bf16Params p) {
   using C = Cfg<D, BQ, SUB>;
   using T = typename C::T;
   constexpr int KB = C::KB, NSUB = C::NSUB;
-  // pyramid lists stepped in half blocks: steps whose two quarters are both
+  // pyramid lists stepped in half blocks: steps whose four eighths are all
   // unselected are left out (they would only compute masked keys)
   constexpr bool SL = PYR && NSUB == 2;
+  // eighth mask of a step with every key selected (4 bits per 32 keys)
+  constexpr int QF = (1 << (4 * KB)) - 1;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
-  // step descriptors: (augmented block << 5) | (half << 4) | quarter bits
+  // step descriptors (see the pyramid step list below)
   __shared__ int32_t steplist[SL ? kStepCap : 1];
   __shared__ int32_t steps_sh;
 
@@ -359,7 +361,7 @@ void attn_bf16_kernel(const Bf16Params p) {
   // (level l region holds N >> l rows).
   auto level_of = [&](int c) -> int {
     if constexpr (!PYR) return 0;
-    return c < p.rb1 ? 0 : (c < p.rb2 ? 1 : 2);
+    return c < p.rb1 ? 0 : (c < p.rb2 ? 1 : (c < p.rb3 ? 2 : 3));
   };
   auto first_key = [&](int c, int part) -> int {
     if constexpr (PYR)
@@ -368,50 +370,51 @@ void attn_bf16_kernel(const Bf16Params p) {
   };
   auto valid_keys = [&](int c, int part) -> int {
     if constexpr (PYR) {
-      if (c < 0 || c >= p.rb3) return 0;  // not an augmented block: nothing read
+      if (c < 0 || c >= p.rb4) return 0;  // not an augmented block: nothing read
       const int l = level_of(c);
-      const int rb_l = l == 0 ? 0 : (l == 1 ? p.rb1 : p.rb2);
+      const int rb_l = l == 0 ? 0 : (l == 1 ? p.rb1 : (l == 2 ? p.rb2 : p.rb3));
       return max(0, min(SUB, (N32 >> l) - ((c - rb_l) * kBk + part * SUB)));
     }
     return max(0, min(SUB, N32 - first_key(c, part)));
   };
-  // Selected quarters of step u's keys, as a 4-bit mask over the step's
-  // (up to) four 16-key quarters (all set outside pyramid lists).
-  auto quarters_of = [&](int u) -> int {
-    if constexpr (!PYR) return 0xF;
-    const int q = load_uniform(p.kv_quarters, e0 + entry_of(u));
-    return NSUB == 2 ? ((q >> (2 * part_of(u))) & 3) | 0xC : q;
+  // Selected eighths of step u's keys, as a mask over the step's 8-key
+  // eighths, bit i = keys 8i .. 8i+7 of the step (all set outside pyramid
+  // lists).
+  auto eighths_of = [&](int u) -> int {
+    if constexpr (!PYR) return QF;
+    const int q = load_uniform(p.kv_eighths, e0 + entry_of(u));
+    return NSUB == 2 ? (q >> (4 * part_of(u))) & 0xF : q;
   };
 
-  // Pyramid step list: wave 0 lists the half steps with a selected quarter
-  // as descriptors (first key row in k or kp / 32 << 10 | valid rows << 4 |
-  // level << 2 | the half's two quarter bits), so that a step needs one LDS
+  // Pyramid step list: wave 0 lists the half steps with a selected eighth
+  // as descriptors (first key row in k or kp / 32 << 12 | valid rows << 6 |
+  // level << 4 | the half's four eighth bits), so that a step needs one LDS
   // word and no address arithmetic on its level.
   bool use_sl = false;
-  auto d_row0 = [](int d) -> int { return (d >> 10) << 5; };
-  auto d_valid = [](int d) -> int { return (d >> 4) & 63; };
-  auto d_level = [](int d) -> int { return (d >> 2) & 3; };
-  auto d_quarters = [](int d) -> int { return (d & 3) | 0xC; };
+  auto d_row0 = [](int d) -> int { return (d >> 12) << 5; };
+  auto d_valid = [](int d) -> int { return (d >> 6) & 63; };
+  auto d_level = [](int d) -> int { return (d >> 4) & 3; };
+  auto d_eighths = [](int d) -> int { return d & 0xF; };
   if constexpr (SL) {
-    // else every half is stepped through (row offsets fit 22 bits below 2^27)
-    if (2 * L <= kStepCap && N32 < (1 << 27)) {
+    // else every half is stepped through (row offsets fit 19 bits below 2^24)
+    if (2 * L <= kStepCap && N32 < (1 << 24)) {
       use_sl = true;
       if (w == 0) {
         int base = 0;
         for (int j0 = 0; j0 < L; j0 += 64) {
           const int j = j0 + lane;
-          const int q = j < L ? p.kv_quarters[e0 + j] : 0;
+          const int q = j < L ? p.kv_eighths[e0 + j] : 0;
           const int c = j < L ? p.kv_idx[e0 + j] : 0;
-          const uint64_t m0 = __builtin_amdgcn_ballot_w64((q & 3) != 0);
-          const uint64_t m1 = __builtin_amdgcn_ballot_w64((q & 12) != 0);
+          const uint64_t m0 = __builtin_amdgcn_ballot_w64((q & 0xF) != 0);
+          const uint64_t m1 = __builtin_amdgcn_ballot_w64((q & 0xF0) != 0);
           const uint64_t below = (1ull << lane) - 1;
           const int pos = base + __popcll(m0 & below) + __popcll(m1 & below);
           auto desc = [&](int part) {
-            return ((first_key(c, part) >> 5) << 10) | (valid_keys(c, part) << 4) |
-                   (level_of(c) << 2) | ((q >> (2 * part)) & 3);
+            return ((first_key(c, part) >> 5) << 12) | (valid_keys(c, part) << 6) |
+                   (level_of(c) << 4) | ((q >> (4 * part)) & 0xF);
           };
-          if (q & 3) steplist[pos] = desc(0);
-          if (q & 12) steplist[pos + ((q & 3) ? 1 : 0)] = desc(1);
+          if (q & 0xF) steplist[pos] = desc(0);
+          if (q & 0xF0) steplist[pos + ((q & 0xF) ? 1 : 0)] = desc(1);
           base += __popcll(m0) + __popcll(m1);
         }
         if (lane == 0) steps_sh = base;
@@ -455,11 +458,11 @@ void attn_bf16_kernel(const Bf16Params p) {
   using V1 = std::integral_constant<uint32_t, vso[1]>;
   constexpr int PART1 = NSUB == 2 ? 1 : 0;  // part of step 1 (and of every odd step)
 
-  // Key blocks of steps it, it+1, it+2 (rolling), their quarter masks and,
+  // Key blocks of steps it, it+1, it+2 (rolling), their eighth masks and,
   // for step lists, their parts; with the pyramid step list in use, c0..c2
   // hold the steps' descriptors instead.
   int c0 = 0, c1 = 0, c2 = 0;
-  int q0 = 0xF, q1 = 0xF, q2 = 0xF;
+  int q0 = QF, q1 = QF, q2 = QF;
   int r0 = 0, r1 = PART1, r2 = 0;
   if (SL && use_sl) {
     if (LS > 0) {
@@ -475,18 +478,18 @@ void attn_bf16_kernel(const Bf16Params p) {
   } else {
     if (LS > 0) {
       c0 = block_of(0);
-      q0 = quarters_of(0);
+      q0 = eighths_of(0);
       issue_k(K0{}, c0, r0);
       issue_v(V0{}, c0, r0);
     }
     if (LS > 1) {
       c1 = block_of(1);
-      q1 = quarters_of(1);
+      q1 = eighths_of(1);
       issue_k(K1{}, c1, r1);
     }
     if (LS > 2) {
       c2 = block_of(2);
-      q2 = quarters_of(2);
+      q2 = eighths_of(2);
     }
   }
 
@@ -556,17 +559,17 @@ void attn_bf16_kernel(const Bf16Params p) {
   // beyond jv (only the last key block can be ragged) are set to -inf first,
   // which also makes their probabilities 0. A step with no valid key (second
   // half of a short last block) has max -inf.
-  // Keys at or beyond jv, and keys in quarters outside qm (pyramid lists),
+  // Keys at or beyond jv, and keys in eighths outside qm (pyramid lists),
   // are set to -inf: they take no part in the max and get probability 0.
   auto mask_keys = [&](f32x16(&sacc)[KB], int jv, int qm) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        if (key_of(kb, j, hh) >= jv || !((qm >> (2 * kb + (j >= 8))) & 1))
+        if (key_of(kb, j, hh) >= jv || !((qm >> (4 * kb + j / 4)) & 1))
           sacc[kb][j] = -INFINITY;
   };
-  auto tile_max = [&](f32x16(&sacc)[KB], bool masked, int jv, int qm = 0xF) -> float {
+  auto tile_max = [&](f32x16(&sacc)[KB], bool masked, int jv, int qm) -> float {
     if (masked) mask_keys(sacc, jv, qm);
     float mloc = -INFINITY;
 #pragma unroll
@@ -661,7 +664,7 @@ void attn_bf16_kernel(const Bf16Params p) {
     else return valid_keys(c, part);
   };
   auto qmask = [&](auto lsl_c, int c, int q) -> int {
-    if constexpr (decltype(lsl_c)::value) return d_quarters(c);
+    if constexpr (decltype(lsl_c)::value) return d_eighths(c);
     else return q;
   };
   auto first_scores = [&](auto lsl_c) __attribute__((always_inline)) {
@@ -672,7 +675,7 @@ void attn_bf16_kernel(const Bf16Params p) {
       barrier();
       scores(smem + kso[0], sA);
       const int jv = vkeys(lsl_c, c0, r0), qm0 = qmask(lsl_c, c0, q0);
-      apply_max(tile_max(sA, jv < SUB || qm0 != 0xF, jv, qm0) + (float)lev(lsl_c, c0), 0, 0);
+      apply_max(tile_max(sA, jv < SUB || qm0 != QF, jv, qm0) + (float)lev(lsl_c, c0), 0, 0);
     }
   };
   if constexpr (!SL) first_scores(std::false_type{});
@@ -764,7 +767,7 @@ void attn_bf16_kernel(const Bf16Params p) {
         }
       asm volatile("" ::"v"(l_lane));
       const int jv = vkeys(lsl_c, c1, pv), qm1 = qmask(lsl_c, c1, q1);
-      if (jv < SUB || qm1 != 0xF) mask_keys(nxt, jv, qm1);
+      if (jv < SUB || qm1 != QF) mask_keys(nxt, jv, qm1);
       // Phase B: slot i issues P V MFMA i of step it and folds MPS scores of
       // step it+1 into the row max.
       float mloc = -INFINITY;
@@ -791,13 +794,13 @@ void attn_bf16_kernel(const Bf16Params p) {
     // of the step: scalar loads count in lgkmcnt and may complete out of
     // order, so one in flight would turn every LDS wait above into a wait for
     // everything.
-    int c3 = 0, q3 = 0xF, r3 = 0;
+    int c3 = 0, q3 = QF, r3 = 0;
     if constexpr (LSL) {
       const int code = wave_uniform(code3);
       if (it + 3 < LS) c3 = code;
     } else {
       c3 = it + 3 < LS ? block_of(it + 3) : 0;
-      q3 = (PYR && it + 3 < LS) ? quarters_of(it + 3) : 0xF;
+      q3 = (PYR && it + 3 < LS) ? eighths_of(it + 3) : QF;
       r3 = (SL && it + 3 < LS) ? part_of(it + 3) : 0;
     }
     c0 = c1;
@@ -904,7 +907,7 @@ hipError_t launch(const Geom& g, const Bf16Params& p, hipStream_t st) {
                        mult);
     hipLaunchKernelGGL((attn_bf16_kernel<D, BQ, SUB, true, false>), dim3((unsigned)rows),
                        dim3(C::NT), 0, st, p);
-  } else if (p.kv_quarters) {
+  } else if (p.kv_eighths) {
     hipLaunchKernelGGL((attn_bf16_kernel<D, BQ, SUB, false, true>), dim3((unsigned)rows),
                        dim3(C::NT), 0, st, p);
   } else {
@@ -936,10 +939,11 @@ hipError_t launch_attn_bf16(const Geom& g, const AttnArgs& a, hipStream_t st) {
   p.vp = (const uint16_t*)a.vp.ptr;
   p.kpsb = a.kp.sb; p.kpsh = a.kp.sh;
   p.vpsb = a.vp.sb; p.vpsh = a.vp.sh;
-  p.kv_quarters = a.kv_quarters;
+  p.kv_eighths = a.kv_eighths;
   p.rb1 = (int32_t)a.pyr_rb[1];
   p.rb2 = (int32_t)a.pyr_rb[2];
   p.rb3 = (int32_t)a.pyr_rb[3];
+  p.rb4 = (int32_t)a.pyr_rb[4];
   // Scores enter every exponent as s * sl2. A zero scale is taken as the
   // smallest normal float instead: finite scores then still contribute
   // 2^(~0) (off by far less than bf16 rounding) while masked keys (-inf)

@@ -49,7 +49,7 @@ hipError_t launch_zero_row_ptr(int32_t* row_ptr, hipStream_t st);
 // rb[0..n_levels] = first augmented block of each level region, then the end.
 hipError_t launch_pyramid_lists(const Geom& g, int32_t n_levels, const int64_t* rb,
                                 const uint8_t* mask, int64_t mhs, int32_t* row_ptr,
-                                int32_t* kv_idx, int32_t* kv_quarters, bool count_only,
+                                int32_t* kv_idx, int32_t* kv_eighths, bool count_only,
                                 hipStream_t st);
 // Pooled key/value levels 1..n_levels-1 (means of 2^l tokens) into k_pyr/v_pyr.
 hipError_t launch_kv_pyramid(const Geom& g, int elem_bytes, int32_t n_levels, const int64_t* rb,
@@ -94,10 +94,10 @@ struct AttnArgs {
   int32_t lists_shared;
   float scale;
   float* tile_gap;
-  // pyramid attention (kv_quarters non-NULL): pooled levels and region starts
+  // pyramid attention (kv_eighths non-NULL): pooled levels and region starts
   TensorArg kp{}, vp{};
-  const int32_t* kv_quarters = nullptr;
-  int64_t pyr_rb[4] = {0, 0, 0, 0};
+  const int32_t* kv_eighths = nullptr;
+  int64_t pyr_rb[5] = {0, 0, 0, 0, 0};
 };
 
 hipError_t launch_attn_bf16(const Geom& g, const AttnArgs& a, hipStream_t st);

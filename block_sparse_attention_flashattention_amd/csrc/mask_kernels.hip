@@ -516,17 +516,17 @@ __device__ inline RowCut select_kth(const double* s, int64_t nK, int T) {
 // branch; lane u keeps the sum before entry c0 + u of each 16-entry chunk, and
 // the levels are set in parallel. Stops after the chunk in which the sum
 // reaches tau_{nl-1} (every later entry is dropped); returns whether it did.
-// The thresholds are non-decreasing; nl is 1..3.
+// The thresholds are non-decreasing; nl is 1..4.
 // CH entries per chunk (16, or 8 where registers are scarce; the sums are
 // the same either way).
 // With run_io the walk continues a row's earlier walk: the sum starts from
 // *run_io and is left there, and the entries are the row's pos0, pos0 + 1, ...
 template <int CH = 16>
 __device__ inline bool walk_mass(const double* pv, const int32_t* idx, int64_t n, double tau0,
-                                 double tau1, double tau2, int nl, uint8_t* flag,
+                                 double tau1, double tau2, double tau3, int nl, uint8_t* flag,
                                  double* run_io = nullptr, int64_t pos0 = 0) {
   const int lane = threadIdx.x & 63;
-  const double last = nl == 1 ? tau0 : (nl == 2 ? tau1 : tau2);
+  const double last = nl == 1 ? tau0 : (nl == 2 ? tau1 : (nl == 3 ? tau2 : tau3));
   double run = run_io ? *run_io : 0.0;
   for (int c0 = 0; c0 < (int)n; c0 += CH) {
     const int m = min(CH, (int)n - c0);
@@ -554,7 +554,7 @@ __device__ inline bool walk_mass(const double* pv, const int32_t* idx, int64_t n
       int lvl = 0;
       if (pos0 + c0 + lane > 0)
         lvl = (ex >= tau0 ? 1 : 0) + (nl > 1 && ex >= tau1 ? 1 : 0) +
-              (nl > 2 && ex >= tau2 ? 1 : 0);
+              (nl > 2 && ex >= tau2 ? 1 : 0) + (nl > 3 && ex >= tau3 ? 1 : 0);
       if (lvl < nl) flag[idx[c0 + lane]] = (uint8_t)(1 + lvl);
     }
     if (run >= last) {
@@ -573,7 +573,7 @@ __device__ inline bool walk_mass(const double* pv, const int32_t* idx, int64_t n
 // one thread would add them (the first wave reads 64 terms per LDS access);
 // the quotients are formed in parallel beforehand.
 __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double param,
-                                     double tau1, double tau2, int32_t n_levels,
+                                     double tau1, double tau2, double tau3, int32_t n_levels,
                                      const double* __restrict__ S, uint8_t* __restrict__ mask,
                                      int32_t only_marked, int64_t R) {
   extern __shared__ double smd[];
@@ -643,7 +643,7 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
         // flags of the first kTopM pairs; if the mass is not reached there,
         // they are a subset of what the full sort below keeps
         if (threadIdx.x < 64) {
-          const bool reached = walk_mass(cs, ci, kTopM, param, param, param, 1, flag);
+          const bool reached = walk_mass(cs, ci, kTopM, param, param, param, param, 1, flag);
           if (threadIdx.x == 0) keep_sh = reached ? 1 : 0;
         }
         __syncthreads();
@@ -687,7 +687,7 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
       // threshold that the running mass including that block has reached
       keep = 0;
       if (threadIdx.x < 64)
-        walk_mass(ks, ki, nK, param, tau1, tau2, mode == 4 ? n_levels : 1, flag);
+        walk_mass(ks, ki, nK, param, tau1, tau2, tau3, mode == 4 ? n_levels : 1, flag);
       __syncthreads();
     }
     for (int t = threadIdx.x; t < keep; t += blockDim.x) flag[ki[t]] = 1;
@@ -927,7 +927,7 @@ __global__ __launch_bounds__(kWave * kSelectRowsPerGroup) void pooled_select_wav
   uint8_t* flag = (uint8_t*)s;  // the exponentials are used up
   for (int64_t c = lane; c < nK; c += kWave) flag[c] = 0;
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  const bool reached = walk_mass<8>(cs, ci, kTopM, param, param, param, 1, flag);
+  const bool reached = walk_mass<8>(cs, ci, kTopM, param, param, param, param, 1, flag);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   if (!reached) {
     if (lane == 0) mrow[0] = kSelectMarker;
@@ -1521,7 +1521,7 @@ struct LongCut {
 };
 
 __global__ __launch_bounds__(kLongThreads) void pooled_select_long_kernel(
-    int64_t nK, int32_t mode, double param, double tau1, double tau2, int32_t n_levels,
+    int64_t nK, int32_t mode, double param, double tau1, double tau2, double tau3, int32_t n_levels,
     const double* __restrict__ S, const double* __restrict__ zrow,
     const double* __restrict__ mrow, uint8_t* __restrict__ mask) {
   __shared__ uint64_t ck[kLongCap];  // step keys, then their probabilities
@@ -1734,7 +1734,7 @@ __global__ __launch_bounds__(kLongThreads) void pooled_select_long_kernel(
         __syncthreads();
         if (tid < 64) {
           double run = run_sh;
-          const bool reached = walk_mass<8>(cs, ci, na, param, tau1, tau2, nl, flag, &run,
+          const bool reached = walk_mass<8>(cs, ci, na, param, tau1, tau2, tau3, nl, flag, &run,
                                             walked);
           if (lane == 0) {
             run_sh = run;
@@ -1760,7 +1760,7 @@ __global__ __launch_bounds__(kLongThreads) void pooled_select_long_kernel(
         __syncthreads();
         if (m > 0 && tid < 64) {
           double run = run_sh;
-          const bool reached = walk_mass<8>((const double*)ck, ci, m, param, tau1, tau2, nl,
+          const bool reached = walk_mass<8>((const double*)ck, ci, m, param, tau1, tau2, tau3, nl,
                                             flag, &run, walked);
           if (lane == 0) {
             run_sh = run;
@@ -1781,31 +1781,32 @@ __global__ __launch_bounds__(kLongThreads) void pooled_select_long_kernel(
 }
 
 // ------------------------------------------------------- pyramid lists
-// Quarter mask (16-row quarters of a 64-row augmented block) that row r
+// Eighth mask (8-row eighths of a 64-row augmented block) that row r
 // selects in augmented block ab ([PSA]: logical block size decoupled from the
 // hardware tile): ab in level region l covers logical blocks
-// c = (ab - rb_l) * 2^l + i, i < 2^l, each owning 4 / 2^l quarters; block c
-// contributes its quarters when its mask value is 1 + l.
+// c = (ab - rb_l) * 2^l + i, i < 2^l, each owning 8 / 2^l eighths; block c
+// contributes its eighths when its mask value is 1 + l (other values select
+// nothing there).
 struct PyrRegions {
-  int64_t rb[4];  // first augmented block of levels 0..2, then the end
+  int64_t rb[5];  // first augmented block of levels 0..3, then the end
   int32_t n_levels;
 };
 
-__device__ inline uint32_t pyr_quarters(const uint8_t* mrow, int64_t nK, const PyrRegions& R,
-                                        int64_t ab) {
+__device__ inline uint32_t pyr_eighths(const uint8_t* mrow, int64_t nK, const PyrRegions& R,
+                                       int64_t ab) {
   int l = 0;
   while (l + 1 < R.n_levels && ab >= R.rb[l + 1]) ++l;
   const int per = 1 << l;            // logical blocks per augmented block
-  const int qpb = 4 >> l;            // quarters per logical block
+  const int epb = 8 >> l;            // eighths per logical block
   uint32_t q = 0;
   for (int i = 0; i < per; ++i) {
     const int64_t c = (ab - R.rb[l]) * per + i;
-    if (c < nK && mrow[c] == 1 + l) q |= ((1u << qpb) - 1) << (i * qpb);
+    if (c < nK && mrow[c] == 1 + l) q |= ((1u << epb) - 1) << (i * epb);
   }
   return q;
 }
 
-// One wave per list row: row_ptr[r + 1] = augmented blocks with a quarter.
+// One wave per list row: row_ptr[r + 1] = augmented blocks with an eighth.
 __global__ void pyr_count_kernel(int64_t R, int64_t nQ, int64_t nK, PyrRegions reg,
                                  const uint8_t* __restrict__ mask, int64_t mhs,
                                  int32_t* __restrict__ row_ptr) {
@@ -1819,7 +1820,7 @@ __global__ void pyr_count_kernel(int64_t R, int64_t nQ, int64_t nK, PyrRegions r
   int32_t cnt = 0;
   for (int64_t a0 = 0; a0 < nA; a0 += kWave) {
     const int64_t ab = a0 + lane;
-    const bool on = ab < nA && pyr_quarters(mrow, nK, reg, ab) != 0;
+    const bool on = ab < nA && pyr_eighths(mrow, nK, reg, ab) != 0;
     cnt += __popcll(__ballot(on));
   }
   if (lane == 0) row_ptr[r + 1] = cnt;
@@ -1829,7 +1830,7 @@ __global__ void pyr_scatter_kernel(int64_t R, int64_t nQ, int64_t nK, PyrRegions
                                    const uint8_t* __restrict__ mask, int64_t mhs,
                                    const int32_t* __restrict__ row_ptr,
                                    int32_t* __restrict__ kv_idx,
-                                   int32_t* __restrict__ kv_quarters) {
+                                   int32_t* __restrict__ kv_eighths) {
   const int lane = threadIdx.x % kWave;
   const int64_t r = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (r >= R) return;
@@ -1840,12 +1841,12 @@ __global__ void pyr_scatter_kernel(int64_t R, int64_t nQ, int64_t nK, PyrRegions
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   for (int64_t a0 = 0; a0 < nA; a0 += kWave) {
     const int64_t ab = a0 + lane;
-    const uint32_t q = ab < nA ? pyr_quarters(mrow, nK, reg, ab) : 0u;
+    const uint32_t q = ab < nA ? pyr_eighths(mrow, nK, reg, ab) : 0u;
     const uint64_t bal = __ballot(q != 0);
     if (q) {
       const int64_t o = out + __popcll(bal & below);
       kv_idx[o] = (int32_t)ab;
-      kv_quarters[o] = (int32_t)q;
+      kv_eighths[o] = (int32_t)q;
     }
     out += __popcll(bal);
   }
@@ -2111,7 +2112,7 @@ hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k
     hipLaunchKernelGGL(pooled_rowz_kernel, dim3((unsigned)((R + kWave - 1) / kWave)),
                        dim3(kWave), 0, st, R, g.nK, S, zrow, mrow, (int32_t*)nullptr);
     hipLaunchKernelGGL(pooled_select_long_kernel, dim3((unsigned)R), dim3(kLongThreads), 0, st,
-                       g.nK, mode, param, levels ? levels[1] : 0.0, levels ? levels[2] : 0.0,
+                       g.nK, mode, param, levels ? levels[1] : 0.0, levels ? levels[2] : 0.0, levels ? levels[3] : 0.0,
                        n_levels, S, zrow, mrow, mask);
     return hipGetLastError();
   }
@@ -2139,7 +2140,7 @@ hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k
   const size_t sh2 = sizeof(double) * (g.nK + P) + sizeof(int32_t) * P + g.nK;
   const int64_t groups = only_marked ? (R + kSelectRowsPerGroup - 1) / kSelectRowsPerGroup : R;
   hipLaunchKernelGGL(pooled_select_kernel, dim3((unsigned)groups), dim3(kSelectThreads), sh2, st,
-                     g.nK, P, mode, param, levels ? levels[1] : 0.0, levels ? levels[2] : 0.0,
+                     g.nK, P, mode, param, levels ? levels[1] : 0.0, levels ? levels[2] : 0.0, levels ? levels[3] : 0.0,
                      n_levels, S, mask, only_marked, R);
   return hipGetLastError();
 }
@@ -2217,11 +2218,11 @@ hipError_t launch_compact_scatter(const Geom& g, int64_t R, const uint8_t* mask,
 
 hipError_t launch_pyramid_lists(const Geom& g, int32_t n_levels, const int64_t* rb,
                                 const uint8_t* mask, int64_t mhs, int32_t* row_ptr,
-                                int32_t* kv_idx, int32_t* kv_quarters, bool count_only,
+                                int32_t* kv_idx, int32_t* kv_eighths, bool count_only,
                                 hipStream_t st) {
   const int64_t R = (int64_t)g.B * g.H * g.nQ;
   PyrRegions reg;
-  for (int i = 0; i < 4; ++i) reg.rb[i] = i <= n_levels ? rb[i] : rb[n_levels];
+  for (int i = 0; i < 5; ++i) reg.rb[i] = i <= n_levels ? rb[i] : rb[n_levels];
   reg.n_levels = n_levels;
   const int waves = 4;
   if (count_only) {
@@ -2233,7 +2234,7 @@ hipError_t launch_pyramid_lists(const Geom& g, int32_t n_levels, const int64_t* 
     return hipGetLastError();
   }
   hipLaunchKernelGGL(pyr_scatter_kernel, dim3(grid_for(R, waves, INT32_MAX)), dim3(waves * kWave),
-                     0, st, R, g.nQ, g.nK, reg, mask, mhs, row_ptr, kv_idx, kv_quarters);
+                     0, st, R, g.nQ, g.nK, reg, mask, mhs, row_ptr, kv_idx, kv_eighths);
   return hipGetLastError();
 }
 

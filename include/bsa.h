@@ -338,7 +338,7 @@ BSA_API bsa_status bsa_update_skip_mask(const bsa_shape* s, const int32_t* row_p
  * block) pair attends at the level its importance earns, set by thresholds;
  * the probabilities stay consistent across levels; the logical block size is
  * decoupled from the hardware tile).
- * Levels l = 0 .. n_levels-1 (n_levels in 1..3; N must be a multiple of
+ * Levels l = 0 .. n_levels-1 (n_levels in 1..4; N must be a multiple of
  * 2^(n_levels-1), else BSA_ERR_UNSUPPORTED): level l of key block c holds
  * block_k / 2^l pooled keys, each the mean of 2^l consecutive tokens of K and
  * of V; a pooled key stands for its 2^l tokens, so its score gets + l ln 2.
@@ -380,35 +380,36 @@ BSA_API bsa_status bsa_build_mask_pyramid(const bsa_shape* s, bsa_dtype dt, bsa_
 /*
  * Lists of augmented tiles for a level mask: per row r = (b*H + h)*nQ + a (one
  * list per (b, h) always), the augmented blocks holding at least one
- * selected 16-row quarter, ascending, and kv_quarters[e] = bit mask of the
- * selected quarters (bit i = rows [16i, 16i+16) of the tile). Key block c at
+ * selected 8-row eighth, ascending, and kv_eighths[e] = bit mask of the
+ * selected eighths (bit i = rows [8i, 8i+8) of the tile). Key block c at
  * level l covers pooled rows [c*block_k/2^l, (c+1)*block_k/2^l) of level l,
- * i.e. 4/2^l quarters of augmented block rb_l + c/2^l.
+ * i.e. 8/2^l eighths of augmented block rb_l + c/2^l. Mask values above
+ * n_levels select nothing.
  *   mask_head_stride  0 (one mask for all heads) or >= nQ*nK
  *   kv_capacity, nnz_host  as in bsa_compact_block_lists (worst case
  *                  B*H*nQ*rb_{n_levels})
  */
 BSA_API bsa_status bsa_compact_pyramid_lists(const bsa_shape* s, int32_t n_levels,
                                      const uint8_t* mask, int64_t mask_head_stride,
-                                     int32_t* row_ptr, int32_t* kv_idx, int32_t* kv_quarters,
+                                     int32_t* row_ptr, int32_t* kv_idx, int32_t* kv_eighths,
                                      int64_t kv_capacity, int64_t* nnz_host, void* stream);
 
 /*
  * Pyramid attention forward (bf16 inputs; fp32 accumulation and softmax, O
  * rounded to bf16). For query i of row block a, the keys are the rows of the
- * selected quarters of the row's augmented tiles (padding rows past a level's
+ * selected eighths of the row's augmented tiles (padding rows past a level's
  * N >> l never count); a key of level l scores scale * q_i . k + l ln 2; o_i
  * is the softmax-weighted mean of the matching value rows, lse_i the natural
  * log of the weight sum (-inf and o_i = 0 for an empty list).
  *   k_pyr, v_pyr  as written by bsa_build_kv_pyramid, with the row stride
  *                 (stride_n) of k and v; ignored for one level
- *   row_ptr, kv_idx, kv_quarters  as written by bsa_compact_pyramid_lists
+ *   row_ptr, kv_idx, kv_eighths  as written by bsa_compact_pyramid_lists
  */
 BSA_API bsa_status bsa_pyramid_attn_fwd(const bsa_shape* s, bsa_dtype dt, bsa_tensor q,
                                 bsa_tensor k, bsa_tensor v, bsa_tensor k_pyr,
                                 bsa_tensor v_pyr, int32_t n_levels, bsa_tensor o, float* lse,
                                 const int32_t* row_ptr, const int32_t* kv_idx,
-                                const int32_t* kv_quarters, float scale, void* stream);
+                                const int32_t* kv_eighths, float scale, void* stream);
 
 /*
  * Debug check of block lists ([Lite] sections 三 and 六: the forward walks only

@@ -209,23 +209,28 @@ def test_pyramid_validation(L):
     assert L.bsa_pyramid_rows(C.byref(s4), 1) == 0
     assert L.bsa_pyramid_rows(C.byref(s4), 2) == 64 * 2      # 80 rows -> 2 blocks
     assert L.bsa_pyramid_rows(C.byref(s4), 3) == 64 * 3      # + 40 rows -> 1 block
-    assert L.bsa_pyramid_rows(C.byref(s4), 4) == -1
+    assert L.bsa_pyramid_rows(C.byref(s4), 4) == 64 * 4      # + 20 rows -> 1 block
+    assert L.bsa_pyramid_rows(C.byref(s4), 5) == -1
     kvp = lambda shape, nl: L.bsa_build_kv_pyramid(C.byref(shape), 0, nl, T(), T(P + 256),
                                                    T(P + 512), T(P + 768), None)
     assert kvp(s4, 0) == INVALID
     assert kvp(s, 2) == UNSUPPORTED                  # N not a multiple of 2
+    assert kvp(S(frames=1, height=4, width=5), 4) == UNSUPPORTED   # N = 20: not of 8
+    assert kvp(s4, 5) == INVALID
     taus = (C.c_double * 3)(0.5, 0.4, 0.9)
     def mk(nl=3, t=taus, ws=P, wsb=1 << 30):
         return L.bsa_build_mask_pyramid(C.byref(s4), 0, T(), T(P + 256), 0.1, nl, t, P, ws, wsb,
                                         None)
     assert mk() == INVALID                           # thresholds must not decrease
     assert mk(t=(C.c_double * 3)(0.0, 0.5, 0.9)) == INVALID
-    assert mk(nl=4, t=(C.c_double * 4)(0.1, 0.2, 0.3, 0.4)) == INVALID
+    assert mk(nl=5, t=(C.c_double * 5)(0.1, 0.2, 0.3, 0.4, 0.5)) == INVALID
+    assert mk(nl=4, t=(C.c_double * 4)(0.1, 0.2, 0.5, 0.4)) == INVALID
     assert mk(t=None) == INVALID
     lists = lambda nl=3, cap=0, rp=P: L.bsa_compact_pyramid_lists(C.byref(s4), nl, P, 0, rp, P,
                                                                   P + 64, cap, None, None)
     assert lists(rp=None) == INVALID
     assert lists(cap=1) == CAPACITY
+    assert lists(nl=5) == INVALID
     fwd = lambda dt=0, nl=3, kp=None, qm=P: L.bsa_pyramid_attn_fwd(
         C.byref(s4), dt, T(), T(P + 256), T(P + 512), kp or T(P + 768), T(P + 1024), nl,
         T(P + 2048), None, P, P, qm, 0.1, None)

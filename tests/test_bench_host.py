@@ -41,3 +41,27 @@ def test_counter_record_keys_name_what_changes_the_lists():
     assert bench.variant_key(ns, synth.workload("skip_carry_480p")) == \
         "skip_carry_480p:tau=10.0:order=radial"
     assert bench.variant_key(ns, synth.workload("wan14b_720p")) == "wan14b_720p"
+
+
+def test_pyramid_flops_count_the_keys_of_each_level():
+    """The forward's flop count of pyramid lists equals 4 d |R_a| times the
+    pooled keys that the level mask gives each row (a level-l block of len
+    tokens holds len / 2^l of them), at 1 to 4 levels and a ragged last block."""
+    import oracle
+    B, H, N, bq, bk, d = 1, 2, 296, 64, 64, 128
+    nQ, nK = -(-N // bq), -(-N // bk)
+    rng = np.random.default_rng(5)
+    for L in (1, 2, 3, 4):
+        mask = rng.integers(0, L + 1, size=(B, H, nQ, nK)).astype(np.uint8)
+        rp, kv, qm = oracle.compact_pyramid(mask, B, H, nQ, nK, N, bk, L, nQ * nK)
+        rb, _ = oracle.pyramid_regions(N, bk, L)
+        got = bench.pyramid_flops(rp, kv, qm, N, bq, bk, d, nQ, rb)
+        want = 0
+        for h in range(H):
+            for a in range(nQ):
+                ra = min(N, (a + 1) * bq) - a * bq
+                for c in range(nK):
+                    m = int(mask[0, h, a, c])
+                    if m:
+                        want += 4 * d * ra * ((min(N, (c + 1) * bk) - c * bk) >> (m - 1))
+        assert got == want, (L, got, want)

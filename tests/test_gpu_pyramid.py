@@ -56,11 +56,11 @@ def run_pyramid(w, x, taus, rows=None):
                 kv=host(kv)[:nnz], qm=host(qm)[:nnz], o=o, lse=lse, nnz=nnz, prow=prow)
 
 
-@pytest.mark.parametrize("L", [2, 3])
+@pytest.mark.parametrize("L", [2, 3, 4])
 def test_kv_pyramid_levels(L):
     w = synth.Workload("pyr_small", 2, 3, 128, 4, 7, 12, 64, 64, "bf16", "pooled", 640, True)
     x = synth.make_qkv(w)
-    out = run_pyramid(w, x, [0.3, 0.6, 0.9][:L])
+    out = run_pyramid(w, x, [0.3, 0.6, 0.9, 0.95][:L])
     rb, rr = oracle.pyramid_regions(w.N, w.Bk, L)
     for name, t in (("k", out["kp"]), ("v", out["vp"])):
         src = x[name].view(np.uint16).astype(np.uint32) << 16
@@ -78,7 +78,8 @@ def test_kv_pyramid_levels(L):
 
 
 @pytest.mark.parametrize("Bq", [64, 128])
-@pytest.mark.parametrize("taus", [(0.4,), (0.3, 0.7), (0.2, 0.5, 0.9), (0.5, 0.5, 0.95)])
+@pytest.mark.parametrize("taus", [(0.4,), (0.3, 0.7), (0.2, 0.5, 0.9), (0.5, 0.5, 0.95),
+                                  (0.2, 0.4, 0.7, 0.95), (0.3, 0.3, 0.6, 1.0)])
 def test_pyramid_small_against_oracle(Bq, taus):
     w = synth.Workload("pyr_small", 2, 3, 128, 5, 12, 16, Bq, 64, "bf16", "pooled", 641, True)
     x = synth.make_qkv(w)
@@ -99,43 +100,48 @@ def test_pyramid_small_against_oracle(Bq, taus):
     compare(og, lg, o_ref, lse_ref, f"pyramid small Bq={Bq} {taus}")
 
 
-def test_pyramid_group_constant_inputs_match_level_zero():
-    """Keys and values constant inside groups of 4 tokens: any level mix gives
-    the level-0 output (consistent probabilities), on the GPU too."""
+@pytest.mark.parametrize("group,taus", [(4, [0.2, 0.5, 1.0]), (8, [0.2, 0.4, 0.6, 1.0])])
+def test_pyramid_group_constant_inputs_match_level_zero(group, taus):
+    """Keys and values constant inside groups of `group` tokens: any level mix
+    gives the level-0 output (consistent probabilities), on the GPU too."""
     w = synth.Workload("pyr_const", 1, 2, 128, 4, 8, 16, 128, 64, "bf16", "pooled", 642, True)
     x = synth.make_qkv(w)
     for name in ("k", "v"):
-        a = x[name].reshape(w.B, w.N // 4, 4, w.H, w.d)
-        x[name] = np.ascontiguousarray(np.repeat(a[:, :, :1], 4, axis=2).reshape(x[name].shape))
-    mixed = run_pyramid(w, x, [0.2, 0.5, 1.0])
+        a = x[name].reshape(w.B, w.N // group, group, w.H, w.d)
+        x[name] = np.ascontiguousarray(np.repeat(a[:, :, :1], group, axis=2)
+                                       .reshape(x[name].shape))
+    mixed = run_pyramid(w, x, taus)
     level0 = run_pyramid(w, x, [1.0])
-    assert (mixed["mask"] > 1).any()
+    assert (mixed["mask"] == len(taus)).any()        # the coarsest level is used
     d = (mixed["o"].float() - level0["o"].float()).abs()
-    note(f"group-constant inputs: level mix vs level 0, max {d.max().item():.3e}")
+    note(f"group-constant inputs ({group}): level mix vs level 0, max {d.max().item():.3e}")
     assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3
 
 
-def test_pyramid_wan13b_480p_sampled():
+@pytest.mark.parametrize("taus", [(0.3048, 0.6, 0.9), (0.25, 0.5, 0.75, 0.9)])
+def test_pyramid_wan13b_480p_sampled(taus):
     w = synth.workload("wan13b_480p")
     x = synth.make_qkv(w)
-    taus = [0.3048, 0.6, 0.9]
+    taus = list(taus)
     out = run_pyramid(w, x, taus)
     mref, _, _ = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, 4, 0,
                                           levels_tau=taus)
     np.testing.assert_array_equal(out["mask"], mref)
-    counts = [int((mref == v).sum()) for v in range(4)]
-    note(f"480p levels (dropped, l0, l1, l2): {counts}; {out['nnz']} augmented tiles")
+    counts = [int((mref == v).sum()) for v in range(len(taus) + 1)]
+    note(f"480p tiles per mask value (dropped, level 0, 1, ...): {counts}; "
+         f"{out['nnz']} augmented tiles")
     rows = sample_rows(w.B, w.H, w.nQ, 3, 41, heads=[0, 6, w.H - 1])
     o_ref, lse_ref = oracle.pyramid_attention(x["q"], x["k"], x["v"], w.Bq, w.Bk, w.scale, mref,
                                               w.nQ * w.nK, rows=rows)
     og, lg = gather_rows(host(out["o"]), host(out["lse"]), rows, w.B, w.H, w.N, w.Bq)
-    compare(og, lg, o_ref, lse_ref, "480p pyramid")
+    compare(og, lg, o_ref, lse_ref, f"480p pyramid {taus}")
 
 
-def test_pyramid_head_dim_64_against_oracle():
+@pytest.mark.parametrize("taus", [(0.3, 0.6, 0.9), (0.2, 0.4, 0.6, 0.9)])
+def test_pyramid_head_dim_64_against_oracle(taus):
     w = synth.Workload("pyr_d64", 1, 2, 64, 4, 9, 16, 64, 64, "bf16", "pooled", 643, True)
     x = synth.make_qkv(w)
-    taus = [0.3, 0.6, 0.9]
+    taus = list(taus)
     out = run_pyramid(w, x, taus)
     mref, _, _ = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, 4, 0,
                                           levels_tau=taus)
@@ -144,10 +150,10 @@ def test_pyramid_head_dim_64_against_oracle():
                                               w.nQ * w.nK)
     rows = np.arange(w.B * w.H * w.nQ)
     og, lg = gather_rows(host(out["o"]), host(out["lse"]), rows, w.B, w.H, w.N, w.Bq)
-    compare(og, lg, o_ref, lse_ref, "pyramid d=64")
+    compare(og, lg, o_ref, lse_ref, f"pyramid d=64 {taus}")
 
 
-@pytest.mark.parametrize("taus", [(1.0,), (0.3, 0.6, 0.9)])
+@pytest.mark.parametrize("taus", [(1.0,), (0.3, 0.6, 0.9), (0.2, 0.4, 0.6, 0.9)])
 def test_pyramid_long_rows_sampled(taus):
     """720p grid, one head at d = 64, row blocks of 64: with tau = 1 every row
     lists all 1,182 key blocks, more than the forward's list of non-empty half
@@ -170,7 +176,7 @@ def test_pyramid_long_rows_sampled(taus):
     compare(og, lg, o_ref, lse_ref, f"pyramid long rows {taus}")
 
 
-@pytest.mark.parametrize("taus", [(1.0,), (0.3, 0.6, 0.9)])
+@pytest.mark.parametrize("taus", [(1.0,), (0.3, 0.6, 0.9), (0.2, 0.4, 0.6, 0.9)])
 def test_pyramid_mask_rows_over_2048_blocks(taus):
     """Level masks over rows of 2,560 key blocks (one workgroup per row, the
     sorted walk in steps of 512), bit-exact against the oracle."""
