@@ -75,8 +75,9 @@ constexpr int kVStages = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
-// Pyramid lists at half-block steps: capacity of the per-workgroup list of
-// non-empty steps (with its count it keeps four 40 KiB workgroups per CU).
+// Pyramid lists at half-block steps: capacity, in 32-bit group descriptors
+// (two per step), of the per-workgroup list of selected 16-row groups (with
+// its count it keeps four 40 KiB workgroups per CU).
 constexpr int kStepCap = 2046;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
 constexpr int kPfK = 3;  // K fragment reads issued ahead of their score MFMA (slots)
@@ -149,6 +150,10 @@ __device__ inline float max_lanes32(float v) {
 
 // Value of lane 0 (an SGPR) for quantities that are uniform across the wave.
 __device__ inline int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline uint64_t wave_uniform64(uint64_t x) {
+  return (uint64_t)(uint32_t)wave_uniform((int)(uint32_t)x) |
+         ((uint64_t)(uint32_t)wave_uniform((int)(uint32_t)(x >> 32)) << 32);
+}
 
 // Wait until at most n vector-memory operations of this wave are in flight.
 template <int n>
@@ -221,16 +226,22 @@ struct LoadPlan {
   uint32_t v[LPW];
 };
 
-template <int D, int NW, int LPW>
+// SPLIT: the second half of the wave's loads fills tile rows 16..31 from a
+// descriptor of its own that starts at the row landing in tile row 16 (the
+// first half covers rows 0..15), so that the two 16-row halves of a stage
+// may come from different places.
+template <int D, int NW, int LPW, bool SPLIT = false>
 __device__ inline void make_plan(LoadPlan<LPW>& lp, int w, int lane, int64_t ksn, int64_t vsn) {
   using T = Tile<D>;
+  static_assert(!SPLIT || T::RPI * NW * (LPW / 2) == 16, "loads split at tile row 16");
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int idx = w + NW * i;
     const int r = T::RPI * idx + lane / T::CPR;
+    const int rg = SPLIT && i >= LPW / 2 ? r - 16 : r;  // row within its descriptor
     const int phys = lane % T::CPR;
-    lp.k[i] = (uint32_t)(r * ksn * 2 + (phys ^ T::fK(r)) * 16);
-    lp.v[i] = (uint32_t)(r * vsn * 2 + (phys ^ T::fV(r)) * 16);
+    lp.k[i] = (uint32_t)(rg * ksn * 2 + (phys ^ T::fK(r)) * 16);
+    lp.v[i] = (uint32_t)(rg * vsn * 2 + (phys ^ T::fV(r)) * 16);
   }
 }
 
@@ -256,6 +267,16 @@ __device__ inline void issue_rows(const uint32_t* off, const i32x4& rs, uint32_t
   if constexpr (I < LPW) {
     dma16<SO + NW * I * 1024>(rs, wave_lds, off[I]);
     issue_rows<NW, LPW, SO, I + 1>(off, rs, wave_lds);
+  }
+}
+
+// issue_rows for a split plan: tile rows 0..15 from rs0, rows 16..31 from rs1.
+template <int NW, int LPW, uint32_t SO, int I = 0>
+__device__ inline void issue_rows2(const uint32_t* off, const i32x4& rs0, const i32x4& rs1,
+                                   uint32_t wave_lds) {
+  if constexpr (I < LPW) {
+    dma16<SO + NW * I * 1024>(I < LPW / 2 ? rs0 : rs1, wave_lds, off[I]);
+    issue_rows2<NW, LPW, SO, I + 1>(off, rs0, rs1, wave_lds);
   }
 }
 
@@ -285,14 +306,20 @@ void attn_bf16_kernel(const Bf16Params p) {
   using C = Cfg<D, BQ, SUB>;
   using T = typename C::T;
   constexpr int KB = C::KB, NSUB = C::NSUB;
-  // pyramid lists stepped in half blocks: steps whose four eighths are all
-  // unselected are left out (they would only compute masked keys)
+  // pyramid lists stepped in 32-key steps of two 16-row groups (SL): groups
+  // with no selected eighth are left out (they would only compute masked
+  // keys), and the selected ones are packed two per step, from any tiles and
+  // levels; each group has its own level, valid rows and load descriptor
   constexpr bool SL = PYR && NSUB == 2;
+  static_assert(!SL || KB == 1, "grouped steps are 32 keys");
   // eighth mask of a step with every key selected (4 bits per 32 keys)
   constexpr int QF = (1 << (4 * KB)) - 1;
+  // step codes: list entries (key blocks), or with the pyramid step list the
+  // 64-bit pair of group descriptors
+  using CodeT = std::conditional_t<SL, uint64_t, int>;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
-  // step descriptors (see the pyramid step list below)
-  __shared__ int32_t steplist[SL ? kStepCap : 1];
+  // group descriptors (see the pyramid step list below)
+  __shared__ __attribute__((aligned(8))) int32_t steplist[SL ? kStepCap : 2];
   __shared__ int32_t steps_sh;
 
   const int tid = threadIdx.x;
@@ -386,71 +413,112 @@ void attn_bf16_kernel(const Bf16Params p) {
     return NSUB == 2 ? (q >> (4 * part_of(u))) & 0xF : q;
   };
 
-  // Pyramid step list: wave 0 lists the half steps with a selected eighth
-  // as descriptors (first key row in k or kp / 32 << 12 | valid rows << 6 |
-  // level << 4 | the half's four eighth bits), so that a step needs one LDS
-  // word and no address arithmetic on its level.
+  // Pyramid step list: wave 0 lists the row's 16-row groups (pairs of
+  // eighths) that hold a selected eighth, in list order, as 32-bit
+  // descriptors: first key row in k or kp / 16 << 11 | valid rows << 4 |
+  // level << 2 | the group's two eighth bits. Step u is groups 2u and 2u+1
+  // (a zero, empty, descriptor pads an odd count), read as one 64-bit LDS
+  // word with no address arithmetic on levels.
   bool use_sl = false;
-  auto d_row0 = [](int d) -> int { return (d >> 12) << 5; };
-  auto d_valid = [](int d) -> int { return (d >> 6) & 63; };
-  auto d_level = [](int d) -> int { return (d >> 4) & 3; };
-  auto d_eighths = [](int d) -> int { return d & 0xF; };
+  auto g_row0 = [](uint32_t d) -> int { return (int)(d >> 11) << 4; };
+  auto g_valid = [](uint32_t d) -> int { return (int)(d >> 4) & 31; };
+  auto g_level = [](uint32_t d) -> int { return (int)(d >> 2) & 3; };
+  auto g_eighths = [](uint32_t d) -> int { return (int)d & 3; };
   if constexpr (SL) {
-    // else every half is stepped through (row offsets fit 19 bits below 2^24)
-    if (2 * L <= kStepCap && N32 < (1 << 24)) {
-      use_sl = true;
+    // else every half block is stepped through (row offsets fit 20 bits
+    // below 2^24; a list longer than the capacity is not used)
+    if (N32 < (1 << 24)) {
       if (w == 0) {
         int base = 0;
+        const uint64_t below = (1ull << lane) - 1;
         for (int j0 = 0; j0 < L; j0 += 64) {
           const int j = j0 + lane;
           const int q = j < L ? p.kv_eighths[e0 + j] : 0;
           const int c = j < L ? p.kv_idx[e0 + j] : 0;
-          const uint64_t m0 = __builtin_amdgcn_ballot_w64((q & 0xF) != 0);
-          const uint64_t m1 = __builtin_amdgcn_ballot_w64((q & 0xF0) != 0);
-          const uint64_t below = (1ull << lane) - 1;
-          const int pos = base + __popcll(m0 & below) + __popcll(m1 & below);
-          auto desc = [&](int part) {
-            return ((first_key(c, part) >> 5) << 12) | (valid_keys(c, part) << 6) |
-                   (level_of(c) << 4) | ((q >> (4 * part)) & 0xF);
-          };
-          if (q & 0xF) steplist[pos] = desc(0);
-          if (q & 0xF0) steplist[pos + ((q & 0xF) ? 1 : 0)] = desc(1);
-          base += __popcll(m0) + __popcll(m1);
+          int pos = base, cnt = 0;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const uint64_t m = __builtin_amdgcn_ballot_w64(((q >> (2 * g)) & 3) != 0);
+            pos += __popcll(m & below);
+            cnt += __popcll(m);
+          }
+          if (q) {
+            const int l = level_of(c);
+            const int rb_l = l == 0 ? 0 : (l == 1 ? p.rb1 : (l == 2 ? p.rb2 : p.rb3));
+            const int row0 = first_key(c, 0), lrow0 = (c - rb_l) * kBk;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int e = (q >> (2 * g)) & 3;
+              if (e) {
+                const int valid = max(0, min(16, (N32 >> l) - (lrow0 + 16 * g)));
+                if (pos < kStepCap)
+                  steplist[pos] = (int32_t)((((uint32_t)(row0 + 16 * g) >> 4) << 11) |
+                                            (uint32_t)(valid << 4) | (uint32_t)(l << 2) |
+                                            (uint32_t)e);
+                ++pos;
+              }
+            }
+          }
+          base += cnt;
         }
-        if (lane == 0) steps_sh = base;
+        if (lane == 0) {
+          if ((base & 1) && base < kStepCap) steplist[base] = 0;
+          steps_sh = base;
+        }
       }
       __syncthreads();
-      LS = steps_sh;
+      const int G = steps_sh;
+      if (G + (G & 1) <= kStepCap) {
+        use_sl = true;
+        LS = (G + 1) / 2;
+      }
     }
   }
-  auto step_code = [&](int u) -> int { return wave_uniform(steplist[u]); };
+  const uint64_t* sl64 = (const uint64_t*)steplist;
+  auto step_code = [&](int u) -> uint64_t { return wave_uniform64(sl64[u]); };
 
   LoadPlan<C::LPW> lp;
-  make_plan<D, C::NW, C::LPW>(lp, w, lane, p.ksn, p.vsn);
+  make_plan<D, C::NW, C::LPW, SL>(lp, w, lane, p.ksn, p.vsn);
   // Stage byte offsets: step u uses K stage u % 2 and V stage u % 2.
   const uint32_t wave_lds =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem + (uint32_t)w * 1024;
   constexpr int kso[2] = {0, T::BYTES};
   constexpr int vso[2] = {C::VOFF, C::VOFF + T::BYTES};
+  // (with the split plan of SL, a half block's two 16-row groups)
   auto issue_k = [&](auto so_c, int c, int part) {
-    const int j0 = first_key(c, part);
+    const int j0 = first_key(c, part), vk = valid_keys(c, part);
     const uint16_t* base = (PYR && c >= p.rb1) ? kpbase : kbase;
-    issue_rows<C::NW, C::LPW, decltype(so_c)::value>(
-        lp.k, rows_rsrc(base, p.ksn, j0, valid_keys(c, part)), wave_lds);
+    if constexpr (SL)
+      issue_rows2<C::NW, C::LPW, decltype(so_c)::value>(
+          lp.k, rows_rsrc(base, p.ksn, j0, min(vk, 16)),
+          rows_rsrc(base, p.ksn, j0 + 16, max(vk - 16, 0)), wave_lds);
+    else
+      issue_rows<C::NW, C::LPW, decltype(so_c)::value>(lp.k, rows_rsrc(base, p.ksn, j0, vk),
+                                                       wave_lds);
   };
   auto issue_v = [&](auto so_c, int c, int part) {
-    const int j0 = first_key(c, part);
+    const int j0 = first_key(c, part), vk = valid_keys(c, part);
     const uint16_t* base = (PYR && c >= p.rb1) ? vpbase : vbase;
-    issue_rows<C::NW, C::LPW, decltype(so_c)::value>(
-        lp.v, rows_rsrc(base, p.vsn, j0, valid_keys(c, part)), wave_lds);
+    if constexpr (SL)
+      issue_rows2<C::NW, C::LPW, decltype(so_c)::value>(
+          lp.v, rows_rsrc(base, p.vsn, j0, min(vk, 16)),
+          rows_rsrc(base, p.vsn, j0 + 16, max(vk - 16, 0)), wave_lds);
+    else
+      issue_rows<C::NW, C::LPW, decltype(so_c)::value>(lp.v, rows_rsrc(base, p.vsn, j0, vk),
+                                                       wave_lds);
   };
-  auto issue_kd = [&](auto so_c, int d) {
-    issue_rows<C::NW, C::LPW, decltype(so_c)::value>(
-        lp.k, rows_rsrc(d_level(d) ? kpbase : kbase, p.ksn, d_row0(d), d_valid(d)), wave_lds);
+  // a step of the pyramid step list: each group from its own level's tensor
+  auto issue_kd = [&](auto so_c, uint64_t d) {
+    const uint32_t g0 = (uint32_t)d, g1 = (uint32_t)(d >> 32);
+    issue_rows2<C::NW, C::LPW, decltype(so_c)::value>(
+        lp.k, rows_rsrc(g_level(g0) ? kpbase : kbase, p.ksn, g_row0(g0), g_valid(g0)),
+        rows_rsrc(g_level(g1) ? kpbase : kbase, p.ksn, g_row0(g1), g_valid(g1)), wave_lds);
   };
-  auto issue_vd = [&](auto so_c, int d) {
-    issue_rows<C::NW, C::LPW, decltype(so_c)::value>(
-        lp.v, rows_rsrc(d_level(d) ? vpbase : vbase, p.vsn, d_row0(d), d_valid(d)), wave_lds);
+  auto issue_vd = [&](auto so_c, uint64_t d) {
+    const uint32_t g0 = (uint32_t)d, g1 = (uint32_t)(d >> 32);
+    issue_rows2<C::NW, C::LPW, decltype(so_c)::value>(
+        lp.v, rows_rsrc(g_level(g0) ? vpbase : vbase, p.vsn, g_row0(g0), g_valid(g0)),
+        rows_rsrc(g_level(g1) ? vpbase : vbase, p.vsn, g_row0(g1), g_valid(g1)), wave_lds);
   };
   using K0 = std::integral_constant<uint32_t, kso[0]>;
   using K1 = std::integral_constant<uint32_t, kso[1]>;
@@ -461,7 +529,7 @@ void attn_bf16_kernel(const Bf16Params p) {
   // Key blocks of steps it, it+1, it+2 (rolling), their eighth masks and,
   // for step lists, their parts; with the pyramid step list in use, c0..c2
   // hold the steps' descriptors instead.
-  int c0 = 0, c1 = 0, c2 = 0;
+  CodeT c0 = 0, c1 = 0, c2 = 0;
   int q0 = QF, q1 = QF, q2 = QF;
   int r0 = 0, r1 = PART1, r2 = 0;
   if (SL && use_sl) {
@@ -569,6 +637,16 @@ void attn_bf16_kernel(const Bf16Params p) {
         if (key_of(kb, j, hh) >= jv || !((qm >> (4 * kb + j / 4)) & 1))
           sacc[kb][j] = -INFINITY;
   };
+  // The same for the two 16-row groups of a pyramid step (keys j < 8 of a
+  // lane's scores are group 0): valid rows jv0 and jv1, eighth bits qm.
+  auto mask_keys2 = [&](f32x16(&sacc)[KB], int jv0, int jv1, int qm) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int key = key_of(0, j, hh);
+      const bool out = j < 8 ? key >= jv0 : key - 16 >= jv1;
+      if (out || !((qm >> (j / 4)) & 1)) sacc[0][j] = -INFINITY;
+    }
+  };
   auto tile_max = [&](f32x16(&sacc)[KB], bool masked, int jv, int qm) -> float {
     if (masked) mask_keys(sacc, jv, qm);
     float mloc = -INFINITY;
@@ -578,6 +656,19 @@ void attn_bf16_kernel(const Bf16Params p) {
       for (int j = 0; j < 16; j += 2) mloc = vmax(vmax(mloc, sacc[kb][j]), sacc[kb][j + 1]);
     mloc = vmax(mloc, other_half(mloc));
     return mloc * p.sl2;
+  };
+  // Row max (log2 units) of a pyramid step whose groups have levels l0, l1:
+  // a key of level l scores + l.
+  auto tile_max2 = [&](f32x16(&sacc)[KB], bool masked, int jv0, int jv1, int qm, float l0,
+                       float l1) -> float {
+    if (masked) mask_keys2(sacc, jv0, jv1, qm);
+    float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) m0 = vmax(vmax(m0, sacc[0][j]), sacc[0][j + 1]);
+#pragma unroll
+    for (int j = 8; j < 16; j += 2) m1 = vmax(vmax(m1, sacc[0][j]), sacc[0][j + 1]);
+    const float m = vmax(fmaf(m0, p.sl2, l0), fmaf(m1, p.sl2, l1));
+    return vmax(m, other_half(m));
   };
   // Tile gap (once the key block's last step is in) and exponent-base update
   // for a step whose row max is m_loc2. O must already hold every earlier
@@ -606,10 +697,12 @@ void attn_bf16_kernel(const Bf16Params p) {
       for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
     }
   };
-  // p = 2^(s*scale*log2e - m) rounded to bf16, and its row sum. Masked keys
-  // hold -inf and give 0 (sl2 > 0 always, see launch_attn_bf16).
-  auto probs = [&](const f32x16(&sacc)[KB], bf16x8(&pb)[KB][2], float bias) {
-    const float neg_m = bias - m_use;
+  // p = 2^(s*scale*log2e + bias - m) rounded to bf16, and its row sum, with
+  // bias0 on values 0..7 of each 16 and bias1 on 8..15 (the two groups of a
+  // pyramid step; equal elsewhere). Masked keys hold -inf and give 0 (sl2 > 0
+  // always, see launch_attn_bf16).
+  auto probs = [&](const f32x16(&sacc)[KB], bf16x8(&pb)[KB][2], float bias0, float bias1) {
+    const float neg_m0 = bias0 - m_use, neg_m1 = bias1 - m_use;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -617,7 +710,8 @@ void attn_bf16_kernel(const Bf16Params p) {
         f32x8 pv;
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-          pv[t] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][half * 8 + t], p.sl2, neg_m));
+          pv[t] = __builtin_amdgcn_exp2f(
+              fmaf(sacc[kb][half * 8 + t], p.sl2, half ? neg_m1 : neg_m0));
         pb[kb][half] = __builtin_convertvector(pv, bf16x8);
 #pragma unroll
         for (int t = 0; t < 8; t += 2)
@@ -654,18 +748,27 @@ void attn_bf16_kernel(const Bf16Params p) {
   // stages last read before that barrier, and waited for at the start of
   // step j+1.
   f32x16 sA[KB], sB[KB];
-  // per-step quantities from a block (and part) or, with LSL, a descriptor
-  auto lev = [&](auto lsl_c, int c) -> int {
-    if constexpr (decltype(lsl_c)::value) return d_level(c);
-    else return level_of(c);
+  // Per-step quantities from a block (and part), or with LSL from a step
+  // code; glev / gvalid per 16-row group g of a pyramid step (SL kernels).
+  auto lev = [&](auto, CodeT c) -> int { return level_of((int)c); };
+  auto vkeys = [&](auto, CodeT c, int part) -> int { return valid_keys((int)c, part); };
+  auto glev = [&](auto lsl_c, CodeT c, int g) -> int {
+    if constexpr (decltype(lsl_c)::value) return g_level((uint32_t)((uint64_t)c >> (32 * g)));
+    else return level_of((int)c);
   };
-  auto vkeys = [&](auto lsl_c, int c, int part) -> int {
-    if constexpr (decltype(lsl_c)::value) return d_valid(c);
-    else return valid_keys(c, part);
+  auto gvalid = [&](auto lsl_c, CodeT c, int part, int g) -> int {
+    if constexpr (decltype(lsl_c)::value) {
+      return g_valid((uint32_t)((uint64_t)c >> (32 * g)));
+    } else {
+      const int vk = valid_keys((int)c, part);
+      return g ? max(vk - 16, 0) : min(vk, 16);
+    }
   };
-  auto qmask = [&](auto lsl_c, int c, int q) -> int {
-    if constexpr (decltype(lsl_c)::value) return d_eighths(c);
-    else return q;
+  auto qmask = [&](auto lsl_c, CodeT c, int q) -> int {
+    if constexpr (decltype(lsl_c)::value)
+      return g_eighths((uint32_t)c) | (g_eighths((uint32_t)((uint64_t)c >> 32)) << 2);
+    else
+      return q;
   };
   auto first_scores = [&](auto lsl_c) __attribute__((always_inline)) {
     if (LS > 0) {
@@ -674,8 +777,16 @@ void attn_bf16_kernel(const Bf16Params p) {
       else wait_vmcnt<C::LPW>();
       barrier();
       scores(smem + kso[0], sA);
-      const int jv = vkeys(lsl_c, c0, r0), qm0 = qmask(lsl_c, c0, q0);
-      apply_max(tile_max(sA, jv < SUB || qm0 != QF, jv, qm0) + (float)lev(lsl_c, c0), 0, 0);
+      if constexpr (SL) {
+        const int jv0 = gvalid(lsl_c, c0, r0, 0), jv1 = gvalid(lsl_c, c0, r0, 1);
+        const int qm0 = qmask(lsl_c, c0, q0);
+        apply_max(tile_max2(sA, jv0 < 16 || jv1 < 16 || qm0 != QF, jv0, jv1, qm0,
+                            (float)glev(lsl_c, c0, 0), (float)glev(lsl_c, c0, 1)),
+                  0, 0);
+      } else {
+        const int jv = vkeys(lsl_c, c0, r0), qm0 = qmask(lsl_c, c0, q0);
+        apply_max(tile_max(sA, jv < SUB || qm0 != QF, jv, qm0) + (float)lev(lsl_c, c0), 0, 0);
+      }
     }
   };
   if constexpr (!SL) first_scores(std::false_type{});
@@ -706,7 +817,8 @@ void attn_bf16_kernel(const Bf16Params p) {
       if (it + 1 < LS) issue_v(VS_{}, c1, pv);
       if (it + 2 < LS) issue_k(KS_{}, c2, pk);
     }
-    const int code3 = LSL ? steplist[min(it + 3, kStepCap - 1)] : 0;
+    CodeT code3 = 0;
+    if constexpr (LSL) code3 = sl64[min(it + 3, kStepCap / 2 - 1)];
     bf16x8 pb[KB][2];
     if (has_next) {
       const char* kt = smem + kso[1 - par];
@@ -732,7 +844,13 @@ void attn_bf16_kernel(const Bf16Params p) {
       // probabilities of step it (exp2, bf16 pair, row-sum dot).
       // a pooled key stands for 2^level tokens: its weight 2^level p, i.e.
       // + level in the log2 exponent
-      const float neg_m = (float)lev(lsl_c, c0) - m_use;
+      float neg_m0, neg_m1;
+      if constexpr (SL) {
+        neg_m0 = (float)glev(lsl_c, c0, 0) - m_use;
+        neg_m1 = (float)glev(lsl_c, c0, 1) - m_use;
+      } else {
+        neg_m0 = neg_m1 = (float)lev(lsl_c, c0) - m_use;
+      }
 #pragma unroll
       for (int i = 0; i < kPfK; ++i) kbuf[i] = kread(i);
       // the first fragment reads go out together, ahead of the first MFMA
@@ -747,6 +865,7 @@ void attn_bf16_kernel(const Bf16Params p) {
 #pragma unroll
         for (int e2 = 0; e2 < C::EPS; e2 += 2) {
           const int e = i * C::EPS + e2, kb2 = e / 16, j = e % 16;
+          const float neg_m = j < 8 ? neg_m0 : neg_m1;  // j, j + 1 in one group
           const float x0 = __builtin_amdgcn_exp2f(fmaf(cur[kb2][j], p.sl2, neg_m));
           const float x1 = __builtin_amdgcn_exp2f(fmaf(cur[kb2][j + 1], p.sl2, neg_m));
           const bf16x2 pr = __builtin_convertvector((f32x2{x0, x1}), bf16x2);
@@ -766,11 +885,17 @@ void attn_bf16_kernel(const Bf16Params p) {
           asm volatile("" ::"v"(pb[kb][half]));
         }
       asm volatile("" ::"v"(l_lane));
-      const int jv = vkeys(lsl_c, c1, pv), qm1 = qmask(lsl_c, c1, q1);
-      if (jv < SUB || qm1 != QF) mask_keys(nxt, jv, qm1);
+      if constexpr (SL) {
+        const int jv0 = gvalid(lsl_c, c1, pv, 0), jv1 = gvalid(lsl_c, c1, pv, 1);
+        const int qm1 = qmask(lsl_c, c1, q1);
+        if (jv0 < 16 || jv1 < 16 || qm1 != QF) mask_keys2(nxt, jv0, jv1, qm1);
+      } else {
+        const int jv = vkeys(lsl_c, c1, pv), qm1 = qmask(lsl_c, c1, q1);
+        if (jv < SUB || qm1 != QF) mask_keys(nxt, jv, qm1);
+      }
       // Phase B: slot i issues P V MFMA i of step it and folds MPS scores of
       // step it+1 into the row max.
-      float mloc = -INFINITY;
+      float mloc = -INFINITY, mloc1 = -INFINITY;  // mloc1: group 1 of SL steps
 #pragma unroll
       for (int i = 0; i < C::NB; ++i) {
         if (i + kPfV < C::NB) vbuf[(i + kPfV) % (kPfV + 1)] = vread(i + kPfV);
@@ -780,23 +905,37 @@ void attn_bf16_kernel(const Bf16Params p) {
 #pragma unroll
         for (int e2 = 0; e2 < C::MPS; e2 += 2) {
           const int e = i * C::MPS + e2, kb2 = e / 16, j = e % 16;
-          mloc = vmax(vmax(mloc, nxt[kb2][j]), nxt[kb2][j + 1]);
+          if (SL && j >= 8)
+            mloc1 = vmax(vmax(mloc1, nxt[kb2][j]), nxt[kb2][j + 1]);
+          else
+            mloc = vmax(vmax(mloc, nxt[kb2][j]), nxt[kb2][j + 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      mloc = vmax(mloc, other_half(mloc));
-      apply_max(mloc * p.sl2 + (float)lev(lsl_c, c1), it + 1, part1);
+      if constexpr (SL) {
+        float m = vmax(fmaf(mloc, p.sl2, (float)glev(lsl_c, c1, 0)),
+                       fmaf(mloc1, p.sl2, (float)glev(lsl_c, c1, 1)));
+        m = vmax(m, other_half(m));
+        apply_max(m, it + 1, part1);
+      } else {
+        mloc = vmax(mloc, other_half(mloc));
+        apply_max(mloc * p.sl2 + (float)lev(lsl_c, c1), it + 1, part1);
+      }
     } else {
-      probs(cur, pb, (float)lev(lsl_c, c0));
+      if constexpr (SL)
+        probs(cur, pb, (float)glev(lsl_c, c0, 0), (float)glev(lsl_c, c0, 1));
+      else
+        probs(cur, pb, (float)lev(lsl_c, c0), (float)lev(lsl_c, c0));
       accumulate(smem + vso[par], pb);
     }
     // The list entries of step it+3 are read here, after the last LDS wait
     // of the step: scalar loads count in lgkmcnt and may complete out of
     // order, so one in flight would turn every LDS wait above into a wait for
     // everything.
-    int c3 = 0, q3 = QF, r3 = 0;
+    CodeT c3 = 0;
+    int q3 = QF, r3 = 0;
     if constexpr (LSL) {
-      const int code = wave_uniform(code3);
+      const uint64_t code = wave_uniform64(code3);
       if (it + 3 < LS) c3 = code;
     } else {
       c3 = it + 3 < LS ? block_of(it + 3) : 0;

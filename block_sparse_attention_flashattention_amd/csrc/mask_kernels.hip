@@ -150,36 +150,41 @@ __global__ void pool_mean_kernel(int64_t N, int32_t H, int32_t D, int32_t Bq, in
 }
 
 // Pooled scores S[bh][a][c] = scale * (sum over x ascending of qbar*kbar),
-// every product and sum rounded on its own (no fused multiply-add). A 16 x 16
-// workgroup computes a 64 x 64 tile, 4 x 4 outputs per thread (rows ty + 16i,
-// columns tx + 16j), with the channels staged through LDS 16 at a time; every
-// output keeps its own sum in ascending channel order. Four outputs per
-// operand read keep LDS bandwidth off the critical path. The next stage's
-// operands are loaded into registers while the current one is computed.
-constexpr int kScoreThreads = 16;                    // per side of the workgroup
-constexpr int kScoreSpan = 4;                        // outputs per thread per side
-constexpr int kScoreTile = kScoreThreads * kScoreSpan;  // outputs per tile side
-constexpr int kScoreX = 16;                          // channels per LDS stage
-__global__ __launch_bounds__(kScoreThreads * kScoreThreads) void pooled_scores_kernel(
+// every product and sum rounded on its own (no fused multiply-add). A
+// workgroup of 8 x 32 threads computes a 64 x 64 tile: thread (ty, tx) owns
+// rows 8ty .. 8ty+7 and columns 2tx, 2tx+1, and every output keeps its own
+// sum in ascending channel order (16 independent chains per thread). The
+// channels are staged through LDS 16 at a time, channel-major, so a thread's
+// eight rows (two columns) are contiguous and come in a few wide reads; the
+// next stage's operands are loaded into registers while the current one is
+// computed. The kernel is bound by the fp64 multiply and add issue.
+constexpr int kScoreTy = 8, kScoreTx = 32;             // threads per column / row of the tile
+constexpr int kScoreRows = 8, kScoreCols = 2;          // outputs per thread
+constexpr int kScoreTile = kScoreTy * kScoreRows;      // 64 rows and 64 columns per tile
+static_assert(kScoreTx * kScoreCols == kScoreTile, "square tile");
+constexpr int kScoreThreads = kScoreTy * kScoreTx;
+constexpr int kScoreX = 16;                            // channels per LDS stage
+__global__ __launch_bounds__(kScoreThreads) void pooled_scores_kernel(
     int32_t D, int64_t nQ, int64_t nK, double scale, const double* __restrict__ qbar,
     const double* __restrict__ kbar, double* __restrict__ S) {
 #pragma clang fp contract(off)
-  __shared__ double qs[kScoreTile][kScoreX + 1];
-  __shared__ double ks[kScoreTile][kScoreX + 1];
+  // [channel][row]; two doubles of padding keep the staging stores spread
+  __shared__ __attribute__((aligned(16))) double qs[kScoreX][kScoreTile + 2];
+  __shared__ __attribute__((aligned(16))) double ks[kScoreX][kScoreTile + 2];
   const int64_t bh = blockIdx.z;
   const int64_t a0 = (int64_t)blockIdx.y * kScoreTile, c0 = (int64_t)blockIdx.x * kScoreTile;
-  const int tx = threadIdx.x, ty = threadIdx.y, tid = ty * kScoreThreads + tx;
-  double acc[kScoreSpan][kScoreSpan];
+  const int tid = threadIdx.x, tx = tid % kScoreTx, ty = tid / kScoreTx;
+  double acc[kScoreRows][kScoreCols];
 #pragma unroll
-  for (int i = 0; i < kScoreSpan; ++i)
+  for (int i = 0; i < kScoreRows; ++i)
 #pragma unroll
-    for (int j = 0; j < kScoreSpan; ++j) acc[i][j] = 0.0;
-  constexpr int kPer = kScoreTile * kScoreX / (kScoreThreads * kScoreThreads);  // per thread
+    for (int j = 0; j < kScoreCols; ++j) acc[i][j] = 0.0;
+  constexpr int kPer = kScoreTile * kScoreX / kScoreThreads;  // staged values per thread
   double pq[kPer], pk[kPer];
   auto fetch = [&](int x0) {
 #pragma unroll
     for (int s = 0; s < kPer; ++s) {
-      const int e = tid + s * kScoreThreads * kScoreThreads;
+      const int e = tid + s * kScoreThreads;  // e = row * kScoreX + channel
       const int r = e / kScoreX, x = x0 + e % kScoreX;
       pq[s] = (a0 + r < nQ && x < D) ? qbar[(bh * nQ + a0 + r) * D + x] : 0.0;
       pk[s] = (c0 + r < nK && x < D) ? kbar[(bh * nK + c0 + r) * D + x] : 0.0;
@@ -189,32 +194,32 @@ __global__ __launch_bounds__(kScoreThreads * kScoreThreads) void pooled_scores_k
   for (int x0 = 0; x0 < D; x0 += kScoreX) {
 #pragma unroll
     for (int s = 0; s < kPer; ++s) {
-      const int e = tid + s * kScoreThreads * kScoreThreads;
-      qs[e / kScoreX][e % kScoreX] = pq[s];
-      ks[e / kScoreX][e % kScoreX] = pk[s];
+      const int e = tid + s * kScoreThreads;
+      qs[e % kScoreX][e / kScoreX] = pq[s];
+      ks[e % kScoreX][e / kScoreX] = pk[s];
     }
     __syncthreads();
     if (x0 + kScoreX < D) fetch(x0 + kScoreX);
     const int xn = min(kScoreX, D - x0);
     for (int xx = 0; xx < xn; ++xx) {
-      double qv[kScoreSpan], kv[kScoreSpan];
+      double qv[kScoreRows], kv[kScoreCols];
 #pragma unroll
-      for (int i = 0; i < kScoreSpan; ++i) qv[i] = qs[ty + kScoreThreads * i][xx];
+      for (int i = 0; i < kScoreRows; ++i) qv[i] = qs[xx][ty * kScoreRows + i];
 #pragma unroll
-      for (int j = 0; j < kScoreSpan; ++j) kv[j] = ks[tx + kScoreThreads * j][xx];
+      for (int j = 0; j < kScoreCols; ++j) kv[j] = ks[xx][tx * kScoreCols + j];
 #pragma unroll
-      for (int i = 0; i < kScoreSpan; ++i)
+      for (int i = 0; i < kScoreRows; ++i)
 #pragma unroll
-        for (int j = 0; j < kScoreSpan; ++j)
+        for (int j = 0; j < kScoreCols; ++j)
           acc[i][j] = __dadd_rn(acc[i][j], __dmul_rn(qv[i], kv[j]));
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < kScoreSpan; ++i)
+  for (int i = 0; i < kScoreRows; ++i)
 #pragma unroll
-    for (int j = 0; j < kScoreSpan; ++j) {
-      const int64_t a = a0 + ty + kScoreThreads * i, c = c0 + tx + kScoreThreads * j;
+    for (int j = 0; j < kScoreCols; ++j) {
+      const int64_t a = a0 + ty * kScoreRows + i, c = c0 + tx * kScoreCols + j;
       if (a < nQ && c < nK) S[(bh * nQ + a) * nK + c] = __dmul_rn(scale, acc[i][j]);
     }
 }
@@ -2099,7 +2104,7 @@ hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k
   if (err != hipSuccess) return err;
   dim3 grid((unsigned)((g.nK + kScoreTile - 1) / kScoreTile),
             (unsigned)((g.nQ + kScoreTile - 1) / kScoreTile), (unsigned)BH);
-  hipLaunchKernelGGL(pooled_scores_kernel, grid, dim3(kScoreThreads, kScoreThreads), 0, st,
+  hipLaunchKernelGGL(pooled_scores_kernel, grid, dim3(kScoreThreads), 0, st,
                      g.D, g.nQ, g.nK, scale, qbar, kbar, S);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
