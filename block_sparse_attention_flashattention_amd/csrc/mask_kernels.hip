@@ -941,6 +941,130 @@ __global__ __launch_bounds__(kWave * kSelectRowsPerGroup) void pooled_select_wav
   for (int64_t c = lane; c < nK; c += kWave) mrow[c] = flag[c];
 }
 
+// Pyramid levels (mode 4) for rows of 129 to 1,024 blocks, one wave per row
+// and up to four rows per workgroup: the walk of the levels runs over most
+// of a row's blocks, so the row is sorted whole, in registers (the bitonic
+// network of sort_keys: element e = 64 i + lane sits in register i of lane
+// e % 64; partners 64 or more apart are two registers of one lane, closer
+// ones come from lane ^ j by a cross-lane shuffle). Same arithmetic as
+// pooled_select_kernel: e = exp(S - max) in block order, Z their sum in
+// ascending block order, p = e / Z of the sorted pairs, and the levels from
+// the running mass (walk_mass).
+template <int NC>
+__device__ inline void sort_wave(uint64_t (&k)[NC], int32_t (&x)[NC]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int kk = 2; kk <= 64 * NC; kk <<= 1) {
+#pragma unroll
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      if (j >= 64) {
+        const int rj = j / 64;
+#pragma unroll
+        for (int r = 0; r < NC; ++r) {
+          if (r & rj) continue;  // r is the lower register of the pair (r, r + rj)
+          const int e = r * 64 + lane;
+          const bool up = (e & kk) == 0;
+          const bool first = k[r] > k[r + rj] || (k[r] == k[r + rj] && x[r] < x[r + rj]);
+          if (first != up) {
+            const uint64_t kt = k[r];
+            const int32_t xt = x[r];
+            k[r] = k[r + rj];
+            x[r] = x[r + rj];
+            k[r + rj] = kt;
+            x[r + rj] = xt;
+          }
+        }
+        continue;
+      }
+#pragma unroll
+      for (int r = 0; r < NC; ++r) {
+        const int e = r * 64 + lane;
+        const uint32_t lo = __shfl_xor((uint32_t)k[r], j);
+        const uint32_t hi = __shfl_xor((uint32_t)(k[r] >> 32), j);
+        const uint64_t ko = ((uint64_t)hi << 32) | lo;
+        const int32_t xo = __shfl_xor(x[r], j);
+        const bool lower = (e & j) == 0, up = (e & kk) == 0;
+        const bool mine_first = k[r] > ko || (k[r] == ko && x[r] < xo);
+        // the lower position of an ascending pair holds the first element
+        const bool keep = (lower == up) == mine_first;
+        k[r] = keep ? k[r] : ko;
+        x[r] = keep ? x[r] : xo;
+      }
+    }
+  }
+}
+
+// LDS of one row of pooled_levels_wave_kernel: exponentials [nK] doubles
+// (then the flags), sorted probabilities [nK] doubles, sorted blocks [nK]
+// int32, each slice 16-byte aligned.
+__host__ __device__ inline size_t levels_slice(int64_t nK, int bytes) {
+  return ((size_t)nK * bytes + 15) / 16 * 16;
+}
+__host__ __device__ inline size_t levels_wave_lds(int64_t nK) {
+  return 2 * levels_slice(nK, 8) + levels_slice(nK, 4);
+}
+
+template <int NC>  // 64-key chunks per row held in registers (nK <= 64 * NC)
+__global__ __launch_bounds__(kWave * kSelectRowsPerGroup) void pooled_levels_wave_kernel(
+    int64_t R, int64_t nK, double tau0, double tau1, double tau2, double tau3,
+    int32_t n_levels, const double* __restrict__ S, uint8_t* __restrict__ mask) {
+  extern __shared__ double sml[];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + w;
+  if (row >= R) return;  // the whole wave (no workgroup barrier below)
+  char* base = (char*)sml + (size_t)w * levels_wave_lds(nK);
+  double* e = (double*)base;
+  double* cs = (double*)(base + levels_slice(nK, 8));
+  int32_t* ci = (int32_t*)(base + 2 * levels_slice(nK, 8));
+  const double* srow = S + row * nK;
+  uint8_t* mrow = mask + row * nK;
+  // scores (all loads in flight together), their sort keys and blocks; keys
+  // past the row are 0, below every score's key, and sort last
+  double v[NC];
+  uint64_t key[NC];
+  int32_t blk[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int64_t c = i * kWave + lane;
+    v[i] = c < nK ? srow[c] : 0.0;
+  }
+  double smax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int64_t c = i * kWave + lane;
+    key[i] = c < nK ? order_key(v[i]) : 0;
+    blk[i] = (int32_t)c;
+    if (c < nK) smax = fmax(smax, v[i]);
+  }
+  for (int off = 32; off >= 1; off >>= 1) smax = fmax(smax, __shfl_xor(smax, off));
+  // e = exp(S - max) in block order, and Z their sum in ascending block order
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int64_t c = i * kWave + lane;
+    if (c < nK) e[c] = exp(v[i] - smax);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const double Z = ordered_sum_ahead(e, nK, 0.0);
+  sort_wave<NC>(key, blk);
+  // p of the sorted pairs, each quotient on its own
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int64_t t = i * kWave + lane;
+    if (t < nK) {
+      cs[t] = e[blk[i]] / Z;
+      ci[t] = blk[i];
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  uint8_t* flag = (uint8_t*)e;  // the exponentials are used up
+  for (int64_t c = lane; c < nK; c += kWave) flag[c] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  walk_mass<8>(cs, ci, nK, tau0, tau1, tau2, tau3, n_levels, flag);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  for (int64_t c = lane; c < nK; c += kWave) mrow[c] = flag[c];
+}
+
 // ------------------------------------------------------- global selection
 // Head-wide selection over every (row block, key block) pair ([VMoBA]
 // section 三: rank all query/block relevances together and serve the
@@ -2119,6 +2243,24 @@ hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k
     hipLaunchKernelGGL(pooled_select_long_kernel, dim3((unsigned)R), dim3(kLongThreads), 0, st,
                        g.nK, mode, param, levels ? levels[1] : 0.0, levels ? levels[2] : 0.0, levels ? levels[3] : 0.0,
                        n_levels, S, zrow, mrow, mask);
+    return hipGetLastError();
+  }
+  if (mode == 4 && g.nK > 2 * kWave && g.nK <= 16 * kWave) {
+    // pyramid levels: one wave per row, the row sorted in registers
+    const size_t per = levels_wave_lds(g.nK);
+    const int64_t rpg = std::max<int64_t>(
+        1, std::min<int64_t>(kSelectRowsPerGroup, (int64_t)(65536 / per)));
+    const dim3 grid((unsigned)((R + rpg - 1) / rpg)), block((unsigned)(kWave * rpg));
+    const double t0 = levels[0], t1 = levels[1], t2 = levels[2], t3 = levels[3];
+    if (g.nK <= 4 * kWave)
+      hipLaunchKernelGGL(pooled_levels_wave_kernel<4>, grid, block, per * rpg, st, R, g.nK, t0,
+                         t1, t2, t3, n_levels, S, mask);
+    else if (g.nK <= 8 * kWave)
+      hipLaunchKernelGGL(pooled_levels_wave_kernel<8>, grid, block, per * rpg, st, R, g.nK, t0,
+                         t1, t2, t3, n_levels, S, mask);
+    else
+      hipLaunchKernelGGL(pooled_levels_wave_kernel<16>, grid, block, per * rpg, st, R, g.nK, t0,
+                         t1, t2, t3, n_levels, S, mask);
     return hipGetLastError();
   }
   int32_t P = 1;

@@ -195,3 +195,46 @@ def test_pyramid_mask_rows_over_2048_blocks(taus):
     note(f"pyramid level mask rows of {w.nK} blocks {taus}: "
          f"{[int((mref == l).sum()) for l in range(len(taus) + 1)]} per level")
     np.testing.assert_array_equal(got, mref)
+
+
+def _level_mask_gpu(w, x, taus):
+    s = shape_of(w)
+    ws = torch.empty(bsa.bsa_pooled_workspace_bytes(s), dtype=torch.uint8, device=DEV)
+    mask = torch.empty(w.B * w.H * w.nQ * w.nK, dtype=torch.uint8, device=DEV)
+    bsa.bsa_build_mask_pyramid(s, dev(x["q"]), dev(x["k"]), w.scale, list(taus), mask, ws)
+    torch.cuda.synchronize()
+    return host(mask).reshape(w.B, w.H, w.nQ, w.nK)
+
+
+@pytest.mark.parametrize("grid,Bq", [((8, 40, 40), 64), ((15, 50, 80), 128)])
+@pytest.mark.parametrize("taus", [(1.0,), (0.3, 0.6, 0.9), (0.2, 0.4, 0.6, 0.9)])
+def test_pyramid_mask_one_wave_rows_bit_exact(grid, Bq, taus):
+    """Level masks of rows of 200 and of 938 key blocks (the last one ragged),
+    where one wave sorts a whole row in registers, bit-exact against the
+    oracle."""
+    w = synth.Workload("pyr_wave_rows", 1, 2, 64, *grid, Bq, 64, "bf16", "pooled", 646, True)
+    assert 128 < w.nK <= 1024
+    x = synth.make_qkv(w)
+    got = _level_mask_gpu(w, x, taus)
+    ref, _, _ = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, 4, 0,
+                                         levels_tau=list(taus))
+    note(f"pyramid level mask, rows of {w.nK} blocks {taus}: "
+         f"{[int((ref == l).sum()) for l in range(len(taus) + 1)]} per level")
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("period", [3, 7])
+@pytest.mark.parametrize("taus", [(0.3, 0.6, 0.9), (0.2, 0.4, 0.6, 0.9)])
+def test_pyramid_mask_tied_rows_bit_exact(period, taus):
+    """Rows of 400 key blocks whose keys repeat every `period` blocks, so every
+    score comes in a tie group of 57 or more blocks: tied blocks take their
+    levels in ascending block order."""
+    w = synth.Workload("pyr_ties", 1, 2, 64, 25, 32, 32, 128, 64, "bf16", "pooled", 647, True)
+    x = synth.make_qkv(w)
+    k = x["k"].reshape(w.B, w.nK, w.Bk, w.H, w.d)
+    x["k"] = np.ascontiguousarray(k[:, np.arange(w.nK) % period].reshape(x["k"].shape))
+    got = _level_mask_gpu(w, x, taus)
+    ref, S, _ = oracle.build_mask_pooled(x["q"], x["k"], w.Bq, w.Bk, w.scale, 4, 0,
+                                         levels_tau=list(taus), want_scores=True)
+    assert np.all(S[..., period:] == S[..., :-period])   # scores repeat with the keys
+    np.testing.assert_array_equal(got, ref)
