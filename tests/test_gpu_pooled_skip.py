@@ -519,3 +519,27 @@ def test_fwd_hunyuan_4x_radial_sampled():
                                          0, rows=rows)
     og, lg = gather_rows(host(o), host(lse), rows, w.B, w.H, w.N, w.Bq)
     compare(og, lg, o_ref, lse_ref, f"{w.name} sampled")
+
+
+def test_fwd_with_tile_gaps_deterministic_run_twice():
+    """Per-head lists with tile gaps (the skip carry's forward): O, LSE and the
+    gaps, folded in with a float atomic max, are the same bit for bit on a
+    second run."""
+    w = synth.Workload("gap_twice", 1, 3, 128, 6, 10, 14, 64, 64, "bf16", "skip", 649, True,
+                       tau=1.0, steps=1)
+    x = synth.make_qkv(w)
+    s = shape_of(w)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    R = w.B * w.H * w.nQ
+    ones = torch.ones(R * w.nK, dtype=torch.uint8, device=DEV)   # one mask per head
+    rp = torch.empty(R + 1, dtype=torch.int32, device=DEV)
+    kv = torch.empty(R * w.nK, dtype=torch.int32, device=DEV)
+    bsa.bsa_compact_block_lists(s, ones, w.nQ * w.nK, None, rp, kv)   # per-head lists
+    assert int(rp[-1]) == R * w.nK
+    nnz = R * w.nK
+    o1, l1, g1 = run_fwd(s, q, k, v, rp, kv, 0, w.scale, gap_len=nnz)
+    o2, l2, g2 = run_fwd(s, q, k, v, rp, kv, 0, w.scale, gap_len=nnz)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+    assert not torch.isnan(g1).any()
+    assert torch.equal(g1, g2)

@@ -238,3 +238,16 @@ def test_pyramid_mask_tied_rows_bit_exact(period, taus):
                                          levels_tau=list(taus), want_scores=True)
     assert np.all(S[..., period:] == S[..., :-period])   # scores repeat with the keys
     np.testing.assert_array_equal(got, ref)
+
+
+def test_pyramid_forward_deterministic_run_twice():
+    """Packed 16-row groups from several levels: the same inputs give the same
+    O and LSE bit for bit (no float atomics on this path)."""
+    w = synth.Workload("pyr_twice", 1, 2, 128, 5, 12, 16, 64, 64, "bf16", "pooled", 648, True)
+    x = synth.make_qkv(w)
+    taus = [0.2, 0.4, 0.7, 0.95]
+    a = run_pyramid(w, x, taus)
+    b = run_pyramid(w, x, taus)
+    assert (a["mask"] == 4).any()
+    assert torch.equal(a["o"].view(torch.int16), b["o"].view(torch.int16))
+    assert torch.equal(a["lse"], b["lse"])
