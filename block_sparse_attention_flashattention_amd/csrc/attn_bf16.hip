@@ -226,19 +226,19 @@ struct LoadPlan {
   uint32_t v[LPW];
 };
 
-// SPLIT: the second half of the wave's loads fills tile rows 16..31 from a
-// descriptor of its own that starts at the row landing in tile row 16 (the
-// first half covers rows 0..15), so that the two 16-row halves of a stage
-// may come from different places.
+// SPLIT: every load fills rows of one 16-row group of the tile (4 or 8
+// rows each) and takes them from that group's own descriptor, which starts
+// at the row landing in the group's first tile row, so that the groups of a
+// stage may come from different places (issue_rows_grouped).
 template <int D, int NW, int LPW, bool SPLIT = false>
 __device__ inline void make_plan(LoadPlan<LPW>& lp, int w, int lane, int64_t ksn, int64_t vsn) {
   using T = Tile<D>;
-  static_assert(!SPLIT || T::RPI * NW * (LPW / 2) == 16, "loads split at tile row 16");
+  static_assert(!SPLIT || 16 % T::RPI == 0, "a load's rows lie in one 16-row group");
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int idx = w + NW * i;
     const int r = T::RPI * idx + lane / T::CPR;
-    const int rg = SPLIT && i >= LPW / 2 ? r - 16 : r;  // row within its descriptor
+    const int rg = SPLIT ? (r & 15) : r;  // row within its descriptor
     const int phys = lane % T::CPR;
     lp.k[i] = (uint32_t)(rg * ksn * 2 + (phys ^ T::fK(r)) * 16);
     lp.v[i] = (uint32_t)(rg * vsn * 2 + (phys ^ T::fV(r)) * 16);
@@ -270,13 +270,39 @@ __device__ inline void issue_rows(const uint32_t* off, const i32x4& rs, uint32_t
   }
 }
 
-// issue_rows for a split plan: tile rows 0..15 from rs0, rows 16..31 from rs1.
-template <int NW, int LPW, uint32_t SO, int I = 0>
-__device__ inline void issue_rows2(const uint32_t* off, const i32x4& rs0, const i32x4& rs1,
-                                   uint32_t wave_lds) {
+// Descriptors of the (2 or 4) 16-row groups of a stage, as named members
+// rather than an array, so that picking one never goes through memory.
+struct GroupRsrc {
+  i32x4 r0, r1, r2, r3;
+  __device__ void set(int g, const i32x4& v) {
+    if (g == 0) r0 = v;
+    else if (g == 1) r1 = v;
+    else if (g == 2) r2 = v;
+    else r3 = v;
+  }
+  __device__ i32x4 get(int g) const { return g == 0 ? r0 : (g == 1 ? r1 : (g == 2 ? r2 : r3)); }
+};
+
+// issue_rows for a split plan: load I of wave w fills tile rows from
+// RPI * (w + NW * I), in group RPI * (w + NW * I) / 16, from that group's
+// descriptor. When one round of the workgroup's loads (RPI * NW rows)
+// divides 16 rows, the group does not depend on the wave and is a constant;
+// otherwise it is picked at run time (one wave-uniform index).
+template <int NW, int LPW, int RPI, uint32_t SO, int I = 0>
+__device__ __attribute__((always_inline)) inline void issue_rows_grouped(
+    const uint32_t* off, const GroupRsrc& rs, int w, uint32_t wave_lds) {
+  static_assert((RPI * NW <= 16 && 16 % (RPI * NW) == 0) || (RPI * NW) % 16 == 0,
+                "loads of one round align with the 16-row groups");
   if constexpr (I < LPW) {
-    dma16<SO + NW * I * 1024>(I < LPW / 2 ? rs0 : rs1, wave_lds, off[I]);
-    issue_rows2<NW, LPW, SO, I + 1>(off, rs0, rs1, wave_lds);
+    i32x4 r;
+    if constexpr (RPI * NW <= 16) {
+      r = rs.get(RPI * NW * I / 16);
+    } else {
+      r = rs.get(wave_uniform(RPI * (w + NW * I) / 16));
+      r = i32x4{wave_uniform(r[0]), wave_uniform(r[1]), wave_uniform(r[2]), wave_uniform(r[3])};
+    }
+    dma16<SO + NW * I * 1024>(r, wave_lds, off[I]);
+    issue_rows_grouped<NW, LPW, RPI, SO, I + 1>(off, rs, w, wave_lds);
   }
 }
 
@@ -299,6 +325,20 @@ __device__ inline bf16x8 join(i16x4 lo, i16x4 hi) {
 // Key of lane value j (0..15) of 32-key block kb: kb*32 + 8*(j/4) + 4*hh + j%4.
 __device__ inline int key_of(int kb, int j, int hh) { return kb * 32 + 8 * (j / 4) + 4 * hh + (j % 4); }
 
+// A step of the pyramid step list: the 32-bit descriptors of its NG 16-row
+// groups (see attn_bf16_kernel); where the step list is not in use, a list
+// entry's key block, in g[0].
+template <int NG>
+struct GroupCode {
+  uint32_t g[NG];
+  __device__ GroupCode() : g{} {}
+  __device__ GroupCode(int v) : g{} { g[0] = (uint32_t)v; }
+  __device__ operator int() const { return (int)g[0]; }
+};
+template <int NG>
+__device__ inline uint32_t code_word(const GroupCode<NG>& c, int i) { return c.g[i]; }
+__device__ inline uint32_t code_word(int, int) { return 0; }  // plain list entry: no groups
+
 template <int D, int BQ, int SUB, bool GAP, bool PYR>
 __global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(const Bf16Params p) {
@@ -306,20 +346,23 @@ void attn_bf16_kernel(const Bf16Params p) {
   using C = Cfg<D, BQ, SUB>;
   using T = typename C::T;
   constexpr int KB = C::KB, NSUB = C::NSUB;
-  // pyramid lists stepped in 32-key steps of two 16-row groups (SL): groups
-  // with no selected eighth are left out (they would only compute masked
-  // keys), and the selected ones are packed two per step, from any tiles and
-  // levels; each group has its own level, valid rows and load descriptor
-  constexpr bool SL = PYR && NSUB == 2;
-  static_assert(!SL || KB == 1, "grouped steps are 32 keys");
+  // pyramid lists stepped as 16-row groups (SL): groups with no selected
+  // eighth are left out (they would only compute masked keys), and the
+  // selected ones are packed GS per step (two per 32-key step, four per
+  // 64-key step), from any tiles and levels; each group has its own level,
+  // valid rows and load descriptor. Keys 16 g .. 16 g + 15 of a step are
+  // group g: a lane's scores j < 8 of 32-key block kb are group 2 kb, the
+  // others group 2 kb + 1.
+  constexpr bool SL = PYR;
+  constexpr int GS = 2 * KB;
   // eighth mask of a step with every key selected (4 bits per 32 keys)
   constexpr int QF = (1 << (4 * KB)) - 1;
   // step codes: list entries (key blocks), or with the pyramid step list the
-  // 64-bit pair of group descriptors
-  using CodeT = std::conditional_t<SL, uint64_t, int>;
+  // group descriptors of the step
+  using CodeT = std::conditional_t<SL, GroupCode<GS>, int>;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
   // group descriptors (see the pyramid step list below)
-  __shared__ __attribute__((aligned(8))) int32_t steplist[SL ? kStepCap : 2];
+  __shared__ __attribute__((aligned(16))) int32_t steplist[SL ? kStepCap : 2];
   __shared__ int32_t steps_sh;
 
   const int tid = threadIdx.x;
@@ -416,9 +459,9 @@ void attn_bf16_kernel(const Bf16Params p) {
   // Pyramid step list: wave 0 lists the row's 16-row groups (pairs of
   // eighths) that hold a selected eighth, in list order, as 32-bit
   // descriptors: first key row in k or kp / 16 << 11 | valid rows << 4 |
-  // level << 2 | the group's two eighth bits. Step u is groups 2u and 2u+1
-  // (a zero, empty, descriptor pads an odd count), read as one 64-bit LDS
-  // word with no address arithmetic on levels.
+  // level << 2 | the group's two eighth bits. Step u is groups GS u ..
+  // GS u + GS - 1 (zero, empty, descriptors pad the last step), read as one
+  // 64- or 128-bit LDS word with no address arithmetic on levels.
   bool use_sl = false;
   auto g_row0 = [](uint32_t d) -> int { return (int)(d >> 11) << 4; };
   auto g_valid = [](uint32_t d) -> int { return (int)(d >> 4) & 31; };
@@ -462,20 +505,35 @@ void attn_bf16_kernel(const Bf16Params p) {
           base += cnt;
         }
         if (lane == 0) {
-          if ((base & 1) && base < kStepCap) steplist[base] = 0;
+          for (int pz = base; pz < kStepCap && pz % GS; ++pz) steplist[pz] = 0;
           steps_sh = base;
         }
       }
       __syncthreads();
-      const int G = steps_sh;
-      if (G + (G & 1) <= kStepCap) {
+      const int G = (steps_sh + GS - 1) / GS * GS;  // groups, padded to whole steps
+      if (G <= kStepCap) {
         use_sl = true;
-        LS = (G + 1) / 2;
+        LS = G / GS;
       }
     }
   }
-  const uint64_t* sl64 = (const uint64_t*)steplist;
-  auto step_code = [&](int u) -> uint64_t { return wave_uniform64(sl64[u]); };
+  // descriptors of step u as read from LDS, and the same made wave-uniform
+  auto step_words = [&](int u) -> CodeT {
+    CodeT d{};
+    if constexpr (SL) {
+#pragma unroll
+      for (int i = 0; i < GS; ++i) d.g[i] = (uint32_t)steplist[u * GS + i];
+    }
+    return d;
+  };
+  auto uniform_code = [&](CodeT d) -> CodeT {
+    if constexpr (SL) {
+#pragma unroll
+      for (int i = 0; i < GS; ++i) d.g[i] = (uint32_t)wave_uniform((int)d.g[i]);
+    }
+    return d;
+  };
+  auto step_code = [&](int u) -> CodeT { return uniform_code(step_words(u)); };
 
   LoadPlan<C::LPW> lp;
   make_plan<D, C::NW, C::LPW, SL>(lp, w, lane, p.ksn, p.vsn);
@@ -484,41 +542,55 @@ void attn_bf16_kernel(const Bf16Params p) {
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem + (uint32_t)w * 1024;
   constexpr int kso[2] = {0, T::BYTES};
   constexpr int vso[2] = {C::VOFF, C::VOFF + T::BYTES};
-  // (with the split plan of SL, a half block's two 16-row groups)
+  // (with the split plan of SL, a step's GS 16-row groups of its block)
   auto issue_k = [&](auto so_c, int c, int part) {
     const int j0 = first_key(c, part), vk = valid_keys(c, part);
     const uint16_t* base = (PYR && c >= p.rb1) ? kpbase : kbase;
-    if constexpr (SL)
-      issue_rows2<C::NW, C::LPW, decltype(so_c)::value>(
-          lp.k, rows_rsrc(base, p.ksn, j0, min(vk, 16)),
-          rows_rsrc(base, p.ksn, j0 + 16, max(vk - 16, 0)), wave_lds);
-    else
+    if constexpr (SL) {
+      GroupRsrc rs;
+#pragma unroll
+      for (int g = 0; g < GS; ++g)
+        rs.set(g, rows_rsrc(base, p.ksn, j0 + 16 * g, max(0, min(16, vk - 16 * g))));
+      issue_rows_grouped<C::NW, C::LPW, T::RPI, decltype(so_c)::value>(lp.k, rs, w, wave_lds);
+    } else {
       issue_rows<C::NW, C::LPW, decltype(so_c)::value>(lp.k, rows_rsrc(base, p.ksn, j0, vk),
                                                        wave_lds);
+    }
   };
   auto issue_v = [&](auto so_c, int c, int part) {
     const int j0 = first_key(c, part), vk = valid_keys(c, part);
     const uint16_t* base = (PYR && c >= p.rb1) ? vpbase : vbase;
-    if constexpr (SL)
-      issue_rows2<C::NW, C::LPW, decltype(so_c)::value>(
-          lp.v, rows_rsrc(base, p.vsn, j0, min(vk, 16)),
-          rows_rsrc(base, p.vsn, j0 + 16, max(vk - 16, 0)), wave_lds);
-    else
+    if constexpr (SL) {
+      GroupRsrc rs;
+#pragma unroll
+      for (int g = 0; g < GS; ++g)
+        rs.set(g, rows_rsrc(base, p.vsn, j0 + 16 * g, max(0, min(16, vk - 16 * g))));
+      issue_rows_grouped<C::NW, C::LPW, T::RPI, decltype(so_c)::value>(lp.v, rs, w, wave_lds);
+    } else {
       issue_rows<C::NW, C::LPW, decltype(so_c)::value>(lp.v, rows_rsrc(base, p.vsn, j0, vk),
                                                        wave_lds);
+    }
   };
   // a step of the pyramid step list: each group from its own level's tensor
-  auto issue_kd = [&](auto so_c, uint64_t d) {
-    const uint32_t g0 = (uint32_t)d, g1 = (uint32_t)(d >> 32);
-    issue_rows2<C::NW, C::LPW, decltype(so_c)::value>(
-        lp.k, rows_rsrc(g_level(g0) ? kpbase : kbase, p.ksn, g_row0(g0), g_valid(g0)),
-        rows_rsrc(g_level(g1) ? kpbase : kbase, p.ksn, g_row0(g1), g_valid(g1)), wave_lds);
+  auto issue_kd = [&](auto so_c, const CodeT& d) {
+    if constexpr (SL) {
+      GroupRsrc rs;
+#pragma unroll
+      for (int g = 0; g < GS; ++g)
+        rs.set(g, rows_rsrc(g_level(d.g[g]) ? kpbase : kbase, p.ksn, g_row0(d.g[g]),
+                            g_valid(d.g[g])));
+      issue_rows_grouped<C::NW, C::LPW, T::RPI, decltype(so_c)::value>(lp.k, rs, w, wave_lds);
+    }
   };
-  auto issue_vd = [&](auto so_c, uint64_t d) {
-    const uint32_t g0 = (uint32_t)d, g1 = (uint32_t)(d >> 32);
-    issue_rows2<C::NW, C::LPW, decltype(so_c)::value>(
-        lp.v, rows_rsrc(g_level(g0) ? vpbase : vbase, p.vsn, g_row0(g0), g_valid(g0)),
-        rows_rsrc(g_level(g1) ? vpbase : vbase, p.vsn, g_row0(g1), g_valid(g1)), wave_lds);
+  auto issue_vd = [&](auto so_c, const CodeT& d) {
+    if constexpr (SL) {
+      GroupRsrc rs;
+#pragma unroll
+      for (int g = 0; g < GS; ++g)
+        rs.set(g, rows_rsrc(g_level(d.g[g]) ? vpbase : vbase, p.vsn, g_row0(d.g[g]),
+                            g_valid(d.g[g])));
+      issue_rows_grouped<C::NW, C::LPW, T::RPI, decltype(so_c)::value>(lp.v, rs, w, wave_lds);
+    }
   };
   using K0 = std::integral_constant<uint32_t, kso[0]>;
   using K1 = std::integral_constant<uint32_t, kso[1]>;
@@ -637,15 +709,16 @@ void attn_bf16_kernel(const Bf16Params p) {
         if (key_of(kb, j, hh) >= jv || !((qm >> (4 * kb + j / 4)) & 1))
           sacc[kb][j] = -INFINITY;
   };
-  // The same for the two 16-row groups of a pyramid step (keys j < 8 of a
-  // lane's scores are group 0): valid rows jv0 and jv1, eighth bits qm.
-  auto mask_keys2 = [&](f32x16(&sacc)[KB], int jv0, int jv1, int qm) {
+  // The same for the GS 16-row groups of a pyramid step: valid rows jv[g]
+  // of group g, eighth bits qm.
+  auto mask_keys_grouped = [&](f32x16(&sacc)[KB], const int (&jv)[GS], int qm) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int key = key_of(0, j, hh);
-      const bool out = j < 8 ? key >= jv0 : key - 16 >= jv1;
-      if (out || !((qm >> (j / 4)) & 1)) sacc[0][j] = -INFINITY;
-    }
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = key_of(kb, j, hh), g = 2 * kb + (j >= 8 ? 1 : 0);
+        if (key - 16 * g >= jv[g] || !((qm >> (4 * kb + j / 4)) & 1)) sacc[kb][j] = -INFINITY;
+      }
   };
   auto tile_max = [&](f32x16(&sacc)[KB], bool masked, int jv, int qm) -> float {
     if (masked) mask_keys(sacc, jv, qm);
@@ -657,17 +730,24 @@ void attn_bf16_kernel(const Bf16Params p) {
     mloc = vmax(mloc, other_half(mloc));
     return mloc * p.sl2;
   };
-  // Row max (log2 units) of a pyramid step whose groups have levels l0, l1:
-  // a key of level l scores + l.
-  auto tile_max2 = [&](f32x16(&sacc)[KB], bool masked, int jv0, int jv1, int qm, float l0,
-                       float l1) -> float {
-    if (masked) mask_keys2(sacc, jv0, jv1, qm);
-    float m0 = -INFINITY, m1 = -INFINITY;
+  // Row max (log2 units) of a pyramid step whose group g has level lv[g]: a
+  // key of level l scores + l.
+  auto tile_max_grouped = [&](f32x16(&sacc)[KB], bool masked, const int (&jv)[GS], int qm,
+                              const float (&lv)[GS]) -> float {
+    if (masked) mask_keys_grouped(sacc, jv, qm);
+    float mg[GS];
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) m0 = vmax(vmax(m0, sacc[0][j]), sacc[0][j + 1]);
+    for (int g = 0; g < GS; ++g) mg[g] = -INFINITY;
 #pragma unroll
-    for (int j = 8; j < 16; j += 2) m1 = vmax(vmax(m1, sacc[0][j]), sacc[0][j + 1]);
-    const float m = vmax(fmaf(m0, p.sl2, l0), fmaf(m1, p.sl2, l1));
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        const int g = 2 * kb + (j >= 8 ? 1 : 0);
+        mg[g] = vmax(vmax(mg[g], sacc[kb][j]), sacc[kb][j + 1]);
+      }
+    float m = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < GS; ++g) m = vmax(m, fmaf(mg[g], p.sl2, lv[g]));
     return vmax(m, other_half(m));
   };
   // Tile gap (once the key block's last step is in) and exponent-base update
@@ -698,11 +778,10 @@ void attn_bf16_kernel(const Bf16Params p) {
     }
   };
   // p = 2^(s*scale*log2e + bias - m) rounded to bf16, and its row sum, with
-  // bias0 on values 0..7 of each 16 and bias1 on 8..15 (the two groups of a
-  // pyramid step; equal elsewhere). Masked keys hold -inf and give 0 (sl2 > 0
-  // always, see launch_attn_bf16).
-  auto probs = [&](const f32x16(&sacc)[KB], bf16x8(&pb)[KB][2], float bias0, float bias1) {
-    const float neg_m0 = bias0 - m_use, neg_m1 = bias1 - m_use;
+  // bias[2 kb + half] on values 8 half .. 8 half + 7 of key block kb (the
+  // groups of a pyramid step; all equal elsewhere). Masked keys hold -inf
+  // and give 0 (sl2 > 0 always, see launch_attn_bf16).
+  auto probs = [&](const f32x16(&sacc)[KB], bf16x8(&pb)[KB][2], const float (&bias)[GS]) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -711,7 +790,7 @@ void attn_bf16_kernel(const Bf16Params p) {
 #pragma unroll
         for (int t = 0; t < 8; ++t)
           pv[t] = __builtin_amdgcn_exp2f(
-              fmaf(sacc[kb][half * 8 + t], p.sl2, half ? neg_m1 : neg_m0));
+              fmaf(sacc[kb][half * 8 + t], p.sl2, bias[2 * kb + half] - m_use));
         pb[kb][half] = __builtin_convertvector(pv, bf16x8);
 #pragma unroll
         for (int t = 0; t < 8; t += 2)
@@ -752,23 +831,40 @@ void attn_bf16_kernel(const Bf16Params p) {
   // code; glev / gvalid per 16-row group g of a pyramid step (SL kernels).
   auto lev = [&](auto, CodeT c) -> int { return level_of((int)c); };
   auto vkeys = [&](auto, CodeT c, int part) -> int { return valid_keys((int)c, part); };
-  auto glev = [&](auto lsl_c, CodeT c, int g) -> int {
-    if constexpr (decltype(lsl_c)::value) return g_level((uint32_t)((uint64_t)c >> (32 * g)));
+  auto glev = [&](auto lsl_c, const CodeT& c, int g) -> int {
+    if constexpr (decltype(lsl_c)::value) return g_level(code_word(c, g));
     else return level_of((int)c);
   };
-  auto gvalid = [&](auto lsl_c, CodeT c, int part, int g) -> int {
+  auto gvalid = [&](auto lsl_c, const CodeT& c, int part, int g) -> int {
     if constexpr (decltype(lsl_c)::value) {
-      return g_valid((uint32_t)((uint64_t)c >> (32 * g)));
+      return g_valid(code_word(c, g));
     } else {
       const int vk = valid_keys((int)c, part);
-      return g ? max(vk - 16, 0) : min(vk, 16);
+      return max(0, min(16, vk - 16 * g));
     }
   };
-  auto qmask = [&](auto lsl_c, CodeT c, int q) -> int {
-    if constexpr (decltype(lsl_c)::value)
-      return g_eighths((uint32_t)c) | (g_eighths((uint32_t)((uint64_t)c >> 32)) << 2);
-    else
+  auto qmask = [&](auto lsl_c, const CodeT& c, int q) -> int {
+    if constexpr (decltype(lsl_c)::value) {
+      int m = 0;
+#pragma unroll
+      for (int g = 0; g < GS; ++g) m |= g_eighths(code_word(c, g)) << (2 * g);
+      return m;
+    } else {
       return q;
+    }
+  };
+  // valid rows and levels of the groups of a pyramid step, and whether any
+  // of its keys must be masked
+  auto group_info = [&](auto lsl_c, const CodeT& c, int part, int qm, int (&jv)[GS],
+                        float (&lv)[GS]) -> bool {
+    bool masked = qm != QF;
+#pragma unroll
+    for (int g = 0; g < GS; ++g) {
+      jv[g] = gvalid(lsl_c, c, part, g);
+      lv[g] = (float)glev(lsl_c, c, g);
+      masked = masked || jv[g] < 16;
+    }
+    return masked;
   };
   auto first_scores = [&](auto lsl_c) __attribute__((always_inline)) {
     if (LS > 0) {
@@ -778,11 +874,11 @@ void attn_bf16_kernel(const Bf16Params p) {
       barrier();
       scores(smem + kso[0], sA);
       if constexpr (SL) {
-        const int jv0 = gvalid(lsl_c, c0, r0, 0), jv1 = gvalid(lsl_c, c0, r0, 1);
+        int jv[GS];
+        float lv[GS];
         const int qm0 = qmask(lsl_c, c0, q0);
-        apply_max(tile_max2(sA, jv0 < 16 || jv1 < 16 || qm0 != QF, jv0, jv1, qm0,
-                            (float)glev(lsl_c, c0, 0), (float)glev(lsl_c, c0, 1)),
-                  0, 0);
+        const bool masked = group_info(lsl_c, c0, r0, qm0, jv, lv);
+        apply_max(tile_max_grouped(sA, masked, jv, qm0, lv), 0, 0);
       } else {
         const int jv = vkeys(lsl_c, c0, r0), qm0 = qmask(lsl_c, c0, q0);
         apply_max(tile_max(sA, jv < SUB || qm0 != QF, jv, qm0) + (float)lev(lsl_c, c0), 0, 0);
@@ -817,8 +913,8 @@ void attn_bf16_kernel(const Bf16Params p) {
       if (it + 1 < LS) issue_v(VS_{}, c1, pv);
       if (it + 2 < LS) issue_k(KS_{}, c2, pk);
     }
-    CodeT code3 = 0;
-    if constexpr (LSL) code3 = sl64[min(it + 3, kStepCap / 2 - 1)];
+    CodeT code3{};
+    if constexpr (LSL) code3 = step_words(min(it + 3, kStepCap / GS - 1));
     bf16x8 pb[KB][2];
     if (has_next) {
       const char* kt = smem + kso[1 - par];
@@ -844,13 +940,10 @@ void attn_bf16_kernel(const Bf16Params p) {
       // probabilities of step it (exp2, bf16 pair, row-sum dot).
       // a pooled key stands for 2^level tokens: its weight 2^level p, i.e.
       // + level in the log2 exponent
-      float neg_m0, neg_m1;
-      if constexpr (SL) {
-        neg_m0 = (float)glev(lsl_c, c0, 0) - m_use;
-        neg_m1 = (float)glev(lsl_c, c0, 1) - m_use;
-      } else {
-        neg_m0 = neg_m1 = (float)lev(lsl_c, c0) - m_use;
-      }
+      float nm[GS];  // bias - m_use of each group of step it
+#pragma unroll
+      for (int g = 0; g < GS; ++g)
+        nm[g] = (float)(SL ? glev(lsl_c, c0, g) : lev(lsl_c, c0)) - m_use;
 #pragma unroll
       for (int i = 0; i < kPfK; ++i) kbuf[i] = kread(i);
       // the first fragment reads go out together, ahead of the first MFMA
@@ -865,7 +958,7 @@ void attn_bf16_kernel(const Bf16Params p) {
 #pragma unroll
         for (int e2 = 0; e2 < C::EPS; e2 += 2) {
           const int e = i * C::EPS + e2, kb2 = e / 16, j = e % 16;
-          const float neg_m = j < 8 ? neg_m0 : neg_m1;  // j, j + 1 in one group
+          const float neg_m = nm[2 * kb2 + (j >= 8 ? 1 : 0)];  // j, j + 1 in one group
           const float x0 = __builtin_amdgcn_exp2f(fmaf(cur[kb2][j], p.sl2, neg_m));
           const float x1 = __builtin_amdgcn_exp2f(fmaf(cur[kb2][j + 1], p.sl2, neg_m));
           const bf16x2 pr = __builtin_convertvector((f32x2{x0, x1}), bf16x2);
@@ -885,17 +978,21 @@ void attn_bf16_kernel(const Bf16Params p) {
           asm volatile("" ::"v"(pb[kb][half]));
         }
       asm volatile("" ::"v"(l_lane));
+      float lv1[GS];  // levels of the groups of step it+1 (SL)
       if constexpr (SL) {
-        const int jv0 = gvalid(lsl_c, c1, pv, 0), jv1 = gvalid(lsl_c, c1, pv, 1);
+        int jv[GS];
         const int qm1 = qmask(lsl_c, c1, q1);
-        if (jv0 < 16 || jv1 < 16 || qm1 != QF) mask_keys2(nxt, jv0, jv1, qm1);
+        if (group_info(lsl_c, c1, pv, qm1, jv, lv1)) mask_keys_grouped(nxt, jv, qm1);
       } else {
         const int jv = vkeys(lsl_c, c1, pv), qm1 = qmask(lsl_c, c1, q1);
         if (jv < SUB || qm1 != QF) mask_keys(nxt, jv, qm1);
       }
       // Phase B: slot i issues P V MFMA i of step it and folds MPS scores of
       // step it+1 into the row max.
-      float mloc = -INFINITY, mloc1 = -INFINITY;  // mloc1: group 1 of SL steps
+      float mloc = -INFINITY;
+      float mg[GS];  // per group (SL)
+#pragma unroll
+      for (int g = 0; g < GS; ++g) mg[g] = -INFINITY;
 #pragma unroll
       for (int i = 0; i < C::NB; ++i) {
         if (i + kPfV < C::NB) vbuf[(i + kPfV) % (kPfV + 1)] = vread(i + kPfV);
@@ -905,16 +1002,19 @@ void attn_bf16_kernel(const Bf16Params p) {
 #pragma unroll
         for (int e2 = 0; e2 < C::MPS; e2 += 2) {
           const int e = i * C::MPS + e2, kb2 = e / 16, j = e % 16;
-          if (SL && j >= 8)
-            mloc1 = vmax(vmax(mloc1, nxt[kb2][j]), nxt[kb2][j + 1]);
-          else
+          if constexpr (SL) {
+            const int g = 2 * kb2 + (j >= 8 ? 1 : 0);
+            mg[g] = vmax(vmax(mg[g], nxt[kb2][j]), nxt[kb2][j + 1]);
+          } else {
             mloc = vmax(vmax(mloc, nxt[kb2][j]), nxt[kb2][j + 1]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (SL) {
-        float m = vmax(fmaf(mloc, p.sl2, (float)glev(lsl_c, c1, 0)),
-                       fmaf(mloc1, p.sl2, (float)glev(lsl_c, c1, 1)));
+        float m = -INFINITY;
+#pragma unroll
+        for (int g = 0; g < GS; ++g) m = vmax(m, fmaf(mg[g], p.sl2, lv1[g]));
         m = vmax(m, other_half(m));
         apply_max(m, it + 1, part1);
       } else {
@@ -922,10 +1022,10 @@ void attn_bf16_kernel(const Bf16Params p) {
         apply_max(mloc * p.sl2 + (float)lev(lsl_c, c1), it + 1, part1);
       }
     } else {
-      if constexpr (SL)
-        probs(cur, pb, (float)glev(lsl_c, c0, 0), (float)glev(lsl_c, c0, 1));
-      else
-        probs(cur, pb, (float)lev(lsl_c, c0), (float)lev(lsl_c, c0));
+      float bias[GS];
+#pragma unroll
+      for (int g = 0; g < GS; ++g) bias[g] = (float)(SL ? glev(lsl_c, c0, g) : lev(lsl_c, c0));
+      probs(cur, pb, bias);
       accumulate(smem + vso[par], pb);
     }
     // The list entries of step it+3 are read here, after the last LDS wait
@@ -935,7 +1035,7 @@ void attn_bf16_kernel(const Bf16Params p) {
     CodeT c3 = 0;
     int q3 = QF, r3 = 0;
     if constexpr (LSL) {
-      const uint64_t code = wave_uniform64(code3);
+      const CodeT code = uniform_code(code3);
       if (it + 3 < LS) c3 = code;
     } else {
       c3 = it + 3 < LS ? block_of(it + 3) : 0;
