@@ -297,8 +297,11 @@ constexpr int kLongCap = 1024;    // LDS entries of a step
 // First mask byte of a row left to the full sort (mask values are 0..3).
 constexpr uint8_t kSelectMarker = 0xFF;
 // Rows per workgroup of the one-wave-per-row select (at most; fewer when their
-// LDS would pass 64 KiB) and of the pass that finishes the rows it marked.
+// LDS would pass 64 KiB), and of the pass that finishes the rows it marked
+// (their markers read by one wave at once).
 constexpr int kSelectRowsPerGroup = 4;
+constexpr int kMarkedRowsPerGroup = 64;
+static_assert(kMarkedRowsPerGroup <= kWave, "one marker per lane");
 
 // Bitonic sort of the pairs (ks[t], ki[t]), t < P, P a power of two, into
 // descending order_key of the score, ascending block index on equal keys
@@ -588,13 +591,25 @@ __global__ void pooled_select_kernel(int64_t nK, int32_t P, int32_t mode, double
   uint8_t* flag = (uint8_t*)(ki + P);  // [nK]
   __shared__ int32_t keep_sh;
   __shared__ double z_sh;
-  // after pooled_select_wave_kernel: only the rows it left marked, a few
-  // rows per workgroup; else one row
-  const int64_t rows_per = only_marked ? kSelectRowsPerGroup : 1;
-  const int64_t row_end = min(R, ((int64_t)blockIdx.x + 1) * rows_per);
-  for (int64_t row = (int64_t)blockIdx.x * rows_per; row < row_end; ++row) {
+  // after pooled_select_wave_kernel: only the rows it left marked, out of
+  // kMarkedRowsPerGroup rows per workgroup whose markers one wave reads at
+  // once (few workgroups, and no row loop, in the usual case of no marked
+  // row); else row blockIdx.x. Bit t of `todo` stands for row row0 + t.
+  const int64_t row0 = (int64_t)blockIdx.x * (only_marked ? kMarkedRowsPerGroup : 1);
+  uint64_t todo = 1;
+  if (only_marked) {
+    __shared__ uint64_t marked_sh;
+    if (threadIdx.x < kWave) {
+      const int64_t r = row0 + threadIdx.x;
+      const uint64_t bits = __ballot(r < R && mask[r * nK] == kSelectMarker);
+      if (threadIdx.x == 0) marked_sh = bits;
+    }
+    __syncthreads();
+    todo = marked_sh;
+  }
+  for (; todo != 0; todo &= todo - 1) {
+    const int64_t row = row0 + __builtin_ctzll(todo);
     uint8_t* mrow = mask + row * nK;
-    if (only_marked && mrow[0] != kSelectMarker) continue;  // uniform: one byte for all
     const double* srow = S + row * nK;
     for (int c = threadIdx.x; c < nK; c += blockDim.x) {
       s[c] = srow[c];
@@ -2285,7 +2300,7 @@ hipError_t launch_pooled_mask(const Geom& g, int dtype, TensorArg q, TensorArg k
     only_marked = 1;
   }
   const size_t sh2 = sizeof(double) * (g.nK + P) + sizeof(int32_t) * P + g.nK;
-  const int64_t groups = only_marked ? (R + kSelectRowsPerGroup - 1) / kSelectRowsPerGroup : R;
+  const int64_t groups = only_marked ? (R + kMarkedRowsPerGroup - 1) / kMarkedRowsPerGroup : R;
   hipLaunchKernelGGL(pooled_select_kernel, dim3((unsigned)groups), dim3(kSelectThreads), sh2, st,
                      g.nK, P, mode, param, levels ? levels[1] : 0.0, levels ? levels[2] : 0.0, levels ? levels[3] : 0.0,
                      n_levels, S, mask, only_marked, R);
