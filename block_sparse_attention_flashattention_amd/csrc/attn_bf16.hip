@@ -75,9 +75,10 @@ constexpr int kVStages = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
-// Pyramid lists at half-block steps: capacity, in 32-bit group descriptors
-// (two per step), of the per-workgroup list of selected 16-row groups (with
-// its count it keeps four 40 KiB workgroups per CU).
+// Pyramid step lists: capacity, in 32-bit group descriptors, of the
+// per-workgroup list of selected 16-row groups (two per step with row blocks
+// of 64, four with row blocks of 128); with its count the LDS still holds
+// four (two) workgroups per CU.
 constexpr int kStepCap = 2046;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
 constexpr int kPfK = 3;  // K fragment reads issued ahead of their score MFMA (slots)
@@ -468,8 +469,9 @@ void attn_bf16_kernel(const Bf16Params p) {
   auto g_level = [](uint32_t d) -> int { return (int)(d >> 2) & 3; };
   auto g_eighths = [](uint32_t d) -> int { return (int)d & 3; };
   if constexpr (SL) {
-    // else every half block is stepped through (row offsets fit 20 bits
-    // below 2^24; a list longer than the capacity is not used)
+    // else every listed tile is stepped through, its groups taken from the
+    // list entry (row offsets fit 20 bits below 2^24; a list longer than the
+    // capacity is not used)
     if (N32 < (1 << 24)) {
       if (w == 0) {
         int base = 0;
