@@ -121,3 +121,22 @@ def test_random_shape_pyramid_matches_oracle(case):
     rows = np.arange(w.B * w.H * w.nQ)
     og, lg = gather_rows(host(out["o"]), host(out["lse"]), rows, w.B, w.H, w.N, w.Bq)
     compare(og, lg, o_ref, lse_ref, f"random pyramid case {case}")
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_shape_skip_carry_matches_oracle(case):
+    """Three denoising steps of the carried skip set: lists, outputs, tile
+    gaps and update decisions against the oracle at every step."""
+    from test_gpu_pooled_skip import _skip_carry
+    r = np.random.default_rng(9800 + case)
+    B, H = int(r.integers(1, 3)), int(r.integers(1, 4))
+    d = int(r.choice([64, 128]))
+    T, Hs, Ws = int(r.integers(1, 7)), int(r.integers(3, 25)), int(r.integers(3, 33))
+    Bq = int(r.choice([64, 128]))
+    tau = float(r.uniform(0.5, 3.0))
+    order = bsa.ORDER_RADIAL if case % 2 else bsa.ORDER_ASCENDING
+    w = synth.Workload(f"rand_skip{case}", B, H, d, T, Hs, Ws, Bq, 64, "bf16", "skip",
+                       9900 + case, True, tau=tau, steps=3)
+    note(f"random skip case {case}: B={B} H={H} d={d} grid {T}x{Hs}x{Ws} (N={w.N}) Bq={Bq} "
+         f"tau={tau:.3f} order={order}")
+    _skip_carry(w, 3, tau, order=order)
