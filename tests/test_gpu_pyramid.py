@@ -15,8 +15,8 @@ import torch
 import block_sparse_attention_flashattention_amd as bsa
 import oracle
 import synth
-from _gpu_util import (DEV, assert_all_written, compare, dev, gather_rows, host, note,
-                       sample_rows, shape_of)
+from _gpu_paths import run_pyramid
+from _gpu_util import DEV, compare, dev, gather_rows, host, note, sample_rows, shape_of
 
 pytestmark = pytest.mark.gpu
 
@@ -26,34 +26,6 @@ def bf16_bits(x32: np.ndarray) -> np.ndarray:
     u = x32.astype(np.float32).view(np.uint32).astype(np.uint64)
     r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
     return r.astype(np.uint16)
-
-
-def run_pyramid(w, x, taus, rows=None):
-    """GPU pipeline: levels of K/V, level mask, lists, forward."""
-    s = shape_of(w)
-    L = len(taus)
-    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
-    prow = bsa.bsa_pyramid_rows(s, L)
-    kp = torch.zeros((w.B, max(prow, 1), w.H, w.d), dtype=q.dtype, device=DEV)
-    vp = torch.zeros_like(kp)
-    bsa.bsa_build_kv_pyramid(s, L, k, v, kp, vp)
-    ws = torch.empty(bsa.bsa_pooled_workspace_bytes(s), dtype=torch.uint8, device=DEV)
-    R = w.B * w.H * w.nQ
-    mask = torch.empty(R * w.nK, dtype=torch.uint8, device=DEV)
-    bsa.bsa_build_mask_pyramid(s, q, k, w.scale, taus, mask, ws)
-    rb, _ = oracle.pyramid_regions(w.N, w.Bk, L)
-    cap = R * int(rb[-1])
-    rp = torch.empty(R + 1, dtype=torch.int32, device=DEV)
-    kv = torch.empty(cap, dtype=torch.int32, device=DEV)
-    qm = torch.empty(cap, dtype=torch.int32, device=DEV)
-    nnz = bsa.bsa_compact_pyramid_lists(s, L, mask, w.nQ * w.nK, rp, kv, qm, want_nnz=True)
-    o = torch.full_like(q, float("nan"))
-    lse = torch.full((R * w.Bq,), float("nan"), dtype=torch.float32, device=DEV)[: w.B * w.H * w.N]
-    bsa.bsa_pyramid_attn_fwd(s, q, k, v, kp, vp, L, o, lse, rp, kv, qm, w.scale)
-    torch.cuda.synchronize()
-    assert_all_written(s, o, lse, rp, 0, f"pyramid {w.name} {L} levels")
-    return dict(kp=kp, vp=vp, mask=host(mask).reshape(w.B, w.H, w.nQ, w.nK), rp=host(rp),
-                kv=host(kv)[:nnz], qm=host(qm)[:nnz], o=o, lse=lse, nnz=nnz, prow=prow)
 
 
 @pytest.mark.parametrize("L", [2, 3, 4])

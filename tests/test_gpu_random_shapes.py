@@ -15,6 +15,7 @@ import torch
 import block_sparse_attention_flashattention_amd as bsa
 import oracle
 import synth
+from _gpu_paths import run_pyramid, skip_carry
 from _gpu_util import (DEV, assert_all_written, compare, dev, gather_rows, host, note, run_fwd,
                        shape_of)
 
@@ -102,7 +103,6 @@ def _draw_pyramid(case: int):
 
 @pytest.mark.parametrize("case", range(12))
 def test_random_shape_pyramid_matches_oracle(case):
-    from test_gpu_pyramid import run_pyramid
     w, taus = _draw_pyramid(case)
     note(f"random pyramid case {case}: B={w.B} H={w.H} d={w.d} grid {w.T}x{w.Hs}x{w.Ws} "
          f"(N={w.N}) Bq={w.Bq} taus={[round(t, 3) for t in taus]}")
@@ -127,7 +127,6 @@ def test_random_shape_pyramid_matches_oracle(case):
 def test_random_shape_skip_carry_matches_oracle(case):
     """Three denoising steps of the carried skip set: lists, outputs, tile
     gaps and update decisions against the oracle at every step."""
-    from test_gpu_pooled_skip import _skip_carry
     r = np.random.default_rng(9800 + case)
     B, H = int(r.integers(1, 3)), int(r.integers(1, 4))
     d = int(r.choice([64, 128]))
@@ -139,4 +138,4 @@ def test_random_shape_skip_carry_matches_oracle(case):
                        9900 + case, True, tau=tau, steps=3)
     note(f"random skip case {case}: B={B} H={H} d={d} grid {T}x{Hs}x{Ws} (N={w.N}) Bq={Bq} "
          f"tau={tau:.3f} order={order}")
-    _skip_carry(w, 3, tau, order=order)
+    skip_carry(w, 3, tau, order=order)
