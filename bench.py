@@ -354,9 +354,9 @@ def main():
         return
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads would shard across GPUs with no exchange; see the design notes). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(heads would shard across GPUs with no exchange). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

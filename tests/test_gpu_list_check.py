@@ -1,6 +1,6 @@
 """GPU side of the debug check of block lists, through the C ABI.
 
-The device check must reach the same verdict (row and rule) as the host
+The device check must reach the same result (row and rule) as the host
 check on the same lists, and with BSA_CHECK=1 the calls that consume lists
 must refuse malformed ones before launching anything. Every list used here
 stays inside its buffers (entries out of range point past the last key
@@ -25,7 +25,7 @@ def _lists(rows):
     return rp, kv
 
 
-def _verdict(s, rp, kv, shared, asc, on_device):
+def _check_result(s, rp, kv, shared, asc, on_device):
     try:
         if on_device:
             bsa.bsa_check_block_lists(s, shared, dev(rp), dev(kv), 0, asc, kv_len=int(rp[-1]))
@@ -56,8 +56,8 @@ def test_device_check_agrees_with_host_check():
             r.shuffle(row)                                          # order only
         rp, kv = _lists(rows)
         for asc in (False, True):
-            host_v = _verdict(s, rp, kv, 0, asc, False)
-            dev_v = _verdict(s, rp, kv, 0, asc, True)
+            host_v = _check_result(s, rp, kv, 0, asc, False)
+            dev_v = _check_result(s, rp, kv, 0, asc, True)
             assert host_v == dev_v, (trial, asc, host_v, dev_v)
             n_bad += bool(host_v)
     note(f"device and host checks agree on 120 list sets ({n_bad} malformed)")
